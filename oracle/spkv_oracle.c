@@ -1,0 +1,246 @@
+/*
+ * spkv_oracle.c -- plain, slow, fp64 CPU oracle for Self-Pruned Key-Value
+ * attention (SP-KV).  TEST INFRASTRUCTURE ONLY: it is loaded by the tests,
+ * by the package's smoke check and by the benchmark's CPU-baseline leg, and
+ * by nothing on the product path.  It shares no code, header or constant
+ * with the HIP library.
+ *
+ * Source of every formula: "Self-Pruned Key-Value Attention: learning when to
+ * write by predicting future utility" (arXiv 2605.14037), section 2.1,
+ * equations (1)-(4), and the paragraph "efficient implementation at
+ * deployment" at the end of section 2.1.
+ *
+ * Precision: every input is a float32 array whose values are exact (bf16
+ * values are a subset of float32); each value is widened to double on use and
+ * all arithmetic is done in double, in fixed index order.
+ *
+ * Parity status of each function is stated in its comment; all three are
+ * pinned by tests that do not call this file's arithmetic a second time
+ * (closed forms, library routines, brute force, worked examples).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define SPKV_ORACLE_VERSION 1
+
+int spkv_oracle_version(void) { return SPKV_ORACLE_VERSION; }
+
+int spkv_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * O1 -- utility gate, SP-KV section 2.1, Eq. (1) and Eq. (2).
+ *
+ *   a_j     = max(0, sum_i W1[j,i] * h_i + b1[j])        (first MLP layer, ReLU)
+ *   logit_k = sum_j W2[k,j] * a_j + b2[k]                 (second layer: one
+ *                                                         output per key head)
+ *   u_k     = 1 / (1 + exp(-logit_k))                     Eq. (1)
+ *   z_k     = 1 if u_k >= tau else 0                      Eq. (2)
+ *
+ * The page leaves the predictor as "a 2-layer MLP" per layer and key head;
+ * the shared d_model -> d_hidden (ReLU) -> n_kv form with biases is the
+ * reading used throughout (a bank of per-head MLPs is the case of a
+ * block-diagonal W2).  A NaN utility compares false, so it gives z = 0.
+ *
+ * H  [n_rows, ld_h] (row r at H + r*ld_h, first d_model entries used)
+ * W1 [d_hidden, d_model], b1 [d_hidden], W2 [n_kv, d_hidden], b2 [n_kv]
+ * u_out / logit_out [n_rows, n_kv] doubles (either may be NULL),
+ * z_out [n_rows, n_kv] bytes (may be NULL).
+ */
+int spkv_oracle_gate(int64_t n_rows, int64_t d_model, int64_t d_hidden,
+                     int64_t n_kv, const float *H, int64_t ld_h,
+                     const float *W1, const float *b1, const float *W2,
+                     const float *b2, double tau, double *u_out,
+                     double *logit_out, uint8_t *z_out, int n_threads)
+{
+    if (n_rows < 0 || d_model <= 0 || d_hidden <= 0 || n_kv <= 0 || ld_h < d_model)
+        return -1;
+    if (d_hidden > 1024)
+        return -2; /* the activations of one row live in a stack buffer */
+    if (n_threads < 1)
+        n_threads = 1;
+    int64_t r;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+#endif
+    for (r = 0; r < n_rows; ++r) {
+        const float *h = H + r * ld_h;
+        double act[1024];
+        for (int64_t j = 0; j < d_hidden; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < d_model; ++i)
+                acc += (double)W1[j * d_model + i] * (double)h[i];
+            acc += (double)b1[j];
+            /* ReLU; a NaN is passed on (NaN < 0 is false), so a corrupted
+             * hidden state yields u = NaN and therefore z = 0 */
+            act[j] = (acc < 0.0) ? 0.0 : acc;
+        }
+        for (int64_t k = 0; k < n_kv; ++k) {
+            double logit = 0.0;
+            for (int64_t j = 0; j < d_hidden; ++j)
+                logit += (double)W2[k * d_hidden + j] * act[j];
+            logit += (double)b2[k];
+            double u = 1.0 / (1.0 + exp(-logit));
+            if (logit_out)
+                logit_out[r * n_kv + k] = logit;
+            if (u_out)
+                u_out[r * n_kv + k] = u;
+            if (z_out)
+                z_out[r * n_kv + k] = (uint8_t)(u >= tau ? 1 : 0);
+        }
+    }
+    return 0;
+}
+
+/*
+ * O2 -- the sparse persistent cache of SP-KV (section 2.1, deployment
+ * paragraph): only pairs with z = 1 are kept, in token order.  For one
+ * sequence whose rows sit at positions pos0, pos0+1, ..., this is the stable
+ * filter of the rows with z[s,g] = 1, for each key head g:
+ *
+ *   pos_out[g * n_rows + i] = pos0 + s_i   where s_0 < s_1 < ... are the rows
+ *                                          with z[s, g] = 1
+ *   len_out[g]              = number of such rows
+ *
+ * The cached key and value of entry i are the input rows s_i, unchanged.
+ */
+int spkv_oracle_compact(int64_t n_rows, int64_t n_kv, const uint8_t *z,
+                        int64_t pos0, int64_t *pos_out, int64_t *len_out)
+{
+    if (n_rows < 0 || n_kv <= 0)
+        return -1;
+    for (int64_t g = 0; g < n_kv; ++g) {
+        int64_t n = 0;
+        for (int64_t s = 0; s < n_rows; ++s) {
+            if (z[s * n_kv + g]) {
+                pos_out[g * n_rows + n] = pos0 + s;
+                ++n;
+            }
+        }
+        len_out[g] = n;
+    }
+    return 0;
+}
+
+/*
+ * O3 -- windowed-plus-gated softmax attention, SP-KV section 2.1, Eq. (3)-(4),
+ * evaluated directly on the full, uncompacted sequence.
+ *
+ * For query row i at position t = t_rows[i] and query head h, key head
+ * g = h / (n_q / n_kv) (contiguous grouped-query heads):
+ *
+ *   visible(s) = (0 <= t - s < w)  or  (z[s,g] = 1 and s <= t),  s in [0, t]
+ *   x_s        = scale * sum_e q[e] * k_s[e]          (scale = 1/sqrt(d_k))
+ *   m          = max over visible s of x_s
+ *   p_s        = exp(x_s - m),   l = sum p_s
+ *   out        = sum p_s v_s / l,  lse = m + log(l)
+ *
+ * Q   [n_rows, n_q, hd] (float), t_rows [n_rows]
+ * K,V row s, head g at  K + s*ld_kv + g*hd  (so [T, n_kv, hd] has ld_kv = n_kv*hd)
+ * z   [T, n_kv] bytes, row s at z + s*n_kv
+ * out [n_rows, n_q, hd] doubles, lse [n_rows, n_q] doubles (lse may be NULL)
+ * Rows whose t is outside [0, T) are rejected (return -1, nothing written).
+ */
+int spkv_oracle_attention(int64_t T, int64_t n_q, int64_t n_kv, int64_t hd,
+                          int64_t w, const float *Q, const int64_t *t_rows,
+                          int64_t n_rows, const float *K, const float *V,
+                          int64_t ld_kv, const uint8_t *z, double scale,
+                          double *out, double *lse, int n_threads)
+{
+    if (T < 0 || n_q <= 0 || n_kv <= 0 || hd <= 0 || w < 1 || n_q % n_kv)
+        return -1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (t_rows[i] < 0 || t_rows[i] >= T)
+            return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t group = n_q / n_kv;
+    int64_t job;
+    const int64_t n_jobs = n_rows * n_q;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+#endif
+    for (job = 0; job < n_jobs; ++job) {
+        const int64_t i = job / n_q;
+        const int64_t h = job % n_q;
+        const int64_t t = t_rows[i];
+        const int64_t g = h / group;
+        const float *q = Q + (i * n_q + h) * hd;
+        double *o = out + (i * n_q + h) * hd;
+
+        /* pass 1: the largest visible score */
+        double m = -INFINITY;
+        for (int64_t s = 0; s <= t; ++s) {
+            int in_window = (t - s) < w;
+            int kept = z[s * n_kv + g] != 0;
+            if (!(in_window || kept))
+                continue;
+            const float *k = K + s * ld_kv + g * hd;
+            double x = 0.0;
+            for (int64_t e = 0; e < hd; ++e)
+                x += (double)q[e] * (double)k[e];
+            x *= scale;
+            if (x > m)
+                m = x;
+        }
+        /* pass 2: normaliser and weighted sum of values */
+        for (int64_t e = 0; e < hd; ++e)
+            o[e] = 0.0;
+        double l = 0.0;
+        for (int64_t s = 0; s <= t; ++s) {
+            int in_window = (t - s) < w;
+            int kept = z[s * n_kv + g] != 0;
+            if (!(in_window || kept))
+                continue;
+            const float *k = K + s * ld_kv + g * hd;
+            const float *v = V + s * ld_kv + g * hd;
+            double x = 0.0;
+            for (int64_t e = 0; e < hd; ++e)
+                x += (double)q[e] * (double)k[e];
+            x *= scale;
+            double p = exp(x - m);
+            l += p;
+            for (int64_t e = 0; e < hd; ++e)
+                o[e] += p * (double)v[e];
+        }
+        for (int64_t e = 0; e < hd; ++e)
+            o[e] /= l;
+        if (lse)
+            lse[i * n_q + h] = m + log(l);
+    }
+    return 0;
+}
+
+/*
+ * Row counts of the visible set of O3, |visible(t)| for head g, for each
+ * query row -- the same predicate as O3, counted.  Used to state the
+ * expected log-normaliser when every key is zero (then lse = log |visible|).
+ */
+int spkv_oracle_visible_count(int64_t T, int64_t n_kv, int64_t w,
+                              const uint8_t *z, const int64_t *t_rows,
+                              int64_t n_rows, int64_t g, int64_t *count_out)
+{
+    if (T < 0 || n_kv <= 0 || w < 1 || g < 0 || g >= n_kv)
+        return -1;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t t = t_rows[i];
+        if (t < 0 || t >= T)
+            return -1;
+        int64_t c = 0;
+        for (int64_t s = 0; s <= t; ++s)
+            if ((t - s) < w || z[s * n_kv + g])
+                ++c;
+        count_out[i] = c;
+    }
+    return 0;
+}

@@ -1,0 +1,359 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test fixes one part of SP-KV (arXiv 2605.14037, section 2.1) by a route
+other than the oracle's own loops: hand-worked examples with closed-form
+answers (tests/golden), closed forms, special cases that reduce to library
+routines (torch's float64 scaled-dot-product attention, numpy's
+flatnonzero), brute force over every keep mask of short sequences, and
+invariants.  A dropped term, a wrong sign, a transposed operand or a wrong
+index in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from learned_kv_cache_sp_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def setup_module(_m):
+    oracle.build(force=False)
+
+
+# ----------------------------------------------------------------------------
+# helpers built from library routines only
+# ----------------------------------------------------------------------------
+
+def sdpa_f64(Q, K, V, allowed, scale):
+    """torch's float64 attention.  Q [n, hd], K/V [T, hd], allowed [n, T] bool."""
+    q = torch.from_numpy(np.asarray(Q, np.float64))[None, None]
+    k = torch.from_numpy(np.asarray(K, np.float64))[None, None]
+    v = torch.from_numpy(np.asarray(V, np.float64))[None, None]
+    m = torch.from_numpy(np.asarray(allowed, bool))[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)
+    s = (q @ k.transpose(-1, -2)) * scale
+    s = s.masked_fill(~m, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o[0, 0].numpy(), lse[0, 0].numpy()
+
+
+def causal_allowed(t_rows, T):
+    return np.arange(T)[None, :] <= np.asarray(t_rows)[:, None]
+
+
+def band_allowed(t_rows, T, w):
+    d = np.asarray(t_rows)[:, None] - np.arange(T)[None, :]
+    return (d >= 0) & (d < w)
+
+
+def rand_seq(T, n_q, n_kv, hd, seed):
+    g = np.random.default_rng(seed)
+    Q = g.standard_normal((T, n_q, hd)).astype(np.float32)
+    K = g.standard_normal((T, n_kv, hd)).astype(np.float32)
+    V = g.standard_normal((T, n_kv, hd)).astype(np.float32)
+    return Q, K, V
+
+
+# ----------------------------------------------------------------------------
+# O1: gate, Eq. (1)-(2)
+# ----------------------------------------------------------------------------
+
+def test_gate_worked_example():
+    fx = json.load(open(os.path.join(GOLDEN, "gate_worked_example.json")))
+    u, logit, z = oracle.gate(np.array(fx["H"]), np.array(fx["W1"]), np.array(fx["b1"]),
+                              np.array(fx["W2"]), np.array(fx["b2"]), fx["tau"])
+    np.testing.assert_allclose(logit, fx["expected_logit"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(u, fx["expected_u"], rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(z, fx["expected_z"])
+
+
+def test_gate_zero_first_layer_is_sigmoid_of_bias():
+    # W1 = 0, b1 = 0 => a = 0 => logit = b2 for every token; compare to scipy's expit.
+    from scipy.special import expit
+    g = np.random.default_rng(1)
+    H = g.standard_normal((7, 16)).astype(np.float32)
+    b2 = np.array([-3.0, -0.25, 0.0, 2.5], np.float32)
+    W2 = g.standard_normal((4, 8)).astype(np.float32)
+    u, logit, z = oracle.gate(H, np.zeros((8, 16)), np.zeros(8), W2, b2, 0.5)
+    np.testing.assert_array_equal(logit, np.broadcast_to(b2.astype(np.float64), (7, 4)))
+    np.testing.assert_allclose(u, np.broadcast_to(expit(b2.astype(np.float64)), (7, 4)), rtol=1e-15)
+    np.testing.assert_array_equal(z, np.broadcast_to(np.array([0, 0, 1, 1], np.uint8), (7, 4)))
+
+
+def test_gate_threshold_is_inclusive():
+    # u = sigmoid(0) = 0.5 exactly; Eq. (2) keeps u >= tau.
+    u, _, z = oracle.gate(np.ones((3, 4)), np.zeros((2, 4)), np.zeros(2), np.ones((1, 2)), np.zeros(1), 0.5)
+    assert np.all(u == 0.5)
+    assert np.all(z == 1)
+    _, _, z2 = oracle.gate(np.ones((3, 4)), np.zeros((2, 4)), np.zeros(2), np.ones((1, 2)), np.zeros(1),
+                           np.nextafter(0.5, 1.0))
+    assert np.all(z2 == 0)
+
+
+def test_gate_linear_regime_closed_form():
+    # With b1 large every pre-activation is positive, ReLU is the identity and
+    # logit = (W2 W1) h + W2 b1 + b2: a different association of the same product.
+    g = np.random.default_rng(2)
+    d, hg, nkv = 24, 10, 3
+    H = g.uniform(-1, 1, (9, d)).astype(np.float32)
+    W1 = g.uniform(-1, 1, (hg, d)).astype(np.float32)
+    b1 = np.full(hg, 100.0, np.float32)
+    W2 = g.uniform(-1, 1, (nkv, hg)).astype(np.float32)
+    b2 = g.uniform(-1, 1, nkv).astype(np.float32)
+    _, logit, _ = oracle.gate(H, W1, b1, W2, b2, 0.5)
+    M = W2.astype(np.float64) @ W1.astype(np.float64)
+    expect = H.astype(np.float64) @ M.T + (W2.astype(np.float64) @ b1.astype(np.float64) + b2)
+    np.testing.assert_allclose(logit, expect, rtol=0, atol=1e-11)
+
+
+def test_gate_relu_cuts_negative_units():
+    # With b1 very negative every unit is cut: logit = b2 regardless of h and W.
+    g = np.random.default_rng(3)
+    H = g.uniform(-1, 1, (5, 12)).astype(np.float32)
+    W1 = g.uniform(-1, 1, (6, 12)).astype(np.float32)
+    W2 = g.uniform(-1, 1, (2, 6)).astype(np.float32)
+    b2 = np.array([0.75, -0.5], np.float32)
+    _, logit, _ = oracle.gate(H, W1, np.full(6, -1000.0), W2, b2, 0.5)
+    np.testing.assert_array_equal(logit, np.broadcast_to(b2.astype(np.float64), (5, 2)))
+
+
+def test_gate_single_unit_projection():
+    # W2 = e_j^T, biases 0 => logit_k = ReLU(w1_j . h): picks row j of W1, not column j.
+    g = np.random.default_rng(4)
+    H = g.standard_normal((11, 6)).astype(np.float32)
+    W1 = g.standard_normal((4, 6)).astype(np.float32)
+    W2 = np.zeros((4, 4), np.float32)
+    np.fill_diagonal(W2, 1.0)
+    _, logit, _ = oracle.gate(H, W1, np.zeros(4), W2, np.zeros(4), 0.5)
+    np.testing.assert_allclose(logit, np.maximum(H.astype(np.float64) @ W1.T.astype(np.float64), 0.0),
+                               rtol=0, atol=1e-12)
+
+
+def test_gate_symmetry_and_monotonicity():
+    wl = inputs.WORKLOADS["tiny"]
+    w = inputs.layer_weights(wl)
+    H = inputs.normal((300, wl.d_model), 5, 0)
+    u, _, z = oracle.gate(H, w["W1"], w["b1"], w["W2"], w["b2"], 0.5)
+    # sigma(-x) = 1 - sigma(x): negating the second layer flips u around 1/2
+    un, _, _ = oracle.gate(H, w["W1"], w["b1"], -w["W2"], -w["b2"], 0.5)
+    np.testing.assert_allclose(un, 1.0 - u, rtol=0, atol=1e-15)
+    # raising b2 can only add kept tokens
+    _, _, z_hi = oracle.gate(H, w["W1"], w["b1"], w["W2"], w["b2"] + 0.3, 0.5)
+    assert np.all(z_hi >= z) and z_hi.sum() > z.sum()
+    # tau = 0 keeps everything; tau > 1 keeps nothing
+    _, _, z0 = oracle.gate(H, w["W1"], w["b1"], w["W2"], w["b2"] - 1000, 0.0)
+    assert np.all(z0 == 1)
+    _, _, z1 = oracle.gate(H, w["W1"], w["b1"], w["W2"], w["b2"] + 1000, 1.5)
+    assert np.all(z1 == 0)
+    # hidden-unit permutation leaves the output unchanged
+    p = np.random.default_rng(0).permutation(wl.d_hidden)
+    up, _, _ = oracle.gate(H, w["W1"][p], w["b1"][p], w["W2"][:, p], w["b2"], 0.5)
+    np.testing.assert_allclose(up, u, rtol=0, atol=1e-14)
+
+
+def test_gate_nan_row_is_not_kept():
+    wl = inputs.WORKLOADS["tiny"]
+    w = inputs.layer_weights(wl)
+    H = inputs.normal((4, wl.d_model), 6, 0)
+    H[2, 17] = np.nan
+    u, _, z = oracle.gate(H, w["W1"], w["b1"], w["W2"], w["b2"] + 50.0, 0.5)
+    assert np.all(z[[0, 1, 3]] == 1)
+    assert np.all(np.isnan(u[2])) and np.all(z[2] == 0)
+
+
+# ----------------------------------------------------------------------------
+# O2: compaction (the sparse persistent cache)
+# ----------------------------------------------------------------------------
+
+def test_compact_matches_flatnonzero_and_invariants():
+    g = np.random.default_rng(7)
+    for n, rates in [(0, [0.5]), (1, [1.0, 0.0]), (257, [0.02, 0.3, 0.9, 1.0]), (4099, [0.15] * 8)]:
+        z = (g.random((n, len(rates))) < np.array(rates)).astype(np.uint8)
+        pos0 = 1234
+        lists = oracle.compact(z, pos0)
+        for k, lst in enumerate(lists):
+            np.testing.assert_array_equal(lst, np.flatnonzero(z[:, k]) + pos0)
+            assert len(lst) == int(z[:, k].sum())
+            assert np.all(np.diff(lst) > 0)
+
+
+def test_compact_concatenates_across_appends():
+    # Appending two halves gives the same cache as one append of the whole.
+    g = np.random.default_rng(8)
+    z = (g.random((1000, 3)) < 0.4).astype(np.uint8)
+    whole = oracle.compact(z, 0)
+    a = oracle.compact(z[:613], 0)
+    b = oracle.compact(z[613:], 613)
+    for k in range(3):
+        np.testing.assert_array_equal(np.concatenate([a[k], b[k]]), whole[k])
+
+
+# ----------------------------------------------------------------------------
+# O3: attention, Eq. (3)-(4)
+# ----------------------------------------------------------------------------
+
+def test_attention_worked_example():
+    fx = json.load(open(os.path.join(GOLDEN, "attention_worked_example.json")))
+    Q = np.array(fx["Q"], np.float32)
+    K = np.array(fx["K"], np.float32)
+    V = np.array(fx["V"], np.float32)
+    z = np.array(fx["z"], np.uint8)
+    rows = np.array(fx["rows"])
+    out, lse = oracle.attention(Q[rows], rows, K, V, z, fx["window"], fx["scale"])
+    for i, t in enumerate(rows):
+        np.testing.assert_allclose(out[i], fx["expected_out"][str(t)], rtol=1e-13, atol=1e-12)
+        np.testing.assert_allclose(lse[i], fx["expected_lse"][str(t)], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("n_q,n_kv,hd", [(4, 2, 8), (8, 8, 16), (4, 1, 4)])
+def test_all_kept_is_dense_causal(n_q, n_kv, hd):
+    T, w = 40, 5
+    Q, K, V = rand_seq(T, n_q, n_kv, hd, 11)
+    z = np.ones((T, n_kv), np.uint8)
+    rows = np.arange(T)
+    out, lse = oracle.attention(Q, rows, K, V, z, w)
+    G = n_q // n_kv
+    for h in range(n_q):
+        o, l = sdpa_f64(Q[:, h], K[:, h // G], V[:, h // G], causal_allowed(rows, T), 1 / math.sqrt(hd))
+        np.testing.assert_allclose(out[:, h], o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[:, h], l, rtol=1e-12, atol=1e-12)
+
+
+def test_nothing_kept_is_sliding_window():
+    T, n_q, n_kv, hd, w = 50, 4, 2, 8, 7
+    Q, K, V = rand_seq(T, n_q, n_kv, hd, 12)
+    z = np.zeros((T, n_kv), np.uint8)
+    rows = np.arange(T)
+    out, lse = oracle.attention(Q, rows, K, V, z, w)
+    for h in range(n_q):
+        o, l = sdpa_f64(Q[:, h], K[:, h // 2], V[:, h // 2], band_allowed(rows, T, w), 1 / math.sqrt(hd))
+        np.testing.assert_allclose(out[:, h], o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[:, h], l, rtol=1e-12, atol=1e-12)
+
+
+def test_window_covering_sequence_is_dense_whatever_z():
+    T, n_q, n_kv, hd = 30, 2, 1, 8
+    Q, K, V = rand_seq(T, n_q, n_kv, hd, 13)
+    z = (np.random.default_rng(0).random((T, 1)) < 0.3).astype(np.uint8)
+    rows = np.arange(T)
+    out, _ = oracle.attention(Q, rows, K, V, z, T)
+    for h in range(n_q):
+        o, _ = sdpa_f64(Q[:, h], K[:, 0], V[:, 0], causal_allowed(rows, T), 1 / math.sqrt(hd))
+        np.testing.assert_allclose(out[:, h], o, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_random_masks(seed):
+    # T <= 64: mask matrix from numpy broadcasting, attention from torch.
+    T, n_q, n_kv, hd = 64, 4, 2, 16
+    g = np.random.default_rng(100 + seed)
+    w = int(g.integers(1, 20))
+    Q, K, V = rand_seq(T, n_q, n_kv, hd, 200 + seed)
+    z = (g.random((T, n_kv)) < 0.35).astype(np.uint8)
+    rows = np.arange(T)
+    out, lse = oracle.attention(Q, rows, K, V, z, w)
+    for h in range(n_q):
+        allowed = causal_allowed(rows, T) & (band_allowed(rows, T, w) | (z[:, h // 2][None, :] == 1))
+        o, l = sdpa_f64(Q[:, h], K[:, h // 2], V[:, h // 2], allowed, 1 / math.sqrt(hd))
+        np.testing.assert_allclose(out[:, h], o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[:, h], l, rtol=1e-12, atol=1e-12)
+
+
+def test_exhaustive_masks_short_sequence():
+    T, hd, w = 9, 4, 3
+    Q, K, V = rand_seq(T, 1, 1, hd, 300)
+    rows = np.arange(T)
+    for bits in range(1 << T):
+        z = np.array([(bits >> s) & 1 for s in range(T)], np.uint8)[:, None]
+        out, lse = oracle.attention(Q, rows, K, V, z, w)
+        allowed = causal_allowed(rows, T) & (band_allowed(rows, T, w) | (z[:, 0][None, :] == 1))
+        o, l = sdpa_f64(Q[:, 0], K[:, 0], V[:, 0], allowed, 0.5)
+        np.testing.assert_allclose(out[:, 0], o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[:, 0], l, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_keys_count_the_visible_set():
+    # K = 0 => every visible key has score 0: lse = log |visible(t)| and out =
+    # the mean of the visible values; |visible(t)| = min(t+1, w) + #{s <= t-w : z_s = 1}.
+    T, hd, w = 500, 8, 32
+    g = np.random.default_rng(14)
+    z = (g.random((T, 1)) < 0.2).astype(np.uint8)
+    Q = g.standard_normal((T, 1, hd)).astype(np.float32)
+    K = np.zeros((T, 1, hd), np.float32)
+    V = g.standard_normal((T, 1, hd)).astype(np.float32)
+    rows = np.arange(T)
+    out, lse = oracle.attention(Q, rows, K, V, z, w)
+    csum = np.concatenate([[0], np.cumsum(z[:, 0])])
+    for t in rows:
+        n = min(t + 1, w) + (csum[t - w + 1] if t - w + 1 > 0 else 0)
+        assert abs(lse[t, 0] - math.log(n)) < 1e-13
+        lo = max(0, t - w + 1)
+        vis = np.concatenate([np.flatnonzero(z[:lo, 0]), np.arange(lo, t + 1)])
+        np.testing.assert_allclose(out[t, 0], V[vis, 0].astype(np.float64).mean(0), rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(oracle.visible_count(z[:, 0], rows, w),
+                                  [min(t + 1, w) + (csum[t - w + 1] if t >= w else 0) for t in rows])
+
+
+def test_special_rows():
+    T, hd = 20, 8
+    Q, K, V = rand_seq(T, 2, 1, hd, 15)
+    z = np.zeros((T, 1), np.uint8)
+    # t = 0 sees only itself
+    out, lse = oracle.attention(Q[:1], [0], K, V, z, 4)
+    np.testing.assert_allclose(out[0, 0], V[0, 0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], float(Q[0, 0].astype(np.float64) @ K[0, 0]) / math.sqrt(hd), rtol=1e-14)
+    # w = 1 and nothing kept: each row sees only itself
+    out, _ = oracle.attention(Q, np.arange(T), K, V, z, 1)
+    np.testing.assert_allclose(out[:, 0], V[:, 0], rtol=0, atol=1e-15)
+
+
+def test_output_in_hull_and_swap_invariance():
+    T, hd, w = 200, 8, 16
+    g = np.random.default_rng(16)
+    Q, K, V = rand_seq(T, 1, 1, hd, 16)
+    z = (g.random((T, 1)) < 0.3).astype(np.uint8)
+    z[10, 0] = z[50, 0] = 1
+    t = T - 1
+    out, lse = oracle.attention(Q[t:t + 1], [t], K, V, z, w)
+    vis = np.concatenate([np.flatnonzero(z[: t - w + 1, 0]), np.arange(t - w + 1, t + 1)])
+    assert np.all(out[0, 0] <= V[vis, 0].max(0) + 1e-12) and np.all(out[0, 0] >= V[vis, 0].min(0) - 1e-12)
+    # swapping two visible far keys (with their values) changes nothing
+    K2, V2 = K.copy(), V.copy()
+    K2[[10, 50]] = K[[50, 10]]
+    V2[[10, 50]] = V[[50, 10]]
+    out2, lse2 = oracle.attention(Q[t:t + 1], [t], K2, V2, z, w)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+    # a key that is neither kept nor in the window has no effect
+    K3 = K.copy()
+    far_dropped = np.flatnonzero(z[: t - w + 1, 0] == 0)[0]
+    K3[far_dropped] = 1e3
+    out3, _ = oracle.attention(Q[t:t + 1], [t], K3, V, z, w)
+    np.testing.assert_array_equal(out3, out)
+
+
+def test_attention_head_matches_full_layout():
+    T, n_q, n_kv, hd, w = 90, 8, 2, 16, 12
+    Q, K, V = rand_seq(T, n_q, n_kv, hd, 17)
+    z = (np.random.default_rng(1).random((T, n_kv)) < 0.3).astype(np.uint8)
+    rows = np.array([0, 5, 47, 89])
+    out, lse = oracle.attention(Q[rows], rows, K, V, z, w)
+    for g in range(n_kv):
+        o, l = oracle.attention_head(Q[rows][:, 4 * g:4 * g + 4], rows, K[:, g], V[:, g], z[:, g], 4, w)
+        np.testing.assert_array_equal(o, out[:, 4 * g:4 * g + 4])
+        np.testing.assert_array_equal(l, lse[:, 4 * g:4 * g + 4])
+
+
+def test_bf16_rounding_helper():
+    x = np.array([1.0, 1.00390625, 1.005859375, -2.5e-3, np.inf, 3.0e38], np.float32)
+    r = inputs.bf16_round(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(r, ref)
+    y = np.random.default_rng(0).standard_normal(100000).astype(np.float32)
+    np.testing.assert_array_equal(inputs.bf16_round(y), torch.from_numpy(y).to(torch.bfloat16).float().numpy())
