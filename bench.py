@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the SP-KV decode hot path on one MI355X.
+
+Workload (default ``decode_32k``): one Llama-3-8B-shaped attention layer
+(d_model 4096, 32 query / 8 key heads, head_dim 128, gate 4096 -> 128 -> 8),
+bf16, batch 8, 32768-token context, ~20 % of tokens kept per key head,
+window 128.  One step = the whole decode path for one new token of every
+sequence:
+
+    spkv_gate           8 hidden rows -> utilities and keep bits (Eq. 1-2)
+    spkv_compact_append keep bits + K/V -> persistent cache and window ring
+    spkv_decode_attn    32 query heads x 8 sequences over window + kept keys
+
+Inputs are synthetic (seeded), resident in HBM before timing starts.  The
+prefix (32768 tokens per sequence) is gated and compacted through the same
+calls during set-up.  Several independent layer caches are used in rotation
+so that one step's working set (~218 MB) cannot stay in the 256 MB Infinity
+Cache between its visits: the figures are HBM figures, as for a model whose
+every layer owns its own cache.
+
+Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the decode
+attention kernel): algorithmic bytes = visible kept + window entries x 512 B
+per launch, divided by the launch time measured with HIP events on the
+launch stream during the timed region.  ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--workload", default="decode_32k", choices=["decode_32k", "decode_131k"])
+    p.add_argument("--layers", type=int, default=4, help="layer caches used in rotation")
+    p.add_argument("--page-size", type=int, default=64)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; the path shards by sequence or key head "
+                                   "(see the design notes) but no multi-GPU run is provided",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from learned_kv_cache_sp_amd import inputs, spkv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = inputs.WORKLOADS[args.workload]
+    B, d, nq, nkv, hd, w = wl.batch, wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.window
+    ctx = wl.context
+    P = args.page_size
+    L = max(1, args.layers)
+    steps, warm = args.steps, args.warmup
+    per_layer_steps = (steps + warm + L - 1) // L + 1
+    scale = 1.0 / math.sqrt(hd)
+    G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
+    seed = wl.seed
+
+    # ---- weights; output bias placed on a calibration sample -----------------
+    wts = inputs.layer_weights(wl)
+    gw = spkv.GateWeights(torch.from_numpy(wts["W1"]).to(dev).to(torch.bfloat16),
+                          torch.from_numpy(wts["b1"]).to(dev), torch.from_numpy(wts["W2"]).to(dev),
+                          torch.zeros(nkv, dtype=torch.float32, device=dev))
+    Hc = inputs.device_normal((65536, d), seed, inputs.STREAM_CAL, torch.bfloat16)
+    u_cal, _ = spkv.spkv_gate(gw, Hc, wl.tau)
+    u64 = u_cal.double().clamp(1e-300, 1 - 1e-16)
+    logit = (torch.log(u64) - torch.log1p(-u64)).cpu().numpy()
+    gw.b2.copy_(torch.from_numpy(inputs.place_output_bias(logit, wl.keep, wl.tau)).to(dev))
+    del Hc, u_cal, u64
+
+    # ---- prefix: gate + compaction of ctx tokens per sequence ----------------
+    n_pre = B * ctx
+    exp_pages = [int(math.ceil((ctx + per_layer_steps) * r / P) * 1.25) + 8 for r in wl.keep]
+    max_pages = int(math.ceil((ctx + per_layer_steps) / P)) + 2
+    n_pages = B * sum(min(max_pages, e) for e in exp_pages)
+    caches = [spkv.Cache(B, nkv, hd, w, P, n_pages, max_pages, torch.bfloat16) for _ in range(L)]
+    zpre = torch.empty((n_pre, nkv), dtype=torch.uint8, device=dev)
+    ro = torch.arange(0, B + 1, dtype=torch.int32, device=dev) * ctx
+    pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
+    CH = 65536
+    for r0 in range(0, n_pre, CH):
+        Hp = inputs.device_normal((min(CH, n_pre - r0), d), seed, 1000 + r0 // CH, torch.bfloat16)
+        spkv.spkv_gate(gw, Hp, wl.tau, keep=zpre[r0:r0 + Hp.shape[0]])
+    del Hp
+    Kp = inputs.device_normal((n_pre, nkv, hd), seed, inputs.STREAM_K, torch.bfloat16)
+    Vp = inputs.device_normal((n_pre, nkv, hd), seed, inputs.STREAM_V, torch.bfloat16)
+    for c in caches:
+        spkv.spkv_compact_append(c, zpre, Kp, Vp, ro, pos0, ctx, G_ | W_)
+    torch.cuda.synchronize()
+    for c in caches:
+        spkv.spkv_cache_check(c)
+    del Kp, Vp
+    kept_frac = zpre.float().mean(0).cpu().numpy()
+
+    # ---- per-step inputs --------------------------------------------------------
+    S = steps + warm
+    Hs = inputs.device_normal((S, B, d), seed, 2001, torch.bfloat16)
+    Qs = inputs.device_normal((S, B, nq, hd), seed, 2002, torch.bfloat16)
+    Ks = inputs.device_normal((S, B, nkv, hd), seed, 2003, torch.bfloat16)
+    Vs = inputs.device_normal((S, B, nkv, hd), seed, 2004, torch.bfloat16)
+    tpos = torch.tensor([[ctx + s // L] * B for s in range(S)], dtype=torch.int32, device=dev)
+    ro1 = torch.arange(0, B + 1, dtype=torch.int32, device=dev)
+    zst = torch.empty((S, B, nkv), dtype=torch.uint8, device=dev)
+    ust = torch.empty((S, B, nkv), dtype=torch.float32, device=dev)
+    out = torch.empty((B, nq, hd), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
+    gate_ws = spkv.workspace(spkv.spkv_gate_ws_bytes(gw, B))
+    dec_ws = [spkv.workspace(spkv.spkv_decode_ws_bytes(c, nq)) for c in caches]
+
+    # pre-marshalled raw calls (keeps host overhead far below the GPU time)
+    lib = spkv.load_library()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    gdesc = gw.desc()
+    cdescs = [c.desc() for c in caches]
+    gws_p, gws_n = (gate_ws.data_ptr(), gate_ws.numel() * 4) if gate_ws is not None else (None, 0)
+
+    def nb(t):
+        return 0 if t is None else t.numel() * t.element_size()
+
+    def step(s):
+        l = s % L
+        rc = lib.spkv_gate(ctypes.byref(gdesc), Hs[s].data_ptr(), B, d, wl.tau, ust[s].data_ptr(),
+                           zst[s].data_ptr(), gws_p, gws_n, sp)
+        rc |= lib.spkv_compact_append(ctypes.byref(cdescs[l]), zst[s].data_ptr(), Ks[s].data_ptr(),
+                                      Vs[s].data_ptr(), nkv * hd, ro1.data_ptr(), tpos[s].data_ptr(), B, 1,
+                                      G_ | W_, None, None, 0, sp)
+        ev0[s].record(stream)
+        rc |= lib.spkv_decode_attn(ctypes.byref(cdescs[l]), nq, Qs[s].data_ptr(), nq * hd, tpos[s].data_ptr(),
+                                   scale, out.data_ptr(), lse.data_ptr(), dec_ws[l].data_ptr(),
+                                   nb(dec_ws[l]), sp)
+        ev1[s].record(stream)
+        if rc:
+            raise RuntimeError(lib.spkv_last_error().decode())
+
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    for s in range(warm):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for s in range(warm, S):
+        step(s)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e_start.elapsed_time(e_end)
+    for c in caches:
+        spkv.spkv_cache_check(c)
+
+    # ---- bytes each decode launch had to read --------------------------------------
+    # visible kept entries of (b, g) at position t: kept positions <= t - w
+    zpre_c = zpre.view(B, ctx, nkv).to(torch.int64).cumsum(1)  # [B, ctx, nkv]
+    dec_ms = np.array([ev0[s].elapsed_time(ev1[s]) for s in range(warm, S)])
+    bytes_per = []
+    zst_i = zst.to(torch.int64)
+    for s in range(warm, S):
+        l = s % L
+        t = ctx + s // L
+        lim = t - w
+        vis = zpre_c[:, min(lim, ctx - 1), :].clone() if lim >= 0 else torch.zeros((B, nkv), dtype=torch.int64,
+                                                                                   device=dev)
+        # kept step tokens of this layer with position <= t - w
+        own = [x for x in range(l, s + 1, L) if ctx + x // L <= lim]
+        if own:
+            vis += zst_i[own].sum(0)
+        win = min(t + 1, w)
+        bytes_per.append(float((vis.sum().item() + B * nkv * win) * 2 * hd * 2))
+    bytes_per = np.array(bytes_per)
+    achieved = float(bytes_per.mean() / (dec_ms.mean() * 1e-3) / 1e9)
+
+    ms_per_step = gpu_ms / steps
+    tok_s = B * steps / (gpu_ms * 1e-3)
+
+    res = {
+        "metric": "gated-KV decode tokens/s + achieved HBM GB/s (% of peak), 8B shape 32K ctx",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "context": ctx, "d_model": d, "n_q_heads": nq,
+                   "n_kv_heads": nkv, "head_dim": hd, "window": w, "gate": f"{d}->{wl.d_hidden}->{nkv}",
+                   "keep_target": list(wl.keep), "keep_measured": [round(float(x), 4) for x in kept_frac],
+                   "page_size": P, "layer_caches_rotated": L,
+                   "step": "spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"},
+        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel<128>", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": float(bytes_per.mean()),
+                     "launch_us_mean": round(float(dec_ms.mean() * 1e3), 2),
+                     "launch_us_p10_p90": [round(float(np.percentile(dec_ms, 10) * 1e3), 2),
+                                           round(float(np.percentile(dec_ms, 90) * 1e3), 2)]},
+        "host_wall_s": round(wall, 4),
+    }
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = a.numel() * 2
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(res))
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """fp64 oracle on a bounded sample of the same decode step, on the host cores.
+
+    Sample: decode steps of 2 of the sequences at the workload's context: the
+    oracle gate for each new token and the oracle attention of all query
+    heads, over a seeded keep mask with the workload's keep rates.  Steps are
+    taken until about `budget_s` seconds have passed (at least 2)."""
+    import oracle
+    from learned_kv_cache_sp_amd import inputs
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n_seq, max_steps = 2, 256
+    T = wl.context + max_steps
+    w = inputs.layer_weights(wl)
+    work = []
+    for b in range(n_seq):
+        tok = {
+            "Q": inputs.normal((max_steps, wl.n_q, wl.head_dim), wl.seed, 3001, b, dtype=wl.dtype),
+            "K": inputs.normal((T, wl.n_kv, wl.head_dim), wl.seed, 3002, b, dtype=wl.dtype),
+            "V": inputs.normal((T, wl.n_kv, wl.head_dim), wl.seed, 3003, b, dtype=wl.dtype),
+            "H": inputs.normal((max_steps, wl.d_model), wl.seed, 3004, b, dtype=wl.dtype),
+        }
+        z = inputs.bernoulli_mask(T, wl.keep, wl.seed, 3005, b)
+        work.append((tok, z))
+    n_tok = 0
+    t0 = time.perf_counter()
+    for i in range(max_steps):
+        for tok, z in work:
+            t = wl.context + i
+            oracle.gate(tok["H"][i:i + 1], w["W1"], w["b1"], w["W2"], w["b2"], wl.tau, threads=threads)
+            oracle.attention(tok["Q"][i:i + 1], [t], tok["K"], tok["V"], z, wl.window, threads=threads)
+            n_tok += 1
+        if time.perf_counter() - t0 > budget_s and i >= 1:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tok} sequence-steps ({n_seq} sequences) of {wl.name} decode at context "
+                      f"{wl.context}: oracle gate of the new token + oracle attention of all {wl.n_q} "
+                      f"query heads over a seeded mask with the workload's keep rates; {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * spkv.h -- C ABI of the SP-KV hot path on MI355X (gfx950).
+ *
+ * SP-KV ("Self-Pruned Key-Value Attention: learning when to write by
+ * predicting future utility", arXiv 2605.14037) gives every (token, key head)
+ * a learned utility u = sigmoid(f(h)) (section 2.1, Eq. 1), keeps the pair in
+ * a persistent cache only when u >= tau (Eq. 2), and attends over the union
+ * of a causal local window of w tokens and the kept pairs (Eq. 3-4).  At
+ * deployment the cache holds only the kept pairs and may be built
+ * incrementally or chunk by chunk (section 2.1, deployment paragraph); the
+ * threshold can be changed after training (section 3.3, threshold paragraph).
+ *
+ * Four calls implement that path:
+ *   spkv_gate            hidden states -> utilities u and keep bits z   (Eq. 1-2)
+ *   spkv_compact_append  keep bits + K/V -> order-preserving append to the
+ *                        paged per-head cache, and the window ring buffer
+ *   spkv_decode_attn     one query per sequence over window + kept pairs (Eq. 3-4)
+ *   spkv_prefill_attn    a chunk of queries of one sequence over window + kept
+ *                        pairs (Eq. 3-4), for chunked prefill
+ *
+ * Conventions
+ *   - Every call returns an int status (SPKV_OK or a negative SPKV_E_*).
+ *     Argument checks happen before any launch; on failure nothing is
+ *     launched and spkv_last_error() (per thread) holds a message.
+ *   - Every device pointer is caller-owned and must stay valid until the work
+ *     queued on `stream` completes.  The library allocates no memory and keeps
+ *     no state between calls except the per-thread error text.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     queued; no call synchronises, except spkv_cache_check.
+ *   - Device pointers must be 16-byte aligned; row strides (`ld_*`) are in
+ *     elements and must be multiples of 8 (bf16) or 4 (f32).
+ *   - dtype applies to hidden, W1, Q, K, V and the cache; b1, W2, b2 are f32;
+ *     outputs are f32.
+ *   - Errors found on the device (capacity, bad row offsets) are recorded as
+ *     sticky bits in cache->status and reported by spkv_cache_check.
+ */
+#ifndef SPKV_H
+#define SPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPKV_VERSION 1
+
+enum {
+    SPKV_OK = 0,
+    SPKV_E_INVALID = -1,     /* null pointer, bad size or stride, misalignment */
+    SPKV_E_UNSUPPORTED = -2, /* head_dim, dtype, group size or d_hidden not supported */
+    SPKV_E_HIP = -3,         /* a HIP runtime call or launch failed */
+    SPKV_E_CAPACITY = -4,    /* device flag: page pool or page table exhausted */
+    SPKV_E_WORKSPACE = -5,   /* workspace smaller than the *_ws_bytes figure */
+    SPKV_E_ROWS = -6         /* device flag: row_offsets inconsistent with n_rows / max_rows */
+};
+
+/* device status bits written by the kernels into cache->status[0] */
+enum {
+    SPKV_STATUS_POOL_FULL = 1,  /* pool_next ran past n_pages; rows were dropped */
+    SPKV_STATUS_TABLE_FULL = 2, /* a head needed more than max_pages_per_head pages */
+    SPKV_STATUS_BAD_ROWS = 4    /* row_offsets not monotone, or a sequence longer than max_rows */
+};
+
+typedef enum { SPKV_F32 = 0, SPKV_BF16 = 1 } spkv_dtype;
+
+enum { SPKV_APPEND_GLOBAL = 1, SPKV_APPEND_WINDOW = 2 };
+
+/*
+ * The utility predictor f of Eq. (1): d_model -> d_hidden (ReLU) -> n_kv,
+ * one output per key head.
+ *   w1 [d_hidden, d_model] dtype (row j = weights of hidden unit j)
+ *   b1 [d_hidden] f32, w2 [n_kv, d_hidden] f32, b2 [n_kv] f32
+ * Supported: d_hidden in {16, 32, 48, ..., 256}, d_model a multiple of 32,
+ * n_kv <= 16.
+ */
+typedef struct spkv_gate_desc {
+    int32_t d_model;
+    int32_t d_hidden;
+    int32_t n_kv;
+    int32_t dtype; /* spkv_dtype */
+    const void *w1;
+    const float *b1;
+    const float *w2;
+    const float *b2;
+} spkv_gate_desc;
+
+/*
+ * One attention layer's SP-KV cache for `batch` sequences.  POD; every
+ * pointer is a caller-owned device buffer.
+ *
+ * Persistent (global) cache, paged per (sequence b, key head g):
+ *   k_pages    [n_pages, page_size, head_dim]   key rows
+ *   v_pages    [n_pages, head_dim, page_size]   value rows, stored transposed
+ *   pos_pages  [n_pages, page_size] int32       token position of each entry
+ *   page_table [batch, n_kv, max_pages_per_head] int32: page id of the i-th
+ *              page of (b, g); entry j of (b, g) is slot j % page_size of
+ *              page page_table[b][g][j / page_size]
+ *   lengths    [batch, n_kv] int32: kept entries appended so far, in token
+ *              order (kept entries still inside the window are counted; the
+ *              attention calls skip them by position)
+ *   pool_next  [1] int32: next free page (device bump allocator)
+ *   status     [1] int32: sticky SPKV_STATUS_* bits
+ * Window ring of the last `window` tokens of every (b, g):
+ *   ring_k     [batch, n_kv, window, head_dim]  slot = position % window
+ *   ring_v     [batch, n_kv, head_dim, window]  transposed
+ * A fresh cache has lengths = 0, pool_next = 0, status = 0 (spkv_cache_reset).
+ * Supported: head_dim in {64, 128}; page_size a power of two in [32, 1024];
+ * window a multiple of 32 in [32, 1024].
+ */
+typedef struct spkv_cache {
+    int32_t batch;
+    int32_t n_kv;
+    int32_t head_dim;
+    int32_t window;
+    int32_t page_size;
+    int32_t n_pages;
+    int32_t max_pages_per_head;
+    int32_t dtype; /* spkv_dtype */
+    void *k_pages;
+    void *v_pages;
+    int32_t *pos_pages;
+    int32_t *page_table;
+    int32_t *lengths;
+    int32_t *pool_next;
+    int32_t *status;
+    void *ring_k;
+    void *ring_v;
+} spkv_cache;
+
+/*
+ * spkv_gate -- Eq. (1)-(2) for n_rows independent rows (rows may mix
+ * sequences and positions).
+ *   a = ReLU(W1 h + b1) (kept in f32), logit = W2 a + b2, u = sigmoid(logit),
+ *   keep = (u >= tau).  A NaN utility gives keep = 0.
+ *   hidden  [n_rows, ld_hidden] dtype (first d_model entries of each row)
+ *   utility [n_rows, n_kv] f32, may be NULL;  keep [n_rows, n_kv] uint8
+ *   ws      workspace of at least spkv_gate_ws_bytes(g, n_rows) bytes
+ *           (may be NULL when that figure is 0)
+ * tau is a runtime argument: the threshold may be changed at inference.
+ */
+int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows,
+              int64_t ld_hidden, float tau, float *utility, uint8_t *keep,
+              void *ws, size_t ws_bytes, void *stream);
+size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows);
+
+/*
+ * spkv_compact_append -- append one batch of rows to the cache.
+ *   Rows of sequence b are rows row_offsets[b] .. row_offsets[b+1]-1 of k, v
+ *   and keep, at token positions pos0[b], pos0[b]+1, ... (consecutive).
+ *   k, v     row r, key head g at  k + r*ld_kv + g*head_dim  (dtype)
+ *   keep     [n_rows, n_kv] uint8; read only with SPKV_APPEND_GLOBAL
+ *   row_offsets [batch+1], pos0 [batch]: int32 device arrays
+ *   max_rows_per_seq: host-side bound on row_offsets[b+1]-row_offsets[b]
+ *   flags: SPKV_APPEND_GLOBAL -- for each (b, g), the rows with keep = 1 are
+ *            appended in row order (stable compaction): key row, value row and
+ *            position copied exactly, lengths[b][g] += count, pages taken from
+ *            the pool as needed;
+ *          SPKV_APPEND_WINDOW -- every row is written to ring slot
+ *            position % window (only the last `window` rows of a sequence
+ *            matter and only those are written).
+ *   append_offsets [batch, n_kv] int32, may be NULL: receives the length of
+ *            each (b, g) before this append.
+ *   ws  at least spkv_compact_ws_bytes(...) bytes.
+ * Capacity overflow drops the rows that do not fit and sets a status bit.
+ */
+int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const void *k,
+                        const void *v, int64_t ld_kv, const int32_t *row_offsets,
+                        const int32_t *pos0, int32_t n_rows,
+                        int32_t max_rows_per_seq, int32_t flags,
+                        int32_t *append_offsets, void *ws, size_t ws_bytes,
+                        void *stream);
+size_t spkv_compact_ws_bytes(const spkv_cache *c, int32_t n_rows,
+                             int32_t max_rows_per_seq);
+
+/*
+ * spkv_decode_attn -- one query row per sequence, Eq. (3)-(4).
+ *   Query head h of sequence b at position t[b] reads key head g = h / G
+ *   (G = n_q_heads / n_kv; contiguous groups) and attends over
+ *     window: positions max(0, t-w+1) .. t, read from the ring, and
+ *     global: cached entries of (b, g) with position <= t - w.
+ *   Precondition: position t[b] (and the w-1 before it) were WINDOW-appended.
+ *   q   [batch, n_q_heads, head_dim] dtype (row b at q + b*ld_q)
+ *   t   [batch] int32 device array
+ *   out [batch, n_q_heads, head_dim] f32; lse [batch, n_q_heads] f32 or NULL
+ *       (natural-log normaliser of each softmax row)
+ *   scale: score multiplier (1/sqrt(head_dim) for Eq. 3)
+ *   ws  at least spkv_decode_ws_bytes(c, n_q_heads) bytes; it must be
+ *       zero-filled before its first use, and every call leaves it ready for
+ *       the next (calls sharing one ws must not overlap).
+ * Supported: G in {1, 2, 4, 8, 16}.
+ */
+int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q,
+                     int64_t ld_q, const int32_t *t, float scale, float *out,
+                     float *lse, void *ws, size_t ws_bytes, void *stream);
+size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads);
+
+/*
+ * spkv_prefill_attn -- n_rows consecutive query rows of sequence b, Eq. (3)-(4).
+ *   Row i is at position t = pos0 + i and attends over
+ *     window: positions max(0, t-w+1) .. t, taken from this chunk's k, v for
+ *             positions >= pos0 and from the ring for positions < pos0;
+ *     global: cached entries of (b, g) with position <= t - w.
+ *   Required order for a chunk: spkv_gate -> spkv_compact_append(GLOBAL) ->
+ *   spkv_prefill_attn -> spkv_compact_append(WINDOW) (so that the ring still
+ *   holds the previous chunk's tail, and kept rows of this chunk are visible
+ *   to later rows of the same chunk).
+ *   q   row i, head h at q + i*ld_q + h*head_dim; k, v row i, key head g at
+ *       k + i*ld_kv + g*head_dim (dtype)
+ *   out [n_rows, n_q_heads, head_dim] f32; lse [n_rows, n_q_heads] f32 or NULL
+ *   ws  at least spkv_prefill_ws_bytes(c, n_q_heads, n_rows) bytes.
+ */
+int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b,
+                      const void *q, int64_t ld_q, const void *k, const void *v,
+                      int64_t ld_kv, int32_t pos0, int32_t n_rows, float scale,
+                      float *out, float *lse, void *ws, size_t ws_bytes,
+                      void *stream);
+size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads,
+                             int32_t n_rows);
+
+/* Sizes in bytes of each cache buffer (k_pages, v_pages, pos_pages,
+ * page_table, lengths, ring_k, ring_v) for the dimensions in *c; returns the
+ * sum.  `sizes` may be NULL. */
+size_t spkv_cache_bytes(const spkv_cache *c, size_t sizes[7]);
+
+/* Queue a reset of lengths, pool_next and status to 0 (page contents are left
+ * as they are; they are unreachable once lengths are 0). */
+int spkv_cache_reset(const spkv_cache *c, void *stream);
+
+/* Synchronise `stream`, read the sticky status and map it to SPKV_OK,
+ * SPKV_E_CAPACITY or SPKV_E_ROWS; *status_bits (may be NULL) receives the bits. */
+int spkv_cache_check(const spkv_cache *c, void *stream, int32_t *status_bits);
+
+const char *spkv_status_str(int status);
+const char *spkv_last_error(void);
+int spkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPKV_H */

@@ -1,0 +1,332 @@
+// C ABI of libspkv: argument checks, workspace sizing and launches.
+// Every check happens before anything is queued; kernels run on the caller's
+// stream and the library allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "spkv.h"
+#include "spkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(SPKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check_cache(const spkv_cache *c) {
+    if (!c) return fail(SPKV_E_INVALID, "cache is NULL");
+    if (c->dtype != SPKV_F32 && c->dtype != SPKV_BF16)
+        return fail(SPKV_E_UNSUPPORTED, "cache dtype %d", c->dtype);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(SPKV_E_UNSUPPORTED, "head_dim %d (64 or 128)", c->head_dim);
+    if (c->batch < 1 || c->n_kv < 1 || c->n_kv > 16)
+        return fail(SPKV_E_INVALID, "batch %d / n_kv %d (n_kv in 1..16)", c->batch, c->n_kv);
+    if ((int64_t)c->batch * c->n_kv > 2048)
+        return fail(SPKV_E_UNSUPPORTED, "batch * n_kv = %lld exceeds 2048",
+                    (long long)c->batch * c->n_kv);
+    if (c->window < 32 || c->window > 1024 || c->window % 32)
+        return fail(SPKV_E_UNSUPPORTED, "window %d (multiple of 32 in [32, 1024])", c->window);
+    if (!pow2(c->page_size) || c->page_size < 32 || c->page_size > 1024)
+        return fail(SPKV_E_UNSUPPORTED, "page_size %d (power of two in [32, 1024])", c->page_size);
+    if (c->n_pages < 0 || c->max_pages_per_head < 0)
+        return fail(SPKV_E_INVALID, "negative n_pages / max_pages_per_head");
+    if ((int64_t)c->max_pages_per_head * c->page_size > INT32_MAX)
+        return fail(SPKV_E_INVALID, "max_pages_per_head * page_size overflows int32");
+    const void *ptrs[] = {c->k_pages, c->v_pages, c->pos_pages, c->page_table, c->lengths,
+                          c->pool_next, c->status, c->ring_k, c->ring_v};
+    const char *names[] = {"k_pages", "v_pages", "pos_pages", "page_table", "lengths",
+                           "pool_next", "status", "ring_k", "ring_v"};
+    for (int i = 0; i < 9; ++i) {
+        if (!ptrs[i]) return fail(SPKV_E_INVALID, "cache->%s is NULL", names[i]);
+        if (!aligned16(ptrs[i]) && i != 5 && i != 6)
+            return fail(SPKV_E_INVALID, "cache->%s is not 16-byte aligned", names[i]);
+    }
+    return SPKV_OK;
+}
+
+int check_ld(int64_t ld, int64_t min_ld, int dtype, const char *what) {
+    const int q = dtype == SPKV_BF16 ? 8 : 4;
+    if (ld < min_ld) return fail(SPKV_E_INVALID, "%s = %lld < %lld", what, (long long)ld, (long long)min_ld);
+    if (ld % q) return fail(SPKV_E_INVALID, "%s = %lld is not a multiple of %d", what, (long long)ld, q);
+    return SPKV_OK;
+}
+
+// persistent grid for the decode kernel: CUs x resident workgroups per CU
+int g_decode_grid = 0;
+
+}  // namespace
+
+extern "C" {
+
+int spkv_version(void) { return SPKV_VERSION; }
+
+const char *spkv_last_error(void) { return g_err; }
+
+const char *spkv_status_str(int status) {
+    switch (status) {
+    case SPKV_OK: return "ok";
+    case SPKV_E_INVALID: return "invalid argument";
+    case SPKV_E_UNSUPPORTED: return "unsupported configuration";
+    case SPKV_E_HIP: return "HIP runtime error";
+    case SPKV_E_CAPACITY: return "cache capacity exhausted (rows dropped)";
+    case SPKV_E_WORKSPACE: return "workspace too small";
+    case SPKV_E_ROWS: return "row offsets inconsistent with n_rows / max_rows_per_seq";
+    default: return "unknown status";
+    }
+}
+
+// ----------------------------------------------------------------------------
+size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows) {
+    if (!g) return 0;
+    return spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->dtype, n_rows);
+}
+
+int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows, int64_t ld_hidden,
+              float tau, float *utility, uint8_t *keep, void *ws, size_t ws_bytes, void *stream) {
+    if (!g) return fail(SPKV_E_INVALID, "gate descriptor is NULL");
+    if (g->dtype != SPKV_F32 && g->dtype != SPKV_BF16)
+        return fail(SPKV_E_UNSUPPORTED, "gate dtype %d", g->dtype);
+    if (g->d_model < 32 || g->d_model % 32)
+        return fail(SPKV_E_UNSUPPORTED, "d_model %d (a positive multiple of 32)", g->d_model);
+    if (g->d_hidden < 16 || g->d_hidden > 256 || g->d_hidden % 16)
+        return fail(SPKV_E_UNSUPPORTED, "d_hidden %d (multiple of 16 in [16, 256])", g->d_hidden);
+    if (g->n_kv < 1 || g->n_kv > 16) return fail(SPKV_E_UNSUPPORTED, "n_kv %d (1..16)", g->n_kv);
+    if (!g->w1 || !g->b1 || !g->w2 || !g->b2) return fail(SPKV_E_INVALID, "gate weights NULL");
+    if (!aligned16(g->w1)) return fail(SPKV_E_INVALID, "w1 not 16-byte aligned");
+    if (n_rows < 0 || n_rows > (int64_t)INT32_MAX) return fail(SPKV_E_INVALID, "n_rows %lld", (long long)n_rows);
+    if (n_rows == 0) return SPKV_OK;
+    if (!hidden || !keep) return fail(SPKV_E_INVALID, "hidden / keep is NULL");
+    if (!aligned16(hidden)) return fail(SPKV_E_INVALID, "hidden not 16-byte aligned");
+    if (int r = check_ld(ld_hidden, g->d_model, g->dtype, "ld_hidden")) return r;
+    if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
+    const size_t need = spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->dtype, n_rows);
+    if (need && (!ws || ws_bytes < need))
+        return fail(SPKV_E_WORKSPACE, "gate workspace %zu < %zu bytes", ws_bytes, need);
+    spkv::GateArgs a;
+    a.d_model = g->d_model;
+    a.d_hidden = g->d_hidden;
+    a.n_kv = g->n_kv;
+    a.dtype = g->dtype;
+    a.w1 = g->w1;
+    a.b1 = g->b1;
+    a.w2 = g->w2;
+    a.b2 = g->b2;
+    a.hidden = hidden;
+    a.n_rows = n_rows;
+    a.ld_hidden = ld_hidden;
+    a.tau = tau;
+    a.utility = utility;
+    a.keep = keep;
+    a.ws = (float *)ws;
+    a.n_split = spkv::gate_split_for(g->d_model, g->dtype, n_rows);
+    hipError_t e = spkv::launch_gate(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gate launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+size_t spkv_compact_ws_bytes(const spkv_cache *c, int32_t n_rows, int32_t max_rows_per_seq) {
+    (void)n_rows;
+    if (!c) return 0;
+    return spkv::compact_ws_bytes(c->batch, c->n_kv, max_rows_per_seq);
+}
+
+int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const void *k, const void *v,
+                        int64_t ld_kv, const int32_t *row_offsets, const int32_t *pos0,
+                        int32_t n_rows, int32_t max_rows_per_seq, int32_t flags,
+                        int32_t *append_offsets, void *ws, size_t ws_bytes, void *stream) {
+    if (int r = check_cache(c)) return r;
+    if (flags & ~(SPKV_APPEND_GLOBAL | SPKV_APPEND_WINDOW))
+        return fail(SPKV_E_INVALID, "unknown flags 0x%x", flags);
+    if (n_rows < 0 || max_rows_per_seq < 0) return fail(SPKV_E_INVALID, "negative n_rows / max_rows");
+    if (n_rows == 0 || flags == 0) return SPKV_OK;
+    if (max_rows_per_seq == 0) return fail(SPKV_E_INVALID, "max_rows_per_seq is 0 with n_rows > 0");
+    if (!k || !v || !row_offsets || !pos0) return fail(SPKV_E_INVALID, "k / v / row_offsets / pos0 NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(SPKV_E_INVALID, "k / v not 16-byte aligned");
+    if ((flags & SPKV_APPEND_GLOBAL) && !keep) return fail(SPKV_E_INVALID, "keep is NULL with GLOBAL");
+    if (int r = check_ld(ld_kv, (int64_t)c->n_kv * c->head_dim, c->dtype, "ld_kv")) return r;
+    const size_t need = spkv::compact_ws_bytes(c->batch, c->n_kv, max_rows_per_seq);
+    if (need && (!ws || ws_bytes < need))
+        return fail(SPKV_E_WORKSPACE, "compaction workspace %zu < %zu bytes", ws_bytes, need);
+    spkv::CompactArgs a;
+    a.c = spkv::make_view(c);
+    a.keep = keep;
+    a.k = (const char *)k;
+    a.v = (const char *)v;
+    a.ld_kv = ld_kv;
+    a.row_offsets = row_offsets;
+    a.pos0 = pos0;
+    a.n_rows = n_rows;
+    a.max_rows = max_rows_per_seq;
+    a.flags = flags;
+    a.append_offsets = append_offsets;
+    a.ws = (int32_t *)ws;
+    a.max_tiles = 0;
+    hipError_t e = spkv::launch_compact(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "compaction launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+static int decode_grid() {
+    if (g_decode_grid > 0) return g_decode_grid;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 512;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    int per_cu = spkv::decode_blocks_per_cu();
+    if (per_cu < 1) per_cu = 1;
+    g_decode_grid = cus * per_cu;
+    return g_decode_grid;
+}
+
+size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads) {
+    if (!c || c->n_kv <= 0 || n_q_heads <= 0) return 0;
+    return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr);
+}
+
+int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int64_t ld_q,
+                     const int32_t *t, float scale, float *out, float *lse, void *ws,
+                     size_t ws_bytes, void *stream) {
+    if (int r = check_cache(c)) return r;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv) return fail(SPKV_E_INVALID, "n_q_heads %d vs n_kv %d", n_q_heads, c->n_kv);
+    const int G = n_q_heads / c->n_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(SPKV_E_UNSUPPORTED, "group size %d (1, 2, 4, 8 or 16)", G);
+    if (!q || !t || !out) return fail(SPKV_E_INVALID, "q / t / out NULL");
+    if (!aligned16(q)) return fail(SPKV_E_INVALID, "q not 16-byte aligned");
+    if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
+    if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
+    int max_items = 0;
+    const int grid = decode_grid();
+    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items);
+    if (need && (!ws || ws_bytes < need))
+        return fail(SPKV_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
+    if (need && !aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
+    spkv::DecodeArgs a;
+    a.c = spkv::make_view(c);
+    a.n_q = n_q_heads;
+    a.group = G;
+    a.q = (const char *)q;
+    a.ld_q = ld_q;
+    a.t = t;
+    a.scale = scale;
+    a.out = out;
+    a.lse = lse;
+    a.ws = (char *)ws;
+    a.grid = grid;
+    a.max_items = max_items;
+    hipError_t e = spkv::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads, int32_t n_rows) {
+    if (!c) return 0;
+    return spkv::prefill_ws_bytes(c, n_q_heads, n_rows);
+}
+
+int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b, const void *q, int64_t ld_q,
+                      const void *k, const void *v, int64_t ld_kv, int32_t pos0, int32_t n_rows,
+                      float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    if (int r = check_cache(c)) return r;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv) return fail(SPKV_E_INVALID, "n_q_heads %d vs n_kv %d", n_q_heads, c->n_kv);
+    const int G = n_q_heads / c->n_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(SPKV_E_UNSUPPORTED, "group size %d (1, 2, 4, 8 or 16)", G);
+    if (b < 0 || b >= c->batch) return fail(SPKV_E_INVALID, "sequence %d of %d", b, c->batch);
+    if (pos0 < 0 || n_rows < 0) return fail(SPKV_E_INVALID, "pos0 %d / n_rows %d", pos0, n_rows);
+    if (n_rows == 0) return SPKV_OK;
+    if ((int64_t)pos0 + n_rows > INT32_MAX) return fail(SPKV_E_INVALID, "positions overflow int32");
+    if (!q || !k || !v || !out) return fail(SPKV_E_INVALID, "q / k / v / out NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(SPKV_E_INVALID, "q / k / v not 16-byte aligned");
+    if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
+    if (int r = check_ld(ld_kv, (int64_t)c->n_kv * c->head_dim, c->dtype, "ld_kv")) return r;
+    if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
+    const size_t need = spkv::prefill_ws_bytes(c, n_q_heads, n_rows);
+    if (need && (!ws || ws_bytes < need))
+        return fail(SPKV_E_WORKSPACE, "prefill workspace %zu < %zu bytes", ws_bytes, need);
+    spkv::PrefillArgs a;
+    a.c = spkv::make_view(c);
+    a.n_q = n_q_heads;
+    a.group = G;
+    a.b = b;
+    a.q = (const char *)q;
+    a.ld_q = ld_q;
+    a.k = (const char *)k;
+    a.v = (const char *)v;
+    a.ld_kv = ld_kv;
+    a.pos0 = pos0;
+    a.n_rows = n_rows;
+    a.scale = scale;
+    a.out = out;
+    a.lse = lse;
+    a.ws = (char *)ws;
+    hipError_t e = spkv::launch_prefill(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+size_t spkv_cache_bytes(const spkv_cache *c, size_t sizes[7]) {
+    if (!c) return 0;
+    const size_t es = c->dtype == SPKV_BF16 ? 2 : 4;
+    const size_t np = (size_t)(c->n_pages > 0 ? c->n_pages : 0);
+    const size_t bg = (size_t)c->batch * c->n_kv;
+    size_t s[7];
+    s[0] = np * c->page_size * c->head_dim * es;
+    s[1] = s[0];
+    s[2] = np * c->page_size * 4;
+    s[3] = bg * (size_t)c->max_pages_per_head * 4;
+    s[4] = bg * 4;
+    s[5] = bg * (size_t)c->window * c->head_dim * es;
+    s[6] = s[5];
+    size_t tot = 0;
+    for (int i = 0; i < 7; ++i) {
+        tot += s[i];
+        if (sizes) sizes[i] = s[i];
+    }
+    return tot;
+}
+
+int spkv_cache_reset(const spkv_cache *c, void *stream) {
+    if (int r = check_cache(c)) return r;
+    hipError_t e = spkv::launch_cache_reset(spkv::make_view(c), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "reset launch");
+    return SPKV_OK;
+}
+
+int spkv_cache_check(const spkv_cache *c, void *stream, int32_t *status_bits) {
+    if (!c || !c->status) return fail(SPKV_E_INVALID, "cache / status NULL");
+    int32_t bits = 0;
+    hipError_t e = hipMemcpyAsync(&bits, c->status, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "status copy");
+    e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    if (status_bits) *status_bits = bits;
+    if (bits & (SPKV_STATUS_POOL_FULL | SPKV_STATUS_TABLE_FULL))
+        return fail(SPKV_E_CAPACITY, "cache status bits 0x%x", bits);
+    if (bits & SPKV_STATUS_BAD_ROWS) return fail(SPKV_E_ROWS, "cache status bits 0x%x", bits);
+    return SPKV_OK;
+}
+
+}  // extern "C"

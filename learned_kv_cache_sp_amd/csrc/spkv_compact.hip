@@ -1,0 +1,395 @@
+// Order-preserving compaction of kept (token, key head) pairs into the paged
+// persistent cache, and the window ring write.
+//
+// SP-KV (arXiv 2605.14037), section 2.1, deployment paragraph: the persistent
+// cache holds only the pairs with z = 1 and may be built incrementally or per
+// chunk; the local window (Eq. 4, indicator 1_win) is always available.
+//
+// For each (sequence b, key head g) the kept rows of one append get ranks by
+// an exclusive prefix count over the keep bits in row order (wavefront ballot
+// + mbcnt inside a tile, a scan over tiles across the sequence), so entry
+// lengths[b][g] + rank receives the rank-th kept row: token order is kept no
+// matter how the work is spread over workgroups.  Pages come from a device
+// bump allocator (one atomic per (b, g) and append); physical page ids may
+// differ between runs, the logical content never does.
+//
+// Layout written: key rows [page][slot][hd] (16-byte coalesced copies), value
+// rows transposed [page][hd][slot] (staged through LDS so that consecutive
+// lanes write consecutive slots), positions [page][slot].
+#include "spkv_internal.h"
+
+namespace spkv {
+namespace {
+
+constexpr int NT = 256;     // threads per workgroup
+constexpr int TILE = 256;   // rows per tile (one row per thread)
+constexpr int STAGE = 64;   // value rows staged in LDS per transpose batch
+constexpr int LDS_V_BYTES = STAGE * (128 + 2) * 4;
+
+template <typename T> struct Pad { static constexpr int value = 1; };
+template <> struct Pad<uint16_t> { static constexpr int value = 2; };
+
+__device__ inline int block_rank(bool flag, int *lds_waves, int *total) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint64_t bal = __ballot(flag);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    __syncthreads();
+    if (lane == 0) lds_waves[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int cnt = lds_waves[w];
+        before += (w < wave) ? cnt : 0;
+        tot += cnt;
+    }
+    *total = tot;
+    return before + rank;
+}
+
+// Rows of sequence b; returns false (and flags the cache) when row_offsets
+// are inconsistent with n_rows / max_rows.
+__device__ inline bool seq_rows(const CompactArgs &a, int b, int *r0, int *nb, bool report) {
+    const int lo = a.row_offsets[b];
+    const int hi = a.row_offsets[b + 1];
+    const int n = hi - lo;
+    if (lo < 0 || n < 0 || n > a.max_rows || hi > a.n_rows) {
+        if (report && threadIdx.x == 0) atomicOr(a.c.status, SPKV_STATUS_BAD_ROWS);
+        return false;
+    }
+    *r0 = lo;
+    *nb = n;
+    return true;
+}
+
+// Take pages so that (b, g) can hold want_len entries; returns the new length
+// (clipped when the page table or the pool runs out).  Called by all threads
+// of the workgroup; thread 0 does the atomic, everyone writes table entries.
+__device__ int grow_head(const CacheView &c, int b, int g, int old_len, int want_len, int *lds) {
+    if (threadIdx.x == 0) {
+        const int P = c.page_size;
+        const int first = (old_len + P - 1) >> c.page_shift;
+        int last = (want_len + P - 1) >> c.page_shift;
+        int new_len = want_len;
+        int bits = 0;
+        if (last > c.max_pages) {
+            last = c.max_pages;
+            new_len = min(new_len, last * P);
+            bits |= SPKV_STATUS_TABLE_FULL;
+        }
+        const int need = last - first;
+        int base = 0, granted = 0;
+        if (need > 0) {
+            base = atomicAdd(c.pool_next, need);
+            granted = need;
+            if (base + need > c.n_pages) {
+                granted = max(0, c.n_pages - base);
+                new_len = min(new_len, (first + granted) * P);
+                bits |= SPKV_STATUS_POOL_FULL;
+            }
+        }
+        if (bits) atomicOr(c.status, bits);
+        lds[0] = max(new_len, old_len);
+        lds[1] = first;
+        lds[2] = base;
+        lds[3] = granted;
+    }
+    __syncthreads();
+    const int first = lds[1], base = lds[2], granted = lds[3];
+    int32_t *pt = c.page_table + ((int64_t)b * c.n_kv + g) * c.max_pages;
+    for (int i = threadIdx.x; i < granted; i += NT) pt[first + i] = base + i;
+    const int new_len = lds[0];
+    __syncthreads();
+    return new_len;
+}
+
+// Copy n rows (source row ids in src_rows[]) of key head g:
+//   key rows  -> kdst(kk) (row-major, 16-byte chunks)
+//   value rows -> vdst(kk, e) (one element each, transposed via LDS)
+template <typename T, typename KDst, typename VDst>
+__device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_rows, KDst kdst,
+                          VDst vdst, char *lds_v) {
+    constexpr int ES = sizeof(T);
+    constexpr int PAD = Pad<T>::value;
+    const int hd = a.c.head_dim;
+    const int cpr = hd * ES / 16;  // 16-byte chunks per row
+    const int64_t ld_bytes = a.ld_kv * ES;
+    // keys: straight row copies
+    for (int idx = threadIdx.x; idx < n * cpr; idx += NT) {
+        const int kk = idx / cpr;
+        const int ch = idx - kk * cpr;
+        const char *src = a.k + (int64_t)src_rows[kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16;
+        *(uint4 *)(kdst(kk) + ch * 16) = *(const uint4 *)src;
+    }
+    // values: stage up to STAGE rows, then write transposed
+    const int stride = hd + PAD;  // elements per staged row
+    for (int s0 = 0; s0 < n; s0 += STAGE) {
+        const int m = min(STAGE, n - s0);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < m * cpr; idx += NT) {
+            const int kk = idx / cpr;
+            const int ch = idx - kk * cpr;
+            const char *src = a.v + (int64_t)src_rows[s0 + kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16;
+            const uint4 val = *(const uint4 *)src;
+            uint32_t *dst = (uint32_t *)(lds_v + ((int64_t)kk * stride) * ES + ch * 16);
+            dst[0] = val.x;
+            dst[1] = val.y;
+            dst[2] = val.z;
+            dst[3] = val.w;
+        }
+        __syncthreads();
+        const T *lv = (const T *)lds_v;
+        for (int idx = threadIdx.x; idx < m * hd; idx += NT) {
+            const int kk = idx % m;
+            const int e = idx / m;
+            *vdst(s0 + kk, e) = lv[kk * stride + e];
+        }
+    }
+    __syncthreads();
+}
+
+// Append the kept rows [row_lo, row_hi) of sequence b, key head g, whose
+// first kept row has destination entry dst0 (entries beyond new_len are
+// dropped).  Rows are ranked inside the tile.
+template <typename T>
+__device__ void scatter_tile(const CompactArgs &a, int b, int g, int r0, int row_lo, int row_hi,
+                             int dst0, int new_len, int pos_base, int *lds_rows, int *lds_waves,
+                             char *lds_v) {
+    const CacheView &c = a.c;
+    const int i = row_lo + threadIdx.x;
+    const bool flag = (i < row_hi) && a.keep[(int64_t)(r0 + i) * c.n_kv + g] != 0;
+    int total;
+    const int rank = block_rank(flag, lds_waves, &total);
+    if (flag) lds_rows[rank] = r0 + i;
+    __syncthreads();
+    const int n = max(0, min(total, new_len - dst0));
+    if (n == 0) return;
+    const int hd = c.head_dim;
+    const int P = c.page_size;
+    const int32_t *pt = c.page_table + ((int64_t)b * c.n_kv + g) * c.max_pages;
+    constexpr int ES = sizeof(T);
+    for (int kk = threadIdx.x; kk < n; kk += NT) {
+        const int j = dst0 + kk;
+        const int page = pt[j >> c.page_shift];
+        c.pos_pages[(int64_t)page * P + (j & (P - 1))] = pos_base + (lds_rows[kk] - r0);
+    }
+    auto kdst = [&](int kk) -> char * {
+        const int j = dst0 + kk;
+        const int page = pt[j >> c.page_shift];
+        return c.k_pages + (((int64_t)page * P + (j & (P - 1))) * hd) * ES;
+    };
+    auto vdst = [&](int kk, int e) -> T * {
+        const int j = dst0 + kk;
+        const int page = pt[j >> c.page_shift];
+        return (T *)c.v_pages + ((int64_t)page * hd + e) * P + (j & (P - 1));
+    };
+    copy_rows<T>(a, g, n, lds_rows, kdst, vdst, lds_v);
+}
+
+// Write rows [row_lo, row_hi) of sequence b (key head g) into the ring.
+template <typename T>
+__device__ void window_rows(const CompactArgs &a, int b, int g, int r0, int row_lo, int row_hi,
+                            int pos_base, int *lds_rows, char *lds_v) {
+    const CacheView &c = a.c;
+    const int n = row_hi - row_lo;
+    if (n <= 0) return;
+    for (int kk = threadIdx.x; kk < n; kk += NT) lds_rows[kk] = r0 + row_lo + kk;
+    __syncthreads();
+    const int hd = c.head_dim;
+    const int w = c.window;
+    constexpr int ES = sizeof(T);
+    const int64_t bg = (int64_t)b * c.n_kv + g;
+    const int first_pos = pos_base + row_lo;
+    auto kdst = [&](int kk) -> char * {
+        const int slot = (first_pos + kk) % w;
+        return c.ring_k + ((bg * w + slot) * hd) * ES;
+    };
+    auto vdst = [&](int kk, int e) -> T * {
+        const int slot = (first_pos + kk) % w;
+        return (T *)c.ring_v + (bg * hd + e) * w + slot;
+    };
+    copy_rows<T>(a, g, n, lds_rows, kdst, vdst, lds_v);
+}
+
+// ---------------------------------------------------------------------------
+// Small appends (every sequence has at most TILE rows): one workgroup per
+// (b, g) does ranking, page allocation and the copies.
+template <typename T>
+__global__ void __launch_bounds__(NT) compact_small_kernel(CompactArgs a) {
+    __shared__ int lds_rows[TILE];
+    __shared__ int lds_waves[NT / 64];
+    __shared__ int lds_misc[4];
+    __shared__ __attribute__((aligned(16))) char lds_v[LDS_V_BYTES];
+    const int b = blockIdx.x;
+    const int g = blockIdx.y;
+    int r0, nb;
+    if (!seq_rows(a, b, &r0, &nb, g == 0)) return;
+    const int p0 = a.pos0[b];
+    const CacheView &c = a.c;
+    if (a.flags & SPKV_APPEND_GLOBAL) {
+        const int64_t bg = (int64_t)b * c.n_kv + g;
+        // count the kept rows first (needed for the page allocation)
+        const bool flag = threadIdx.x < nb && a.keep[(int64_t)(r0 + threadIdx.x) * c.n_kv + g] != 0;
+        int total;
+        (void)block_rank(flag, lds_waves, &total);
+        const int old_len = c.lengths[bg];
+        const int new_len = grow_head(c, b, g, old_len, old_len + total, lds_misc);
+        if (threadIdx.x == 0) {
+            c.lengths[bg] = new_len;
+            if (a.append_offsets) a.append_offsets[bg] = old_len;
+        }
+        scatter_tile<T>(a, b, g, r0, 0, nb, old_len, new_len, p0, lds_rows, lds_waves, lds_v);
+    }
+    if (a.flags & SPKV_APPEND_WINDOW) {
+        __syncthreads();
+        window_rows<T>(a, b, g, r0, max(0, nb - c.window), nb, p0, lds_rows, lds_v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large appends: (1) per-tile kept counts, (2) per-(b, g) scan over tiles and
+// page allocation, (3) per-(tile, b, g) ranking and copies.
+__global__ void __launch_bounds__(NT) compact_count_kernel(CompactArgs a) {
+    __shared__ int lds_cnt[NT / 64][16];
+    const int j = blockIdx.x;
+    const int b = blockIdx.y;
+    int r0, nb;
+    if (!seq_rows(a, b, &r0, &nb, j == 0)) return;
+    const CacheView &c = a.c;
+    const int i = j * TILE + threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int g = 0; g < c.n_kv; ++g) {
+        const bool flag = i < nb && a.keep[(int64_t)(r0 + i) * c.n_kv + g] != 0;
+        const uint64_t bal = __ballot(flag);
+        if (lane == 0) lds_cnt[wave][g] = __popcll(bal);
+    }
+    __syncthreads();
+    if (threadIdx.x < c.n_kv) {
+        int s = 0;
+        for (int w = 0; w < NT / 64; ++w) s += lds_cnt[w][threadIdx.x];
+        a.ws[((int64_t)b * c.n_kv + threadIdx.x) * a.max_tiles + j] = s;
+    }
+}
+
+__global__ void __launch_bounds__(NT) compact_plan_kernel(CompactArgs a) {
+    __shared__ int lds_scan[NT];
+    __shared__ int lds_misc[4];
+    const int b = blockIdx.x;
+    const int g = blockIdx.y;
+    int r0, nb;
+    if (!seq_rows(a, b, &r0, &nb, false)) return;
+    const CacheView &c = a.c;
+    const int64_t bg = (int64_t)b * c.n_kv + g;
+    int32_t *cnt = a.ws + bg * a.max_tiles;
+    const int n_tiles = (nb + TILE - 1) / TILE;
+    int carry = 0;
+    for (int base = 0; base < n_tiles; base += NT) {
+        const int j = base + threadIdx.x;
+        const int x = j < n_tiles ? cnt[j] : 0;
+        lds_scan[threadIdx.x] = x;
+        __syncthreads();
+        // Hillis-Steele inclusive scan over NT values
+        for (int off = 1; off < NT; off <<= 1) {
+            const int y = threadIdx.x >= off ? lds_scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            lds_scan[threadIdx.x] += y;
+            __syncthreads();
+        }
+        if (j < n_tiles) cnt[j] = carry + lds_scan[threadIdx.x] - x;  // exclusive offset
+        carry += lds_scan[NT - 1];
+        __syncthreads();
+    }
+    const int old_len = c.lengths[bg];
+    const int new_len = grow_head(c, b, g, old_len, old_len + carry, lds_misc);
+    if (threadIdx.x == 0) {
+        c.lengths[bg] = new_len;
+        if (a.append_offsets) a.append_offsets[bg] = old_len;
+        int32_t *lens = a.ws + (int64_t)c.batch * c.n_kv * a.max_tiles;
+        lens[bg * 2] = old_len;
+        lens[bg * 2 + 1] = new_len;
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(NT) compact_scatter_kernel(CompactArgs a) {
+    __shared__ int lds_rows[TILE];
+    __shared__ int lds_waves[NT / 64];
+    __shared__ __attribute__((aligned(16))) char lds_v[LDS_V_BYTES];
+    const int j = blockIdx.x;
+    const int b = blockIdx.y;
+    const int g = blockIdx.z;
+    int r0, nb;
+    if (!seq_rows(a, b, &r0, &nb, false)) return;
+    const int row_lo = j * TILE;
+    if (row_lo >= nb) return;
+    const int row_hi = min(nb, row_lo + TILE);
+    const int p0 = a.pos0[b];
+    const CacheView &c = a.c;
+    const int64_t bg = (int64_t)b * c.n_kv + g;
+    if (a.flags & SPKV_APPEND_GLOBAL) {
+        const int32_t *lens = a.ws + (int64_t)c.batch * c.n_kv * a.max_tiles;
+        const int old_len = lens[bg * 2];
+        const int new_len = lens[bg * 2 + 1];
+        const int dst0 = old_len + a.ws[bg * a.max_tiles + j];
+        scatter_tile<T>(a, b, g, r0, row_lo, row_hi, dst0, new_len, p0, lds_rows, lds_waves, lds_v);
+    }
+    if (a.flags & SPKV_APPEND_WINDOW) {
+        const int w_lo = max(row_lo, nb - c.window);
+        if (w_lo < row_hi) {
+            __syncthreads();
+            window_rows<T>(a, b, g, r0, w_lo, row_hi, p0, lds_rows, lds_v);
+        }
+    }
+}
+
+__global__ void cache_reset_kernel(CacheView c) {
+    const int n = c.batch * c.n_kv;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        c.lengths[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *c.pool_next = 0;
+        *c.status = 0;
+    }
+}
+
+}  // namespace
+
+size_t compact_ws_bytes(int batch, int n_kv, int32_t max_rows) {
+    if (max_rows <= TILE) return 0;
+    const int64_t max_tiles = (max_rows + TILE - 1) / TILE;
+    return (size_t)((int64_t)batch * n_kv * (max_tiles + 2)) * sizeof(int32_t);
+}
+
+hipError_t launch_compact(const CompactArgs &a0, hipStream_t s) {
+    CompactArgs a = a0;
+    const CacheView &c = a.c;
+    const bool bf16 = c.dtype == SPKV_BF16;
+    if (a.max_rows <= TILE) {
+        dim3 grid(c.batch, c.n_kv);
+        if (bf16)
+            hipLaunchKernelGGL(compact_small_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
+        else
+            hipLaunchKernelGGL(compact_small_kernel<float>, grid, dim3(NT), 0, s, a);
+        return hipGetLastError();
+    }
+    a.max_tiles = (a.max_rows + TILE - 1) / TILE;
+    if (a.flags & SPKV_APPEND_GLOBAL) {
+        hipLaunchKernelGGL(compact_count_kernel, dim3(a.max_tiles, c.batch), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL(compact_plan_kernel, dim3(c.batch, c.n_kv), dim3(NT), 0, s, a);
+    }
+    dim3 grid(a.max_tiles, c.batch, c.n_kv);
+    if (bf16)
+        hipLaunchKernelGGL(compact_scatter_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL(compact_scatter_kernel<float>, grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_reset(const CacheView &c, hipStream_t s) {
+    hipLaunchKernelGGL(cache_reset_kernel, dim3(1), dim3(256), 0, s, c);
+    return hipGetLastError();
+}
+
+}  // namespace spkv

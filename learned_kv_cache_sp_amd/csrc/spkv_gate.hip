@@ -1,0 +1,227 @@
+// The utility gate of SP-KV (arXiv 2605.14037), section 2.1, Eq. (1)-(2):
+//   a = ReLU(W1 h + b1), logit = W2 a + b2, u = sigmoid(logit), z = [u >= tau]
+// one output per key head.  The hidden activation a stays in f32 between the
+// two layers (a bf16 rounding there could move u by ~1e-3).
+//
+// bf16: the first layer is a GEMM [rows x d_model] . [d_model x d_hidden] on
+// v_mfma_f32_16x16x32_bf16; both operands are K-contiguous rows (hidden
+// states, W1 rows), so lanes load 16-byte pieces straight from memory.  The
+// epilogue (bias, ReLU, second layer, sigmoid, threshold) runs from LDS in
+// the same kernel.  For a handful of rows (decode) d_model is split over
+// several workgroups; the last one to finish (device-scope counter) adds the
+// slices in a fixed order and runs the epilogue.
+// f32: a plain VALU kernel.
+#include "spkv_internal.h"
+
+namespace spkv {
+namespace {
+
+constexpr int NT = 256;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Second layer + sigmoid + threshold for `rows` rows whose activations
+// (after bias and ReLU) are in act[r * ld + j].
+__device__ void gate_epilogue(const GateArgs &a, const float *act, int ld, int64_t row0, int rows) {
+    const int nkv = a.n_kv;
+    for (int idx = threadIdx.x; idx < rows * nkv; idx += blockDim.x) {
+        const int r = idx / nkv;
+        const int k = idx - r * nkv;
+        const int64_t row = row0 + r;
+        if (row >= a.n_rows) continue;
+        const float *w2 = a.w2 + (int64_t)k * a.d_hidden;
+        const float *ar = act + r * ld;
+        float acc = 0.f;
+        for (int j = 0; j < a.d_hidden; ++j) acc = fmaf(w2[j], ar[j], acc);
+        const float logit = acc + a.b2[k];
+        const float u = sigmoid_f(logit);
+        if (a.utility) a.utility[row * nkv + k] = u;
+        a.keep[row * nkv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+    }
+}
+
+__device__ inline float relu_keep_nan(float x) { return x < 0.f ? 0.f : x; }
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel.  Workgroup tile: (16 * WM) rows x HG hidden units; waves
+// are arranged WM (rows) x (4 / WM) (hidden units).  blockIdx.y = d_model
+// slice when n_split > 1.
+template <int WM, int HG>
+__global__ void __launch_bounds__(NT) gate_bf16_kernel(GateArgs a) {
+    constexpr int WN = 4 / WM;
+    constexpr int BM = 16 * WM;
+    constexpr int NTW = HG / 16 / WN;  // 16-wide unit tiles per wave
+    static_assert(NTW >= 1, "d_hidden too small for this wave layout");
+    __shared__ float act[BM][HG + 1];
+    __shared__ int last_flag;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN;
+    const int wn = wave - wm * WN;
+    const int i16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int64_t row0 = (int64_t)blockIdx.x * BM;
+    const int split = blockIdx.y;
+    const int steps_total = a.d_model / 32;
+    const int steps = steps_total / a.n_split;
+    const int k_lo = split * steps * 32;
+
+    f32x4 acc[NTW];
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t my_row = row0 + wm * 16 + i16;
+    const bool row_ok = my_row < a.n_rows;
+    const __bf16 *hrow = (const __bf16 *)a.hidden + (row_ok ? my_row : 0) * a.ld_hidden + k_lo + 8 * q4;
+    const __bf16 *w1 = (const __bf16 *)a.w1;
+    const __bf16 *wrow[NTW];
+#pragma unroll
+    for (int n = 0; n < NTW; ++n)
+        wrow[n] = w1 + (int64_t)((wn * NTW + n) * 16 + i16) * a.d_model + k_lo + 8 * q4;
+
+    for (int s = 0; s < steps; ++s) {
+        bf16x8 av = row_ok ? *(const bf16x8 *)(hrow + 32 * s) : bf16x8{};
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) {
+            const bf16x8 bv = *(const bf16x8 *)(wrow[n] + 32 * s);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
+        }
+    }
+
+    if (a.n_split == 1) {
+        // D layout: lane holds rows 4*q4 + r, unit 16*tile + i16
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) {
+            const int j = (wn * NTW + n) * 16 + i16;
+            const float bias = a.b1[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) act[wm * 16 + 4 * q4 + r][j] = relu_keep_nan(acc[n][r] + bias);
+        }
+        __syncthreads();
+        gate_epilogue(a, &act[0][0], HG + 1, row0, BM);
+        return;
+    }
+
+    // split d_model: write this slice's sums, the last slice finishes
+    const int n_tiles = gridDim.x;
+    float *part = a.ws;  // [n_split][n_tiles * BM][HG]
+    int32_t *cnt = (int32_t *)(a.ws + (size_t)a.n_split * n_tiles * BM * HG);
+    const size_t slab = (size_t)n_tiles * BM * HG;
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) {
+        const int j = (wn * NTW + n) * 16 + i16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = (int)(blockIdx.x * BM) + wm * 16 + 4 * q4 + r;
+            part[split * slab + (size_t)rr * HG + j] = acc[n][r];
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last_flag = (atomicAdd(&cnt[blockIdx.x], 1) == a.n_split - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+    for (int idx = threadIdx.x; idx < BM * HG; idx += NT) {
+        const int r = idx / HG;
+        const int j = idx - r * HG;
+        const size_t off = (size_t)(blockIdx.x * BM + r) * HG + j;
+        float s = 0.f;
+        for (int sp = 0; sp < a.n_split; ++sp) s += __builtin_nontemporal_load(part + sp * slab + off);
+        act[r][j] = relu_keep_nan(s + a.b1[j]);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) cnt[blockIdx.x] = 0;
+    gate_epilogue(a, &act[0][0], HG + 1, row0, BM);
+}
+
+// ---------------------------------------------------------------------------
+// f32 (and any d_hidden) VALU kernel: one workgroup per row.
+template <typename T>
+__global__ void __launch_bounds__(NT) gate_valu_kernel(GateArgs a) {
+    __shared__ float part[NT];
+    __shared__ float act[256];
+    const int64_t row = blockIdx.x;
+    const int hg = a.d_hidden;
+    const int per = NT / hg;  // threads per hidden unit (>= 1 since hg <= 256)
+    const int j = threadIdx.x % hg;
+    const int p = threadIdx.x / hg;
+    float acc = 0.f;
+    if (p < per) {
+        const T *h = (const T *)a.hidden + row * a.ld_hidden;
+        const T *w = (const T *)a.w1 + (int64_t)j * a.d_model;
+        for (int i = p; i < a.d_model; i += per) acc = fmaf((float)w[i], (float)h[i], acc);
+    }
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < hg) {
+        float s = 0.f;
+        for (int q = 0; q < per; ++q) s += part[q * hg + threadIdx.x];
+        act[threadIdx.x] = relu_keep_nan(s + a.b1[threadIdx.x]);
+    }
+    __syncthreads();
+    gate_epilogue(a, act, 0, row, 1);
+}
+
+constexpr int SMALL_ROWS = 64;
+
+}  // namespace
+
+int gate_split_for(int d_model, int dtype, int64_t n_rows) {
+    if (dtype != SPKV_BF16 || n_rows > SMALL_ROWS) return 1;
+    const int steps = d_model / 32;
+    int split = 1;
+    while (split * 2 <= 16 && steps % (split * 2) == 0) split *= 2;
+    return split;
+}
+
+static bool mfma_hidden(int hg) { return hg == 32 || hg == 64 || hg == 128 || hg == 256; }
+
+// rows per workgroup on the small-row (split) path: 16 * WM with WM = 2 for
+// d_hidden = 32 (two 16-unit tiles) and 1 otherwise
+static int small_bm(int hg) { return hg == 32 ? 32 : 16; }
+
+size_t gate_ws_bytes(int d_model, int d_hidden, int dtype, int64_t n_rows) {
+    const int split = gate_split_for(d_model, dtype, n_rows);
+    if (split == 1 || !mfma_hidden(d_hidden)) return 0;
+    const int bm = small_bm(d_hidden);
+    const int64_t tiles = (n_rows + bm - 1) / bm;
+    return (size_t)split * tiles * bm * d_hidden * sizeof(float) + (size_t)tiles * sizeof(int32_t) + 256;
+}
+
+template <int WM>
+static void launch_mfma(const GateArgs &a, int tiles, hipStream_t s) {
+    const dim3 grid(tiles, a.n_split);
+    switch (a.d_hidden) {
+    case 32: hipLaunchKernelGGL((gate_bf16_kernel<(WM < 2 ? 2 : WM), 32>), grid, dim3(NT), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((gate_bf16_kernel<WM, 64>), grid, dim3(NT), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((gate_bf16_kernel<WM, 128>), grid, dim3(NT), 0, s, a); break;
+    default: hipLaunchKernelGGL((gate_bf16_kernel<WM, 256>), grid, dim3(NT), 0, s, a); break;
+    }
+}
+
+hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
+    GateArgs a = a0;
+    if (a.dtype == SPKV_BF16 && mfma_hidden(a.d_hidden)) {
+        if (a.n_split > 1) {
+            const int bm = small_bm(a.d_hidden);
+            const int tiles = (int)((a.n_rows + bm - 1) / bm);
+            launch_mfma<1>(a, tiles, s);
+        } else {
+            const int tiles = (int)((a.n_rows + 63) / 64);
+            launch_mfma<4>(a, tiles, s);
+        }
+    } else {
+        a.n_split = 1;
+        if (a.dtype == SPKV_BF16)
+            hipLaunchKernelGGL(gate_valu_kernel<__bf16>, dim3((unsigned)a.n_rows), dim3(NT), 0, s, a);
+        else
+            hipLaunchKernelGGL(gate_valu_kernel<float>, dim3((unsigned)a.n_rows), dim3(NT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace spkv

@@ -1,0 +1,123 @@
+// Internal declarations shared by the host API and the HIP kernels of libspkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "spkv.h"
+
+namespace spkv {
+
+// Kernel-side view of an spkv_cache (passed by value to kernels).
+struct CacheView {
+    int32_t batch, n_kv, head_dim, window, page_size, n_pages, max_pages, dtype;
+    int32_t page_shift;  // log2(page_size)
+    char *k_pages;
+    char *v_pages;
+    int32_t *pos_pages;
+    int32_t *page_table;
+    int32_t *lengths;
+    int32_t *pool_next;
+    int32_t *status;
+    char *ring_k;
+    char *ring_v;
+};
+
+inline CacheView make_view(const spkv_cache *c) {
+    CacheView v;
+    v.batch = c->batch;
+    v.n_kv = c->n_kv;
+    v.head_dim = c->head_dim;
+    v.window = c->window;
+    v.page_size = c->page_size;
+    v.n_pages = c->n_pages;
+    v.max_pages = c->max_pages_per_head;
+    v.dtype = c->dtype;
+    int s = 0;
+    while ((1 << s) < c->page_size) ++s;
+    v.page_shift = s;
+    v.k_pages = (char *)c->k_pages;
+    v.v_pages = (char *)c->v_pages;
+    v.pos_pages = c->pos_pages;
+    v.page_table = c->page_table;
+    v.lengths = c->lengths;
+    v.pool_next = c->pool_next;
+    v.status = c->status;
+    v.ring_k = (char *)c->ring_k;
+    v.ring_v = (char *)c->ring_v;
+    return v;
+}
+
+inline int elem_bytes(int dtype) { return dtype == SPKV_BF16 ? 2 : 4; }
+
+// ---- gate ------------------------------------------------------------------
+struct GateArgs {
+    int32_t d_model, d_hidden, n_kv, dtype;
+    const void *w1;
+    const float *b1, *w2, *b2;
+    const void *hidden;
+    int64_t n_rows, ld_hidden;
+    float tau;
+    float *utility;
+    uint8_t *keep;
+    float *ws;          // split-K partials [n_split, n_rows_pad, d_hidden] + counters
+    int32_t n_split;    // number of slices of d_model (1 = no workspace)
+};
+size_t gate_ws_bytes(int d_model, int d_hidden, int dtype, int64_t n_rows);
+int gate_split_for(int d_model, int dtype, int64_t n_rows);
+hipError_t launch_gate(const GateArgs &a, hipStream_t s);
+
+// ---- compaction ------------------------------------------------------------
+struct CompactArgs {
+    CacheView c;
+    const uint8_t *keep;
+    const char *k;
+    const char *v;
+    int64_t ld_kv;  // elements
+    const int32_t *row_offsets;
+    const int32_t *pos0;
+    int32_t n_rows, max_rows, flags;
+    int32_t *append_offsets;
+    int32_t *ws;  // large path: tile counts/offsets [B*Hkv*max_tiles] + lens [B*Hkv*2]
+    int32_t max_tiles;
+};
+size_t compact_ws_bytes(int batch, int n_kv, int32_t max_rows);
+hipError_t launch_compact(const CompactArgs &a, hipStream_t s);
+
+// ---- decode ----------------------------------------------------------------
+struct DecodeArgs {
+    CacheView c;
+    int32_t n_q, group;
+    const char *q;
+    int64_t ld_q;
+    const int32_t *t;
+    float scale;
+    float *out, *lse;
+    char *ws;
+    int32_t grid;       // persistent workgroups
+    int32_t max_items;  // partial slots in ws
+};
+size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out);
+int decode_blocks_per_cu();
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+// ---- prefill ---------------------------------------------------------------
+struct PrefillArgs {
+    CacheView c;
+    int32_t n_q, group, b;
+    const char *q;
+    int64_t ld_q;
+    const char *k, *v;
+    int64_t ld_kv;
+    int32_t pos0, n_rows;
+    float scale;
+    float *out, *lse;
+    char *ws;
+};
+size_t prefill_ws_bytes(const spkv_cache *c, int n_q, int n_rows);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+hipError_t launch_cache_reset(const CacheView &c, hipStream_t s);
+
+}  // namespace spkv

@@ -1,0 +1,392 @@
+"""Python binding of libspkv (the SP-KV hot path on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libspkv.so.  torch supplies device memory and the stream.  The functions
+``spkv_gate``, ``spkv_compact_append``, ``spkv_decode_attn`` and
+``spkv_prefill_attn`` mirror the C calls of include/spkv.h one to one and
+take torch tensors in place of pointers.  ``Cache`` and ``GateWeights``
+allocate the buffers the C structs point to.
+
+There is no fallback: if libspkv.so is missing or no GPU is visible, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspkv.so")
+
+SPKV_OK = 0
+SPKV_E_INVALID = -1
+SPKV_E_UNSUPPORTED = -2
+SPKV_E_HIP = -3
+SPKV_E_CAPACITY = -4
+SPKV_E_WORKSPACE = -5
+SPKV_E_ROWS = -6
+
+SPKV_F32 = 0
+SPKV_BF16 = 1
+SPKV_APPEND_GLOBAL = 1
+SPKV_APPEND_WINDOW = 2
+
+STATUS_POOL_FULL = 1
+STATUS_TABLE_FULL = 2
+STATUS_BAD_ROWS = 4
+
+
+class SpkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+class GateDesc(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p),
+    ]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+        ("max_pages_per_head", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p), ("pos_pages", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("lengths", ctypes.c_void_p), ("pool_next", ctypes.c_void_p),
+        ("status", ctypes.c_void_p), ("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = [
+    "spkv_gate", "spkv_gate_ws_bytes", "spkv_compact_append", "spkv_compact_ws_bytes",
+    "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_prefill_attn", "spkv_prefill_ws_bytes",
+    "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
+    "spkv_last_error", "spkv_version",
+]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with learned_kv_cache_sp_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    G, C = ctypes.POINTER(GateDesc), ctypes.POINTER(CacheDesc)
+    sig = {
+        "spkv_gate": ([G, vp, i64, i64, f32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "spkv_gate_ws_bytes": ([G, i64], sz),
+        "spkv_compact_append": ([C, vp, vp, vp, i64, vp, vp, i32, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+        "spkv_compact_ws_bytes": ([C, i32, i32], sz),
+        "spkv_decode_attn": ([C, i32, vp, i64, vp, f32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "spkv_decode_ws_bytes": ([C, i32], sz),
+        "spkv_prefill_attn": ([C, i32, i32, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp, vp, sz, vp],
+                              ctypes.c_int),
+        "spkv_prefill_ws_bytes": ([C, i32, i32], sz),
+        "spkv_cache_bytes": ([C, vp], sz),
+        "spkv_cache_reset": ([C, vp], ctypes.c_int),
+        "spkv_cache_check": ([C, vp, vp], ctypes.c_int),
+        "spkv_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "spkv_last_error": ([], ctypes.c_char_p),
+        "spkv_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != SPKV_OK:
+        lib = load_library()
+        raise SpkvError(rc, lib.spkv_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not isinstance(t, int) and not t.is_cuda:
+            raise ValueError("libspkv works on device tensors only")
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return SPKV_BF16
+    if dt == torch.float32:
+        return SPKV_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _torch_dtype(code: int):
+    return torch.bfloat16 if code == SPKV_BF16 else torch.float32
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    """Elements between consecutive rows (dim 0) of a tensor whose other dims are packed."""
+    if t.dim() == 1:
+        return t.shape[0]
+    if t.shape[0] == 0:
+        return max(1, int(np.prod(t.shape[1:])))
+    inner = t[0]
+    if not inner.is_contiguous():
+        raise ValueError("rows must be contiguous")
+    return t.stride(0)
+
+
+# ----------------------------------------------------------------------------
+# buffers
+# ----------------------------------------------------------------------------
+
+@dataclass
+class GateWeights:
+    """W1 [d_hidden, d_model] (dtype), b1 [d_hidden], W2 [n_kv, d_hidden], b2 [n_kv] (f32)."""
+    w1: torch.Tensor
+    b1: torch.Tensor
+    w2: torch.Tensor
+    b2: torch.Tensor
+
+    def desc(self) -> GateDesc:
+        _need_gpu(self.w1, self.b1, self.w2, self.b2)
+        for t in (self.b1, self.w2, self.b2):
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("b1, w2, b2 must be contiguous float32")
+        if not self.w1.is_contiguous():
+            raise ValueError("w1 must be contiguous")
+        d = GateDesc()
+        d.d_hidden, d.d_model = self.w1.shape
+        d.n_kv = self.w2.shape[0]
+        d.dtype = _dtype_code(self.w1.dtype)
+        d.w1, d.b1, d.w2, d.b2 = (_ptr(self.w1), _ptr(self.b1), _ptr(self.w2), _ptr(self.b2))
+        self._desc = d  # keep alive
+        return d
+
+
+class Cache:
+    """Device buffers of one layer's SP-KV cache (see include/spkv.h, spkv_cache)."""
+
+    def __init__(self, batch: int, n_kv: int, head_dim: int, window: int, page_size: int,
+                 n_pages: int, max_pages_per_head: int, dtype=torch.bfloat16, device="cuda"):
+        dt = dtype
+        self.batch, self.n_kv, self.head_dim, self.window = batch, n_kv, head_dim, window
+        self.page_size, self.n_pages, self.max_pages_per_head = page_size, n_pages, max_pages_per_head
+        self.dtype = dt
+        z = lambda shape, d=dt: torch.zeros(shape, dtype=d, device=device)  # noqa: E731
+        self.k_pages = z((n_pages, page_size, head_dim))
+        self.v_pages = z((n_pages, head_dim, page_size))
+        self.pos_pages = z((n_pages, page_size), torch.int32)
+        self.page_table = torch.full((batch, n_kv, max_pages_per_head), -1, dtype=torch.int32, device=device)
+        self.lengths = z((batch, n_kv), torch.int32)
+        self.pool_next = z((1,), torch.int32)
+        self.status = z((1,), torch.int32)
+        self.ring_k = z((batch, n_kv, window, head_dim))
+        self.ring_v = z((batch, n_kv, head_dim, window))
+        self._desc = None
+
+    @staticmethod
+    def pages_needed(lengths_per_head, page_size: int) -> int:
+        return int(sum((int(n) + page_size - 1) // page_size for n in lengths_per_head))
+
+    def desc(self) -> CacheDesc:
+        if self._desc is None:
+            d = CacheDesc()
+            d.batch, d.n_kv, d.head_dim, d.window = self.batch, self.n_kv, self.head_dim, self.window
+            d.page_size, d.n_pages, d.max_pages_per_head = self.page_size, self.n_pages, self.max_pages_per_head
+            d.dtype = _dtype_code(self.dtype)
+            for name in ("k_pages", "v_pages", "pos_pages", "page_table", "lengths", "pool_next",
+                         "status", "ring_k", "ring_v"):
+                setattr(d, name, _ptr(getattr(self, name)))
+            self._desc = d
+        return self._desc
+
+    def nbytes(self) -> int:
+        return int(load_library().spkv_cache_bytes(ctypes.byref(self.desc()), None))
+
+    # ---- logical read-back (host side; for checks and tools) ---------------
+    def read_head(self, b: int, g: int):
+        """Cached entries of (b, g) in logical order: (K [n, hd], V [n, hd], pos [n])."""
+        n = int(self.lengths[b, g].item())
+        P = self.page_size
+        npg = (n + P - 1) // P
+        pages = self.page_table[b, g, :npg].long()
+        k = self.k_pages[pages].reshape(npg * P, self.head_dim)[:n]
+        v = self.v_pages[pages].transpose(1, 2).reshape(npg * P, self.head_dim)[:n]
+        pos = self.pos_pages[pages].reshape(npg * P)[:n]
+        return k, v, pos
+
+    def read_ring(self, b: int, g: int):
+        """Ring of (b, g): K [w, hd], V [w, hd] indexed by slot = position % w."""
+        return self.ring_k[b, g], self.ring_v[b, g].transpose(0, 1)
+
+    def snapshot(self) -> dict:
+        return {n: getattr(self, n).clone() for n in ("k_pages", "v_pages", "pos_pages", "page_table",
+                                                      "lengths", "pool_next", "status", "ring_k", "ring_v")}
+
+    def restore(self, snap: dict):
+        for n, t in snap.items():
+            getattr(self, n).copy_(t)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
+    """Zero-filled device workspace (16-byte aligned)."""
+    if nbytes == 0:
+        return None
+    return torch.zeros(((nbytes + 15) // 16) * 4, dtype=torch.int32, device=device)
+
+
+# ----------------------------------------------------------------------------
+# the four calls
+# ----------------------------------------------------------------------------
+
+def spkv_gate_ws_bytes(weights: GateWeights, n_rows: int) -> int:
+    return int(load_library().spkv_gate_ws_bytes(ctypes.byref(weights.desc()), n_rows))
+
+
+def spkv_gate(weights: GateWeights, hidden: torch.Tensor, tau: float, utility=None, keep=None,
+              ws=None, stream=None):
+    """Eq. (1)-(2) for every row of hidden [n_rows, d_model].  Returns (utility, keep)."""
+    lib = load_library()
+    desc = weights.desc()
+    n = hidden.shape[0]
+    dev = hidden.device
+    if keep is None:
+        keep = torch.empty((n, desc.n_kv), dtype=torch.uint8, device=dev)
+    if utility is None:
+        utility = torch.empty((n, desc.n_kv), dtype=torch.float32, device=dev)
+    _need_gpu(hidden, keep, utility)
+    if hidden.dtype != weights.w1.dtype:
+        raise ValueError("hidden and w1 dtypes differ")
+    need = spkv_gate_ws_bytes(weights, n)
+    if ws is None and need:
+        ws = workspace(need, dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.spkv_gate(ctypes.byref(desc), _ptr(hidden), n, _row_stride(hidden), float(tau),
+                         _ptr(utility), _ptr(keep), _ptr(ws), ws_bytes, _stream(stream)))
+    return utility, keep
+
+
+def spkv_compact_ws_bytes(cache: Cache, n_rows: int, max_rows_per_seq: int) -> int:
+    return int(load_library().spkv_compact_ws_bytes(ctypes.byref(cache.desc()), n_rows, max_rows_per_seq))
+
+
+def spkv_compact_append(cache: Cache, keep, k: torch.Tensor, v: torch.Tensor, row_offsets: torch.Tensor,
+                        pos0: torch.Tensor, max_rows_per_seq: int, flags: int, append_offsets=None,
+                        ws=None, stream=None):
+    """Append rows [n_rows, n_kv, hd] (CSR by row_offsets) to the cache; see spkv.h."""
+    lib = load_library()
+    _need_gpu(keep, k, v, row_offsets, pos0, append_offsets)
+    if k.dtype != cache.dtype or v.dtype != cache.dtype:
+        raise ValueError("k / v dtype differs from the cache")
+    if row_offsets.dtype != torch.int32 or pos0.dtype != torch.int32:
+        raise ValueError("row_offsets and pos0 must be int32")
+    if keep is not None and keep.dtype != torch.uint8:
+        raise ValueError("keep must be uint8")
+    n = k.shape[0]
+    ld = _row_stride(k)
+    if _row_stride(v) != ld:
+        raise ValueError("k and v must share a row stride")
+    need = spkv_compact_ws_bytes(cache, n, max_rows_per_seq)
+    if ws is None and need:
+        ws = workspace(need, k.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.spkv_compact_append(ctypes.byref(cache.desc()), _ptr(keep), _ptr(k), _ptr(v), ld,
+                                   _ptr(row_offsets), _ptr(pos0), n, int(max_rows_per_seq), int(flags),
+                                   _ptr(append_offsets), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def spkv_decode_ws_bytes(cache: Cache, n_q_heads: int) -> int:
+    return int(load_library().spkv_decode_ws_bytes(ctypes.byref(cache.desc()), n_q_heads))
+
+
+def spkv_decode_attn(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: float, out=None, lse=None,
+                     ws=None, stream=None):
+    """One query per sequence: q [batch, n_q, hd], t [batch] int32.  Returns (out, lse)."""
+    lib = load_library()
+    B, nq, hd = q.shape
+    if out is None:
+        out = torch.empty((B, nq, hd), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+    _need_gpu(q, t, out, lse)
+    if q.dtype != cache.dtype:
+        raise ValueError("q dtype differs from the cache")
+    if t.dtype != torch.int32:
+        raise ValueError("t must be int32")
+    need = spkv_decode_ws_bytes(cache, nq)
+    if ws is None and need:
+        ws = workspace(need, q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.spkv_decode_attn(ctypes.byref(cache.desc()), nq, _ptr(q), _row_stride(q), _ptr(t),
+                                float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def spkv_prefill_ws_bytes(cache: Cache, n_q_heads: int, n_rows: int) -> int:
+    return int(load_library().spkv_prefill_ws_bytes(ctypes.byref(cache.desc()), n_q_heads, n_rows))
+
+
+def spkv_prefill_attn(cache: Cache, b: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos0: int,
+                      scale: float, out=None, lse=None, ws=None, stream=None):
+    """Rows pos0 .. pos0+n-1 of sequence b: q [n, n_q, hd], k/v [n, n_kv, hd].  Returns (out, lse)."""
+    lib = load_library()
+    n, nq, hd = q.shape
+    if out is None:
+        out = torch.empty((n, nq, hd), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((n, nq), dtype=torch.float32, device=q.device)
+    _need_gpu(q, k, v, out, lse)
+    for x in (q, k, v):
+        if x.dtype != cache.dtype:
+            raise ValueError("q / k / v dtype differs from the cache")
+    need = spkv_prefill_ws_bytes(cache, nq, n)
+    if ws is None and need:
+        ws = workspace(need, q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ld_kv = _row_stride(k)
+    if _row_stride(v) != ld_kv:
+        raise ValueError("k and v must share a row stride")
+    _check(lib.spkv_prefill_attn(ctypes.byref(cache.desc()), nq, int(b), _ptr(q), _row_stride(q), _ptr(k),
+                                 _ptr(v), ld_kv, int(pos0), n, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                 ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def spkv_cache_reset(cache: Cache, stream=None):
+    _check(load_library().spkv_cache_reset(ctypes.byref(cache.desc()), _stream(stream)))
+
+
+def spkv_cache_check(cache: Cache, stream=None) -> int:
+    """Synchronise and return the sticky status bits; raises on capacity / row errors."""
+    bits = ctypes.c_int32(0)
+    rc = load_library().spkv_cache_check(ctypes.byref(cache.desc()), _stream(stream), ctypes.byref(bits))
+    if rc != SPKV_OK:
+        raise SpkvError(rc, load_library().spkv_last_error().decode() + f" bits={bits.value}")
+    return bits.value

@@ -1,0 +1,161 @@
+"""Shared helpers of the GPU parity tests.
+
+Inputs come from learned_kv_cache_sp_amd.inputs (seeded draws only); expected
+values come from the fp64 oracle; the HIP path is reached only through the
+binding of libspkv.  Nothing computed on the GPU is ever fed to the oracle.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from learned_kv_cache_sp_amd import inputs  # noqa: E402
+
+BAND = 1e-3          # utilities this close to tau are redrawn (mask decisions stay exact)
+TOL_F32 = 1e-5       # max-abs on attention outputs, f32 workloads
+TOL_BF16 = 2e-2      # max-abs on attention outputs, bf16 in / f32 accumulate
+TOL_REGRESS = 1e-3   # tighter internal bound for bf16 outputs
+U_TOL = 2e-5         # utilities: f32 on the device vs f64 in the oracle
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+@dataclass
+class LayerInputs:
+    wl: inputs.Workload
+    W1: np.ndarray
+    b1: np.ndarray
+    W2: np.ndarray
+    b2: np.ndarray
+    H: list          # per sequence [T_b, d_model]
+    Q: list          # per sequence [T_b, n_q, hd]
+    K: list          # per sequence [T_b, n_kv, hd]
+    V: list
+    z: list          # per sequence [T_b, n_kv] (oracle gate)
+    u: list          # per sequence [T_b, n_kv] (oracle gate, f64)
+
+
+def calibrated_weights(wl: inputs.Workload, seed: int | None = None, n_cal: int = 4096):
+    """Layer weights with b2 placed (on an oracle-evaluated calibration sample) for wl.keep."""
+    w = inputs.layer_weights(wl, seed)
+    H_cal = inputs.normal((n_cal, wl.d_model), wl.seed if seed is None else seed, inputs.STREAM_CAL,
+                          dtype=wl.dtype)
+    _, logit, _ = oracle.gate(H_cal, w["W1"], w["b1"], w["W2"], w["b2"], wl.tau, threads=oracle_threads())
+    w["b2"] = inputs.place_output_bias(logit, wl.keep, wl.tau)
+    return w
+
+
+def resample_band(wl, w, H: np.ndarray, seed: int, stream: int, max_rounds: int = 50):
+    """Redraw hidden rows whose oracle utility lies within BAND of tau.
+
+    Returns (H, u, z) with every |u - tau| >= BAND."""
+    th = oracle_threads()
+    u, _, z = oracle.gate(H, w["W1"], w["b1"], w["W2"], w["b2"], wl.tau, threads=th)
+    for attempt in range(max_rounds):
+        bad = np.flatnonzero(np.any(np.abs(u - wl.tau) < BAND, axis=1))
+        if bad.size == 0:
+            return H, u, z
+        H[bad] = inputs.normal((bad.size, wl.d_model), seed, inputs.STREAM_RESAMPLE, stream, attempt,
+                               dtype=wl.dtype)
+        u2, _, z2 = oracle.gate(H[bad], w["W1"], w["b1"], w["W2"], w["b2"], wl.tau, threads=th)
+        u[bad] = u2
+        z[bad] = z2
+    raise RuntimeError("band resampling did not converge")
+
+
+def layer_inputs(wl: inputs.Workload, lengths, seed: int | None = None) -> LayerInputs:
+    s = wl.seed if seed is None else seed
+    w = calibrated_weights(wl, s)
+    H, Q, K, V, Z, U = [], [], [], [], [], []
+    for b, T in enumerate(lengths):
+        tok = inputs.tokens(wl, int(T), s, b)
+        h, u, z = resample_band(wl, w, tok["H"], s, b)
+        H.append(h), Q.append(tok["Q"]), K.append(tok["K"]), V.append(tok["V"]), Z.append(z), U.append(u)
+    return LayerInputs(wl, w["W1"], w["b1"], w["W2"], w["b2"], H, Q, K, V, Z, U)
+
+
+def small_workload(name: str, **over) -> inputs.Workload:
+    """A named workload with some fields replaced (smaller sizes for oracle-checked runs)."""
+    import dataclasses
+    return dataclasses.replace(inputs.WORKLOADS[name], **over)
+
+
+def max_abs(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def scale_for(hd: int) -> float:
+    return 1.0 / math.sqrt(hd)
+
+
+# ----------------------------------------------------------------------------
+# device helpers (torch + the binding; imported lazily so CPU tests need no GPU)
+# ----------------------------------------------------------------------------
+
+def torch_dtype(wl_or_dtype):
+    import torch
+    d = wl_or_dtype.dtype if hasattr(wl_or_dtype, "dtype") else wl_or_dtype
+    return torch.bfloat16 if d == "bf16" else torch.float32
+
+
+def dev(x: np.ndarray, dtype=None):
+    """float32 numpy array (holding values exact in `dtype`) -> device tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return t.to(dtype) if dtype is not None else t
+
+
+def gate_weights(li_or_w, dtype):
+    import torch
+    from learned_kv_cache_sp_amd import spkv
+    if isinstance(li_or_w, dict):
+        W1, b1, W2, b2 = li_or_w["W1"], li_or_w["b1"], li_or_w["W2"], li_or_w["b2"]
+    else:
+        W1, b1, W2, b2 = li_or_w.W1, li_or_w.b1, li_or_w.W2, li_or_w.b2
+    return spkv.GateWeights(dev(W1, dtype), dev(b1, torch.float32), dev(W2, torch.float32),
+                            dev(b2, torch.float32))
+
+
+def new_cache(wl, batch: int, max_len: int, page_size: int = 64, spare_pages: int = 1):
+    from learned_kv_cache_sp_amd import spkv
+    per_head = (max_len + page_size - 1) // page_size + spare_pages
+    return spkv.Cache(batch, wl.n_kv, wl.head_dim, wl.window, page_size, batch * wl.n_kv * per_head,
+                      per_head, torch_dtype(wl))
+
+
+def append(cache, rows_z, rows_k, rows_v, pos0s, flags, stream=None, append_offsets=None):
+    """Append per-sequence row blocks (lists of numpy arrays; a None block = no rows)."""
+    import torch
+    from learned_kv_cache_sp_amd import spkv
+    B = cache.batch
+    counts = [0 if r is None else r.shape[0] for r in rows_k]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n = int(offs[-1])
+    dt = cache.dtype
+    hd, nkv = cache.head_dim, cache.n_kv
+    K = np.concatenate([r for r in rows_k if r is not None]) if n else np.zeros((0, nkv, hd), np.float32)
+    V = np.concatenate([r for r in rows_v if r is not None]) if n else np.zeros((0, nkv, hd), np.float32)
+    if rows_z is not None:
+        Z = np.concatenate([r for r in rows_z if r is not None]) if n else np.zeros((0, nkv), np.uint8)
+        keep = dev(Z.astype(np.uint8))
+    else:
+        keep = None
+    kd, vd = dev(K, dt), dev(V, dt)
+    ro = dev(offs)
+    p0 = dev(np.asarray(pos0s, np.int32))
+    spkv.spkv_compact_append(cache, keep, kd, vd, ro, p0, max(1, max(counts)), flags,
+                             append_offsets=append_offsets, stream=stream)
+    return n
