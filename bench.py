@@ -78,7 +78,8 @@ def main():
     P = args.page_size
     L = max(1, args.layers)
     steps, warm = args.steps, args.warmup
-    per_layer_steps = (steps + warm + L - 1) // L + 1
+    S = warm + 2 * steps  # warm-up, the timed pass, the per-launch timing pass
+    per_layer_steps = (S + L - 1) // L + 1
     scale = 1.0 / math.sqrt(hd)
     G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
     seed = wl.seed
@@ -120,7 +121,6 @@ def main():
     kept_frac = zpre.float().mean(0).cpu().numpy()
 
     # ---- per-step inputs --------------------------------------------------------
-    S = steps + warm
     Hs = inputs.device_normal((S, B, d), seed, 2001, torch.bfloat16)
     Qs = inputs.device_normal((S, B, nq, hd), seed, 2002, torch.bfloat16)
     Ks = inputs.device_normal((S, B, nkv, hd), seed, 2003, torch.bfloat16)
@@ -145,46 +145,54 @@ def main():
     def nb(t):
         return 0 if t is None else t.numel() * t.element_size()
 
-    def step(s):
+    def step(s, timed_decode=False):
         l = s % L
         rc = lib.spkv_gate(ctypes.byref(gdesc), Hs[s].data_ptr(), B, d, wl.tau, ust[s].data_ptr(),
                            zst[s].data_ptr(), gws_p, gws_n, sp)
         rc |= lib.spkv_compact_append(ctypes.byref(cdescs[l]), zst[s].data_ptr(), Ks[s].data_ptr(),
                                       Vs[s].data_ptr(), nkv * hd, ro1.data_ptr(), tpos[s].data_ptr(), B, 1,
                                       G_ | W_, None, None, 0, sp)
-        ev0[s].record(stream)
+        if timed_decode:
+            ev0[s].record(stream)
         rc |= lib.spkv_decode_attn(ctypes.byref(cdescs[l]), nq, Qs[s].data_ptr(), nq * hd, tpos[s].data_ptr(),
                                    scale, out.data_ptr(), lse.data_ptr(), dec_ws[l].data_ptr(),
                                    nb(dec_ws[l]), sp)
-        ev1[s].record(stream)
+        if timed_decode:
+            ev1[s].record(stream)
         if rc:
             raise RuntimeError(lib.spkv_last_error().decode())
 
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    ev0 = {s: torch.cuda.Event(enable_timing=True) for s in range(warm + steps, S)}
+    ev1 = {s: torch.cuda.Event(enable_timing=True) for s in range(warm + steps, S)}
     for s in range(warm):
         step(s)
     torch.cuda.synchronize()
+    # pass 1 (the figure of merit): K whole steps, bracketed by two events
     t0 = time.perf_counter()
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     e_start.record(stream)
-    for s in range(warm, S):
+    for s in range(warm, warm + steps):
         step(s)
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e_start.elapsed_time(e_end)
+    # pass 2: the same K steps again with events around every decode launch
+    # (event records add gaps to the stream, so they stay out of pass 1)
+    for s in range(warm + steps, S):
+        step(s, timed_decode=True)
+    torch.cuda.synchronize()
     for c in caches:
         spkv.spkv_cache_check(c)
 
     # ---- bytes each decode launch had to read --------------------------------------
     # visible kept entries of (b, g) at position t: kept positions <= t - w
     zpre_c = zpre.view(B, ctx, nkv).to(torch.int64).cumsum(1)  # [B, ctx, nkv]
-    dec_ms = np.array([ev0[s].elapsed_time(ev1[s]) for s in range(warm, S)])
+    dec_ms = np.array([ev0[s].elapsed_time(ev1[s]) for s in range(warm + steps, S)])
     bytes_per = []
     zst_i = zst.to(torch.int64)
-    for s in range(warm, S):
+    for s in range(warm + steps, S):
         l = s % L
         t = ctx + s // L
         lim = t - w
@@ -220,7 +228,8 @@ def main():
                    "keep_target": list(wl.keep), "keep_measured": [round(float(x), 4) for x in kept_frac],
                    "page_size": P, "layer_caches_rotated": L,
                    "step": "spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"},
-        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel<128>", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "spkv_decode_attn (split-K pass + merge)",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "bytes_per_launch": float(bytes_per.mean()),
                      "launch_us_mean": round(float(dec_ms.mean() * 1e3), 2),

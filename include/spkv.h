@@ -186,9 +186,9 @@ size_t spkv_compact_ws_bytes(const spkv_cache *c, int32_t n_rows,
  *   out [batch, n_q_heads, head_dim] f32; lse [batch, n_q_heads] f32 or NULL
  *       (natural-log normaliser of each softmax row)
  *   scale: score multiplier (1/sqrt(head_dim) for Eq. 3)
- *   ws  at least spkv_decode_ws_bytes(c, n_q_heads) bytes; it must be
- *       zero-filled before its first use, and every call leaves it ready for
- *       the next (calls sharing one ws must not overlap).
+ *   ws  at least spkv_decode_ws_bytes(c, n_q_heads) bytes of scratch
+ *       (split-K partials); calls that share one ws must not overlap.
+ *   Launches two kernels: the split-K pass and the merge of its partials.
  * Supported: G in {1, 2, 4, 8, 16}.
  */
 int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q,

@@ -8,7 +8,7 @@
 // states, W1 rows), so lanes load 16-byte pieces straight from memory.  The
 // epilogue (bias, ReLU, second layer, sigmoid, threshold) runs from LDS in
 // the same kernel.  For a handful of rows (decode) d_model is split over
-// several workgroups; the last one to finish (device-scope counter) adds the
+// several workgroups that write partial sums; a second small kernel adds the
 // slices in a fixed order and runs the epilogue.
 // f32: a plain VALU kernel.
 #include "spkv_internal.h"
@@ -23,19 +23,31 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ inline float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // Second layer + sigmoid + threshold for `rows` rows whose activations
-// (after bias and ReLU) are in act[r * ld + j].
-__device__ void gate_epilogue(const GateArgs &a, const float *act, int ld, int64_t row0, int rows) {
+// (after bias and ReLU) are in act[r * ld + j].  W2 and b2 are staged in LDS
+// first (one coalesced pass), so the dot products never wait on memory.
+template <int HG>
+__device__ void gate_epilogue(const GateArgs &a, const float *act, int ld, int64_t row0, int rows,
+                              float *lds_w2 /* [n_kv][HG + 1] */) {
     const int nkv = a.n_kv;
+    for (int i = threadIdx.x; i < nkv * HG; i += blockDim.x) {
+        const int k = i / HG;
+        lds_w2[k * (HG + 1) + (i - k * HG)] = a.w2[i];
+    }
+    __syncthreads();
     for (int idx = threadIdx.x; idx < rows * nkv; idx += blockDim.x) {
         const int r = idx / nkv;
         const int k = idx - r * nkv;
         const int64_t row = row0 + r;
         if (row >= a.n_rows) continue;
-        const float *w2 = a.w2 + (int64_t)k * a.d_hidden;
+        const float *w2 = lds_w2 + k * (HG + 1);
         const float *ar = act + r * ld;
-        float acc = 0.f;
-        for (int j = 0; j < a.d_hidden; ++j) acc = fmaf(w2[j], ar[j], acc);
-        const float logit = acc + a.b2[k];
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 16
+        for (int j = 0; j < HG; j += 2) {
+            acc0 = fmaf(w2[j], ar[j], acc0);
+            acc1 = fmaf(w2[j + 1], ar[j + 1], acc1);
+        }
+        const float logit = (acc0 + acc1) + a.b2[k];
         const float u = sigmoid_f(logit);
         if (a.utility) a.utility[row * nkv + k] = u;
         a.keep[row * nkv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
@@ -55,7 +67,7 @@ __global__ void __launch_bounds__(NT) gate_bf16_kernel(GateArgs a) {
     constexpr int NTW = HG / 16 / WN;  // 16-wide unit tiles per wave
     static_assert(NTW >= 1, "d_hidden too small for this wave layout");
     __shared__ float act[BM][HG + 1];
-    __shared__ int last_flag;
+    __shared__ float lds_w2[16 * (HG + 1)];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -101,14 +113,13 @@ __global__ void __launch_bounds__(NT) gate_bf16_kernel(GateArgs a) {
             for (int r = 0; r < 4; ++r) act[wm * 16 + 4 * q4 + r][j] = relu_keep_nan(acc[n][r] + bias);
         }
         __syncthreads();
-        gate_epilogue(a, &act[0][0], HG + 1, row0, BM);
+        gate_epilogue<HG>(a, &act[0][0], HG + 1, row0, BM, lds_w2);
         return;
     }
 
-    // split d_model: write this slice's sums, the last slice finishes
+    // split d_model: write this slice's sums; gate_split_epilogue adds them
     const int n_tiles = gridDim.x;
     float *part = a.ws;  // [n_split][n_tiles * BM][HG]
-    int32_t *cnt = (int32_t *)(a.ws + (size_t)a.n_split * n_tiles * BM * HG);
     const size_t slab = (size_t)n_tiles * BM * HG;
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
@@ -119,23 +130,27 @@ __global__ void __launch_bounds__(NT) gate_bf16_kernel(GateArgs a) {
             part[split * slab + (size_t)rr * HG + j] = acc[n][r];
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last_flag = (atomicAdd(&cnt[blockIdx.x], 1) == a.n_split - 1);
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
+}
+
+// Sum of the d_model slices in slice order (deterministic), then bias, ReLU
+// and the epilogue.  One workgroup per row tile of the split launch.
+template <int BM, int HG>
+__global__ void __launch_bounds__(NT) gate_split_epilogue(GateArgs a) {
+    __shared__ float act[BM][HG + 1];
+    __shared__ float lds_w2[16 * (HG + 1)];
+    const size_t slab = (size_t)gridDim.x * BM * HG;
+    const float *part = a.ws;
     for (int idx = threadIdx.x; idx < BM * HG; idx += NT) {
         const int r = idx / HG;
         const int j = idx - r * HG;
         const size_t off = (size_t)(blockIdx.x * BM + r) * HG + j;
-        float s = 0.f;
-        for (int sp = 0; sp < a.n_split; ++sp) s += __builtin_nontemporal_load(part + sp * slab + off);
-        act[r][j] = relu_keep_nan(s + a.b1[j]);
+        float sum = 0.f;
+#pragma unroll 16
+        for (int sp = 0; sp < a.n_split; ++sp) sum += part[sp * slab + off];
+        act[r][j] = relu_keep_nan(sum + a.b1[j]);
     }
     __syncthreads();
-    if (threadIdx.x == 0) cnt[blockIdx.x] = 0;
-    gate_epilogue(a, &act[0][0], HG + 1, row0, BM);
+    gate_epilogue<HG>(a, &act[0][0], HG + 1, (int64_t)blockIdx.x * BM, BM, lds_w2);
 }
 
 // ---------------------------------------------------------------------------
@@ -163,7 +178,15 @@ __global__ void __launch_bounds__(NT) gate_valu_kernel(GateArgs a) {
         act[threadIdx.x] = relu_keep_nan(s + a.b1[threadIdx.x]);
     }
     __syncthreads();
-    gate_epilogue(a, act, 0, row, 1);
+    if (threadIdx.x < a.n_kv) {
+        const int k = threadIdx.x;
+        const float *w2 = a.w2 + (int64_t)k * hg;
+        float acc = 0.f;
+        for (int j = 0; j < hg; ++j) acc = fmaf(w2[j], act[j], acc);
+        const float u = sigmoid_f(acc + a.b2[k]);
+        if (a.utility) a.utility[row * a.n_kv + k] = u;
+        a.keep[row * a.n_kv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+    }
 }
 
 constexpr int SMALL_ROWS = 64;
@@ -189,17 +212,22 @@ size_t gate_ws_bytes(int d_model, int d_hidden, int dtype, int64_t n_rows) {
     if (split == 1 || !mfma_hidden(d_hidden)) return 0;
     const int bm = small_bm(d_hidden);
     const int64_t tiles = (n_rows + bm - 1) / bm;
-    return (size_t)split * tiles * bm * d_hidden * sizeof(float) + (size_t)tiles * sizeof(int32_t) + 256;
+    return (size_t)split * tiles * bm * d_hidden * sizeof(float);
+}
+
+template <int WM, int HG>
+static void launch_mfma_hg(const GateArgs &a, int tiles, hipStream_t s) {
+    hipLaunchKernelGGL((gate_bf16_kernel<WM, HG>), dim3(tiles, a.n_split), dim3(NT), 0, s, a);
+    if (a.n_split > 1) hipLaunchKernelGGL((gate_split_epilogue<16 * WM, HG>), dim3(tiles), dim3(NT), 0, s, a);
 }
 
 template <int WM>
 static void launch_mfma(const GateArgs &a, int tiles, hipStream_t s) {
-    const dim3 grid(tiles, a.n_split);
     switch (a.d_hidden) {
-    case 32: hipLaunchKernelGGL((gate_bf16_kernel<(WM < 2 ? 2 : WM), 32>), grid, dim3(NT), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((gate_bf16_kernel<WM, 64>), grid, dim3(NT), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((gate_bf16_kernel<WM, 128>), grid, dim3(NT), 0, s, a); break;
-    default: hipLaunchKernelGGL((gate_bf16_kernel<WM, 256>), grid, dim3(NT), 0, s, a); break;
+    case 32: launch_mfma_hg<(WM < 2 ? 2 : WM), 32>(a, tiles, s); break;
+    case 64: launch_mfma_hg<WM, 64>(a, tiles, s); break;
+    case 128: launch_mfma_hg<WM, 128>(a, tiles, s); break;
+    default: launch_mfma_hg<WM, 256>(a, tiles, s); break;
     }
 }
 
