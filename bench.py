@@ -1,33 +1,50 @@
 #!/usr/bin/env python3
-"""Benchmark of the SP-KV decode hot path on one MI355X.
+"""Benchmark of the SP-KV hot path on one MI355X.
 
-Workload (default ``decode_32k``): one Llama-3-8B-shaped attention layer
+Default workload ``decode_32k``: one Llama-3-8B-shaped attention layer
 (d_model 4096, 32 query / 8 key heads, head_dim 128, gate 4096 -> 128 -> 8),
 bf16, batch 8, 32768-token context, ~20 % of tokens kept per key head,
 window 128.  One step = the whole decode path for one new token of every
 sequence:
 
-    spkv_gate           8 hidden rows -> utilities and keep bits (Eq. 1-2)
+    spkv_gate           hidden rows -> utilities and keep bits (Eq. 1-2)
     spkv_compact_append keep bits + K/V -> persistent cache and window ring
-    spkv_decode_attn    32 query heads x 8 sequences over window + kept keys
+    spkv_decode_attn    every query head of every sequence over window + kept keys
 
-Inputs are synthetic (seeded), resident in HBM before timing starts.  The
-prefix (32768 tokens per sequence) is gated and compacted through the same
-calls during set-up.  Several independent layer caches are used in rotation
-so that one step's working set (~218 MB) cannot stay in the 256 MB Infinity
-Cache between its visits: the figures are HBM figures, as for a model whose
-every layer owns its own cache.
+Other workloads (``--workload``): ``decode_131k`` (batch 4, 131072 tokens,
+per-head keep 2-60 %), ``ragged_32`` (batch 32, contexts 4096-65536, 15 %,
+hidden states buffered: window append + attention every step, gate + kept
+append of all 32 x 128 buffered rows every 128 steps) and ``prefill_64k``
+(one step = chunked prefill of a 65536-token sequence in 16384-token chunks:
+gate, kept append, prefill attention, window append per chunk).
 
-Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the decode
-attention kernel): algorithmic bytes = visible kept + window entries x 512 B
-per launch, divided by the launch time measured with HIP events on the
-launch stream during the timed region.  ``cpu_baseline`` times the fp64
-oracle on a bounded sample of the same workload on the host cores.
+Inputs are synthetic (seeded) and resident in HBM before timing starts.
+Decode prefixes are gated and compacted through the same calls during set-up.
+Several independent layer caches are used in rotation so that one step's
+working set cannot stay in the 256 MB Infinity Cache between its visits: the
+figures are HBM figures, as for a model whose every layer owns its cache.
+
+Prints ONE JSON line.  ``roofline`` is for the dominant kernel: decode
+attention (algorithmic bytes = visible kept + window entries x 512 B per
+launch) or prefill attention (4 hd flops per visible (row, key) pair and
+query head), divided by the launch time measured with HIP events on the
+launch stream in a second pass over the same number of steps.  ``traffic``
+is read from the committed rocprofv3 counter summary for that kernel and
+workload when its recorded source hash matches the kernel source in this
+tree, else null.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
+of the same workload on the host cores.
+
+Profile summaries (no GPU needed):
+    python bench.py --summarize-stats DIR
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernel NAME --workload W
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import math
 import os
@@ -41,97 +58,229 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "gated-KV decode tokens/s + achieved HBM GB/s (% of peak), 8B shape 32K ctx"
+KERNEL_SOURCES = {
+    "decode_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_decode.hip",
+    "prefill_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_prefill.hip",
+    "gate_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_gate.hip",
+    "compact_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
+    "compact_small_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
+}
+CALIBRATION_BYTES = 1 << 30  # the plain copy: 1 GiB read + 1 GiB written
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=256)
-    p.add_argument("--warmup", type=int, default=16)
-    p.add_argument("--workload", default="decode_32k", choices=["decode_32k", "decode_131k"])
-    p.add_argument("--layers", type=int, default=4, help="layer caches used in rotation")
+    p.add_argument("--steps", type=int, default=None, help="timed steps (decode 256, prefill 4)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
+    p.add_argument("--workload", default="decode_32k",
+                   choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k"])
+    p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+                   help="also run a plain 1 GiB elementwise copy (for scaling HBM counters)")
+    p.add_argument("--summarize-stats", metavar="DIR")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--kernel", default="decode_bf16_kernel")
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; the path shards by sequence or key head "
-                                   "(see the design notes) but no multi-GPU run is provided",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+# ----------------------------------------------------------------------------
+# profile summaries and the stored traffic figure
+# ----------------------------------------------------------------------------
 
-    import torch
-    from learned_kv_cache_sp_amd import inputs, spkv
+def _short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    n = n.replace("spkv::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            n = n[:i]
+            break
+    return n if len(n) <= 72 else n[:69] + "..."
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    dev = "cuda"
-    wl = inputs.WORKLOADS[args.workload]
-    B, d, nq, nkv, hd, w = wl.batch, wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.window
-    ctx = wl.context
-    P = args.page_size
-    L = max(1, args.layers)
-    steps, warm = args.steps, args.warmup
-    S = warm + 2 * steps  # warm-up, the timed pass, the per-launch timing pass
-    per_layer_steps = (S + L - 1) // L + 1
-    scale = 1.0 / math.sqrt(hd)
-    G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
-    seed = wl.seed
 
-    # ---- weights; output bias placed on a calibration sample -----------------
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def summarize_stats(d: str) -> str:
+    rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"{'kernel':72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows[:16]:
+        out.append(f"{_short(r['Name']):72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    return "\n".join(out)
+
+
+def _source_hash(kernel: str) -> str:
+    path = os.path.join(ROOT, KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def _pmc_means(d: str, counter: str):
+    """Per kernel: (dispatches, mean counter value), and the calibration copy's value."""
+    per, calib = {}, []
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        if "neg_kernel" in r["Kernel_Name"]:
+            calib.append(v)
+            continue
+        per.setdefault(_short(r["Kernel_Name"]), []).append(v)
+    return {k: (len(v), float(np.mean(v))) for k, v in per.items()}, (max(calib) if calib else None)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, workload: str) -> str:
+    f_per, f_cal = _pmc_means(fetch_dir, "FETCH_SIZE")
+    w_per, w_cal = _pmc_means(write_dir, "WRITE_SIZE")
+    if f_cal is None or w_cal is None:
+        raise SystemExit("the calibration copy (run with --copy-calibration) is missing")
+    f_fac = CALIBRATION_BYTES / (f_cal * 1024.0)
+    w_fac = CALIBRATION_BYTES / (w_cal * 1024.0)
+    out = [f"calibration copy of {CALIBRATION_BYTES} B: FETCH_SIZE {f_cal:.0f} KiB -> factor {f_fac:.4f}; "
+           f"WRITE_SIZE {w_cal:.0f} KiB -> factor {w_fac:.4f}",
+           f"{'kernel':72s} {'n':>4s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'scaled_MB':>10s}"]
+    for k in sorted(set(f_per) | set(w_per)):
+        if not any(x in k for x in ("gate", "compact", "decode", "prefill", "cache_reset")):
+            continue
+        nf, fv = f_per.get(k, (0, 0.0))
+        _, wv = w_per.get(k, (0, 0.0))
+        out.append(f"{k:72s} {nf:4d} {fv:12.1f} {wv:12.1f} {(fv * f_fac + wv * w_fac) * 1024 / 1e6:10.2f}")
+    hits = [k for k in f_per if k.startswith(kernel)]
+    if hits:
+        k = max(hits, key=lambda x: f_per[x][0])
+        wv = w_per.get(k, (0, 0.0))[1]
+        rec = {"kernel": k, "workload": workload,
+               "fetch_kib": round(f_per[k][1], 1), "write_kib": round(wv, 1),
+               "fetch_factor": round(f_fac, 5), "write_factor": round(w_fac, 5),
+               "bytes_per_launch": round((f_per[k][1] * f_fac + wv * w_fac) * 1024),
+               "source": KERNEL_SOURCES[kernel], "source_sha256": _source_hash(kernel)}
+        out.append("traffic_json: " + json.dumps(rec))
+    return "\n".join(out)
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the kernel source in this tree; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json: "):
+            rec = json.loads(line[len("traffic_json: "):])
+            if rec.get("workload") == workload and rec.get("source_sha256") == _source_hash(kernel):
+                return float(rec["bytes_per_launch"])
+    return None
+
+
+# ----------------------------------------------------------------------------
+# shared set-up
+# ----------------------------------------------------------------------------
+
+def gate_weights(wl, torch, inputs, spkv, dev):
+    """Gate weights with the output bias placed for the workload's keep rates on
+    65536 device-drawn calibration rows (evaluated by the gate itself)."""
     wts = inputs.layer_weights(wl)
     gw = spkv.GateWeights(torch.from_numpy(wts["W1"]).to(dev).to(torch.bfloat16),
                           torch.from_numpy(wts["b1"]).to(dev), torch.from_numpy(wts["W2"]).to(dev),
-                          torch.zeros(nkv, dtype=torch.float32, device=dev))
-    Hc = inputs.device_normal((65536, d), seed, inputs.STREAM_CAL, torch.bfloat16)
+                          torch.zeros(wl.n_kv, dtype=torch.float32, device=dev))
+    Hc = inputs.device_normal((65536, wl.d_model), wl.seed, inputs.STREAM_CAL, torch.bfloat16)
     u_cal, _ = spkv.spkv_gate(gw, Hc, wl.tau)
     u64 = u_cal.double().clamp(1e-300, 1 - 1e-16)
     logit = (torch.log(u64) - torch.log1p(-u64)).cpu().numpy()
     gw.b2.copy_(torch.from_numpy(inputs.place_output_bias(logit, wl.keep, wl.tau)).to(dev))
-    del Hc, u_cal, u64
+    return gw
 
-    # ---- prefix: gate + compaction of ctx tokens per sequence ----------------
-    n_pre = B * ctx
-    exp_pages = [int(math.ceil((ctx + per_layer_steps) * r / P) * 1.25) + 8 for r in wl.keep]
-    max_pages = int(math.ceil((ctx + per_layer_steps) / P)) + 2
-    n_pages = B * sum(min(max_pages, e) for e in exp_pages)
+
+def _stats_us(ms):
+    ms = np.asarray(ms)
+    return {"mean": round(float(ms.mean() * 1e3), 2),
+            "p10_p90": [round(float(np.percentile(ms, 10) * 1e3), 2),
+                        round(float(np.percentile(ms, 90) * 1e3), 2)]}
+
+
+# ----------------------------------------------------------------------------
+# decode workloads
+# ----------------------------------------------------------------------------
+
+def bench_decode(args, wl):
+    import torch
+    from learned_kv_cache_sp_amd import inputs, spkv
+
+    dev = "cuda"
+    B, d, nq, nkv, hd, w = wl.batch, wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.window
+    ctxs = [int(c) for c in inputs.ragged_contexts(wl)]
+    P, L = args.page_size, max(1, args.layers)
+    steps = 256 if args.steps is None else args.steps
+    warm = 16 if args.warmup is None else args.warmup
+    S = warm + 2 * steps                 # warm-up, the timed pass, the per-launch timing pass
+    buf = wl.buffer if wl.buffer > 0 else 1
+    n_loc = -(-S // L)                   # steps per layer cache
+    n_fl = -(-n_loc // buf)              # gate groups per layer cache
+    scale = 1.0 / math.sqrt(hd)
+    G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
+    seed = wl.seed
+
+    gw = gate_weights(wl, torch, inputs, spkv, dev)
+
+    # ---- prefix: gate + compaction of every sequence's context ---------------
+    offs = np.concatenate([[0], np.cumsum(ctxs)]).astype(np.int64)
+    n_pre = int(offs[-1])
+    grow = n_fl * buf
+    max_pages = int(math.ceil((max(ctxs) + grow) / P)) + 2
+    n_pages = sum(min(max_pages, int(math.ceil((c + grow) * r / P * 1.25)) + 8) for c in ctxs for r in wl.keep)
     caches = [spkv.Cache(B, nkv, hd, w, P, n_pages, max_pages, torch.bfloat16) for _ in range(L)]
     zpre = torch.empty((n_pre, nkv), dtype=torch.uint8, device=dev)
-    ro = torch.arange(0, B + 1, dtype=torch.int32, device=dev) * ctx
+    ro_pre = torch.tensor(offs, dtype=torch.int32, device=dev)
     pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
     CH = 65536
     for r0 in range(0, n_pre, CH):
         Hp = inputs.device_normal((min(CH, n_pre - r0), d), seed, 1000 + r0 // CH, torch.bfloat16)
         spkv.spkv_gate(gw, Hp, wl.tau, keep=zpre[r0:r0 + Hp.shape[0]])
-    del Hp
+        del Hp
     Kp = inputs.device_normal((n_pre, nkv, hd), seed, inputs.STREAM_K, torch.bfloat16)
     Vp = inputs.device_normal((n_pre, nkv, hd), seed, inputs.STREAM_V, torch.bfloat16)
     for c in caches:
-        spkv.spkv_compact_append(c, zpre, Kp, Vp, ro, pos0, ctx, G_ | W_)
+        spkv.spkv_compact_append(c, zpre, Kp, Vp, ro_pre, pos0, max(ctxs), G_ | W_)
     torch.cuda.synchronize()
     for c in caches:
         spkv.spkv_cache_check(c)
     del Kp, Vp
     kept_frac = zpre.float().mean(0).cpu().numpy()
 
-    # ---- per-step inputs --------------------------------------------------------
-    Hs = inputs.device_normal((S, B, d), seed, 2001, torch.bfloat16)
-    Qs = inputs.device_normal((S, B, nq, hd), seed, 2002, torch.bfloat16)
-    Ks = inputs.device_normal((S, B, nkv, hd), seed, 2003, torch.bfloat16)
-    Vs = inputs.device_normal((S, B, nkv, hd), seed, 2004, torch.bfloat16)
-    tpos = torch.tensor([[ctx + s // L] * B for s in range(S)], dtype=torch.int32, device=dev)
+    # ---- per-step inputs, laid out per layer cache and gate group -------------
+    # a gate group holds `buf` consecutive tokens of every sequence, sequence-major
+    Hl = inputs.device_normal((L, n_fl, B, buf, d), seed, 2001, torch.bfloat16)
+    Ql = inputs.device_normal((L, n_loc, B, nq, hd), seed, 2002, torch.bfloat16)
+    Kl = inputs.device_normal((L, n_fl, B, buf, nkv, hd), seed, 2003, torch.bfloat16)
+    Vl = inputs.device_normal((L, n_fl, B, buf, nkv, hd), seed, 2004, torch.bfloat16)
+    ctx_t = torch.tensor(ctxs, dtype=torch.int32, device=dev)
+    tpos = (ctx_t[None, :] + torch.arange(n_loc, dtype=torch.int32, device=dev)[:, None]).contiguous()
+    gpos = (ctx_t[None, :] + buf * torch.arange(n_fl, dtype=torch.int32, device=dev)[:, None]).contiguous()
+    zl = torch.zeros((L, n_fl, B, buf, nkv), dtype=torch.uint8, device=dev)
+    ul = torch.zeros((L, n_fl, B, buf, nkv), dtype=torch.float32, device=dev)
     ro1 = torch.arange(0, B + 1, dtype=torch.int32, device=dev)
-    zst = torch.empty((S, B, nkv), dtype=torch.uint8, device=dev)
-    ust = torch.empty((S, B, nkv), dtype=torch.float32, device=dev)
+    robuf = (ro1 * buf).contiguous()
     out = torch.empty((B, nq, hd), dtype=torch.float32, device=dev)
     lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
-    gate_ws = spkv.workspace(spkv.spkv_gate_ws_bytes(gw, B))
+    gate_ws = spkv.workspace(spkv.spkv_gate_ws_bytes(gw, B * buf))
+    comp_ws = spkv.workspace(spkv.spkv_compact_ws_bytes(caches[0], B * buf, buf))
     dec_ws = [spkv.workspace(spkv.spkv_decode_ws_bytes(c, nq)) for c in caches]
 
     # pre-marshalled raw calls (keeps host overhead far below the GPU time)
@@ -140,30 +289,52 @@ def main():
     sp = ctypes.c_void_p(stream.cuda_stream)
     gdesc = gw.desc()
     cdescs = [c.desc() for c in caches]
-    gws_p, gws_n = (gate_ws.data_ptr(), gate_ws.numel() * 4) if gate_ws is not None else (None, 0)
 
-    def nb(t):
-        return 0 if t is None else t.numel() * t.element_size()
+    def pn(t):
+        return (None, 0) if t is None else (t.data_ptr(), t.numel() * t.element_size())
 
-    def step(s, timed_decode=False):
-        l = s % L
-        rc = lib.spkv_gate(ctypes.byref(gdesc), Hs[s].data_ptr(), B, d, wl.tau, ust[s].data_ptr(),
-                           zst[s].data_ptr(), gws_p, gws_n, sp)
-        rc |= lib.spkv_compact_append(ctypes.byref(cdescs[l]), zst[s].data_ptr(), Ks[s].data_ptr(),
-                                      Vs[s].data_ptr(), nkv * hd, ro1.data_ptr(), tpos[s].data_ptr(), B, 1,
-                                      G_ | W_, None, None, 0, sp)
-        if timed_decode:
-            ev0[s].record(stream)
-        rc |= lib.spkv_decode_attn(ctypes.byref(cdescs[l]), nq, Qs[s].data_ptr(), nq * hd, tpos[s].data_ptr(),
-                                   scale, out.data_ptr(), lse.data_ptr(), dec_ws[l].data_ptr(),
-                                   nb(dec_ws[l]), sp)
-        if timed_decode:
-            ev1[s].record(stream)
+    gws, cws = pn(gate_ws), pn(comp_ws)
+    dws = [pn(x) for x in dec_ws]
+    ld_step = buf * nkv * hd
+    ev = {}
+
+    def record(key):
+        if key is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev.setdefault(key, []).append(e)
+
+    def step(s, timing=False):
+        l, i = s % L, s // L
+        f, j = i // buf, i % buf
+        cd = ctypes.byref(cdescs[l])
+        rc = 0
+        if buf == 1:
+            rc |= lib.spkv_gate(ctypes.byref(gdesc), Hl[l, f].data_ptr(), B, d, wl.tau, ul[l, f].data_ptr(),
+                                zl[l, f].data_ptr(), gws[0], gws[1], sp)
+            rc |= lib.spkv_compact_append(cd, zl[l, f].data_ptr(), Kl[l, f].data_ptr(), Vl[l, f].data_ptr(),
+                                          nkv * hd, ro1.data_ptr(), tpos[i].data_ptr(), B, 1, G_ | W_, None,
+                                          cws[0], cws[1], sp)
+        else:
+            rc |= lib.spkv_compact_append(cd, None, Kl[l, f, 0, j].data_ptr(), Vl[l, f, 0, j].data_ptr(),
+                                          ld_step, ro1.data_ptr(), tpos[i].data_ptr(), B, 1, W_, None,
+                                          cws[0], cws[1], sp)
+        record("d0" if timing else None)
+        rc |= lib.spkv_decode_attn(cd, nq, Ql[l, i].data_ptr(), nq * hd, tpos[i].data_ptr(), scale,
+                                   out.data_ptr(), lse.data_ptr(), dws[l][0], dws[l][1], sp)
+        record("d1" if timing else None)
+        if buf > 1 and j == buf - 1:
+            # the buffer of this layer cache is full: gate all B x buf rows, append the kept ones
+            record("f0" if timing else None)
+            rc |= lib.spkv_gate(ctypes.byref(gdesc), Hl[l, f].data_ptr(), B * buf, d, wl.tau,
+                                ul[l, f].data_ptr(), zl[l, f].data_ptr(), gws[0], gws[1], sp)
+            rc |= lib.spkv_compact_append(cd, zl[l, f].data_ptr(), Kl[l, f].data_ptr(), Vl[l, f].data_ptr(),
+                                          nkv * hd, robuf.data_ptr(), gpos[f].data_ptr(), B * buf, buf, G_,
+                                          None, cws[0], cws[1], sp)
+            record("f1" if timing else None)
         if rc:
             raise RuntimeError(lib.spkv_last_error().decode())
 
-    ev0 = {s: torch.cuda.Event(enable_timing=True) for s in range(warm + steps, S)}
-    ev1 = {s: torch.cuda.Event(enable_timing=True) for s in range(warm + steps, S)}
     for s in range(warm):
         step(s)
     torch.cuda.synchronize()
@@ -178,94 +349,235 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e_start.elapsed_time(e_end)
-    # pass 2: the same K steps again with events around every decode launch
-    # (event records add gaps to the stream, so they stay out of pass 1)
+    # pass 2: the same number of steps again with events around every decode
+    # launch (event records add gaps to the stream, so they stay out of pass 1)
     for s in range(warm + steps, S):
-        step(s, timed_decode=True)
+        step(s, timing=True)
     torch.cuda.synchronize()
     for c in caches:
         spkv.spkv_cache_check(c)
 
-    # ---- bytes each decode launch had to read --------------------------------------
-    # visible kept entries of (b, g) at position t: kept positions <= t - w
-    zpre_c = zpre.view(B, ctx, nkv).to(torch.int64).cumsum(1)  # [B, ctx, nkv]
-    dec_ms = np.array([ev0[s].elapsed_time(ev1[s]) for s in range(warm + steps, S)])
+    # ---- bytes each decode launch had to read --------------------------------
+    # visible entries of (b, g) at position t: window min(t+1, w) + kept positions <= t - w
+    zpre_h = zpre.cpu().numpy().astype(np.int64)
+    Epre = np.vstack([np.zeros((1, nkv), np.int64), np.cumsum(zpre_h, 0)])
+    zl_h = zl.cpu().numpy().astype(np.int64)              # [L, n_fl, B, buf, nkv]
+    Estep = np.zeros((L, B, n_fl * buf + 1, nkv), np.int64)
+    for l in range(L):
+        for b in range(B):
+            Estep[l, b, 1:] = np.cumsum(zl_h[l, :, b].reshape(n_fl * buf, nkv), 0)
     bytes_per = []
-    zst_i = zst.to(torch.int64)
     for s in range(warm + steps, S):
-        l = s % L
-        t = ctx + s // L
-        lim = t - w
-        vis = zpre_c[:, min(lim, ctx - 1), :].clone() if lim >= 0 else torch.zeros((B, nkv), dtype=torch.int64,
-                                                                                   device=dev)
-        # kept step tokens of this layer with position <= t - w
-        own = [x for x in range(l, s + 1, L) if ctx + x // L <= lim]
-        if own:
-            vis += zst_i[own].sum(0)
-        win = min(t + 1, w)
-        bytes_per.append(float((vis.sum().item() + B * nkv * win) * 2 * hd * 2))
+        l, i = s % L, s // L
+        tot = 0
+        for b in range(B):
+            t = ctxs[b] + i
+            p = t - w
+            if p >= 0:
+                q = min(p, ctxs[b] - 1)
+                vis = Epre[offs[b] + q + 1] - Epre[offs[b]]
+                if p >= ctxs[b]:
+                    vis = vis + Estep[l, b, p - ctxs[b] + 1]
+                tot += int(vis.sum())
+            tot += nkv * min(t + 1, w)
+        bytes_per.append(float(tot * 2 * hd * 2))
     bytes_per = np.array(bytes_per)
+    dec_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["d0"], ev["d1"])])
     achieved = float(bytes_per.mean() / (dec_ms.mean() * 1e-3) / 1e9)
 
-    ms_per_step = gpu_ms / steps
-    tok_s = B * steps / (gpu_ms * 1e-3)
-
     res = {
-        "metric": "gated-KV decode tokens/s + achieved HBM GB/s (% of peak), 8B shape 32K ctx",
-        "value": round(tok_s, 1),
+        "metric": METRIC,
+        "value": round(B * steps / (gpu_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warm,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(gpu_ms / steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "context": ctx, "d_model": d, "n_q_heads": nq,
-                   "n_kv_heads": nkv, "head_dim": hd, "window": w, "gate": f"{d}->{wl.d_hidden}->{nkv}",
-                   "keep_target": list(wl.keep), "keep_measured": [round(float(x), 4) for x in kept_frac],
-                   "page_size": P, "layer_caches_rotated": L,
-                   "step": "spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"},
-        "roofline": {"bound": "hbm", "kernel": "spkv_decode_attn (split-K pass + merge)",
-                     "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": float(bytes_per.mean()),
-                     "launch_us_mean": round(float(dec_ms.mean() * 1e3), 2),
-                     "launch_us_p10_p90": [round(float(np.percentile(dec_ms, 10) * 1e3), 2),
-                                           round(float(np.percentile(dec_ms, 90) * 1e3), 2)]},
+        "config": {"workload": wl.name, "batch": B,
+                   "context": ctxs[0] if not wl.ragged else {"min": min(ctxs), "max": max(ctxs),
+                                                             "mean": round(float(np.mean(ctxs)), 1)},
+                   "d_model": d, "n_q_heads": nq, "n_kv_heads": nkv, "head_dim": hd, "window": w,
+                   "gate": f"{d}->{wl.d_hidden}->{nkv}", "keep_target": list(wl.keep),
+                   "keep_measured": [round(float(x), 4) for x in kept_frac],
+                   "page_size": P, "layer_caches_rotated": L, "gate_buffer": buf,
+                   "step": ("spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"
+                            if buf == 1 else
+                            f"spkv_compact_append(window) + spkv_decode_attn every step; spkv_gate + "
+                            f"spkv_compact_append(kept) of {B}x{buf} buffered rows when a buffer fills")},
+        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel (spkv_decode_attn)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic("decode_bf16_kernel", wl.name),
+                     "bytes_per_launch": float(bytes_per.mean()),
+                     "launch_us": _stats_us(dec_ms)},
         "host_wall_s": round(wall, 4),
     }
-
-    if args.copy_calibration:
-        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
-        b_ = torch.empty_like(a)
-        b_.copy_(a)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = a.numel() * 2
-
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-    print(json.dumps(res))
+    if "f0" in ev:
+        fl_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["f0"], ev["f1"])])
+        res["buffer_flush"] = {"rows": B * buf, "every_n_steps_per_layer": buf, "us": _stats_us(fl_ms),
+                               "in_timed_pass": sum(1 for s in range(warm, warm + steps)
+                                                    if (s // L) % buf == buf - 1)}
+    return res
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
-    """fp64 oracle on a bounded sample of the same decode step, on the host cores.
+# ----------------------------------------------------------------------------
+# chunked prefill
+# ----------------------------------------------------------------------------
 
-    Sample: decode steps of 2 of the sequences at the workload's context: the
-    oracle gate for each new token and the oracle attention of all query
-    heads, over a seeded keep mask with the workload's keep rates.  Steps are
-    taken until about `budget_s` seconds have passed (at least 2)."""
+def bench_prefill(args, wl):
+    import torch
+    from learned_kv_cache_sp_amd import inputs, spkv
+
+    dev = "cuda"
+    d, nq, nkv, hd, w = wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.window
+    T, CH, G = wl.context, wl.chunk, wl.group
+    P = args.page_size
+    steps = 4 if args.steps is None else args.steps
+    warm = 1 if args.warmup is None else args.warmup
+    scale = 1.0 / math.sqrt(hd)
+    G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
+    seed = wl.seed
+
+    gw = gate_weights(wl, torch, inputs, spkv, dev)
+    H = inputs.device_normal((T, d), seed, inputs.STREAM_H, torch.bfloat16)
+    Q = inputs.device_normal((T, nq, hd), seed, inputs.STREAM_Q, torch.bfloat16)
+    K = inputs.device_normal((T, nkv, hd), seed, inputs.STREAM_K, torch.bfloat16)
+    V = inputs.device_normal((T, nkv, hd), seed, inputs.STREAM_V, torch.bfloat16)
+    per = -(-T // P) + 2
+    cache = spkv.Cache(1, nkv, hd, w, P, nkv * per, per, torch.bfloat16)
+    z = torch.zeros((T, nkv), dtype=torch.uint8, device=dev)
+    u = torch.zeros((T, nkv), dtype=torch.float32, device=dev)
+    out = torch.empty((CH, nq, hd), dtype=torch.float32, device=dev)
+    lse = torch.empty((CH, nq), dtype=torch.float32, device=dev)
+    chunks = [(c0, min(CH, T - c0)) for c0 in range(0, T, CH)]
+    ro = [torch.tensor([0, n], dtype=torch.int32, device=dev) for _, n in chunks]
+    p0 = [torch.tensor([c0], dtype=torch.int32, device=dev) for c0, _ in chunks]
+    gate_ws = spkv.workspace(spkv.spkv_gate_ws_bytes(gw, CH))
+    comp_ws = spkv.workspace(spkv.spkv_compact_ws_bytes(cache, CH, CH))
+    pre_ws = spkv.workspace(spkv.spkv_prefill_ws_bytes(cache, nq, CH))
+    stream = torch.cuda.current_stream()
+    ev = {}
+
+    def record(key):
+        if key is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev.setdefault(key, []).append(e)
+
+    def step(timing=False):
+        spkv.spkv_cache_reset(cache)
+        for k, (c0, n) in enumerate(chunks):
+            record("g0" if timing else None)
+            spkv.spkv_gate(gw, H[c0:c0 + n], wl.tau, utility=u[c0:c0 + n], keep=z[c0:c0 + n], ws=gate_ws)
+            record("c0" if timing else None)
+            spkv.spkv_compact_append(cache, z[c0:c0 + n], K[c0:c0 + n], V[c0:c0 + n], ro[k], p0[k], n, G_,
+                                     ws=comp_ws)
+            record("a0" if timing else None)
+            spkv.spkv_prefill_attn(cache, 0, Q[c0:c0 + n], K[c0:c0 + n], V[c0:c0 + n], c0, scale,
+                                   out=out[:n], lse=lse[:n], ws=pre_ws)
+            record("a1" if timing else None)
+            spkv.spkv_compact_append(cache, None, K[c0:c0 + n], V[c0:c0 + n], ro[k], p0[k], n, W_, ws=comp_ws)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for _ in range(steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e_start.elapsed_time(e_end)
+    for _ in range(steps):
+        step(timing=True)
+    torch.cuda.synchronize()
+    spkv.spkv_cache_check(cache)
+
+    # flops of each prefill launch: 4 hd per visible (row, key) pair and query head
+    zh = z.cpu().numpy().astype(np.int64)
+    E = np.vstack([np.zeros((1, nkv), np.int64), np.cumsum(zh, 0)])
+    t = np.arange(T)
+    win = np.minimum(t + 1, w).astype(np.int64)
+    kept = np.where((t - w)[:, None] >= 0, E[np.clip(t - w + 1, 0, T)], 0)      # [T, nkv]
+    vis = win[:, None] + kept
+    flops = np.array([4.0 * hd * G * float(vis[c0:c0 + n].sum()) for c0, n in chunks])
+    nc = len(chunks)
+    a_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["a0"], ev["a1"])])
+    g_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["g0"], ev["c0"])])
+    c_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["c0"], ev["a0"])])
+    fl = np.tile(flops, steps)
+    achieved = float((fl / (a_ms * 1e-3)).mean() / 1e12)
+    kept_rows = zh.sum(0)
+    res = {
+        "metric": "chunked-prefill tokens/s (gate + compaction + masked attention), 8B shape 64K",
+        "value": round(T * steps / (gpu_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(gpu_ms / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": 1, "tokens": T, "chunk": CH, "d_model": d, "n_q_heads": nq,
+                   "n_kv_heads": nkv, "head_dim": hd, "window": w, "gate": f"{d}->{wl.d_hidden}->{nkv}",
+                   "keep_target": list(wl.keep),
+                   "keep_measured": [round(float(x), 4) for x in kept_rows / T], "page_size": P,
+                   "step": "per chunk: spkv_gate, spkv_compact_append(kept), spkv_prefill_attn, "
+                           "spkv_compact_append(window)"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (spkv_prefill_attn)",
+                     "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic("prefill_bf16_kernel", wl.name),
+                     "flops_per_launch": float(flops.mean()), "launch_us": _stats_us(a_ms)},
+        "components_per_chunk": {
+            "gate": {"us": _stats_us(g_ms), "hbm_GBs": round(float((CH * d * 2 + wl.d_hidden * d * 2)
+                                                                   / (g_ms.mean() * 1e-3) / 1e9), 1),
+                     "TFLOPs": round(float(2.0 * CH * d * wl.d_hidden / (g_ms.mean() * 1e-3) / 1e12), 1)},
+            "compaction": {"us": _stats_us(c_ms),
+                           "hbm_GBs": round(float((2 * kept_rows.sum() / nc * 2 * hd * 2 + CH * nkv)
+                                                  / (c_ms.mean() * 1e-3) / 1e9), 1)},
+        },
+        "host_wall_s": round(wall, 4),
+    }
+    return res
+
+
+# ----------------------------------------------------------------------------
+# the oracle on the host cores
+# ----------------------------------------------------------------------------
+
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def cpu_baseline_decode(wl, budget_s: float) -> dict:
+    """fp64 oracle on a bounded sample of the same decode steps, on the host cores.
+
+    Sample: decode steps of 2 of the sequences at their contexts: the oracle
+    gate of each new token and the oracle attention of all query heads over a
+    seeded keep mask with the workload's keep rates.  Steps are taken until
+    about `budget_s` seconds have passed (at least 2)."""
     import oracle
     from learned_kv_cache_sp_amd import inputs
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    n_seq, max_steps = 2, 256
-    T = wl.context + max_steps
+    threads = _threads()
+    ctxs = [int(c) for c in inputs.ragged_contexts(wl)][:2]
+    max_steps = 256
     w = inputs.layer_weights(wl)
     work = []
-    for b in range(n_seq):
+    for b, ctx in enumerate(ctxs):
+        T = ctx + max_steps
         tok = {
             "Q": inputs.normal((max_steps, wl.n_q, wl.head_dim), wl.seed, 3001, b, dtype=wl.dtype),
             "K": inputs.normal((T, wl.n_kv, wl.head_dim), wl.seed, 3002, b, dtype=wl.dtype),
@@ -273,22 +585,87 @@ def cpu_baseline(wl, budget_s: float) -> dict:
             "H": inputs.normal((max_steps, wl.d_model), wl.seed, 3004, b, dtype=wl.dtype),
         }
         z = inputs.bernoulli_mask(T, wl.keep, wl.seed, 3005, b)
-        work.append((tok, z))
+        work.append((ctx, tok, z))
     n_tok = 0
     t0 = time.perf_counter()
     for i in range(max_steps):
-        for tok, z in work:
-            t = wl.context + i
+        for ctx, tok, z in work:
             oracle.gate(tok["H"][i:i + 1], w["W1"], w["b1"], w["W2"], w["b2"], wl.tau, threads=threads)
-            oracle.attention(tok["Q"][i:i + 1], [t], tok["K"], tok["V"], z, wl.window, threads=threads)
+            oracle.attention(tok["Q"][i:i + 1], [ctx + i], tok["K"], tok["V"], z, wl.window, threads=threads)
             n_tok += 1
         if time.perf_counter() - t0 > budget_s and i >= 1:
             break
     dt = time.perf_counter() - t0
     return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_tok} sequence-steps ({n_seq} sequences) of {wl.name} decode at context "
-                      f"{wl.context}: oracle gate of the new token + oracle attention of all {wl.n_q} "
-                      f"query heads over a seeded mask with the workload's keep rates; {dt:.1f} s"}
+            "sample": f"{n_tok} sequence-steps of {wl.name} decode at contexts {ctxs}: oracle gate of "
+                      f"the new token + oracle attention of all {wl.n_q} query heads over a seeded mask "
+                      f"with the workload's keep rates; {dt:.1f} s"}
+
+
+def cpu_baseline_prefill(wl, budget_s: float) -> dict:
+    """fp64 oracle on rows drawn uniformly from the 65536-token sequence: the
+    gate of the row and the attention of all its query heads (the mean cost per
+    token of the whole prefill), until about `budget_s` seconds have passed."""
+    import oracle
+    from learned_kv_cache_sp_amd import inputs
+
+    threads = _threads()
+    T = wl.context
+    w = inputs.layer_weights(wl)
+    K = inputs.normal((T, wl.n_kv, wl.head_dim), wl.seed, 3102, dtype=wl.dtype)
+    V = inputs.normal((T, wl.n_kv, wl.head_dim), wl.seed, 3103, dtype=wl.dtype)
+    z = inputs.bernoulli_mask(T, wl.keep, wl.seed, 3105)
+    rows = inputs.rng(wl.seed, 3106).integers(0, T, 4096)
+    Q = inputs.normal((len(rows), wl.n_q, wl.head_dim), wl.seed, 3101, dtype=wl.dtype)
+    H = inputs.normal((len(rows), wl.d_model), wl.seed, 3104, dtype=wl.dtype)
+    n, t0 = 0, time.perf_counter()
+    while n < len(rows):
+        r = slice(n, n + 8)
+        oracle.gate(H[r], w["W1"], w["b1"], w["W2"], w["b2"], wl.tau, threads=threads)
+        oracle.attention(Q[r], rows[r], K, V, z, wl.window, threads=threads)
+        n += len(rows[r])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} rows drawn uniformly from the {T}-token sequence: oracle gate + oracle attention "
+                      f"of all {wl.n_q} query heads over a seeded mask with keep {wl.keep[0]}; {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.kernel, args.workload))
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "one GPU only: this benchmark measures the path on one MI355X; "
+                                   "more than one GPU is not supported", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from learned_kv_cache_sp_amd import inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    wl = inputs.WORKLOADS[args.workload]
+    res = bench_prefill(args, wl) if wl.chunk else bench_decode(args, wl)
+
+    if args.copy_calibration:
+        a = torch.zeros(CALIBRATION_BYTES // 2, dtype=torch.int16, device="cuda")
+        b_ = torch.empty_like(a)
+        torch.neg(a, out=b_)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = CALIBRATION_BYTES
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, args.cpu_budget)
+    print(json.dumps(res))
 
 
 if __name__ == "__main__":

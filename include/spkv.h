@@ -180,15 +180,24 @@ size_t spkv_compact_ws_bytes(const spkv_cache *c, int32_t n_rows,
  *   (G = n_q_heads / n_kv; contiguous groups) and attends over
  *     window: positions max(0, t-w+1) .. t, read from the ring, and
  *     global: cached entries of (b, g) with position <= t - w.
- *   Precondition: position t[b] (and the w-1 before it) were WINDOW-appended.
+ *   Preconditions: position t[b] (and the w-1 before it) were WINDOW-appended,
+ *   and no entry of (b, g) has a position > t[b] (appends come in token
+ *   order), so only the last `window` entries can fall inside the window.
  *   q   [batch, n_q_heads, head_dim] dtype (row b at q + b*ld_q)
  *   t   [batch] int32 device array
  *   out [batch, n_q_heads, head_dim] f32; lse [batch, n_q_heads] f32 or NULL
  *       (natural-log normaliser of each softmax row)
  *   scale: score multiplier (1/sqrt(head_dim) for Eq. 3)
  *   ws  at least spkv_decode_ws_bytes(c, n_q_heads) bytes of scratch
- *       (split-K partials); calls that share one ws must not overlap.
- *   Launches two kernels: the split-K pass and the merge of its partials.
+ *       (0 for f32 caches).  Its head holds one arrival counter per (b, g)
+ *       and the rest holds split-K partials.  The counters must be zero
+ *       before the first call that uses ws (zero-fill it once after
+ *       allocation); every call leaves them at zero again.  Calls that share
+ *       one ws must not overlap (queue them on one stream).
+ *   Launches one kernel.  bf16: a persistent grid (compute units x resident
+ *   workgroups) splits the concatenated per-(b, g) key lists evenly; the
+ *   last workgroup to finish a (b, g) merges its partials in a fixed order,
+ *   so results are deterministic.  f32: one wavefront per (b, query head).
  * Supported: G in {1, 2, 4, 8, 16}.
  */
 int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q,
