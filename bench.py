@@ -229,8 +229,11 @@ def bench_decode(args, wl):
     P, L = args.page_size, max(1, args.layers)
     steps = 256 if args.steps is None else args.steps
     warm = 16 if args.warmup is None else args.warmup
-    S = warm + 2 * steps                 # warm-up, the timed pass, the per-launch timing pass
     buf = wl.buffer if wl.buffer > 0 else 1
+    if buf > 1:
+        # whole buffer periods, so the timed pass holds its share of gate + append flushes
+        steps = -(-steps // (buf * L)) * buf * L
+    S = warm + 2 * steps                 # warm-up, the timed pass, the per-launch timing pass
     n_loc = -(-S // L)                   # steps per layer cache
     n_fl = -(-n_loc // buf)              # gate groups per layer cache
     scale = 1.0 / math.sqrt(hd)

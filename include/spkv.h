@@ -137,7 +137,14 @@ typedef struct spkv_cache {
  *   hidden  [n_rows, ld_hidden] dtype (first d_model entries of each row)
  *   utility [n_rows, n_kv] f32, may be NULL;  keep [n_rows, n_kv] uint8
  *   ws      workspace of at least spkv_gate_ws_bytes(g, n_rows) bytes
- *           (may be NULL when that figure is 0)
+ *           (may be NULL when that figure is 0).  Its first 256 bytes hold
+ *           an arrival counter that must be zero before the first call that
+ *           uses ws (zero-fill it once after allocation); every call leaves
+ *           it at zero.  Calls sharing one ws must not overlap.
+ *   Launches: up to 16 rows, one kernel (one workgroup per hidden unit; the
+ *   last to finish adds the per-unit shares of each logit in unit order);
+ *   bf16 up to 64 rows, two kernels (d_model split, then the epilogue);
+ *   otherwise one kernel.  Results do not depend on scheduling.
  * tau is a runtime argument: the threshold may be changed at inference.
  */
 int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows,

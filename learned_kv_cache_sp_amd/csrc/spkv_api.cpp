@@ -96,7 +96,7 @@ const char *spkv_status_str(int status) {
 // ----------------------------------------------------------------------------
 size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows) {
     if (!g) return 0;
-    return spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->dtype, n_rows);
+    return spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->n_kv, g->dtype, n_rows);
 }
 
 int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows, int64_t ld_hidden,
@@ -117,7 +117,7 @@ int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows, int64
     if (!aligned16(hidden)) return fail(SPKV_E_INVALID, "hidden not 16-byte aligned");
     if (int r = check_ld(ld_hidden, g->d_model, g->dtype, "ld_hidden")) return r;
     if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
-    const size_t need = spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->dtype, n_rows);
+    const size_t need = spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->n_kv, g->dtype, n_rows);
     if (need && (!ws || ws_bytes < need))
         return fail(SPKV_E_WORKSPACE, "gate workspace %zu < %zu bytes", ws_bytes, need);
     spkv::GateArgs a;

@@ -248,6 +248,94 @@ __global__ void __launch_bounds__(NT) compact_small_kernel(CompactArgs a) {
     }
 }
 
+// One row per sequence (decode): one wavefront per (b, g).  Row offsets,
+// position, length and the page-table entry of the next slot are read
+// together; the key/value row and the keep bit in a second round; then the
+// ring and (when kept) the cache entry are written.  A new page costs one
+// more round trip (the pool atomic) once every page_size kept rows.
+template <typename T>
+__global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
+    const CacheView &c = a.c;
+    const int b = blockIdx.x;
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int64_t bg = (int64_t)b * c.n_kv + g;
+    const bool global = (a.flags & SPKV_APPEND_GLOBAL) != 0;
+    const int lo = a.row_offsets[b];
+    const int hi = a.row_offsets[b + 1];
+    const int pos = a.pos0[b];
+    const int old_len = global ? c.lengths[bg] : 0;
+    int32_t *pt = c.page_table + bg * c.max_pages;
+    const int P = c.page_size;
+    const int pidx = min(old_len >> c.page_shift, c.max_pages - 1);
+    const int cur_page = (global && (old_len & (P - 1)) != 0) ? pt[pidx] : -1;
+    const int n = hi - lo;
+    if (lo < 0 || n < 0 || n > a.max_rows || hi > a.n_rows) {
+        if (g == 0 && lane == 0) atomicOr(c.status, SPKV_STATUS_BAD_ROWS);
+        return;
+    }
+    if (global && lane == 0 && a.append_offsets) a.append_offsets[bg] = old_len;
+    if (n == 0) return;
+
+    constexpr int ES = sizeof(T);
+    constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
+    const int hd = c.head_dim;
+    const int cpr = hd / EPC;     // chunks per row (<= 32)
+    const bool kept = global && a.keep[(int64_t)lo * c.n_kv + g] != 0;
+    const int64_t src = (int64_t)lo * a.ld_kv * ES + (int64_t)g * hd * ES + lane * 16;
+    uint4 kv = {}, vv = {};
+    if (lane < cpr) {
+        kv = *(const uint4 *)(a.k + src);
+        vv = *(const uint4 *)(a.v + src);
+    }
+    T ve[EPC];
+    __builtin_memcpy(ve, &vv, 16);
+
+    if (a.flags & SPKV_APPEND_WINDOW) {
+        const int w = c.window;
+        const int slot = pos % w;
+        if (lane < cpr) {
+            *(uint4 *)(c.ring_k + ((bg * w + slot) * hd) * ES + lane * 16) = kv;
+            T *rv = (T *)c.ring_v + (bg * hd + lane * EPC) * w + slot;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) rv[(int64_t)e * w] = ve[e];
+        }
+    }
+    if (!kept) return;
+    int page = cur_page;
+    if ((old_len & (P - 1)) == 0) {
+        // the entry opens a new page
+        int got = -1;
+        if (lane == 0) {
+            const int first = old_len >> c.page_shift;
+            if (first >= c.max_pages) {
+                atomicOr(c.status, SPKV_STATUS_TABLE_FULL);
+            } else {
+                const int base = atomicAdd(c.pool_next, 1);
+                if (base >= c.n_pages) {
+                    atomicOr(c.status, SPKV_STATUS_POOL_FULL);
+                } else {
+                    pt[first] = base;
+                    got = base;
+                }
+            }
+        }
+        page = __shfl(got, 0);
+        if (page < 0) return;  // dropped: no room
+    }
+    const int j = old_len & (P - 1);
+    if (lane < cpr) {
+        *(uint4 *)(c.k_pages + (((int64_t)page * P + j) * hd) * ES + lane * 16) = kv;
+        T *dv = (T *)c.v_pages + ((int64_t)page * hd + lane * EPC) * P + j;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) dv[(int64_t)e * P] = ve[e];
+    }
+    if (lane == 0) {
+        c.pos_pages[(int64_t)page * P + j] = pos;
+        c.lengths[bg] = old_len + 1;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Large appends: (1) per-tile kept counts, (2) per-(b, g) scan over tiles and
 // page allocation, (3) per-(tile, b, g) ranking and copies.
@@ -366,6 +454,14 @@ hipError_t launch_compact(const CompactArgs &a0, hipStream_t s) {
     CompactArgs a = a0;
     const CacheView &c = a.c;
     const bool bf16 = c.dtype == SPKV_BF16;
+    if (a.max_rows == 1) {
+        dim3 grid(c.batch, c.n_kv);
+        if (bf16)
+            hipLaunchKernelGGL(compact_row_kernel<uint16_t>, grid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL(compact_row_kernel<float>, grid, dim3(64), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.max_rows <= TILE) {
         dim3 grid(c.batch, c.n_kv);
         if (bf16)

@@ -15,12 +15,16 @@
 //   (b, g) are laid end to end and every wave of the (resident, persistent)
 //   grid takes an equal contiguous share of that flat list: the load is
 //   balanced whatever the per-head lengths (they differ by 30x in the skewed
-//   workloads), and a wave streams its share with two steps in flight, never
-//   draining its pipeline between work items.  Where its share crosses from
-//   one (b, g) to the next, a wave writes a partial (max, sum, unnormalised
-//   output) per query head.  A second, small kernel merges the partials of
-//   every (b, g) in wave order -- deterministic -- and writes out and lse (the
-//   kernel boundary makes the partials visible, with no cache flush).
+//   workloads).  The grid is persistent (compute units x resident
+//   workgroups); workgroup x takes the contiguous share [x*spg, (x+1)*spg)
+//   and its 4 waves interleave over it, two steps in flight each.
+//   A (b, g) wholly inside one share is finished by that workgroup (the 4
+//   wave states combined in LDS, output written).  A (b, g) spread over
+//   several shares gets one partial (max, sum, unnormalised output per query
+//   head) from each; a workgroup publishes its (at most two) partials after
+//   its last step, with device-scope stores, then bumps the (b, g) arrival
+//   counter; the workgroup that arrives last merges the partials in share
+//   order -- deterministic -- and writes out and lse.
 //   Page ids and the number of visible entries of each step are staged in
 //   LDS per wave before its steps run, so the streaming loop issues no vector
 //   loads other than the key/value loads themselves.
@@ -34,6 +38,7 @@
 //   The G query heads of the key head share every K/V load (rows >= G of the
 //   query operand are zero).  Online softmax in the log2 domain.
 #include "spkv_internal.h"
+#include "spkv_device.h"
 
 namespace spkv {
 namespace {
@@ -57,9 +62,11 @@ __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x);
 // every record starts 16-byte aligned)
 __host__ __device__ inline int rec_floats(int G, int HD) { return G * HD + 32; }
 
-// workspace: one arrival counter per (b, g) (ints, padded; zero between
-// calls), then the partials
-__host__ __device__ inline size_t ws_header_bytes(int BG) { return ((size_t)(BG + 1) * 4 + 255) & ~(size_t)255; }
+// workspace: one arrival counter per (b, g), each in its own 256-byte line
+// (the end-of-launch arrivals of all workgroups would otherwise queue on a
+// few lines; zero between calls), then the partials
+constexpr int CNT_STRIDE = 64;  // ints
+__host__ __device__ inline size_t ws_header_bytes(int BG) { return (size_t)BG * CNT_STRIDE * 4; }
 
 // Inclusive block scan of val(i), i < n, into out[1..n] (out[0] = 0); returns the total.
 template <typename Fn>
@@ -238,15 +245,6 @@ __device__ inline void compute_step(WaveState<HD> &st, const bf16x8 *qlds,
 }
 
 
-// device-scope (L2-bypassing) accesses used to hand partials between
-// workgroups: stores complete at the device-coherent level before the
-// counter is bumped (s_waitcnt), and the merging workgroup reads them back
-// past its own L2, so no cache-wide flush or invalidate is needed
-__device__ inline void store_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline float load_dev(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 
 template <int HD>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) decode_bf16_kernel(DecodeArgs a) {
@@ -254,14 +252,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     __shared__ int lds_len[MAX_BG];
     __shared__ int lds_t[MAX_BG];
     __shared__ int lds_red[NW];
-    __shared__ int lds_flag;
+    __shared__ int lds_flag[2];
     __shared__ int lds_sbg[NW][ROUND];    // per wave: (b, g) of each staged step
     __shared__ int lds_spg[NW][ROUND];    //           page id (-1: ring step)
     __shared__ int lds_snv[NW][ROUND];    //           visible keys (a prefix of the step)
     __shared__ bf16x8 lds_q[NW][HD / 32][64];  // per wave: query operand of each lane
-    __shared__ float lds_wm[NW][16], lds_wl[NW][16];
-    __shared__ float lds_o[NW][16][HD];   // wave states at a (b, g) boundary; merge scratch
-    __shared__ float lds_sc[16];
+    // wave states at (b, g) boundaries, two slots (slot 0 doubles as merge scratch)
+    __shared__ float lds_wm[2][NW][16], lds_wl[2][NW][16];
+    __shared__ __attribute__((aligned(16))) float lds_o[2][NW][16][HD];
 
     const CacheView &c = a.c;
     const int BG = c.batch * c.n_kv;
@@ -316,30 +314,46 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     };
 
     // ---- per-wave staging of (b, g), page and visible count of its steps ----
+    // Phase A (page ids) comes before the first loads of a round; phase B
+    // (visible counts, which need the positions of the last entries of each
+    // (b, g)) runs while those loads are in flight.
     int r0 = 0, r1 = 0;
-    auto stage = [&](int from) {
+    auto stage_pages = [&](int from) {
         r0 = from;
         r1 = min(nk, from + ROUND);
         for (int k = r0 + lane; k < r1; k += 64) {
             const int s = W0 + wave + NW * k;
             const int bg = find_owner(lds_F, BG, s);
             const int ls = s - lds_F[bg];
+            int page = -1;
+            if (ls >= nws) page = c.page_table[(int64_t)bg * c.max_pages + (((ls - nws) * KSTEP) >> c.page_shift)];
+            lds_sbg[wave][k - r0] = bg;
+            lds_spg[wave][k - r0] = page;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+    };
+    auto stage_counts = [&]() {
+        for (int k = r0 + lane; k < r1; k += 64) {
+            const int s = W0 + wave + NW * k;
+            const int bg = lds_sbg[wave][k - r0];
+            const int ls = s - lds_F[bg];
             const int len = lds_len[bg];
             const int t = lds_t[bg / c.n_kv];
             const int limit = t - w;
-            int page = -1, nv;
+            int nv;
             if (ls < nws) {
                 // ring slot s holds position t - ((t - s) mod w): visible iff s <= t
                 nv = min(KSTEP, max(0, t - ls * KSTEP + 1));
             } else {
                 const int j0 = (ls - nws) * KSTEP;
-                page = c.page_table[(int64_t)bg * c.max_pages + (j0 >> c.page_shift)];
                 if (limit >= 0 && j0 + KSTEP <= len - w) {
                     nv = KSTEP;  // older than the window: every entry visible
                 } else {
                     // visible = index < len and position <= t - w: a prefix,
                     // since positions increase along the list; the 32
                     // positions of the step are one aligned 128-byte run
+                    const int page = lds_spg[wave][k - r0];
                     const i32x4 *pp = (const i32x4 *)(c.pos_pages + (int64_t)page * P + (j0 & (P - 1)));
                     const int lim_n = min(KSTEP, len - j0);
                     i32x4 pv[KSTEP / 4];
@@ -350,8 +364,6 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     for (int u = 0; u < KSTEP; ++u) nv += (u < lim_n && pv[u >> 2][u & 3] <= limit) ? 1 : 0;
                 }
             }
-            lds_sbg[wave][k - r0] = bg;
-            lds_spg[wave][k - r0] = page;
             lds_snv[wave][k - r0] = nv;
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -382,13 +394,180 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const uint32_t valid = (uint32_t)((1u << min(8, max(0, nv - 8 * q4))) - 1u);
         compute_step<HD, true>(st, &lds_q[wave][0][lane], kr, vr, valid, sl2);
     };
+    // this wave's state -> LDS state slot `sl` (the lane groups' sums added)
+    auto save_state = [&](int sl) {
+        float lsum = st.l;
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        if (q4 == 0) {
+            lds_wm[sl][wave][head] = st.m;
+            lds_wl[sl][wave][head] = lsum;
+        }
+#pragma unroll
+        for (int nt = 0; nt < HD / 16; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lds_o[sl][wave][head][16 * nt + 4 * q4 + r] = st.o[nt][r];
+    };
+    // combination of the NW wave states of slot sl for outputs (h, d..d+3):
+    // M and O, L relative to 2^M
+    auto combine4 = [&](int sl, int h, int d, float &M, f32x4 &O, float &L) {
+        M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) M = fmaxf(M, lds_wm[sl][v][h]);
+        const float bse = (M == -INFINITY) ? 0.f : M;
+        O = f32x4{0.f, 0.f, 0.f, 0.f};
+        L = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const float f = exp2f(lds_wm[sl][v][h] - bse);
+            O += f * *(const f32x4 *)&lds_o[sl][v][h][d];
+            L += f * lds_wl[sl][v][h];
+        }
+    };
+    auto out_index = [&](int bg, int h) -> int64_t {
+        const int b = bg / c.n_kv;
+        return (int64_t)b * a.n_q + (bg - b * c.n_kv) * G + h;
+    };
+    auto parts_of = [&](int bg, int &part0, int &n_parts) {
+        part0 = lds_F[bg] / spg + bg;  // first slot of (b, g)
+        n_parts = (lds_F[bg + 1] - 1) / spg + bg - part0 + 1;
+    };
+    // Partials are handed between workgroups with 16-byte device-scope
+    // (sc1) buffer stores and loads: they bypass the non-coherent per-XCD L2
+    // copies, so the only ordering needed is the producer's s_waitcnt before
+    // its arrival atomic.
+    const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(part, (uint32_t)((size_t)a.max_items * rec * sizeof(float)));
+    constexpr int CPOL_SC1 = 16;
+    // publish the combined state of slot sl as the partial of (b, g) at slot
+    // blockIdx + bg; threads t0, t0 + stride, ... take one float4 each
+    auto publish = [&](int sl, int bg, int t0, int stride) {
+        const uint32_t base = (uint32_t)((size_t)(blockIdx.x + bg) * rec * sizeof(float));
+        for (int f = t0; f < G * HD / 4; f += stride) {
+            const int h = (4 * f) / HD;
+            const int d = 4 * f - h * HD;
+            float M, L;
+            f32x4 O;
+            combine4(sl, h, d, M, O, L);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, O), prs, base + 16 * f, 0, CPOL_SC1);
+            if (d == 0) {
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, M), prs, base + 4 * (G * HD + h), 0, CPOL_SC1);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, L), prs, base + 4 * (G * HD + G + h), 0, CPOL_SC1);
+            }
+        }
+    };
+    // Merge of the partials of up to two (b, g) (this workgroup arrived last
+    // for each), in slot order -- deterministic.  Per batch of MB slots, the
+    // maxima and sums go to LDS and each thread loads the float4 outputs it
+    // owns, all loads issued before any is used: a batch costs one trip to
+    // memory and one barrier.  Uses state slot 0 of LDS as scratch.
+    auto merge = [&](int nm, const int *bgs) {
+        constexpr int MB = 8;
+        constexpr int MAXC = (2 * 16 * HD / 4 + NT - 1) / NT;  // float4 chunks per thread
+        const int GH = G * HD;
+        const int n4 = nm * GH / 4;
+        int p0[2] = {0, 0}, np[2] = {0, 0};
+        for (int m = 0; m < nm; ++m) parts_of(bgs[m], p0[m], np[m]);
+        const int np_max = max(np[0], np[1]);
+        float *cm = &lds_o[0][0][0][0];  // [2][MB][16] maxima
+        float *cl = cm + 2 * MB * 16;     // [2][MB][16] sums
+        f32x4 Oa[MAXC];
+        float Ma[MAXC], La[MAXC];
+#pragma unroll
+        for (int ch = 0; ch < MAXC; ++ch) {
+            Oa[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Ma[ch] = -INFINITY;
+            La[ch] = 0.f;
+        }
+        for (int c0 = 0; c0 < np_max; c0 += MB) {
+            if (c0 > 0) __syncthreads();  // the previous batch's maxima are consumed
+            f32x4 ov[MAXC][MB];
+#pragma unroll
+            for (int ch = 0; ch < MAXC; ++ch) {
+                if (ch * NT >= n4) break;  // uniform
+                const int f = ch * NT + threadIdx.x;
+                const int m = 4 * f >= GH ? 1 : 0;
+                const uint32_t off = (uint32_t)(((size_t)p0[m] * rec + (4 * f - m * GH)) * sizeof(float));
+#pragma unroll
+                for (int kk = 0; kk < MB; ++kk)
+                    ov[ch][kk] = (f < n4 && c0 + kk < np[m])
+                                     ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    prs, off + (uint32_t)((c0 + kk) * rec * 4), 0, CPOL_SC1))
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if (threadIdx.x < 2 * MB * G) {
+                const int m = threadIdx.x / (MB * G);
+                const int kk = (threadIdx.x / G) % MB;
+                const int h = threadIdx.x % G;
+                const bool ok = m < nm && c0 + kk < np[m];
+                const uint32_t off = (uint32_t)(((size_t)(p0[m] + c0 + kk) * rec + GH + h) * sizeof(float));
+                const float mv = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, CPOL_SC1)) : -INFINITY;
+                const float lv = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, off + 4 * G, 0, CPOL_SC1)) : 0.f;
+                cm[(m * MB + kk) * 16 + h] = mv;
+                cl[(m * MB + kk) * 16 + h] = lv;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ch = 0; ch < MAXC; ++ch) {
+                if (ch * NT >= n4) break;
+                const int f = ch * NT + threadIdx.x;
+                if (f < n4) {
+                    const int m = 4 * f >= GH ? 1 : 0;
+                    const int h = (4 * f - m * GH) / HD;
+                    const float *mk = cm + m * MB * 16 + h;
+                    const float *lk = cl + m * MB * 16 + h;
+                    float M = Ma[ch];
+#pragma unroll
+                    for (int kk = 0; kk < MB; ++kk) M = fmaxf(M, mk[kk * 16]);
+                    const float bse = (M == -INFINITY) ? 0.f : M;
+                    const float so = exp2f(Ma[ch] - bse);
+                    f32x4 O = Oa[ch] * so;
+                    float L = La[ch] * so;
+#pragma unroll
+                    for (int kk = 0; kk < MB; ++kk) {
+                        const float fw = exp2f(mk[kk * 16] - bse);  // empty slot: -inf -> 0
+                        O += fw * ov[ch][kk];
+                        L += fw * lk[kk * 16];
+                    }
+                    Oa[ch] = O;
+                    La[ch] = L;
+                    Ma[ch] = M;
+                }
+            }
+        }
+#pragma unroll
+        for (int ch = 0; ch < MAXC; ++ch) {
+            if (ch * NT >= n4) break;
+            const int f = ch * NT + threadIdx.x;
+            if (f < n4) {
+                const int m = 4 * f >= GH ? 1 : 0;
+                const int h = (4 * f - m * GH) / HD;
+                const int d = 4 * f - m * GH - h * HD;
+                const float L = La[ch];
+                const int64_t oi = out_index(bgs[m], h);
+                *(f32x4 *)(a.out + oi * HD + d) = L > 0.f ? Oa[ch] * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+                if (d == 0 && a.lse) a.lse[oi] = L > 0.f ? (Ma[ch] + log2f(L)) * LN2 : -INFINITY;
+            }
+        }
+        if (threadIdx.x < nm) reset_dev(&cnt[bgs[threadIdx.x] * CNT_STRIDE]);
+    };
 
     // ---- the (b, g) segments of this workgroup's range -----------------------
+    // A (b, g) that lies wholly inside the range is finished here (its output
+    // written from the 4 wave states).  At most two are shared with other
+    // workgroups: the first (it starts before W0) and the last (it goes on
+    // past W1).  Each is published (4 wave states combined, stored as one
+    // partial) and counted as soon as this workgroup is done with it.
+    const bool first_split = lds_F[bg_first] < W0;
+    const bool last_split = lds_F[bg_last + 1] > W1;
+    const bool one = bg_first == bg_last;
+    const bool pub_first = !one && first_split;                            // slot 1
+    const bool pub_last = one ? (first_split || last_split) : last_split;  // slot 0
     reset(bg_first);
     int k = 0;  // next step of this wave to compute (its loads are in flight)
     if (nk > 0) {
-        stage(0);
+        stage_pages(0);
         issue(0, kA, vA);
+        stage_counts();
     }
     for (int bg = bg_first; bg <= bg_last; ++bg) {
         const int seg_end = min(W1, lds_F[bg + 1]);
@@ -403,139 +582,64 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             }
             ++k;
             if (k < nk && k == r1) {
-                stage(k);
+                stage_pages(k);
                 if ((k & 1) == 0) issue(k, kA, vA); else issue(k, kB, vB);
+                stage_counts();
             }
         }
-        // ---- end of this (b, g) in the workgroup: merge the 4 wave states ----
-        {
-            float lsum = st.l;
-            lsum += __shfl_xor(lsum, 16);
-            lsum += __shfl_xor(lsum, 32);
-            if (q4 == 0) {
-                lds_wm[wave][head] = st.m;
-                lds_wl[wave][head] = lsum;
-            }
-#pragma unroll
-            for (int nt = 0; nt < HD / 16; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lds_o[wave][head][16 * nt + 4 * q4 + r] = st.o[nt][r];
-        }
-        __syncthreads();
-        const int slot = blockIdx.x + bg;
-        const int part0 = lds_F[bg] / spg + bg;                  // first slot of (b, g)
-        const int n_parts = (lds_F[bg + 1] - 1) / spg + bg - part0 + 1;
-        float *my = part + (size_t)slot * rec;
-        for (int idx = threadIdx.x; idx < G * HD; idx += NT) {
-            const int h = idx / HD;
-            const int d = idx - h * HD;
-            float M = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < NW; ++v) M = fmaxf(M, lds_wm[v][h]);
-            const float bse = (M == -INFINITY) ? 0.f : M;
-            float O = 0.f;
-#pragma unroll
-            for (int v = 0; v < NW; ++v) O += exp2f(lds_wm[v][h] - bse) * lds_o[v][h][d];
-            store_dev(my + h * HD + d, O);
-            if (d == 0) {
-                float L = 0.f;
-#pragma unroll
-                for (int v = 0; v < NW; ++v) L += exp2f(lds_wm[v][h] - bse) * lds_wl[v][h];
-                store_dev(my + G * HD + h, M);
-                store_dev(my + G * HD + G + h, L);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
-        __syncthreads();
-        if (threadIdx.x == 0)
-            lds_flag = __hip_atomic_fetch_add(&cnt[bg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_parts - 1;
-        __syncthreads();
-        if (lds_flag) {
-            // the last workgroup of (b, g): merge its partials in slot order.
-            // Partials are taken MB at a time; every load of a batch (maxima,
-            // sums and outputs) is issued before any is used, so a batch costs
-            // one trip to memory.
-            constexpr int MB = 8;
-            constexpr int PER = (16 * HD + NT - 1) / NT;  // outputs per thread
-            const float *pb = part + (size_t)part0 * rec;
-            float *cm = &lds_o[0][0][0];  // [MB][16] maxima -> weights
-            float *cl = cm + MB * 16;     // [MB][16] sums
-            float Oacc[PER];
-#pragma unroll
-            for (int j = 0; j < PER; ++j) Oacc[j] = 0.f;
-            float Mrun = -INFINITY, Lrun = 0.f;  // (threads < G: head threadIdx.x)
-            for (int c0 = 0; c0 < n_parts; c0 += MB) {
-                const int m_n = min(MB, n_parts - c0);
-                float ov[MB][PER];
-#pragma unroll
-                for (int kk = 0; kk < MB; ++kk)
-#pragma unroll
-                    for (int j = 0; j < PER; ++j) {
-                        const int idx = threadIdx.x + j * NT;
-                        ov[kk][j] = (kk < m_n && idx < G * HD) ? load_dev(pb + (size_t)(c0 + kk) * rec + idx) : 0.f;
-                    }
-                if (threadIdx.x < m_n * G) {
-                    const int kk = threadIdx.x / G;
-                    const int h = threadIdx.x - kk * G;
-                    cm[kk * 16 + h] = load_dev(pb + (size_t)(c0 + kk) * rec + G * HD + h);
-                    cl[kk * 16 + h] = load_dev(pb + (size_t)(c0 + kk) * rec + G * HD + G + h);
-                }
-                __syncthreads();
-                if (threadIdx.x < G) {
-                    const int h = threadIdx.x;
-                    float M = Mrun;
-                    for (int kk = 0; kk < m_n; ++kk) M = fmaxf(M, cm[kk * 16 + h]);
-                    const float bse = (M == -INFINITY) ? 0.f : M;
-                    const float so = exp2f(Mrun - bse);
-                    float L = Lrun * so;
-                    for (int kk = 0; kk < m_n; ++kk) {
-                        const float f = exp2f(cm[kk * 16 + h] - bse);
-                        cm[kk * 16 + h] = f;
-                        L += f * cl[kk * 16 + h];
-                    }
-                    lds_sc[h] = so;
-                    Mrun = M;
-                    Lrun = L;
-                }
-                __syncthreads();
-#pragma unroll
-                for (int j = 0; j < PER; ++j) {
-                    const int idx = threadIdx.x + j * NT;
-                    if (idx < G * HD) {
-                        const int h = idx / HD;
-                        float O = Oacc[j] * lds_sc[h];
-#pragma unroll
-                        for (int kk = 0; kk < MB; ++kk)
-                            if (kk < m_n) O += cm[kk * 16 + h] * ov[kk][j];
-                        Oacc[j] = O;
-                    }
-                }
-                __syncthreads();
-            }
-            if (threadIdx.x < G) {
-                lds_wm[0][threadIdx.x] = Mrun;
-                lds_wl[0][threadIdx.x] = Lrun;
+        if (bg == bg_first && pub_first) {
+            // publish and arrive now, so that arrivals are spread over the
+            // launch instead of all falling at its end
+            save_state(1);
+            __syncthreads();
+            publish(1, bg_first, threadIdx.x, NT);
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int p0, np;
+                parts_of(bg_first, p0, np);
+                lds_flag[0] = arrive_dev(&cnt[bg_first * CNT_STRIDE]) == np - 1;
             }
             __syncthreads();
-            const int b = bg / c.n_kv;
-            const int g = bg - b * c.n_kv;
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int idx = threadIdx.x + j * NT;
-                if (idx < G * HD) {
-                    const int h = idx / HD;
-                    const int d = idx - h * HD;
-                    const float L = lds_wl[0][h];
-                    const int64_t oidx = (int64_t)b * a.n_q + g * G + h;
-                    a.out[oidx * HD + d] = L > 0.f ? Oacc[j] / L : 0.f;
-                    if (d == 0 && a.lse) a.lse[oidx] = L > 0.f ? (lds_wm[0][h] + log2f(L)) * LN2 : -INFINITY;
-                }
+            if (lds_flag[0]) {
+                const int one_bg = bg_first;
+                merge(1, &one_bg);
+                __syncthreads();
             }
-            if (threadIdx.x == 0) __hip_atomic_store(&cnt[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (bg == bg_last && pub_last) {
+            save_state(0);
+        } else {
+            // whole (b, g) in this workgroup: normalise and write the output
+            save_state(0);
+            __syncthreads();
+            for (int f = threadIdx.x; f < G * HD / 4; f += NT) {
+                const int h = (4 * f) / HD;
+                const int d = 4 * f - h * HD;
+                float M, L;
+                f32x4 O;
+                combine4(0, h, d, M, O, L);
+                const int64_t oi = out_index(bg, h);
+                *(f32x4 *)(a.out + oi * HD + d) = L > 0.f ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+                if (d == 0 && a.lse) a.lse[oi] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
+            }
+            __syncthreads();
         }
-        __syncthreads();
         if (bg < bg_last) reset(bg + 1);
     }
+
+    // ---- the last (b, g), if shared: publish, arrive, the last arrival merges
+    if (!pub_last) return;
+    __syncthreads();
+    publish(0, bg_last, threadIdx.x, NT);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int p0, np;
+        parts_of(bg_last, p0, np);
+        lds_flag[1] = arrive_dev(&cnt[bg_last * CNT_STRIDE]) == np - 1;
+    }
+    __syncthreads();
+    if (lds_flag[1]) merge(1, &bg_last);
 }
 
 // ---------------------------------------------------------------------------

@@ -7,16 +7,25 @@
 // v_mfma_f32_16x16x32_bf16; both operands are K-contiguous rows (hidden
 // states, W1 rows), so lanes load 16-byte pieces straight from memory.  The
 // epilogue (bias, ReLU, second layer, sigmoid, threshold) runs from LDS in
-// the same kernel.  For a handful of rows (decode) d_model is split over
-// several workgroups that write partial sums; a second small kernel adds the
-// slices in a fixed order and runs the epilogue.
-// f32: a plain VALU kernel.
+// the same kernel.  For up to 64 rows d_model is split over several
+// workgroups that write partial sums; a second small kernel adds the slices
+// in a fixed order and runs the epilogue.
+// Up to 16 rows (decode, either dtype): one launch with one workgroup per
+// hidden unit; each adds its unit's share W2[:, j] a_j of every logit to a
+// workspace slot, and the workgroup that finishes last sums the shares in
+// unit order, so the result does not depend on scheduling.
+// f32 with more rows, or d_hidden outside {32, 64, 128, 256}: a plain VALU
+// kernel.
 #include "spkv_internal.h"
+#include "spkv_device.h"
 
 namespace spkv {
 namespace {
 
 constexpr int NT = 256;
+// the workspace starts with a 256-byte header holding the arrival counter of
+// the few-row kernel; partial sums follow it
+constexpr int WS_HEADER_FLOATS = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -119,7 +128,7 @@ __global__ void __launch_bounds__(NT) gate_bf16_kernel(GateArgs a) {
 
     // split d_model: write this slice's sums; gate_split_epilogue adds them
     const int n_tiles = gridDim.x;
-    float *part = a.ws;  // [n_split][n_tiles * BM][HG]
+    float *part = a.ws + WS_HEADER_FLOATS;  // [n_split][n_tiles * BM][HG]
     const size_t slab = (size_t)n_tiles * BM * HG;
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
@@ -139,7 +148,7 @@ __global__ void __launch_bounds__(NT) gate_split_epilogue(GateArgs a) {
     __shared__ float act[BM][HG + 1];
     __shared__ float lds_w2[16 * (HG + 1)];
     const size_t slab = (size_t)gridDim.x * BM * HG;
-    const float *part = a.ws;
+    const float *part = a.ws + WS_HEADER_FLOATS;
     for (int idx = threadIdx.x; idx < BM * HG; idx += NT) {
         const int r = idx / HG;
         const int j = idx - r * HG;
@@ -189,12 +198,126 @@ __global__ void __launch_bounds__(NT) gate_valu_kernel(GateArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (n_rows <= NR <= 16): workgroup j computes hidden unit j for every
+// row over the whole d_model (16-byte loads of W1 row j and of each hidden
+// row), reduces across the workgroup in a fixed tree, applies bias and ReLU,
+// and stores its share W2[k][j] * a_j of logit (row, k).  The last workgroup
+// to arrive adds the shares in unit order, then sigmoid and threshold.
+template <typename T, int NR>
+__global__ void __launch_bounds__(NT) gate_tiny_kernel(GateArgs a) {
+    constexpr int V = 16 / sizeof(T);
+    typedef T tvec __attribute__((ext_vector_type(V)));
+    __shared__ float red[NT / 64][NR];
+    __shared__ int lds_last;
+    const int j = blockIdx.x;
+    const int n = (int)a.n_rows;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const T *w = (const T *)a.w1 + (int64_t)j * a.d_model;
+    const T *h = (const T *)a.hidden;
+    // second-layer weight and first-layer bias of this unit, fetched up front
+    const int nkv = a.n_kv;
+    const int my_k = threadIdx.x % nkv;
+    const float w2j = a.w2[(size_t)my_k * a.d_hidden + j];
+    const float b1j = a.b1[j];
+    // final sum (last workgroup only): TPO threads per logit, a power of two
+    const int outs = n * nkv;
+    int tpo = 1;
+    while (tpo * 2 * outs <= NT && tpo < 32) tpo *= 2;
+    const int o = threadIdx.x / tpo;
+    const int q = threadIdx.x - o * tpo;
+    const float b2o = o < outs ? a.b2[o % nkv] : 0.f;
+    float acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+    const int nvec = a.d_model / V;
+    // rows past n_rows re-read the last row (their sums are never used), so
+    // that every load is unconditional and all of them are in flight at once
+    int64_t roff[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) roff[r] = (int64_t)(r < n ? r : n - 1) * a.ld_hidden;
+#pragma unroll 2
+    for (int c = threadIdx.x; c < nvec; c += NT) {
+        const tvec wv = *(const tvec *)(w + (int64_t)c * V);
+        tvec hv[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) hv[r] = *(const tvec *)(h + roff[r] + (int64_t)c * V);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[r] = fmaf((float)wv[e], (float)hv[r][e], acc[r]);
+    }
+    // butterfly over the wave, all rows interleaved so the lane exchanges overlap
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] += __shfl_xor(acc[r], off);
+    if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) red[wave][r] = acc[r];
+    __syncthreads();
+
+    int *cnt = (int *)a.ws;
+    float *part = a.ws + WS_HEADER_FLOATS;  // [d_hidden][NR][n_kv]
+    if (threadIdx.x < NR * nkv) {
+        const int r = threadIdx.x / nkv;
+        const int k = threadIdx.x - r * nkv;  // == my_k
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < NT / 64; ++v) s += red[v][r];
+        const float act = relu_keep_nan(s + b1j);
+        store_dev(part + ((size_t)j * NR + r) * nkv + k, w2j * act);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's share is stored
+    __syncthreads();
+    if (threadIdx.x == 0) lds_last = arrive_dev(cnt) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!lds_last) return;
+
+    // thread q of a logit adds the shares of units q, q + TPO, ... (all its
+    // loads issued before any add); the TPO sums are then added in a fixed tree
+    float s = 0.f;
+    if (o < outs) {
+        const int r = o / nkv;
+        const int k = o - r * nkv;
+        const float *p = part + (size_t)r * nkv + k;
+        const size_t stride = (size_t)NR * nkv;
+        const int hg = a.d_hidden;
+        for (int j0 = q; j0 < hg; j0 += 32 * tpo) {
+            float v[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const int jj = j0 + e * tpo;
+                v[e] = jj < hg ? load_dev(p + (size_t)jj * stride) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 32; ++e) s += v[e];
+        }
+    }
+    // combine the TPO partial sums of each logit in q order (lanes of a logit
+    // are consecutive and TPO <= 32 divides the wave)
+    for (int off = 1; off < tpo; off <<= 1) {
+        const float y = __shfl_down(s, off);
+        if ((q & (2 * off - 1)) == 0) s += y;
+    }
+    if (o < outs && q == 0) {
+        const int r = o / nkv;
+        const int k = o - r * nkv;
+        const float u = sigmoid_f(s + b2o);
+        if (a.utility) a.utility[(int64_t)r * nkv + k] = u;
+        a.keep[(int64_t)r * nkv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+    }
+    if (threadIdx.x == 0) reset_dev(cnt);
+}
+
 constexpr int SMALL_ROWS = 64;
+constexpr int TINY_ROWS = 16;
 
 }  // namespace
 
 int gate_split_for(int d_model, int dtype, int64_t n_rows) {
-    if (dtype != SPKV_BF16 || n_rows > SMALL_ROWS) return 1;
+    if (dtype != SPKV_BF16 || n_rows > SMALL_ROWS || n_rows <= TINY_ROWS) return 1;
     const int steps = d_model / 32;
     int split = 1;
     while (split * 2 <= 16 && steps % (split * 2) == 0) split *= 2;
@@ -207,12 +330,25 @@ static bool mfma_hidden(int hg) { return hg == 32 || hg == 64 || hg == 128 || hg
 // d_hidden = 32 (two 16-unit tiles) and 1 otherwise
 static int small_bm(int hg) { return hg == 32 ? 32 : 16; }
 
-size_t gate_ws_bytes(int d_model, int d_hidden, int dtype, int64_t n_rows) {
+size_t gate_ws_bytes(int d_model, int d_hidden, int n_kv, int dtype, int64_t n_rows) {
+    const size_t header = WS_HEADER_FLOATS * sizeof(float);
+    if (n_rows > 0 && n_rows <= TINY_ROWS) return header + (size_t)d_hidden * TINY_ROWS * n_kv * sizeof(float);
     const int split = gate_split_for(d_model, dtype, n_rows);
     if (split == 1 || !mfma_hidden(d_hidden)) return 0;
     const int bm = small_bm(d_hidden);
     const int64_t tiles = (n_rows + bm - 1) / bm;
-    return (size_t)split * tiles * bm * d_hidden * sizeof(float);
+    return header + (size_t)split * tiles * bm * d_hidden * sizeof(float);
+}
+
+template <typename T>
+static void launch_tiny(const GateArgs &a, hipStream_t s) {
+    const dim3 grid(a.d_hidden);
+    if (a.n_rows <= 4)
+        hipLaunchKernelGGL((gate_tiny_kernel<T, 4>), grid, dim3(NT), 0, s, a);
+    else if (a.n_rows <= 8)
+        hipLaunchKernelGGL((gate_tiny_kernel<T, 8>), grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gate_tiny_kernel<T, 16>), grid, dim3(NT), 0, s, a);
 }
 
 template <int WM, int HG>
@@ -233,7 +369,12 @@ static void launch_mfma(const GateArgs &a, int tiles, hipStream_t s) {
 
 hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
     GateArgs a = a0;
-    if (a.dtype == SPKV_BF16 && mfma_hidden(a.d_hidden)) {
+    if (a.n_rows <= TINY_ROWS) {
+        if (a.dtype == SPKV_BF16)
+            launch_tiny<__bf16>(a, s);
+        else
+            launch_tiny<float>(a, s);
+    } else if (a.dtype == SPKV_BF16 && mfma_hidden(a.d_hidden)) {
         if (a.n_split > 1) {
             const int bm = small_bm(a.d_hidden);
             const int tiles = (int)((a.n_rows + bm - 1) / bm);

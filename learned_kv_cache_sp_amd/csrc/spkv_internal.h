@@ -61,10 +61,10 @@ struct GateArgs {
     float tau;
     float *utility;
     uint8_t *keep;
-    float *ws;          // split-K partials [n_split, n_rows_pad, d_hidden] + counters
+    float *ws;          // 256-byte header (arrival counter) + partial sums
     int32_t n_split;    // number of slices of d_model (1 = no workspace)
 };
-size_t gate_ws_bytes(int d_model, int d_hidden, int dtype, int64_t n_rows);
+size_t gate_ws_bytes(int d_model, int d_hidden, int n_kv, int dtype, int64_t n_rows);
 int gate_split_for(int d_model, int dtype, int64_t n_rows);
 hipError_t launch_gate(const GateArgs &a, hipStream_t s);
 

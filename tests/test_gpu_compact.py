@@ -169,3 +169,72 @@ def test_host_side_argument_errors():
     with pytest.raises(spkv.SpkvError) as ei:
         spkv.spkv_compact_append(bad, None, k, k, ro, p0, 10, W_)
     assert ei.value.code in (spkv.SPKV_E_UNSUPPORTED, spkv.SPKV_E_INVALID)
+
+
+@pytest.mark.parametrize("name,page", [("decode_32k", 64), ("tiny", 32)])
+def test_one_row_appends(name, page):
+    # decode-style appends: at most one row per sequence per call, with page
+    # boundaries crossed many times and sequences that sit out some calls
+    wl = inputs.WORKLOADS[name]
+    B = 3
+    rates = [0.0, 1.0] + [0.4] * (wl.n_kv - 2)
+    T = [300, 70, 200]
+    K, V, Z = zip(*[_seq_data(wl, T[b], b, 31, rates) for b in range(B)])
+    cache = tl.new_cache(wl, B, max(T), page_size=page)
+    done = [0] * B
+    step = 0
+    while any(done[b] < T[b] for b in range(B)):
+        rz, rk, rv, p0 = [], [], [], []
+        for b in range(B):
+            take = done[b] < T[b] and not (b == 2 and step % 3 == 1)
+            sl = slice(done[b], done[b] + 1)
+            rz.append(Z[b][sl] if take else None)
+            rk.append(K[b][sl] if take else None)
+            rv.append(V[b][sl] if take else None)
+            p0.append(done[b])
+            done[b] += int(take)
+        ao = torch.full((B, wl.n_kv), -7, dtype=torch.int32, device="cuda")
+        before = cache.lengths.clone()
+        tl.append(cache, rz, rk, rv, p0, G_ | W_, append_offsets=ao)
+        torch.cuda.synchronize()
+        assert torch.equal(ao, before)
+        step += 1
+    assert spkv.spkv_cache_check(cache) == 0
+    _check_cache(cache, wl, K, V, Z, T)
+    w = wl.window
+    for b in range(B):
+        for g in range(wl.n_kv):
+            rk_, rv_ = cache.read_ring(b, g)
+            for p in range(max(0, T[b] - w), T[b]):
+                np.testing.assert_array_equal(rk_[p % w].float().cpu().numpy(), K[b][p, g])
+                np.testing.assert_array_equal(rv_[p % w].float().cpu().numpy(), V[b][p, g])
+
+
+def test_one_row_appends_capacity_and_bad_rows():
+    wl = inputs.WORKLOADS["decode_32k"]
+    K, V, Z = _seq_data(wl, 200, 0, 13, [1.0] * 8)
+    from learned_kv_cache_sp_amd.spkv import Cache
+    cache = Cache(1, wl.n_kv, wl.head_dim, wl.window, 32, n_pages=20, max_pages_per_head=3,
+                  dtype=torch.bfloat16)
+    for t in range(200):
+        tl.append(cache, [Z[t:t + 1]], [K[t:t + 1]], [V[t:t + 1]], [t], G_ | W_)
+    torch.cuda.synchronize()
+    with pytest.raises(spkv.SpkvError) as ei:
+        spkv.spkv_cache_check(cache)
+    assert ei.value.code == spkv.SPKV_E_CAPACITY
+    lens = cache.lengths[0].cpu().numpy()
+    assert lens.sum() <= 20 * 32 and np.all(lens <= 3 * 32)
+    for g in range(wl.n_kv):
+        k, v, pos = cache.read_head(0, g)
+        np.testing.assert_array_equal(pos.cpu().numpy(), np.arange(len(pos)))
+        np.testing.assert_array_equal(v.float().cpu().numpy(), V[: len(pos), g])
+    # two rows for a sequence while max_rows_per_seq = 1
+    cache2 = tl.new_cache(wl, 2, 10)
+    kd, vd = tl.dev(K[:3], torch.bfloat16), tl.dev(V[:3], torch.bfloat16)
+    spkv.spkv_compact_append(cache2, tl.dev(Z[:3]), kd, vd, tl.dev(np.array([0, 2, 3], np.int32)),
+                             tl.dev(np.array([0, 0], np.int32)), 1, G_)
+    torch.cuda.synchronize()
+    with pytest.raises(spkv.SpkvError) as ei:
+        spkv.spkv_cache_check(cache2)
+    assert ei.value.code == spkv.SPKV_E_ROWS
+    assert int(cache2.lengths[0].sum()) == 0 and int(cache2.lengths[1].sum()) == wl.n_kv

@@ -31,7 +31,14 @@ def _run(wl, n_rows, seed=7, tau=None, d_hidden=None):
 @pytest.mark.parametrize("name,n_rows,d_hidden", [
     ("tiny", 1024, None),          # f32, VALU
     ("tiny", 37, None),
-    ("decode_32k", 8, None),       # bf16, d_model split over workgroups (decode step)
+    ("tiny", 1, None),             # few rows: one workgroup per hidden unit
+    ("tiny", 16, None),
+    ("decode_32k", 1, None),
+    ("decode_32k", 8, None),       # bf16 decode step (few-row kernel)
+    ("decode_32k", 16, None),      # largest few-row batch
+    ("decode_32k", 3, 256),
+    ("decode_32k", 12, 48),
+    ("decode_32k", 17, None),      # bf16, d_model split over workgroups
     ("decode_32k", 64, None),      # largest split batch
     ("decode_32k", 65, None),      # first full-tile batch, ragged tail
     ("decode_32k", 1500, None),    # several 64-row tiles
@@ -71,3 +78,18 @@ def test_gate_is_deterministic():
     u1, _ = spkv.spkv_gate(gw, H, 0.5)
     u2, _ = spkv.spkv_gate(gw, H, 0.5)
     assert torch.equal(u1, u2)
+
+
+def test_gate_workspace_reuse_across_batch_sizes():
+    # one workspace shared by consecutive calls of every launch shape; each
+    # call leaves it ready for the next
+    wl = inputs.WORKLOADS["decode_32k"]
+    w = tl.calibrated_weights(wl)
+    gw = tl.gate_weights(w, torch.bfloat16)
+    sizes = [16, 5, 40, 3, 1, 64, 8]
+    ws = spkv.workspace(max(spkv.spkv_gate_ws_bytes(gw, n) for n in sizes))
+    for i, n in enumerate(sizes):
+        H = tl.dev(inputs.normal((n, wl.d_model), 6, i, dtype=wl.dtype), torch.bfloat16)
+        u1, z1 = spkv.spkv_gate(gw, H, 0.5, ws=ws)
+        u2, z2 = spkv.spkv_gate(gw, H, 0.5)
+        assert torch.equal(u1, u2) and torch.equal(z1, z2)
