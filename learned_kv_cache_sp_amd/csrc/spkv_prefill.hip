@@ -7,17 +7,21 @@
 // row also sees kept keys of its own chunk once they leave its window (Eq. 4
 // is per token).
 //
-// bf16 (MFMA): a workgroup of 4 waves takes 256 (row, query head) pairs of
-// one key head -- 64 / G query positions per wave, all G heads of the group --
-// and walks one list of 32-key blocks: the cached entries visible to its
-// first row (no mask), the staircase of cached entries that only later rows
-// see (mask pos <= t - w), and the window band (mask 0 <= t - s < w).  Each
-// block is staged once in LDS (keys row-major, values transposed, rows padded
-// against bank conflicts) and read by all four waves; the next block's loads
-// are in flight while the current one is computed.  Per wave and block:
+// bf16 (MFMA): a workgroup of 8 waves (2 per SIMD) takes 256 (row, query
+// head) pairs of one key head -- 32 / G query positions per wave, all G
+// heads of the group -- and walks one list of 64-key blocks: the cached
+// entries visible to its first row (no mask), the staircase of cached
+// entries that only later rows see (mask pos <= t - w), and the window band
+// (mask 0 <= t - s < w).  Whole cached blocks stream into LDS through a
+// 3-stage pipeline of direct global->LDS loads (keys row-major, values
+// already transposed in the cache); the last, partial cached block and the
+// band blocks go through registers (zeroing invalid slots, transposing chunk
+// values).  Both layouts are XOR-swizzled so MFMA operand reads are free of
+// bank conflicts.  Per wave and 32 keys:
 //   S^T[32 keys x 16 pairs] = K . Q^T       (v_mfma_f32_16x16x32_bf16)
 //   O^T[hd x 16 pairs]     += V^T . P^T     (P as a bf16 pair, f32-accurate)
-// for each of its 4 pair tiles, online softmax with a lazily updated max.
+// for each of its 2 pair tiles, online softmax with a lazily updated max.
+// Row tiles are handed out last-first: later rows see more keys.
 //
 // f32 (and a fallback for shapes the MFMA tiling does not take): VALU, one
 // wave per (row, query head), online softmax over the key list.
@@ -94,10 +98,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int PF_NW = 4;           // waves per workgroup
+constexpr int PF_NW = 8;           // waves per workgroup (2 per SIMD)
 constexpr int PF_NT = PF_NW * 64;
-constexpr int PF_PT = 4;           // 16-pair MFMA column tiles per wave
-constexpr int PF_KB = 32;          // keys per block
+constexpr int PF_PT = 2;           // 16-pair MFMA column tiles per wave
+constexpr int PF_KB = 64;          // keys per block
+constexpr int PF_ST = 3;           // LDS stages of the direct-load pipeline
+constexpr int PF_PTMAX = 4096;     // page-table entries staged in LDS
 constexpr float PF_LOG2E = 1.4426950408889634f;
 constexpr float PF_LN2 = 0.6931471805599453f;
 
@@ -140,15 +146,36 @@ __device__ int count_upto(const CacheView &c, const int32_t *pt, int len, int x,
     return lo + 1 + lds_cnt[1];
 }
 
+// LDS layouts of one 64-key block (byte offsets), XOR-swizzled so that the
+// 16 lanes that read one MFMA operand row group hit 16 different 16-byte
+// bank groups:
+//   keys:   row r (HD bf16), 16-byte chunk c at r*2*HD + 16*(c ^ swz_k(r))
+//   values: transposed, row e (64 keys), chunk c at e*128 + 16*(c ^ swz_v(e))
 template <int HD>
-__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__device__ inline int swz_k(int r) {
+    return HD == 128 ? ((r & 3) | (((r >> 3) & 3) << 2)) : (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
+}
+__device__ inline int swz_v(int e) { return (e >> 1) & 7; }
+template <int HD>
+__device__ inline int koff(int r, int c) { return r * (2 * HD) + ((c ^ swz_k<HD>(r)) << 4); }
+__device__ inline int voff(int e, int c) { return e * (2 * PF_KB) + ((c ^ swz_v(e)) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int HD>
+__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a) {
-    constexpr int KROW = HD + 8;         // padded key row (elements)
-    constexpr int VROW = PF_KB + 8;      // padded transposed value row
-    constexpr int CPR = HD / 8;          // 16-byte chunks per key row
-    __shared__ __bf16 lds_k[2][PF_KB][KROW];
-    __shared__ __bf16 lds_vt[2][HD][VROW];
-    __shared__ int lds_pos[2][PF_KB];
+    constexpr int CPR = HD / 8;                  // 16-byte chunks per key row
+    constexpr int KBYTES = PF_KB * 2 * HD;       // key block
+    constexpr int VBYTES = HD * 2 * PF_KB;       // transposed value block
+    constexpr int KI = KBYTES / 1024;            // 1 KB direct loads per key block
+    constexpr int VI = VBYTES / 1024;
+    constexpr int KRPI = 1024 / (2 * HD);        // key rows per direct load
+    constexpr int LPB = (KI + VI) / PF_NW + 1;   // direct loads per wave and block (+ positions)
+    __shared__ __attribute__((aligned(1024))) char lds_kb[PF_ST][KBYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_vb[PF_ST][VBYTES];
+    __shared__ __attribute__((aligned(16))) int lds_pos[PF_ST][PF_KB];
+    __shared__ int lds_pt[PF_PTMAX];
     __shared__ int lds_cnt[2];
 
     const CacheView &c = a.c;
@@ -160,7 +187,8 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int P = c.page_size;
     const int rows_wave = (16 * PF_PT) / G;           // query positions per wave
     const int rows_wg = rows_wave * PF_NW;
-    const int r_base = blockIdx.x * rows_wg;           // chunk-relative first row
+    // the last row tiles see the most keys: hand them out first
+    const int r_base = (gridDim.x - 1 - blockIdx.x) * rows_wg;  // chunk-relative first row
     const int t_min = a.pos0 + r_base;
     const int t_max = a.pos0 + min(a.n_rows, r_base + rows_wg) - 1;
     const int32_t *pt = c.page_table + (int64_t)bg * c.max_pages;
@@ -170,9 +198,14 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int n_full = count_upto(c, pt, len, t_min - w, lds_cnt);  // visible to every row
     const int n_part = count_upto(c, pt, len, t_max - w, lds_cnt);  // visible to the last row
     const int s_lo = max(0, t_min - w + 1);                          // window band
-    const int nb_g = (n_part + PF_KB - 1) / PF_KB;
-    const int nb_b = (t_max - s_lo + 1 + PF_KB - 1) / PF_KB;
-    const int nb = nb_g + nb_b;
+    const int nb_d = n_part / PF_KB;                        // whole cached blocks (direct loads)
+    const int nb_g = (n_part + PF_KB - 1) / PF_KB;          // all cached blocks
+    const int nb_b = (t_max - s_lo + 1 + PF_KB - 1) / PF_KB;  // band blocks
+    const bool pt_lds = nb_d > 0 && ((nb_d * PF_KB - 1) >> c.page_shift) < PF_PTMAX;
+    if (pt_lds) {
+        const int np_ = ((nb_d * PF_KB - 1) >> c.page_shift) + 1;
+        for (int i = threadIdx.x; i < np_; i += PF_NT) lds_pt[i] = pt[i];
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = pf_uniform(threadIdx.x >> 6);
@@ -195,46 +228,80 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int cc = 0; cc < HD / 32; ++cc) qr[ptl][cc] = ok ? *(const bf16x8 *)(qp + 32 * cc) : bf16x8{};
     }
+    __syncthreads();  // page ids staged
 
-    // ---- staging: thread (key kk = tid / CPR, chunk ch = tid % CPR) for keys,
-    // and (dim row e = tid / 4, chunk of 8 keys) for the transposed values ----
-    // Each block needs 32 x CPR key chunks and HD x 4 value chunks; with 256
-    // threads and HD = 128 that is two of each per thread.
-    constexpr int KCH = PF_KB * CPR / PF_NT;     // key chunks per thread
-    constexpr int VCH = HD * (PF_KB / 8) / PF_NT; // value chunks per thread
+    // ---- whole cached blocks: direct global -> LDS loads ---------------------
+    auto page_of = [&](int ent) -> int { return pt_lds ? lds_pt[ent >> c.page_shift] : pt[ent >> c.page_shift]; };
+    auto issue_direct = [&](int j, int st) {
+        const int e0 = j * PF_KB;
+#pragma unroll
+        for (int u = 0; u < KI / PF_NW; ++u) {
+            const int i = wave + PF_NW * u;
+            const int r = i * KRPI + lane / CPR;
+            const int cch = (lane % CPR) ^ swz_k<HD>(r);
+            const int ent = e0 + r;
+            const char *src = c.k_pages + (((int64_t)page_of(ent) * P + (ent & (P - 1))) * HD + 8 * cch) * 2;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_kb[st] + i * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < VI / PF_NW; ++u) {
+            const int i = wave + PF_NW * u;
+            const int e = i * 8 + (lane >> 3);
+            const int cch = (lane & 7) ^ swz_v(e);
+            const int ent = e0 + 8 * cch;
+            const char *src = c.v_pages + (((int64_t)page_of(ent) * HD + e) * P + (ent & (P - 1))) * 2;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_vb[st] + i * 1024), 16, 0, 0);
+        }
+        {
+            // positions of the 64 entries (every wave loads the same values)
+            const int ent = e0 + lane;
+            const int32_t *src = c.pos_pages + (int64_t)page_of(ent) * P + (ent & (P - 1));
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)&lds_pos[st][0], 4, 0, 0);
+        }
+    };
+
+    // ---- the partial cached block and the band: staged through registers ----
+    constexpr int KCH = PF_KB * CPR / PF_NT;        // key chunks per thread
+    constexpr int VCH = HD * (PF_KB / 8) / PF_NT;   // value chunks per thread
     i32x4 kst[KCH], vst[VCH];
     int pst = 0;
-    // value staging for band keys taken from this chunk's rows (row-major V):
-    // thread loads V[key][8 dims] and scatters it into 8 transposed rows
-    auto load_block = [&](int blk) {
+    auto load_staged = [&](int blk) {
         if (blk < nb_g) {
+            // cached block with n_ok < 64 valid entries: invalid keys get zero
+            // values (their slots may hold anything) and position INT_MAX
             const int j0 = blk * PF_KB;
-            const int page = pt[j0 >> c.page_shift];
-            const int slot0 = j0 & (P - 1);
             const int n_ok = min(PF_KB, n_part - j0);
 #pragma unroll
             for (int u = 0; u < KCH; ++u) {
                 const int id = threadIdx.x + u * PF_NT;
                 const int kk = id / CPR, ch = id % CPR;
-                kst[u] = kk < n_ok ? *(const i32x4 *)((const __bf16 *)c.k_pages + ((int64_t)page * P + slot0 + kk) * HD + 8 * ch)
+                const int ent = j0 + kk;
+                kst[u] = kk < n_ok ? *(const i32x4 *)((const __bf16 *)c.k_pages +
+                                                      ((int64_t)pt[ent >> c.page_shift] * P + (ent & (P - 1))) * HD + 8 * ch)
                                    : i32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < VCH; ++u) {
                 const int id = threadIdx.x + u * PF_NT;
                 const int e = id / (PF_KB / 8), kc = id % (PF_KB / 8);
-                i32x4 v = *(const i32x4 *)((const __bf16 *)c.v_pages + ((int64_t)page * HD + e) * P + slot0 + 8 * kc);
-                // keys beyond n_part hold other data: zero them
-                const int first = 8 * kc;
+                const int ent = j0 + 8 * kc;
+                i32x4 v = i32x4{0, 0, 0, 0};
+                if (8 * kc < n_ok) {
+                    v = *(const i32x4 *)((const __bf16 *)c.v_pages + ((int64_t)pt[ent >> c.page_shift] * HD + e) * P +
+                                         (ent & (P - 1)));
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int k0 = first + 2 * q;
-                    const uint32_t mk = (k0 < n_ok ? 0x0000ffffu : 0u) | (k0 + 1 < n_ok ? 0xffff0000u : 0u);
-                    v[q] &= (int32_t)mk;
+                    for (int q = 0; q < 4; ++q) {
+                        const int k0 = 8 * kc + 2 * q;
+                        const uint32_t mk = (k0 < n_ok ? 0x0000ffffu : 0u) | (k0 + 1 < n_ok ? 0xffff0000u : 0u);
+                        v[q] &= (int32_t)mk;
+                    }
                 }
                 vst[u] = v;
             }
-            if (threadIdx.x < PF_KB) pst = threadIdx.x < n_ok ? c.pos_pages[(int64_t)page * P + slot0 + threadIdx.x] : INT_MAX;
+            if (threadIdx.x < PF_KB) {
+                const int ent = j0 + threadIdx.x;
+                pst = threadIdx.x < n_ok ? c.pos_pages[(int64_t)pt[ent >> c.page_shift] * P + (ent & (P - 1))] : INT_MAX;
+            }
         } else {
             const int s0 = s_lo + (blk - nb_g) * PF_KB;
 #pragma unroll
@@ -251,13 +318,11 @@ prefill_bf16_kernel(PrefillArgs a) {
                 }
                 kst[u] = kv;
             }
-            // values: from chunk rows (row-major) -> chunk of 8 dims of one key;
-            // from the ring (transposed) -> 8 keys of one dim.  Band keys below
-            // pos0 come first in the band, so a block mixes the two only once.
+            // values: key kk2, dims 8*dc .. 8*dc+7 (row-major source, or 8
+            // gathers from the transposed ring), scattered on store
 #pragma unroll
             for (int u = 0; u < VCH; ++u) {
                 const int id = threadIdx.x + u * PF_NT;
-                // row-major source: key kk2, dims 8*dc .. 8*dc+7
                 const int kk2 = id / CPR, dc = id % CPR;
                 const int s = s0 + kk2;
                 i32x4 vv = i32x4{0, 0, 0, 0};
@@ -277,19 +342,19 @@ prefill_bf16_kernel(PrefillArgs a) {
             if (threadIdx.x < PF_KB) pst = s0 + threadIdx.x;
         }
     };
-    auto store_block = [&](int blk, int buf) {
+    auto store_staged = [&](int blk, int st) {
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
             const int id = threadIdx.x + u * PF_NT;
             const int kk = id / CPR, ch = id % CPR;
-            *(i32x4 *)&lds_k[buf][kk][8 * ch] = kst[u];
+            *(i32x4 *)(lds_kb[st] + koff<HD>(kk, ch)) = kst[u];
         }
         if (blk < nb_g) {
 #pragma unroll
             for (int u = 0; u < VCH; ++u) {
                 const int id = threadIdx.x + u * PF_NT;
                 const int e = id / (PF_KB / 8), kc = id % (PF_KB / 8);
-                *(i32x4 *)&lds_vt[buf][e][8 * kc] = vst[u];
+                *(i32x4 *)(lds_vb[st] + voff(e, kc)) = vst[u];
             }
         } else {
 #pragma unroll
@@ -298,13 +363,14 @@ prefill_bf16_kernel(PrefillArgs a) {
                 const int kk2 = id / CPR, dc = id % CPR;
                 const bf16x8 vv = __builtin_bit_cast(bf16x8, vst[u]);
 #pragma unroll
-                for (int e2 = 0; e2 < 8; ++e2) lds_vt[buf][8 * dc + e2][kk2] = vv[e2];
+                for (int e2 = 0; e2 < 8; ++e2)
+                    *(__bf16 *)(lds_vb[st] + voff(8 * dc + e2, kk2 >> 3) + 2 * (kk2 & 7)) = vv[e2];
             }
         }
-        if (threadIdx.x < PF_KB) lds_pos[buf][threadIdx.x] = pst;
+        if (threadIdx.x < PF_KB) lds_pos[st][threadIdx.x] = pst;
     };
 
-    // ---- per-wave online softmax state over its 4 pair tiles ----------------
+    // ---- per-wave online softmax state over its pair tiles -------------------
     f32x4 o[PF_PT][HD / 16];
     float m[PF_PT], l[PF_PT];
 #pragma unroll
@@ -315,87 +381,142 @@ prefill_bf16_kernel(PrefillArgs a) {
         l[ptl] = 0.f;
     }
 
-    if (nb > 0) {
-        load_block(0);
-        store_block(0, 0);
-    }
-    __syncthreads();
-    for (int blk = 0; blk < nb; ++blk) {
-        const int buf = blk & 1;
-        if (blk + 1 < nb) load_block(blk + 1);
-        // kind of block: 0 fully visible cached, 1 staircase cached, 2 band
-        const int kind = blk < nb_g ? ((blk + 1) * PF_KB <= n_full ? 0 : 1) : 2;
-        // key rows of the A operand: tile tt row i -> key 8*(i/4) + 4*tt + i%4
-        bf16x8 ka[2][HD / 32];
+    // LDS operand addresses: with the swizzles above, the XOR term of every
+    // operand row a lane reads is a lane constant
+    //   key row 32*hh + 8*(i16/4) + 4*tt + i16%4, chunk 4*cc + q4
+    //   value row 16*nt + i16, chunk 4*hh + q4
+    const int k_lane = (8 * (i16 >> 2) + (i16 & 3)) * (2 * HD);
+    const int k_x = swz_k<HD>(8 * (i16 >> 2) + (i16 & 3));
+    const int v_lane = i16 * (2 * PF_KB);
+    const int v_x = swz_v(i16);
+
+    // one 64-key block from stage st; kind 0: every key visible to every row,
+    // 1: cached keys visible iff position <= t - w, 2: band keys visible iff
+    // 0 <= t - position < w.  Per 32-key half: the score tiles (pair tiles
+    // x 2 key tiles) accumulate side by side, and the value products
+    // of the pair tiles alternate, so that no MFMA waits on the one before.
+    auto compute_block = [&](int st, int kind) {
+        const char *kb = lds_kb[st];
+        const char *vb = lds_vb[st];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int key = 8 * (i16 >> 2) + 4 * tt + (i16 & 3);
+        for (int hh = 0; hh < 2; ++hh) {
+            bf16x8 ka[2][HD / 32];
 #pragma unroll
-            for (int cc = 0; cc < HD / 32; ++cc) ka[tt][cc] = *(const bf16x8 *)&lds_k[buf][key][32 * cc + 8 * q4];
-        }
-        // this lane's 8 keys: 8*q4 + e (positions / entry positions)
-        int kpos[8];
-        if (kind != 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kpos[e] = lds_pos[buf][8 * q4 + e];
-        }
-        bf16x8 pb[PF_PT], pl[PF_PT];
-#pragma unroll
-        for (int ptl = 0; ptl < PF_PT; ++ptl) {
-            f32x4 sacc[2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int cc = 0; cc < HD / 32; ++cc)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], acc, 0, 0, 0);
-                sacc[tt] = acc;
-            }
-            const int t = trow[ptl];
-            float x[8];
-            float mloc = -INFINITY;
+                    ka[tt][cc] = *(const bf16x8 *)(kb + k_lane + (32 * hh + 4 * tt) * (2 * HD) +
+                                                   (((4 * cc + q4) ^ k_x) << 4));
+            f32x4 sc[PF_PT][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = sacc[e >> 2][e & 3] * sl2;
-                if (kind == 1) v = (kpos[e] <= t - w) ? v : -INFINITY;
-                else if (kind == 2) v = (t - kpos[e] >= 0 && t - kpos[e] < w) ? v : -INFINITY;
-                x[e] = v;
-                mloc = fmaxf(mloc, v);
-            }
-            if (__ballot(mloc > m[ptl] + 8.f) != 0) {
-                mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-                mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-                const float m_new = fmaxf(m[ptl], mloc);
-                if (m_new != m[ptl]) {
-                    const float alpha = __builtin_amdgcn_exp2f(m[ptl] - m_new);
+            for (int ptl = 0; ptl < PF_PT; ++ptl)
 #pragma unroll
-                    for (int nt = 0; nt < HD / 16; ++nt) o[ptl][nt] *= alpha;
-                    l[ptl] *= alpha;
-                    m[ptl] = m_new;
+                for (int tt = 0; tt < 2; ++tt) sc[ptl][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cc = 0; cc < HD / 32; ++cc)
+#pragma unroll
+                for (int ptl = 0; ptl < PF_PT; ++ptl)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        sc[ptl][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], sc[ptl][tt], 0, 0, 0);
+            // this lane's 8 keys of the half: 8*q4 + e
+            int kpos[8];
+            if (kind != 0) {
+                const i32x4 p0 = *(const i32x4 *)&lds_pos[st][32 * hh + 8 * q4];
+                const i32x4 p1 = *(const i32x4 *)&lds_pos[st][32 * hh + 8 * q4 + 4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kpos[e] = p0[e];
+                    kpos[4 + e] = p1[e];
                 }
             }
-            const float base = (m[ptl] == -INFINITY) ? 0.f : m[ptl];
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(x[e] - base);
-                psum += pe;
-                pb[ptl][e] = (__bf16)pe;
-                pl[ptl][e] = (__bf16)(pe - (float)pb[ptl][e]);
-            }
-            l[ptl] += psum;
-        }
-        // O^T += V^T . P^T; the V^T operand is shared by the 4 pair tiles
-#pragma unroll
-        for (int nt = 0; nt < HD / 16; ++nt) {
-            const bf16x8 va = *(const bf16x8 *)&lds_vt[buf][16 * nt + i16][8 * q4];
+            bf16x8 pb[PF_PT], pl[PF_PT];
 #pragma unroll
             for (int ptl = 0; ptl < PF_PT; ++ptl) {
-                o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ptl], o[ptl][nt], 0, 0, 0);
-                o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[ptl], o[ptl][nt], 0, 0, 0);
+                const int t = trow[ptl];
+                float x[8];
+                float mraw = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float v = sc[ptl][e >> 2][e & 3];
+                    if (kind == 1) v = (kpos[e] <= t - w) ? v : -INFINITY;
+                    else if (kind == 2) v = ((unsigned)(t - kpos[e]) < (unsigned)w) ? v : -INFINITY;
+                    x[e] = v;
+                    mraw = fmaxf(mraw, v);
+                }
+                float mloc = mraw * sl2;  // scores in the log2 domain
+                // lazily updated reference max (exact result; see the decode kernel)
+                if (__ballot(mloc > m[ptl] + 8.f) != 0) {
+                    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+                    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+                    const float m_new = fmaxf(m[ptl], mloc);
+                    if (m_new != m[ptl]) {
+                        const float alpha = __builtin_amdgcn_exp2f(m[ptl] - m_new);
+#pragma unroll
+                        for (int nt = 0; nt < HD / 16; ++nt) o[ptl][nt] *= alpha;
+                        l[ptl] *= alpha;
+                        m[ptl] = m_new;
+                    }
+                }
+                const float nbase = (m[ptl] == -INFINITY) ? 0.f : -m[ptl];
+                float psum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(x[e], sl2, nbase));  // -inf -> 0
+                    psum += pe;
+                    pb[ptl][e] = (__bf16)pe;
+                    pl[ptl][e] = (__bf16)(pe - (float)pb[ptl][e]);
+                }
+                l[ptl] += psum;
+            }
+            // O^T += V^T . P^T; the V^T operand is shared by the pair tiles
+#pragma unroll
+            for (int nt = 0; nt < HD / 16; ++nt) {
+                const bf16x8 va = *(const bf16x8 *)(vb + v_lane + nt * 16 * (2 * PF_KB) + (((4 * hh + q4) ^ v_x) << 4));
+#pragma unroll
+                for (int ptl = 0; ptl < PF_PT; ++ptl)
+                    o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ptl], o[ptl][nt], 0, 0, 0);
+#pragma unroll
+                for (int ptl = 0; ptl < PF_PT; ++ptl)
+                    o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[ptl], o[ptl][nt], 0, 0, 0);
             }
         }
-        if (blk + 1 < nb) store_block(blk + 1, buf ^ 1);
+    };
+
+    // ---- phase 1: whole cached blocks, PF_ST-stage pipeline -----------------
+    // Block j lives in stage j % PF_ST.  Before computing j a wave waits for
+    // its own loads of j (those of j + 1 may stay in flight), then the
+    // barrier makes every wave's loads of j visible and guarantees that every
+    // wave is done with j - 1, whose stage then receives j + 2.
+    constexpr int WAIT_ONE = (LPB & 15) | (7 << 4) | (15 << 8) | ((LPB >> 4) << 14);  // vmcnt(LPB)
+    constexpr int WAIT_ALL = (7 << 4) | (15 << 8);                                      // vmcnt(0)
+    if (nb_d > 0) issue_direct(0, 0);
+    if (nb_d > 1) issue_direct(1, 1);
+    for (int j = 0; j < nb_d; ++j) {
+        if (j + 1 < nb_d) __builtin_amdgcn_s_waitcnt(WAIT_ONE);
+        else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+        __syncthreads();
+        if (j + 2 < nb_d) issue_direct(j + 2, (j + 2) % PF_ST);
+        compute_block(j % PF_ST, (j + 1) * PF_KB <= n_full ? 0 : 1);
+    }
+    __syncthreads();  // every stage is free again
+
+    // ---- phase 2: partial cached block and band blocks (a few per
+    // workgroup), staged through registers; the stores of block blk + 1 go
+    // to the other stage while blk is computed from its stage ---------------
+    const int b0 = nb_d, nb = nb_g + nb_b;
+    if (b0 < nb) {
+        load_staged(b0);
+        store_staged(b0, 0);
+    }
+    __syncthreads();
+    for (int blk = b0; blk < nb; ++blk) {
+        const int st = (blk - b0) & 1;
+        if (blk + 1 < nb) {
+            load_staged(blk + 1);
+            store_staged(blk + 1, st ^ 1);
+        }
+        compute_block(st, blk < nb_g ? 1 : 2);
         __syncthreads();
     }
 
