@@ -392,12 +392,15 @@ prefill_bf16_kernel(PrefillArgs a) {
 
     // one 64-key block from stage st; kind 0: every key visible to every row,
     // 1: cached keys visible iff position <= t - w, 2: band keys visible iff
-    // 0 <= t - position < w.  Per 32-key half: the score tiles (pair tiles
-    // x 2 key tiles) accumulate side by side, and the value products
-    // of the pair tiles alternate, so that no MFMA waits on the one before.
+    // 0 <= t - position < w.  The scores of both 32-key halves are formed
+    // first (score tiles accumulating side by side), then one max check per
+    // pair tile for the whole block, then exponentials and value products
+    // without branches, the products of the pair tiles alternating so that
+    // no MFMA waits on the one before.
     auto compute_block = [&](int st, int kind) {
         const char *kb = lds_kb[st];
         const char *vb = lds_vb[st];
+        f32x4 sc[2][PF_PT][2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             bf16x8 ka[2][HD / 32];
@@ -407,62 +410,71 @@ prefill_bf16_kernel(PrefillArgs a) {
                 for (int cc = 0; cc < HD / 32; ++cc)
                     ka[tt][cc] = *(const bf16x8 *)(kb + k_lane + (32 * hh + 4 * tt) * (2 * HD) +
                                                    (((4 * cc + q4) ^ k_x) << 4));
-            f32x4 sc[PF_PT][2];
 #pragma unroll
             for (int ptl = 0; ptl < PF_PT; ++ptl)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) sc[ptl][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int tt = 0; tt < 2; ++tt) sc[hh][ptl][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int cc = 0; cc < HD / 32; ++cc)
 #pragma unroll
                 for (int ptl = 0; ptl < PF_PT; ++ptl)
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt)
-                        sc[ptl][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], sc[ptl][tt], 0, 0, 0);
-            // this lane's 8 keys of the half: 8*q4 + e
-            int kpos[8];
-            if (kind != 0) {
+                        sc[hh][ptl][tt] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], sc[hh][ptl][tt], 0, 0, 0);
+        }
+        // masks; this lane's keys are 32*hh + 8*q4 + e
+        if (kind != 0) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
                 const i32x4 p0 = *(const i32x4 *)&lds_pos[st][32 * hh + 8 * q4];
                 const i32x4 p1 = *(const i32x4 *)&lds_pos[st][32 * hh + 8 * q4 + 4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kpos[e] = p0[e];
-                    kpos[4 + e] = p1[e];
+                for (int ptl = 0; ptl < PF_PT; ++ptl) {
+                    const int t = trow[ptl];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int kp = e < 4 ? p0[e] : p1[e - 4];
+                        const bool vis = kind == 1 ? (kp <= t - w) : ((unsigned)(t - kp) < (unsigned)w);
+                        if (!vis) sc[hh][ptl][e >> 2][e & 3] = -INFINITY;
+                    }
                 }
             }
+        }
+        // lazily updated reference max, one check per pair tile and block
+        // (exact result; see the decode kernel)
+        float nbase[PF_PT];
+#pragma unroll
+        for (int ptl = 0; ptl < PF_PT; ++ptl) {
+            float mraw = -INFINITY;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mraw = fmaxf(mraw, sc[hh][ptl][e >> 2][e & 3]);
+            float mloc = mraw * sl2;  // log2 domain
+            if (__ballot(mloc > m[ptl] + 8.f) != 0) {
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+                const float m_new = fmaxf(m[ptl], mloc);
+                if (m_new != m[ptl]) {
+                    const float alpha = __builtin_amdgcn_exp2f(m[ptl] - m_new);
+#pragma unroll
+                    for (int nt = 0; nt < HD / 16; ++nt) o[ptl][nt] *= alpha;
+                    l[ptl] *= alpha;
+                    m[ptl] = m_new;
+                }
+            }
+            nbase[ptl] = (m[ptl] == -INFINITY) ? 0.f : -m[ptl];
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
             bf16x8 pb[PF_PT], pl[PF_PT];
 #pragma unroll
             for (int ptl = 0; ptl < PF_PT; ++ptl) {
-                const int t = trow[ptl];
-                float x[8];
-                float mraw = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float v = sc[ptl][e >> 2][e & 3];
-                    if (kind == 1) v = (kpos[e] <= t - w) ? v : -INFINITY;
-                    else if (kind == 2) v = ((unsigned)(t - kpos[e]) < (unsigned)w) ? v : -INFINITY;
-                    x[e] = v;
-                    mraw = fmaxf(mraw, v);
-                }
-                float mloc = mraw * sl2;  // scores in the log2 domain
-                // lazily updated reference max (exact result; see the decode kernel)
-                if (__ballot(mloc > m[ptl] + 8.f) != 0) {
-                    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-                    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-                    const float m_new = fmaxf(m[ptl], mloc);
-                    if (m_new != m[ptl]) {
-                        const float alpha = __builtin_amdgcn_exp2f(m[ptl] - m_new);
-#pragma unroll
-                        for (int nt = 0; nt < HD / 16; ++nt) o[ptl][nt] *= alpha;
-                        l[ptl] *= alpha;
-                        m[ptl] = m_new;
-                    }
-                }
-                const float nbase = (m[ptl] == -INFINITY) ? 0.f : -m[ptl];
                 float psum = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(fmaf(x[e], sl2, nbase));  // -inf -> 0
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(sc[hh][ptl][e >> 2][e & 3], sl2, nbase[ptl]));  // -inf -> 0
                     psum += pe;
                     pb[ptl][e] = (__bf16)pe;
                     pl[ptl][e] = (__bf16)(pe - (float)pb[ptl][e]);
