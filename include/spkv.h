@@ -17,6 +17,8 @@
  *   spkv_decode_attn     one query per sequence over window + kept pairs (Eq. 3-4)
  *   spkv_prefill_attn    a chunk of queries of one sequence over window + kept
  *                        pairs (Eq. 3-4), for chunked prefill
+ * and spkv_decode_step runs gate, append and decode attention of one decode
+ * step in a single launch.
  *
  * Conventions
  *   - Every call returns an int status (SPKV_OK or a negative SPKV_E_*).
@@ -60,7 +62,8 @@ enum {
 enum {
     SPKV_STATUS_POOL_FULL = 1,  /* pool_next ran past n_pages; rows were dropped */
     SPKV_STATUS_TABLE_FULL = 2, /* a head needed more than max_pages_per_head pages */
-    SPKV_STATUS_BAD_ROWS = 4    /* row_offsets not monotone, or a sequence longer than max_rows */
+    SPKV_STATUS_BAD_ROWS = 4    /* row_offsets not monotone, a sequence longer than max_rows,
+                                   or a negative position; that sequence's rows were skipped */
 };
 
 typedef enum { SPKV_F32 = 0, SPKV_BF16 = 1 } spkv_dtype;
@@ -211,6 +214,46 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q,
                      int64_t ld_q, const int32_t *t, float scale, float *out,
                      float *lse, void *ws, size_t ws_bytes, void *stream);
 size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads);
+
+/*
+ * spkv_decode_step -- one whole decode step of one layer in one launch:
+ *   spkv_gate on the new token's hidden state of every sequence (Eq. 1-2),
+ *   spkv_compact_append of its key/value row with
+ *   SPKV_APPEND_GLOBAL | SPKV_APPEND_WINDOW at position t[b] (only kept
+ *   pairs enter the persistent cache: section 2.1, deployment paragraph),
+ *   and spkv_decode_attn of its query at t[b] (Eq. 3-4).
+ *   The appended global entries have position t > t - w, so they are not
+ *   part of this step's attention (the new row is seen through the window);
+ *   the attention plans from the lengths before the step, and the new
+ *   lengths are stored when the launch ends.
+ *   hidden [batch, d_model] dtype (row b at hidden + b*ld_hidden)
+ *   k, v   [batch, n_kv, head_dim] dtype (row b at k + b*ld_kv)
+ *   q, t, scale, out, lse: as for spkv_decode_attn
+ *   utility [batch, n_kv] f32 or NULL; keep [batch, n_kv] uint8
+ *   ws  at least spkv_decode_step_ws_bytes(c, g, n_q_heads) bytes, zero-filled
+ *       once after allocation (every call leaves its counters at zero; a ws
+ *       of this size also serves spkv_decode_attn).  Calls sharing a ws
+ *       must not overlap.
+ *   Results: utility, keep, the cache contents, lengths and the ring are
+ *   those of the three separate calls, bit for bit; out and lse differ from
+ *   spkv_decode_attn's only in the rounding of the split-K merge (the keys
+ *   are split among workgroups at other points), and are deterministic.
+ * Supported: a bf16 cache with batch <= 16, n_kv <= 16, the gate shapes of
+ *   spkv_gate, d_hidden <= the resident decode grid (compute units x
+ *   workgroups per unit), G as for spkv_decode_attn; otherwise
+ *   SPKV_E_UNSUPPORTED (make the three calls instead).
+ * Capacity overflow drops the row and sets a status bit, and a negative
+ * t[b] writes nothing for that sequence and sets SPKV_STATUS_BAD_ROWS, as
+ * for spkv_compact_append.
+ */
+int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g,
+                     int32_t n_q_heads, const void *hidden, int64_t ld_hidden,
+                     float tau, const void *k, const void *v, int64_t ld_kv,
+                     const void *q, int64_t ld_q, const int32_t *t,
+                     float scale, float *utility, uint8_t *keep, float *out,
+                     float *lse, void *ws, size_t ws_bytes, void *stream);
+size_t spkv_decode_step_ws_bytes(const spkv_cache *c, const spkv_gate_desc *g,
+                                 int32_t n_q_heads);
 
 /*
  * spkv_prefill_attn -- n_rows consecutive query rows of sequence b, Eq. (3)-(4).

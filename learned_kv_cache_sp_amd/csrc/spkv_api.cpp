@@ -221,7 +221,7 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int6
     if (need && (!ws || ws_bytes < need))
         return fail(SPKV_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
     if (need && !aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
-    spkv::DecodeArgs a;
+    spkv::DecodeArgs a = {};
     a.c = spkv::make_view(c);
     a.n_q = n_q_heads;
     a.group = G;
@@ -236,6 +236,88 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int6
     a.max_items = max_items;
     hipError_t e = spkv::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+// attention steps the gate workgroups give up in the fused step (they spend
+// about that long on their hidden unit before planning)
+static const int kFusedShareCut = 3;
+
+size_t spkv_decode_step_ws_bytes(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_heads) {
+    if (!c || !g || c->n_kv <= 0 || n_q_heads <= 0) return 0;
+    return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr, g->d_hidden);
+}
+
+int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_heads, const void *hidden,
+                     int64_t ld_hidden, float tau, const void *k, const void *v, int64_t ld_kv, const void *q,
+                     int64_t ld_q, const int32_t *t, float scale, float *utility, uint8_t *keep, float *out,
+                     float *lse, void *ws, size_t ws_bytes, void *stream) {
+    if (int r = check_cache(c)) return r;
+    if (!g) return fail(SPKV_E_INVALID, "gate descriptor is NULL");
+    if (g->dtype != c->dtype) return fail(SPKV_E_INVALID, "gate dtype %d differs from the cache's", g->dtype);
+    if (g->n_kv != c->n_kv) return fail(SPKV_E_INVALID, "gate n_kv %d vs cache n_kv %d", g->n_kv, c->n_kv);
+    if (g->d_model < 32 || g->d_model % 32)
+        return fail(SPKV_E_UNSUPPORTED, "d_model %d (a positive multiple of 32)", g->d_model);
+    if (g->d_hidden < 16 || g->d_hidden > 256 || g->d_hidden % 16)
+        return fail(SPKV_E_UNSUPPORTED, "d_hidden %d (multiple of 16 in [16, 256])", g->d_hidden);
+    if (!g->w1 || !g->b1 || !g->w2 || !g->b2) return fail(SPKV_E_INVALID, "gate weights NULL");
+    if (!aligned16(g->w1)) return fail(SPKV_E_INVALID, "w1 not 16-byte aligned");
+    if (n_q_heads < 1 || n_q_heads % c->n_kv) return fail(SPKV_E_INVALID, "n_q_heads %d vs n_kv %d", n_q_heads, c->n_kv);
+    const int G = n_q_heads / c->n_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(SPKV_E_UNSUPPORTED, "group size %d (1, 2, 4, 8 or 16)", G);
+    const int grid = decode_grid();
+    if (!spkv::decode_fused_ok(c, g->d_hidden, grid))
+        return fail(SPKV_E_UNSUPPORTED, "fused step needs a bf16 cache, batch <= 16 and d_hidden <= %d; "
+                                        "use spkv_gate, spkv_compact_append and spkv_decode_attn", grid);
+    if (!hidden || !k || !v || !q || !t || !keep || !out)
+        return fail(SPKV_E_INVALID, "hidden / k / v / q / t / keep / out NULL");
+    if (!aligned16(hidden) || !aligned16(k) || !aligned16(v) || !aligned16(q))
+        return fail(SPKV_E_INVALID, "hidden / k / v / q not 16-byte aligned");
+    if (int r = check_ld(ld_hidden, g->d_model, g->dtype, "ld_hidden")) return r;
+    if (int r = check_ld(ld_kv, (int64_t)c->n_kv * c->head_dim, c->dtype, "ld_kv")) return r;
+    if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
+    if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
+    if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
+    int max_items = 0;
+    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items, g->d_hidden);
+    if (!ws || ws_bytes < need) return fail(SPKV_E_WORKSPACE, "decode step workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
+    spkv::DecodeArgs a = {};
+    a.c = spkv::make_view(c);
+    a.n_q = n_q_heads;
+    a.group = G;
+    a.q = (const char *)q;
+    a.ld_q = ld_q;
+    a.t = t;
+    a.scale = scale;
+    a.out = out;
+    a.lse = lse;
+    a.ws = (char *)ws;
+    a.grid = grid;
+    a.max_items = max_items;
+    a.n_cut = g->d_hidden;
+    a.share_cut = kFusedShareCut;
+    a.gate.d_model = g->d_model;
+    a.gate.d_hidden = g->d_hidden;
+    a.gate.n_kv = g->n_kv;
+    a.gate.dtype = g->dtype;
+    a.gate.w1 = g->w1;
+    a.gate.b1 = g->b1;
+    a.gate.w2 = g->w2;
+    a.gate.b2 = g->b2;
+    a.gate.hidden = hidden;
+    a.gate.n_rows = c->batch;
+    a.gate.ld_hidden = ld_hidden;
+    a.gate.tau = tau;
+    a.gate.utility = utility;
+    a.gate.keep = keep;
+    a.k_new = (const char *)k;
+    a.v_new = (const char *)v;
+    a.ld_new = ld_kv;
+    hipError_t e = spkv::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode step launch");
     return SPKV_OK;
 }
 

@@ -55,7 +55,8 @@ __device__ inline bool seq_rows(const CompactArgs &a, int b, int *r0, int *nb, b
     const int lo = a.row_offsets[b];
     const int hi = a.row_offsets[b + 1];
     const int n = hi - lo;
-    if (lo < 0 || n < 0 || n > a.max_rows || hi > a.n_rows) {
+    const int p0 = a.pos0[b];
+    if (lo < 0 || n < 0 || n > a.max_rows || hi > a.n_rows || p0 < 0 || p0 > INT32_MAX - n) {
         if (report && threadIdx.x == 0) atomicOr(a.c.status, SPKV_STATUS_BAD_ROWS);
         return false;
     }
@@ -270,7 +271,7 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
     const int pidx = min(old_len >> c.page_shift, c.max_pages - 1);
     const int cur_page = (global && (old_len & (P - 1)) != 0) ? pt[pidx] : -1;
     const int n = hi - lo;
-    if (lo < 0 || n < 0 || n > a.max_rows || hi > a.n_rows) {
+    if (lo < 0 || n < 0 || n > a.max_rows || hi > a.n_rows || pos < 0 || pos > INT32_MAX - n) {
         if (g == 0 && lane == 0) atomicOr(c.status, SPKV_STATUS_BAD_ROWS);
         return;
     }

@@ -39,6 +39,7 @@
 //   query operand are zero).  Online softmax in the log2 domain.
 #include "spkv_internal.h"
 #include "spkv_device.h"
+#include "spkv_gate_dev.h"
 
 namespace spkv {
 namespace {
@@ -62,11 +63,22 @@ __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x);
 // every record starts 16-byte aligned)
 __host__ __device__ inline int rec_floats(int G, int HD) { return G * HD + 32; }
 
-// workspace: one arrival counter per (b, g), each in its own 256-byte line
-// (the end-of-launch arrivals of all workgroups would otherwise queue on a
-// few lines; zero between calls), then the partials
+// workspace head: one arrival counter per (b, g), each in its own 256-byte
+// line (the end-of-launch arrivals of all workgroups would otherwise queue on
+// a few lines), then one line with the fused step's two counters (gate
+// arrivals at int 0, launch-end arrivals at int 32).  Every call leaves all
+// of them at zero, so one workspace may serve both entry points.
 constexpr int CNT_STRIDE = 64;  // ints
-__host__ __device__ inline size_t ws_header_bytes(int BG) { return (size_t)BG * CNT_STRIDE * 4; }
+__host__ __device__ inline size_t ws_header_bytes(int BG) { return ((size_t)BG * CNT_STRIDE + 64) * 4; }
+// then, for the fused step only, the new lengths (BG ints) and the gate
+// shares ([d_hidden][16][n_kv] floats), each rounded to 256 bytes; then the
+// split-K partials
+constexpr int FUSED_ROWS = 16;  // batch rows the fused gate takes
+__host__ __device__ inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t fused_bytes(int BG, int n_kv, int d_hidden) {
+    return d_hidden <= 0 ? 0
+                         : round256((size_t)BG * 4) + round256((size_t)d_hidden * FUSED_ROWS * n_kv * 4);
+}
 
 // Inclusive block scan of val(i), i < n, into out[1..n] (out[0] = 0); returns the total.
 template <typename Fn>
@@ -147,7 +159,7 @@ __device__ inline StepLanes<HD> step_lanes(int vstride) {
     return o;
 }
 
-template <int HD>
+template <int HD, int CPOL = 0>
 __device__ inline void load_step(const __bf16 *kblk, const __bf16 *vblk, int vstride, const StepLanes<HD> &ln,
                                  bf16x8 (&kr)[2][HD / 32], bf16x8 (&vr)[HD / 16]) {
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kblk, KSTEP * HD * 2);
@@ -156,10 +168,10 @@ __device__ inline void load_step(const __bf16 *kblk, const __bf16 *vblk, int vst
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int cc = 0; cc < HD / 32; ++cc)
-            kr[t][cc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off[t] + 64 * cc, 0, 0));
+            kr[t][cc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off[t] + 64 * cc, 0, CPOL));
 #pragma unroll
     for (int nt = 0; nt < HD / 16; ++nt)
-        vr[nt] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.v_off, nt * 16 * vstride * 2, 0));
+        vr[nt] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.v_off, nt * 16 * vstride * 2, CPOL));
 }
 
 // valid: bit e set when key 8*(lane/16)+e of the step is visible (used only
@@ -246,13 +258,77 @@ __device__ inline void compute_step(WaveState<HD> &st, const bf16x8 *qlds,
 
 
 
+// Fused step: append the new row of every (b, g) whose keep bit is set
+// (SP-KV section 2.1, deployment paragraph: only kept pairs enter the
+// persistent cache), as spkv_compact_append does for one row per sequence.
+// 16 threads per (b, g); the new length goes to lnext (device scope).
 template <int HD>
+__device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, int32_t *lnext) {
+    const CacheView &c = a.c;
+    const int BG = c.batch * c.n_kv;
+    const int P = c.page_size;
+    constexpr int TPP = 16;
+    const int sub = threadIdx.x % TPP;
+    for (int p0 = 0; p0 < BG; p0 += NT / TPP) {
+        const int bg = p0 + (int)threadIdx.x / TPP;
+        if (bg < BG) {
+            const int old = c.lengths[bg];
+            const int tb = a.t[bg / c.n_kv];
+            int newlen = old;
+            if (tb < 0) {
+                // a negative position is refused, as spkv_compact_append does
+                if (sub == 0) atomicOr(c.status, SPKV_STATUS_BAD_ROWS);
+            } else if (keep[bg]) {
+                int32_t *ptab = c.page_table + (int64_t)bg * c.max_pages;
+                int page = -1;
+                if ((old & (P - 1)) == 0) {
+                    // the entry opens a new page
+                    if (sub == 0) {
+                        const int first = old >> c.page_shift;
+                        if (first >= c.max_pages) {
+                            atomicOr(c.status, SPKV_STATUS_TABLE_FULL);
+                        } else {
+                            const int base = atomicAdd(c.pool_next, 1);
+                            if (base >= c.n_pages) {
+                                atomicOr(c.status, SPKV_STATUS_POOL_FULL);
+                            } else {
+                                ptab[first] = base;
+                                page = base;
+                            }
+                        }
+                    }
+                    page = __shfl(page, (int)(threadIdx.x & 63) & ~(TPP - 1));
+                } else {
+                    page = ptab[old >> c.page_shift];
+                }
+                if (page >= 0) {
+                    const int b = bg / c.n_kv;
+                    const int g = bg - b * c.n_kv;
+                    const __bf16 *kn = (const __bf16 *)a.k_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
+                    const __bf16 *vn = (const __bf16 *)a.v_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
+                    const int j = old & (P - 1);
+                    if (sub < HD / 8)
+                        *(bf16x8 *)((__bf16 *)c.k_pages + ((int64_t)page * P + j) * HD + 8 * sub) =
+                            *(const bf16x8 *)(kn + 8 * sub);
+                    for (int e = sub; e < HD; e += TPP) ((__bf16 *)c.v_pages)[((int64_t)page * HD + e) * P + j] = vn[e];
+                    if (sub == 0) c.pos_pages[(int64_t)page * P + j] = tb;
+                    newlen = old + 1;
+                }
+            }
+            if (sub == 0) __hip_atomic_store(&lnext[bg], newlen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int HD, bool FUSED>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) decode_bf16_kernel(DecodeArgs a) {
     __shared__ int lds_F[MAX_BG + 1];     // first flat step of each (b, g)
     __shared__ int lds_len[MAX_BG];
     __shared__ int lds_t[MAX_BG];
     __shared__ int lds_red[NW];
     __shared__ int lds_flag[2];
+    __shared__ int lds_fin;
+    __shared__ uint8_t lds_keep[FUSED_ROWS * 16];  // fused step: keep bits of the new rows
     __shared__ int lds_sbg[NW][ROUND];    // per wave: (b, g) of each staged step
     __shared__ int lds_spg[NW][ROUND];    //           page id (-1: ring step)
     __shared__ int lds_snv[NW][ROUND];    //           visible keys (a prefix of the step)
@@ -267,6 +343,49 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int w = c.window;
     const int nws = w / KSTEP;  // ring steps per (b, g)
     const int P = c.page_size;
+    int32_t *cnt = (int32_t *)a.ws;
+    const size_t fb = FUSED ? fused_bytes(BG, c.n_kv, a.gate.d_hidden) : 0;
+    int32_t *fcnt = cnt + (size_t)BG * CNT_STRIDE;                 // fused: [0] gate, [32] launch end
+    int32_t *lnext = (int32_t *)(a.ws + ws_header_bytes(BG));      // fused: new lengths
+    float *gshare = (float *)(a.ws + ws_header_bytes(BG) + round256((size_t)BG * 4));
+    float *part = (float *)(a.ws + ws_header_bytes(BG) + fb);
+
+    if constexpr (FUSED) {
+        // ---- gate of the new rows: workgroup j < d_hidden takes hidden unit
+        // j; the last of them finishes the gate and appends the kept rows.
+        // New lengths go to lnext and are published when the launch ends, so
+        // that every workgroup plans from the same lengths; the appended
+        // entries (position t) are not visible to this attention anyway.
+        if ((int)blockIdx.x < a.gate.d_hidden) {
+            float *red = &lds_o[0][0][0][0];
+            gate_unit_share<__bf16, FUSED_ROWS, NT>(a.gate, blockIdx.x, gshare, red);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0) lds_fin = arrive_dev(&fcnt[0]) == a.gate.d_hidden - 1;
+            __syncthreads();
+            if (lds_fin) {
+                gate_finish<FUSED_ROWS, NT>(a.gate, gshare, lds_keep);
+                __syncthreads();
+                append_new_rows<HD>(a, lds_keep, lnext);
+                if (threadIdx.x == 0) reset_dev(&fcnt[0]);
+            }
+            __syncthreads();
+        }
+    }
+    // launch end (fused step): the last workgroup out publishes the new lengths
+    auto finish = [&]() {
+        if constexpr (FUSED) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0) lds_fin = arrive_dev(&fcnt[32]) == (int)gridDim.x - 1;
+            __syncthreads();
+            if (lds_fin) {
+                for (int i = threadIdx.x; i < BG; i += NT)
+                    c.lengths[i] = __hip_atomic_load(&lnext[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (threadIdx.x == 0) reset_dev(&fcnt[32]);
+            }
+        }
+    };
 
     // ---- flat step list; every workgroup derives it identically ------------
     for (int i = threadIdx.x; i < BG; i += NT) lds_len[i] = c.lengths[i];
@@ -274,14 +393,25 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     __syncthreads();
     const int total = uniform(block_scan(BG, [&](int i) { return nws + (lds_len[i] + KSTEP - 1) / KSTEP; },
                                          lds_F, lds_red));
-    const int spg = (total + gridDim.x - 1) / gridDim.x;  // steps per workgroup
+    // Shares: workgroup x takes [w0(x), w0(x+1)); the first n_cut workgroups
+    // (in a fused step they ran a gate unit first) take cut steps fewer.
+    const int spg0 = (total + gridDim.x - 1) / gridDim.x;
+    const int n_cut = FUSED ? min(a.n_cut, (int)gridDim.x) : 0;
+    const int cut = FUSED ? min(a.share_cut, spg0 / 2) : 0;
+    const int spg = (total + n_cut * cut + gridDim.x - 1) / gridDim.x;  // >= 2 * cut
+    const int cut_end = n_cut * (spg - cut);
+    auto w0 = [&](int x) -> int { return x * spg - min(x, n_cut) * cut; };
+    auto owner = [&](int s) -> int { return s < cut_end ? s / (spg - cut) : n_cut + (s - cut_end) / spg; };
     // One partial per (workgroup, (b, g)) that meet, at slot workgroup + bg:
     // ranges are contiguous and in order, so if workgroup x meets (b, g) then
     // x+1 cannot meet an earlier (b, g) -- the slots are distinct, and those
-    // of one (b, g) are consecutive, from F[bg]/spg + bg to (F[bg+1]-1)/spg + bg.
-    const int W0 = blockIdx.x * spg;
-    const int W1 = min(total, W0 + spg);
-    if (W0 >= W1) return;  // (uniform over the workgroup)
+    // of one (b, g) are consecutive, from owner(F[bg]) + bg to owner(F[bg+1]-1) + bg.
+    const int W0 = min(total, w0(blockIdx.x));
+    const int W1 = min(total, w0(blockIdx.x + 1));
+    if (W0 >= W1) {  // (uniform over the workgroup)
+        finish();
+        return;
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -289,8 +419,6 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int q4 = lane >> 4;
     const float sl2 = a.scale * LOG2E;
     const int rec = rec_floats(G, HD);
-    int32_t *cnt = (int32_t *)a.ws;
-    float *part = (float *)(a.ws + ws_header_bytes(BG));
     const StepLanes<HD> lanes_ring = step_lanes<HD>(w);
     const StepLanes<HD> lanes_page = step_lanes<HD>(P);
     // this wave's steps: W0 + wave + NW * k (the 4 waves of the workgroup
@@ -379,6 +507,25 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         if (page < 0) {
             const __bf16 *kb = (const __bf16 *)c.ring_k + ((int64_t)bg * w + ls * KSTEP) * HD;
             const __bf16 *vb = (const __bf16 *)c.ring_v + (int64_t)bg * HD * w + ls * KSTEP;
+            if constexpr (FUSED) {
+                const int b = bg / c.n_kv;
+                const int tb = uniform(lds_t[b]);
+                if (tb >= 0 && ls == (tb % w) / KSTEP) {
+                    // this step holds the new token: write its row into the
+                    // ring first, then read the step past the L1 cache
+                    const int g = bg - b * c.n_kv;
+                    const int slot = tb % w;
+                    const __bf16 *kn = (const __bf16 *)a.k_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
+                    const __bf16 *vn = (const __bf16 *)a.v_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
+                    if (lane < HD / 8)
+                        *(bf16x8 *)((__bf16 *)c.ring_k + ((int64_t)bg * w + slot) * HD + 8 * lane) =
+                            *(const bf16x8 *)(kn + 8 * lane);
+                    for (int e = lane; e < HD; e += 64) ((__bf16 *)c.ring_v)[((int64_t)bg * HD + e) * w + slot] = vn[e];
+                    __builtin_amdgcn_s_waitcnt(0);
+                    load_step<HD, 1>(kb, vb, w, lanes_ring, kr, vr);
+                    return;
+                }
+            }
             load_step<HD>(kb, vb, w, lanes_ring, kr, vr);
         } else {
             const int slot0 = ((ls - nws) * KSTEP) & (P - 1);
@@ -429,8 +576,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         return (int64_t)b * a.n_q + (bg - b * c.n_kv) * G + h;
     };
     auto parts_of = [&](int bg, int &part0, int &n_parts) {
-        part0 = lds_F[bg] / spg + bg;  // first slot of (b, g)
-        n_parts = (lds_F[bg + 1] - 1) / spg + bg - part0 + 1;
+        part0 = owner(lds_F[bg]) + bg;  // first slot of (b, g)
+        n_parts = owner(lds_F[bg + 1] - 1) + bg - part0 + 1;
     };
     // Partials are handed between workgroups with 16-byte device-scope
     // (sc1) buffer stores and loads: they bypass the non-coherent per-XCD L2
@@ -628,7 +775,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }
 
     // ---- the last (b, g), if shared: publish, arrive, the last arrival merges
-    if (!pub_last) return;
+    if (!pub_last) {
+        finish();
+        return;
+    }
     __syncthreads();
     publish(0, bg_last, threadIdx.x, NT);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
@@ -640,6 +790,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }
     __syncthreads();
     if (lds_flag[1]) merge(1, &bg_last);
+    finish();
 }
 
 // ---------------------------------------------------------------------------
@@ -696,7 +847,7 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
 
 }  // namespace
 
-size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out) {
+size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_hidden) {
     if (c->dtype != SPKV_BF16) {
         if (max_items_out) *max_items_out = 0;
         return 0;
@@ -707,25 +858,39 @@ size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_ou
     // segment, and consecutive (b, g) share at most one workgroup
     const int max_slots = grid + BG;
     if (max_items_out) *max_items_out = max_slots;
-    return ws_header_bytes(BG) + (size_t)max_slots * rec_floats(G, c->head_dim) * sizeof(float);
+    return ws_header_bytes(BG) + fused_bytes(BG, c->n_kv, fused_hidden) +
+           (size_t)max_slots * rec_floats(G, c->head_dim) * sizeof(float);
+}
+
+bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid) {
+    return c->dtype == SPKV_BF16 && c->batch <= FUSED_ROWS && d_hidden <= grid && c->n_kv <= 16;
 }
 
 int decode_blocks_per_cu() {
-    int n128 = 0, n64 = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n128, decode_bf16_kernel<128>, NT, 0) != hipSuccess)
-        n128 = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n64, decode_bf16_kernel<64>, NT, 0) != hipSuccess)
-        n64 = 1;
-    return max(1, min(n128, n64));
+    int n = 1 << 20;
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, false>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, false>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, true>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, true>, NT, 0) == hipSuccess) n = min(n, v);
+    return max(1, n == (1 << 20) ? 1 : n);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const CacheView &c = a.c;
+    const bool fused = a.gate.d_hidden > 0;
     if (c.dtype == SPKV_BF16) {
-        if (c.head_dim == 128)
-            hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3(a.grid), dim3(NT), 0, s, a);
-        else
-            hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(a.grid), dim3(NT), 0, s, a);
+        if (c.head_dim == 128) {
+            if (fused)
+                hipLaunchKernelGGL((decode_bf16_kernel<128, true>), dim3(a.grid), dim3(NT), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_bf16_kernel<128, false>), dim3(a.grid), dim3(NT), 0, s, a);
+        } else {
+            if (fused)
+                hipLaunchKernelGGL((decode_bf16_kernel<64, true>), dim3(a.grid), dim3(NT), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_bf16_kernel<64, false>), dim3(a.grid), dim3(NT), 0, s, a);
+        }
     } else {
         const dim3 grid(c.batch * a.n_q);
         if (c.head_dim == 128)

@@ -18,6 +18,7 @@
 // kernel.
 #include "spkv_internal.h"
 #include "spkv_device.h"
+#include "spkv_gate_dev.h"
 
 namespace spkv {
 namespace {
@@ -200,114 +201,22 @@ __global__ void __launch_bounds__(NT) gate_valu_kernel(GateArgs a) {
 
 // ---------------------------------------------------------------------------
 // Few rows (n_rows <= NR <= 16): workgroup j computes hidden unit j for every
-// row over the whole d_model (16-byte loads of W1 row j and of each hidden
-// row), reduces across the workgroup in a fixed tree, applies bias and ReLU,
-// and stores its share W2[k][j] * a_j of logit (row, k).  The last workgroup
-// to arrive adds the shares in unit order, then sigmoid and threshold.
+// row over the whole d_model and stores its share W2[k][j] * a_j of logit
+// (row, k); the last workgroup to arrive adds the shares in unit order, then
+// sigmoid and threshold (gate_unit_share / gate_finish).
 template <typename T, int NR>
 __global__ void __launch_bounds__(NT) gate_tiny_kernel(GateArgs a) {
-    constexpr int V = 16 / sizeof(T);
-    typedef T tvec __attribute__((ext_vector_type(V)));
-    __shared__ float red[NT / 64][NR];
+    __shared__ float red[(NT / 64) * NR];
     __shared__ int lds_last;
-    const int j = blockIdx.x;
-    const int n = (int)a.n_rows;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const T *w = (const T *)a.w1 + (int64_t)j * a.d_model;
-    const T *h = (const T *)a.hidden;
-    // second-layer weight and first-layer bias of this unit, fetched up front
-    const int nkv = a.n_kv;
-    const int my_k = threadIdx.x % nkv;
-    const float w2j = a.w2[(size_t)my_k * a.d_hidden + j];
-    const float b1j = a.b1[j];
-    // final sum (last workgroup only): TPO threads per logit, a power of two
-    const int outs = n * nkv;
-    int tpo = 1;
-    while (tpo * 2 * outs <= NT && tpo < 32) tpo *= 2;
-    const int o = threadIdx.x / tpo;
-    const int q = threadIdx.x - o * tpo;
-    const float b2o = o < outs ? a.b2[o % nkv] : 0.f;
-    float acc[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-    const int nvec = a.d_model / V;
-    // rows past n_rows re-read the last row (their sums are never used), so
-    // that every load is unconditional and all of them are in flight at once
-    int64_t roff[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) roff[r] = (int64_t)(r < n ? r : n - 1) * a.ld_hidden;
-#pragma unroll 2
-    for (int c = threadIdx.x; c < nvec; c += NT) {
-        const tvec wv = *(const tvec *)(w + (int64_t)c * V);
-        tvec hv[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) hv[r] = *(const tvec *)(h + roff[r] + (int64_t)c * V);
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[r] = fmaf((float)wv[e], (float)hv[r][e], acc[r]);
-    }
-    // butterfly over the wave, all rows interleaved so the lane exchanges overlap
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r] += __shfl_xor(acc[r], off);
-    if (lane == 0)
-#pragma unroll
-        for (int r = 0; r < NR; ++r) red[wave][r] = acc[r];
-    __syncthreads();
-
     int *cnt = (int *)a.ws;
     float *part = a.ws + WS_HEADER_FLOATS;  // [d_hidden][NR][n_kv]
-    if (threadIdx.x < NR * nkv) {
-        const int r = threadIdx.x / nkv;
-        const int k = threadIdx.x - r * nkv;  // == my_k
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < NT / 64; ++v) s += red[v][r];
-        const float act = relu_keep_nan(s + b1j);
-        store_dev(part + ((size_t)j * NR + r) * nkv + k, w2j * act);
-    }
+    gate_unit_share<T, NR, NT>(a, blockIdx.x, part, red);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's share is stored
     __syncthreads();
     if (threadIdx.x == 0) lds_last = arrive_dev(cnt) == (int)gridDim.x - 1;
     __syncthreads();
     if (!lds_last) return;
-
-    // thread q of a logit adds the shares of units q, q + TPO, ... (all its
-    // loads issued before any add); the TPO sums are then added in a fixed tree
-    float s = 0.f;
-    if (o < outs) {
-        const int r = o / nkv;
-        const int k = o - r * nkv;
-        const float *p = part + (size_t)r * nkv + k;
-        const size_t stride = (size_t)NR * nkv;
-        const int hg = a.d_hidden;
-        for (int j0 = q; j0 < hg; j0 += 32 * tpo) {
-            float v[32];
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                const int jj = j0 + e * tpo;
-                v[e] = jj < hg ? load_dev(p + (size_t)jj * stride) : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 32; ++e) s += v[e];
-        }
-    }
-    // combine the TPO partial sums of each logit in q order (lanes of a logit
-    // are consecutive and TPO <= 32 divides the wave)
-    for (int off = 1; off < tpo; off <<= 1) {
-        const float y = __shfl_down(s, off);
-        if ((q & (2 * off - 1)) == 0) s += y;
-    }
-    if (o < outs && q == 0) {
-        const int r = o / nkv;
-        const int k = o - r * nkv;
-        const float u = sigmoid_f(s + b2o);
-        if (a.utility) a.utility[(int64_t)r * nkv + k] = u;
-        a.keep[(int64_t)r * nkv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
-    }
+    gate_finish<NR, NT>(a, part, nullptr);
     if (threadIdx.x == 0) reset_dev(cnt);
 }
 

@@ -67,7 +67,8 @@ class CacheDesc(ctypes.Structure):
 
 EXPORTS = [
     "spkv_gate", "spkv_gate_ws_bytes", "spkv_compact_append", "spkv_compact_ws_bytes",
-    "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_prefill_attn", "spkv_prefill_ws_bytes",
+    "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_decode_step", "spkv_decode_step_ws_bytes",
+    "spkv_prefill_attn", "spkv_prefill_ws_bytes",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
     "spkv_last_error", "spkv_version",
 ]
@@ -92,6 +93,9 @@ def load_library(path: str = LIB_PATH):
         "spkv_compact_ws_bytes": ([C, i32, i32], sz),
         "spkv_decode_attn": ([C, i32, vp, i64, vp, f32, vp, vp, vp, sz, vp], ctypes.c_int),
         "spkv_decode_ws_bytes": ([C, i32], sz),
+        "spkv_decode_step": ([C, G, i32, vp, i64, f32, vp, vp, i64, vp, i64, vp, f32, vp, vp, vp, vp, vp, sz, vp],
+                             ctypes.c_int),
+        "spkv_decode_step_ws_bytes": ([C, G, i32], sz),
         "spkv_prefill_attn": ([C, i32, i32, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp, vp, sz, vp],
                               ctypes.c_int),
         "spkv_prefill_ws_bytes": ([C, i32, i32], sz),
@@ -347,6 +351,50 @@ def spkv_decode_attn(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: floa
     _check(lib.spkv_decode_attn(ctypes.byref(cache.desc()), nq, _ptr(q), _row_stride(q), _ptr(t),
                                 float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
     return out, lse
+
+
+def spkv_decode_step_ws_bytes(cache: Cache, weights: GateWeights, n_q_heads: int) -> int:
+    return int(load_library().spkv_decode_step_ws_bytes(ctypes.byref(cache.desc()), ctypes.byref(weights.desc()),
+                                                        n_q_heads))
+
+
+def spkv_decode_step(cache: Cache, weights: GateWeights, hidden: torch.Tensor, tau: float, k: torch.Tensor,
+                     v: torch.Tensor, q: torch.Tensor, t: torch.Tensor, scale: float, utility=None, keep=None,
+                     out=None, lse=None, ws=None, stream=None):
+    """Gate + append (GLOBAL | WINDOW) + decode attention of one step in one launch.
+    hidden [batch, d_model], k / v [batch, n_kv, hd], q [batch, n_q, hd], t [batch] int32.
+    Returns (utility, keep, out, lse)."""
+    lib = load_library()
+    B, nq, hd = q.shape
+    dev = q.device
+    nkv = weights.desc().n_kv
+    if keep is None:
+        keep = torch.empty((B, nkv), dtype=torch.uint8, device=dev)
+    if utility is None:
+        utility = torch.empty((B, nkv), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, nq, hd), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
+    _need_gpu(hidden, k, v, q, t, keep, utility, out, lse)
+    if hidden.dtype != weights.w1.dtype:
+        raise ValueError("hidden and w1 dtypes differ")
+    if q.dtype != cache.dtype or k.dtype != cache.dtype or v.dtype != cache.dtype:
+        raise ValueError("q / k / v dtype differs from the cache")
+    if t.dtype != torch.int32:
+        raise ValueError("t must be int32")
+    ld = _row_stride(k)
+    if _row_stride(v) != ld:
+        raise ValueError("k and v must share a row stride")
+    need = spkv_decode_step_ws_bytes(cache, weights, nq)
+    if ws is None and need:
+        ws = workspace(need, dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.spkv_decode_step(ctypes.byref(cache.desc()), ctypes.byref(weights.desc()), nq, _ptr(hidden),
+                                _row_stride(hidden), float(tau), _ptr(k), _ptr(v), ld, _ptr(q), _row_stride(q),
+                                _ptr(t), float(scale), _ptr(utility), _ptr(keep), _ptr(out), _ptr(lse), _ptr(ws),
+                                ws_bytes, _stream(stream)))
+    return utility, keep, out, lse
 
 
 def spkv_prefill_ws_bytes(cache: Cache, n_q_heads: int, n_rows: int) -> int:
