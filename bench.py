@@ -11,6 +11,9 @@ sequence:
     spkv_compact_append keep bits + K/V -> persistent cache and window ring
     spkv_decode_attn    every query head of every sequence over window + kept keys
 
+run as one spkv_decode_step launch that does all three (``--step-mode
+separate`` times the three calls instead).
+
 Other workloads (``--workload``): ``decode_131k`` (batch 4, 131072 tokens,
 per-head keep 2-60 %), ``ragged_32`` (batch 32, contexts 4096-65536, 15 %,
 hidden states buffered: window append + attention every step, gate + kept
@@ -79,6 +82,9 @@ def parse():
                    choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k"])
     p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
+    p.add_argument("--step-mode", choices=("auto", "fused", "separate"), default="auto",
+                   help="decode without a gate buffer: one spkv_decode_step launch per step (fused; auto "
+                        "where the batch allows) or spkv_gate + spkv_compact_append + spkv_decode_attn")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     p.add_argument("--copy-calibration", action="store_true",
@@ -182,15 +188,17 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, workload: str) ->
     return "\n".join(out)
 
 
-def stored_traffic(kernel: str, workload: str):
+def stored_traffic(kernel: str, workload: str, variant: str | None = None):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the kernel source in this tree; else None."""
+    on the kernel source in this tree (and on this instantiation); else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc_traffic.txt")
     if not os.path.exists(path):
         return None
     for line in open(path):
         if line.startswith("traffic_json: "):
             rec = json.loads(line[len("traffic_json: "):])
+            if variant is not None and rec.get("kernel") != variant:
+                return None
             if rec.get("workload") == workload and rec.get("source_sha256") == _source_hash(kernel):
                 return float(rec["bytes_per_launch"])
     return None
@@ -291,7 +299,13 @@ def bench_decode(args, wl):
     lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
     gate_ws = spkv.workspace(spkv.spkv_gate_ws_bytes(gw, B * buf))
     comp_ws = spkv.workspace(spkv.spkv_compact_ws_bytes(caches[0], B * buf, buf))
-    dec_ws = [spkv.workspace(spkv.spkv_decode_ws_bytes(c, nq)) for c in caches]
+    fused = buf == 1 and args.step_mode != "separate" and B <= 16
+    if args.step_mode == "fused" and not fused:
+        raise SystemExit("the fused step takes up to 16 sequences and no gate buffer")
+    if fused:
+        dec_ws = [spkv.workspace(spkv.spkv_decode_step_ws_bytes(c, gw, nq)) for c in caches]
+    else:
+        dec_ws = [spkv.workspace(spkv.spkv_decode_ws_bytes(c, nq)) for c in caches]
 
     # pre-marshalled raw calls (keeps host overhead far below the GPU time)
     lib = spkv.load_library()
@@ -316,6 +330,8 @@ def bench_decode(args, wl):
 
     def pre(s):
         """work of step s before its decode: gate + append (or window append)"""
+        if fused:
+            return
         l, i = s % L, s // L
         f, j = i // buf, i % buf
         cd = ctypes.byref(cdescs[l])
@@ -335,6 +351,15 @@ def bench_decode(args, wl):
 
     def dec(s):
         l, i = s % L, s // L
+        if fused:
+            rc = lib.spkv_decode_step(ctypes.byref(cdescs[l]), ctypes.byref(gdesc), nq, Hl[l, i].data_ptr(), d,
+                                      wl.tau, Kl[l, i].data_ptr(), Vl[l, i].data_ptr(), nkv * hd,
+                                      Ql[l, i].data_ptr(), nq * hd, tpos[i].data_ptr(), scale, ul[l, i].data_ptr(),
+                                      zl[l, i].data_ptr(), out.data_ptr(), lse.data_ptr(), dws[l][0], dws[l][1],
+                                      sp)
+            if rc:
+                raise RuntimeError(lib.spkv_last_error().decode())
+            return
         rc = lib.spkv_decode_attn(ctypes.byref(cdescs[l]), nq, Ql[l, i].data_ptr(), nq * hd, tpos[i].data_ptr(),
                                   scale, out.data_ptr(), lse.data_ptr(), dws[l][0], dws[l][1], sp)
         if rc:
@@ -418,7 +443,15 @@ def bench_decode(args, wl):
                     vis = vis + Estep[l, b, p - ctxs[b] + 1]
                 tot += int(vis.sum())
             tot += nkv * min(t + 1, w)
-        bytes_per.append(float(tot * 2 * hd * 2))
+        extra = 0
+        if fused:
+            # the launch also reads W1 and the hidden rows (gate), reads the new
+            # K/V rows and writes them to the ring, and writes the kept ones
+            # (K, V, position) to the pages
+            kept_now = int(zl_h[l, i].sum())
+            extra = (wl.d_hidden * d * 2 + B * d * 2 + 2 * B * nkv * hd * 2 * 2
+                     + kept_now * (2 * hd * 2 + 4))
+        bytes_per.append(float(tot * 2 * hd * 2 + extra))
     bytes_per = np.array(bytes_per)
     grp_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["d0"], ev["d1"])])
     dec_ms = grp_ms / np.array(ev["n"])          # mean launch time within each bracket
@@ -444,14 +477,18 @@ def bench_decode(args, wl):
                    "gate": f"{d}->{wl.d_hidden}->{nkv}", "keep_target": list(wl.keep),
                    "keep_measured": [round(float(x), 4) for x in kept_frac],
                    "page_size": P, "layer_caches_rotated": L, "gate_buffer": buf,
-                   "step": ("spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"
+                   "step": ("spkv_decode_step: gate, kept-row + window append and decode attention in "
+                            "one launch (one token per sequence)" if fused else
+                            "spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"
                             if buf == 1 else
                             f"spkv_compact_append(window) + spkv_decode_attn every step; spkv_gate + "
                             f"spkv_compact_append(kept) of {B}x{buf} buffered rows when a buffer fills")},
-        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel (spkv_decode_attn)",
+        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel (%s)" % (
+                         "spkv_decode_step" if fused else "spkv_decode_attn"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic("decode_bf16_kernel", wl.name),
+                     "traffic": stored_traffic("decode_bf16_kernel", wl.name,
+                                               f"decode_bf16_kernel<{hd}, {'true' if fused else 'false'}>"),
                      "bytes_per_launch": float(bytes_per.mean()),
                      "launch_us": _stats_us(dec_ms), "launches_per_bracket": L},
         "host_wall_s": round(wall, 4),

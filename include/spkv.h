@@ -55,15 +55,19 @@ enum {
     SPKV_E_HIP = -3,         /* a HIP runtime call or launch failed */
     SPKV_E_CAPACITY = -4,    /* device flag: page pool or page table exhausted */
     SPKV_E_WORKSPACE = -5,   /* workspace smaller than the *_ws_bytes figure */
-    SPKV_E_ROWS = -6         /* device flag: row_offsets inconsistent with n_rows / max_rows */
+    SPKV_E_ROWS = -6,        /* device flag: row_offsets inconsistent with n_rows / max_rows */
+    SPKV_E_TIMEOUT = -7      /* device flag: a wait inside spkv_decode_step ran out */
 };
 
 /* device status bits written by the kernels into cache->status[0] */
 enum {
     SPKV_STATUS_POOL_FULL = 1,  /* pool_next ran past n_pages; rows were dropped */
     SPKV_STATUS_TABLE_FULL = 2, /* a head needed more than max_pages_per_head pages */
-    SPKV_STATUS_BAD_ROWS = 4    /* row_offsets not monotone, a sequence longer than max_rows,
+    SPKV_STATUS_BAD_ROWS = 4,   /* row_offsets not monotone, a sequence longer than max_rows,
                                    or a negative position; that sequence's rows were skipped */
+    SPKV_STATUS_STEP_TIMEOUT = 8 /* spkv_decode_step: arrivals it waits for did not come (the
+                                   launch had fewer workgroups resident than it needs); the
+                                   step's append or new lengths were not stored */
 };
 
 typedef enum { SPKV_F32 = 0, SPKV_BF16 = 1 } spkv_dtype;
@@ -224,23 +228,27 @@ size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads);
  *   and spkv_decode_attn of its query at t[b] (Eq. 3-4).
  *   The appended global entries have position t > t - w, so they are not
  *   part of this step's attention (the new row is seen through the window);
- *   the attention plans from the lengths before the step, and the new
- *   lengths are stored when the launch ends.
+ *   the attention plans from the lengths before the step.
+ *   Launches one kernel on the resident decode grid: the last workgroup
+ *   finishes the gate, appends the kept rows and stores the new lengths once
+ *   every other workgroup has read the old ones; it waits for the others'
+ *   arrivals (bounded polls: if they never come -- fewer workgroups resident
+ *   than the grid, e.g. compute units reserved by another process -- it sets
+ *   SPKV_STATUS_STEP_TIMEOUT and leaves the append or lengths undone).
  *   hidden [batch, d_model] dtype (row b at hidden + b*ld_hidden)
  *   k, v   [batch, n_kv, head_dim] dtype (row b at k + b*ld_kv)
  *   q, t, scale, out, lse: as for spkv_decode_attn
  *   utility [batch, n_kv] f32 or NULL; keep [batch, n_kv] uint8
  *   ws  at least spkv_decode_step_ws_bytes(c, g, n_q_heads) bytes, zero-filled
  *       once after allocation (every call leaves its counters at zero; a ws
- *       of this size also serves spkv_decode_attn).  Calls sharing a ws
- *       must not overlap.
+ *       of this size also serves spkv_decode_attn; zero it again after a
+ *       step timeout).  Calls sharing a ws must not overlap.
  *   Results: utility, keep, the cache contents, lengths and the ring are
  *   those of the three separate calls, bit for bit; out and lse differ from
  *   spkv_decode_attn's only in the rounding of the split-K merge (the keys
  *   are split among workgroups at other points), and are deterministic.
  * Supported: a bf16 cache with batch <= 16, n_kv <= 16, the gate shapes of
- *   spkv_gate, d_hidden <= the resident decode grid (compute units x
- *   workgroups per unit), G as for spkv_decode_attn; otherwise
+ *   spkv_gate, G as for spkv_decode_attn; otherwise
  *   SPKV_E_UNSUPPORTED (make the three calls instead).
  * Capacity overflow drops the row and sets a status bit, and a negative
  * t[b] writes nothing for that sequence and sets SPKV_STATUS_BAD_ROWS, as
@@ -288,7 +296,8 @@ size_t spkv_cache_bytes(const spkv_cache *c, size_t sizes[7]);
 int spkv_cache_reset(const spkv_cache *c, void *stream);
 
 /* Synchronise `stream`, read the sticky status and map it to SPKV_OK,
- * SPKV_E_CAPACITY or SPKV_E_ROWS; *status_bits (may be NULL) receives the bits. */
+ * SPKV_E_CAPACITY, SPKV_E_ROWS or SPKV_E_TIMEOUT; *status_bits (may be NULL)
+ * receives the bits. */
 int spkv_cache_check(const spkv_cache *c, void *stream, int32_t *status_bits);
 
 const char *spkv_status_str(int status);

@@ -89,6 +89,7 @@ const char *spkv_status_str(int status) {
     case SPKV_E_CAPACITY: return "cache capacity exhausted (rows dropped)";
     case SPKV_E_WORKSPACE: return "workspace too small";
     case SPKV_E_ROWS: return "row offsets inconsistent with n_rows / max_rows_per_seq";
+    case SPKV_E_TIMEOUT: return "a wait inside a fused decode step ran out";
     default: return "unknown status";
     }
 }
@@ -241,12 +242,12 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int6
 
 // ----------------------------------------------------------------------------
 // attention steps the gate workgroups give up in the fused step (they spend
-// about that long on their hidden unit before planning)
-static const int kFusedShareCut = 3;
+// about that long on their gate item before planning)
+static const int kFusedShareCut = 10;
 
 size_t spkv_decode_step_ws_bytes(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_heads) {
     if (!c || !g || c->n_kv <= 0 || n_q_heads <= 0) return 0;
-    return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr, g->d_hidden);
+    return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr, g->d_model, g->d_hidden);
 }
 
 int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_heads, const void *hidden,
@@ -269,8 +270,8 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
         return fail(SPKV_E_UNSUPPORTED, "group size %d (1, 2, 4, 8 or 16)", G);
     const int grid = decode_grid();
     if (!spkv::decode_fused_ok(c, g->d_hidden, grid))
-        return fail(SPKV_E_UNSUPPORTED, "fused step needs a bf16 cache, batch <= 16 and d_hidden <= %d; "
-                                        "use spkv_gate, spkv_compact_append and spkv_decode_attn", grid);
+        return fail(SPKV_E_UNSUPPORTED, "fused step needs a bf16 cache and batch <= 16; "
+                                        "use spkv_gate, spkv_compact_append and spkv_decode_attn");
     if (!hidden || !k || !v || !q || !t || !keep || !out)
         return fail(SPKV_E_INVALID, "hidden / k / v / q / t / keep / out NULL");
     if (!aligned16(hidden) || !aligned16(k) || !aligned16(v) || !aligned16(q))
@@ -281,7 +282,7 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
     if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
     if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
     int max_items = 0;
-    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items, g->d_hidden);
+    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items, g->d_model, g->d_hidden);
     if (!ws || ws_bytes < need) return fail(SPKV_E_WORKSPACE, "decode step workspace %zu < %zu bytes", ws_bytes, need);
     if (!aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
     spkv::DecodeArgs a = {};
@@ -297,7 +298,6 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
     a.ws = (char *)ws;
     a.grid = grid;
     a.max_items = max_items;
-    a.n_cut = g->d_hidden;
     a.share_cut = kFusedShareCut;
     a.gate.d_model = g->d_model;
     a.gate.d_hidden = g->d_hidden;
@@ -408,6 +408,7 @@ int spkv_cache_check(const spkv_cache *c, void *stream, int32_t *status_bits) {
     if (bits & (SPKV_STATUS_POOL_FULL | SPKV_STATUS_TABLE_FULL))
         return fail(SPKV_E_CAPACITY, "cache status bits 0x%x", bits);
     if (bits & SPKV_STATUS_BAD_ROWS) return fail(SPKV_E_ROWS, "cache status bits 0x%x", bits);
+    if (bits & SPKV_STATUS_STEP_TIMEOUT) return fail(SPKV_E_TIMEOUT, "cache status bits 0x%x", bits);
     return SPKV_OK;
 }
 

@@ -65,20 +65,23 @@ __host__ __device__ inline int rec_floats(int G, int HD) { return G * HD + 32; }
 
 // workspace head: one arrival counter per (b, g), each in its own 256-byte
 // line (the end-of-launch arrivals of all workgroups would otherwise queue on
-// a few lines), then one line with the fused step's two counters (gate
-// arrivals at int 0, launch-end arrivals at int 32).  Every call leaves all
+// a few lines), then the fused step's two counters (gate units stored,
+// workgroups that have read the lengths), a line each.  Every call leaves all
 // of them at zero, so one workspace may serve both entry points.
 constexpr int CNT_STRIDE = 64;  // ints
-__host__ __device__ inline size_t ws_header_bytes(int BG) { return ((size_t)BG * CNT_STRIDE + 64) * 4; }
-// then, for the fused step only, the new lengths (BG ints) and the gate
-// shares ([d_hidden][16][n_kv] floats), each rounded to 256 bytes; then the
-// split-K partials
+__host__ __device__ inline size_t ws_header_bytes(int BG) { return ((size_t)BG * CNT_STRIDE + 2 * 64) * 4; }
+// then, for the fused step only, the gate's partial first-layer sums
+// ([items][16 rows][16 units] floats, rounded to 256 bytes); then the split-K
+// partials
 constexpr int FUSED_ROWS = 16;  // batch rows the fused gate takes
 __host__ __device__ inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-__host__ __device__ inline size_t fused_bytes(int BG, int n_kv, int d_hidden) {
-    return d_hidden <= 0 ? 0
-                         : round256((size_t)BG * 4) + round256((size_t)d_hidden * FUSED_ROWS * n_kv * 4);
+__host__ __device__ inline size_t fused_bytes(int d_model, int d_hidden) {
+    return d_hidden <= 0 ? 0 : round256((size_t)gate_tile_items(d_model, d_hidden) * 256 * 4);
 }
+// polls of the fused step's waits before they give up (each poll takes a
+// device-scope round trip, about a microsecond; the waits normally end within
+// tens of microseconds)
+constexpr int FUSED_SPIN_LIMIT = 1 << 20;
 
 // Inclusive block scan of val(i), i < n, into out[1..n] (out[0] = 0); returns the total.
 template <typename Fn>
@@ -261,9 +264,9 @@ __device__ inline void compute_step(WaveState<HD> &st, const bf16x8 *qlds,
 // Fused step: append the new row of every (b, g) whose keep bit is set
 // (SP-KV section 2.1, deployment paragraph: only kept pairs enter the
 // persistent cache), as spkv_compact_append does for one row per sequence.
-// 16 threads per (b, g); the new length goes to lnext (device scope).
+// 16 threads per (b, g); the new lengths go to new_len (LDS).
 template <int HD>
-__device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, int32_t *lnext) {
+__device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, int *new_len) {
     const CacheView &c = a.c;
     const int BG = c.batch * c.n_kv;
     const int P = c.page_size;
@@ -315,9 +318,44 @@ __device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, int32_
                     newlen = old + 1;
                 }
             }
-            if (sub == 0) __hip_atomic_store(&lnext[bg], newlen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (sub == 0) new_len[bg] = newlen;
         }
     }
+}
+
+// Fused step, the last workgroup of the launch (it takes no attention work):
+// once every gate unit's shares are stored, finish the gate (utilities, keep
+// bits), append the kept rows, and once every other workgroup has read the
+// lengths for its plan, store the new lengths.  The waits are bounded: if
+// one runs out, the step's append or lengths are left undone and a status
+// bit says so.
+template <int HD>
+__device__ void fused_finisher(const DecodeArgs &a, const float *gshare, int *gate_cnt, int *plan_cnt,
+                               float *lds_act, uint8_t *lds_keep, int *lds_new_len, int *lds_flag) {
+    const CacheView &c = a.c;
+    const int BG = c.batch * c.n_kv;
+    const int items = gate_tile_items(a.gate.d_model, a.gate.d_hidden);
+    if (threadIdx.x == 0) lds_flag[0] = wait_count_dev(gate_cnt, items, FUSED_SPIN_LIMIT);
+    __syncthreads();
+    if (!lds_flag[0]) {
+        if (threadIdx.x == 0) atomicOr(c.status, SPKV_STATUS_STEP_TIMEOUT);
+        return;
+    }
+    gate_tile_finish(a.gate, gshare, lds_act, lds_keep);
+    __syncthreads();
+    append_new_rows<HD>(a, lds_keep, lds_new_len);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        reset_dev(gate_cnt);
+        lds_flag[1] = wait_count_dev(plan_cnt, (int)gridDim.x - 1, FUSED_SPIN_LIMIT);
+    }
+    __syncthreads();
+    if (!lds_flag[1]) {
+        if (threadIdx.x == 0) atomicOr(c.status, SPKV_STATUS_STEP_TIMEOUT);
+        return;
+    }
+    for (int i = threadIdx.x; i < BG; i += NT) c.lengths[i] = lds_new_len[i];
+    if (threadIdx.x == 0) reset_dev(plan_cnt);
 }
 
 template <int HD, bool FUSED>
@@ -327,7 +365,6 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     __shared__ int lds_t[MAX_BG];
     __shared__ int lds_red[NW];
     __shared__ int lds_flag[2];
-    __shared__ int lds_fin;
     __shared__ uint8_t lds_keep[FUSED_ROWS * 16];  // fused step: keep bits of the new rows
     __shared__ int lds_sbg[NW][ROUND];    // per wave: (b, g) of each staged step
     __shared__ int lds_spg[NW][ROUND];    //           page id (-1: ring step)
@@ -344,61 +381,52 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int nws = w / KSTEP;  // ring steps per (b, g)
     const int P = c.page_size;
     int32_t *cnt = (int32_t *)a.ws;
-    const size_t fb = FUSED ? fused_bytes(BG, c.n_kv, a.gate.d_hidden) : 0;
-    int32_t *fcnt = cnt + (size_t)BG * CNT_STRIDE;                 // fused: [0] gate, [32] launch end
-    int32_t *lnext = (int32_t *)(a.ws + ws_header_bytes(BG));      // fused: new lengths
-    float *gshare = (float *)(a.ws + ws_header_bytes(BG) + round256((size_t)BG * 4));
+    const size_t fb = FUSED ? fused_bytes(a.gate.d_model, a.gate.d_hidden) : 0;
+    const int g_items = FUSED ? gate_tile_items(a.gate.d_model, a.gate.d_hidden) : 0;
+    int32_t *gate_cnt = cnt + (size_t)BG * CNT_STRIDE;  // fused: gate units stored
+    int32_t *plan_cnt = gate_cnt + 64;                  // fused: workgroups that read the lengths
+    float *gshare = (float *)(a.ws + ws_header_bytes(BG));
     float *part = (float *)(a.ws + ws_header_bytes(BG) + fb);
+    // attention workgroups (the fused step keeps the last one for its finisher)
+    const int n_att = FUSED ? (int)gridDim.x - 1 : (int)gridDim.x;
 
     if constexpr (FUSED) {
-        // ---- gate of the new rows: workgroup j < d_hidden takes hidden unit
-        // j; the last of them finishes the gate and appends the kept rows.
-        // New lengths go to lnext and are published when the launch ends, so
-        // that every workgroup plans from the same lengths; the appended
-        // entries (position t) are not visible to this attention anyway.
-        if ((int)blockIdx.x < a.gate.d_hidden) {
+        // The new rows' gate: workgroup x stores the partial sums of gate
+        // items x, x + n_att, ... (16-unit tiles of the first layer over a
+        // part of d_model) and counts them, without waiting; the finisher
+        // completes the gate and appends the kept rows.  It stores the new lengths only after
+        // every workgroup has read the old ones for its plan (the appended
+        // entries, at position t, are outside this step's global set).
+        if ((int)blockIdx.x == n_att) {
+            fused_finisher<HD>(a, gshare, gate_cnt, plan_cnt, &lds_o[0][0][0][0], lds_keep, lds_len, lds_flag);
+            return;
+        }
+        if ((int)blockIdx.x < g_items) {
             float *red = &lds_o[0][0][0][0];
-            gate_unit_share<__bf16, FUSED_ROWS, NT>(a.gate, blockIdx.x, gshare, red);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (threadIdx.x == 0) lds_fin = arrive_dev(&fcnt[0]) == a.gate.d_hidden - 1;
-            __syncthreads();
-            if (lds_fin) {
-                gate_finish<FUSED_ROWS, NT>(a.gate, gshare, lds_keep);
-                __syncthreads();
-                append_new_rows<HD>(a, lds_keep, lnext);
-                if (threadIdx.x == 0) reset_dev(&fcnt[0]);
+            int units = 0;
+            for (int j = blockIdx.x; j < g_items; j += n_att) {
+                if (units++) __syncthreads();  // red is reused
+                gate_tile_share(a.gate, j, gshare, red);
             }
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's shares are stored
             __syncthreads();
+            if (threadIdx.x == 0) arrive_nr_dev(gate_cnt, units);
         }
     }
-    // launch end (fused step): the last workgroup out publishes the new lengths
-    auto finish = [&]() {
-        if constexpr (FUSED) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (threadIdx.x == 0) lds_fin = arrive_dev(&fcnt[32]) == (int)gridDim.x - 1;
-            __syncthreads();
-            if (lds_fin) {
-                for (int i = threadIdx.x; i < BG; i += NT)
-                    c.lengths[i] = __hip_atomic_load(&lnext[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (threadIdx.x == 0) reset_dev(&fcnt[32]);
-            }
-        }
-    };
 
     // ---- flat step list; every workgroup derives it identically ------------
     for (int i = threadIdx.x; i < BG; i += NT) lds_len[i] = c.lengths[i];
     for (int i = threadIdx.x; i < c.batch; i += NT) lds_t[i] = a.t[i];
     __syncthreads();
+    if (FUSED && threadIdx.x == 0) arrive_nr_dev(plan_cnt);  // the lengths are read
     const int total = uniform(block_scan(BG, [&](int i) { return nws + (lds_len[i] + KSTEP - 1) / KSTEP; },
                                          lds_F, lds_red));
     // Shares: workgroup x takes [w0(x), w0(x+1)); the first n_cut workgroups
     // (in a fused step they ran a gate unit first) take cut steps fewer.
-    const int spg0 = (total + gridDim.x - 1) / gridDim.x;
-    const int n_cut = FUSED ? min(a.n_cut, (int)gridDim.x) : 0;
+    const int spg0 = (total + n_att - 1) / n_att;
+    const int n_cut = FUSED ? min(g_items, n_att) : 0;
     const int cut = FUSED ? min(a.share_cut, spg0 / 2) : 0;
-    const int spg = (total + n_cut * cut + gridDim.x - 1) / gridDim.x;  // >= 2 * cut
+    const int spg = (total + n_cut * cut + n_att - 1) / n_att;  // >= 2 * cut
     const int cut_end = n_cut * (spg - cut);
     auto w0 = [&](int x) -> int { return x * spg - min(x, n_cut) * cut; };
     auto owner = [&](int s) -> int { return s < cut_end ? s / (spg - cut) : n_cut + (s - cut_end) / spg; };
@@ -408,10 +436,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // of one (b, g) are consecutive, from owner(F[bg]) + bg to owner(F[bg+1]-1) + bg.
     const int W0 = min(total, w0(blockIdx.x));
     const int W1 = min(total, w0(blockIdx.x + 1));
-    if (W0 >= W1) {  // (uniform over the workgroup)
-        finish();
-        return;
-    }
+    if (W0 >= W1) return;  // (uniform over the workgroup)
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -508,20 +533,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             const __bf16 *kb = (const __bf16 *)c.ring_k + ((int64_t)bg * w + ls * KSTEP) * HD;
             const __bf16 *vb = (const __bf16 *)c.ring_v + (int64_t)bg * HD * w + ls * KSTEP;
             if constexpr (FUSED) {
-                const int b = bg / c.n_kv;
-                const int tb = uniform(lds_t[b]);
+                const int tb = uniform(lds_t[bg / c.n_kv]);
                 if (tb >= 0 && ls == (tb % w) / KSTEP) {
-                    // this step holds the new token: write its row into the
-                    // ring first, then read the step past the L1 cache
-                    const int g = bg - b * c.n_kv;
-                    const int slot = tb % w;
-                    const __bf16 *kn = (const __bf16 *)a.k_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
-                    const __bf16 *vn = (const __bf16 *)a.v_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
-                    if (lane < HD / 8)
-                        *(bf16x8 *)((__bf16 *)c.ring_k + ((int64_t)bg * w + slot) * HD + 8 * lane) =
-                            *(const bf16x8 *)(kn + 8 * lane);
-                    for (int e = lane; e < HD; e += 64) ((__bf16 *)c.ring_v)[((int64_t)bg * HD + e) * w + slot] = vn[e];
-                    __builtin_amdgcn_s_waitcnt(0);
+                    // the step holding the new token (this wave wrote it into
+                    // the ring before its first loads): read past the L1 cache
                     load_step<HD, 1>(kb, vb, w, lanes_ring, kr, vr);
                     return;
                 }
@@ -709,6 +724,26 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const bool one = bg_first == bg_last;
     const bool pub_first = !one && first_split;                            // slot 1
     const bool pub_last = one ? (first_split || last_split) : last_split;  // slot 0
+    if constexpr (FUSED) {
+        // the new token's row goes into ring slot t % w; the wave that reads
+        // that ring step writes it now, so that the wait at the end of its
+        // first staging covers these stores
+        for (int bg = bg_first; bg <= bg_last; ++bg) {
+            const int b = bg / c.n_kv;
+            const int tb = lds_t[b];
+            if (tb < 0) continue;
+            const int sn = lds_F[bg] + (tb % w) / KSTEP;
+            if (sn < W0 || sn >= W1 || (sn - W0) % NW != wave) continue;
+            const int g = bg - b * c.n_kv;
+            const int slot = tb % w;
+            const __bf16 *kn = (const __bf16 *)a.k_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
+            const __bf16 *vn = (const __bf16 *)a.v_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
+            if (lane < HD / 8)
+                *(bf16x8 *)((__bf16 *)c.ring_k + ((int64_t)bg * w + slot) * HD + 8 * lane) =
+                    *(const bf16x8 *)(kn + 8 * lane);
+            for (int e = lane; e < HD; e += 64) ((__bf16 *)c.ring_v)[((int64_t)bg * HD + e) * w + slot] = vn[e];
+        }
+    }
     reset(bg_first);
     int k = 0;  // next step of this wave to compute (its loads are in flight)
     if (nk > 0) {
@@ -775,10 +810,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }
 
     // ---- the last (b, g), if shared: publish, arrive, the last arrival merges
-    if (!pub_last) {
-        finish();
-        return;
-    }
+    if (!pub_last) return;
     __syncthreads();
     publish(0, bg_last, threadIdx.x, NT);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
@@ -790,7 +822,6 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }
     __syncthreads();
     if (lds_flag[1]) merge(1, &bg_last);
-    finish();
 }
 
 // ---------------------------------------------------------------------------
@@ -847,7 +878,8 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
 
 }  // namespace
 
-size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_hidden) {
+size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_model,
+                       int fused_hidden) {
     if (c->dtype != SPKV_BF16) {
         if (max_items_out) *max_items_out = 0;
         return 0;
@@ -858,12 +890,13 @@ size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_ou
     // segment, and consecutive (b, g) share at most one workgroup
     const int max_slots = grid + BG;
     if (max_items_out) *max_items_out = max_slots;
-    return ws_header_bytes(BG) + fused_bytes(BG, c->n_kv, fused_hidden) +
+    return ws_header_bytes(BG) + fused_bytes(fused_model, fused_hidden) +
            (size_t)max_slots * rec_floats(G, c->head_dim) * sizeof(float);
 }
 
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid) {
-    return c->dtype == SPKV_BF16 && c->batch <= FUSED_ROWS && d_hidden <= grid && c->n_kv <= 16;
+    // the last workgroup is the finisher; the gate units go to the others
+    return c->dtype == SPKV_BF16 && c->batch <= FUSED_ROWS && d_hidden >= 1 && grid >= 2 && c->n_kv <= 16;
 }
 
 int decode_blocks_per_cu() {

@@ -23,5 +23,22 @@ __device__ inline int arrive_dev(int *counter) {
 __device__ inline void reset_dev(int *counter) {
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// arrival whose count nobody waits for here (the atomic returns nothing)
+__device__ inline void arrive_nr_dev(int *counter, int n = 1) {
+    (void)__hip_atomic_fetch_add(counter, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int load_dev(const int *p) {
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Poll *counter until it reaches n, at most `limit` times; false if it never
+// did.  Only for counts that are bumped by workgroups which never wait for
+// the poller, so the wait ends once they have run.
+__device__ inline bool wait_count_dev(const int *counter, int n, int limit) {
+    for (int i = 0; i < limit; ++i) {
+        if (load_dev(counter) >= n) return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
 
 }  // namespace spkv

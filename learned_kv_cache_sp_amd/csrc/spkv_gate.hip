@@ -10,10 +10,11 @@
 // the same kernel.  For up to 64 rows d_model is split over several
 // workgroups that write partial sums; a second small kernel adds the slices
 // in a fixed order and runs the epilogue.
-// Up to 16 rows (decode, either dtype): one launch with one workgroup per
-// hidden unit; each adds its unit's share W2[:, j] a_j of every logit to a
-// workspace slot, and the workgroup that finishes last sums the shares in
-// unit order, so the result does not depend on scheduling.
+// Up to 16 rows (decode), one launch: bf16 -- one workgroup per 16-unit tile
+// and d_model part on MFMA, storing its partial first-layer sums; f32 -- one
+// workgroup per hidden unit, storing its share W2[:, j] a_j of every logit.
+// The workgroup that finishes last adds the pieces in a fixed order, so the
+// result does not depend on scheduling.
 // f32 with more rows, or d_hidden outside {32, 64, 128, 256}: a plain VALU
 // kernel.
 #include "spkv_internal.h"
@@ -220,6 +221,25 @@ __global__ void __launch_bounds__(NT) gate_tiny_kernel(GateArgs a) {
     if (threadIdx.x == 0) reset_dev(cnt);
 }
 
+// bf16, up to 16 rows: one workgroup per (16-unit tile, d_model part), on
+// MFMA; the last workgroup to arrive finishes (gate_tile_share /
+// gate_tile_finish).
+__global__ void __launch_bounds__(NT) gate_tile_kernel(GateArgs a) {
+    __shared__ float red[4 * 16 * 17];
+    __shared__ float act[16 * 256];
+    __shared__ int lds_last;
+    int *cnt = (int *)a.ws;
+    float *part = a.ws + WS_HEADER_FLOATS;  // [items][16][16]
+    gate_tile_share(a, blockIdx.x, part, red);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's sums are stored
+    __syncthreads();
+    if (threadIdx.x == 0) lds_last = arrive_dev(cnt) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!lds_last) return;
+    gate_tile_finish(a, part, act, nullptr);
+    if (threadIdx.x == 0) reset_dev(cnt);
+}
+
 constexpr int SMALL_ROWS = 64;
 constexpr int TINY_ROWS = 16;
 
@@ -241,7 +261,10 @@ static int small_bm(int hg) { return hg == 32 ? 32 : 16; }
 
 size_t gate_ws_bytes(int d_model, int d_hidden, int n_kv, int dtype, int64_t n_rows) {
     const size_t header = WS_HEADER_FLOATS * sizeof(float);
-    if (n_rows > 0 && n_rows <= TINY_ROWS) return header + (size_t)d_hidden * TINY_ROWS * n_kv * sizeof(float);
+    if (n_rows > 0 && n_rows <= TINY_ROWS) {
+        if (dtype == SPKV_BF16) return header + (size_t)gate_tile_items(d_model, d_hidden) * 256 * sizeof(float);
+        return header + (size_t)d_hidden * TINY_ROWS * n_kv * sizeof(float);
+    }
     const int split = gate_split_for(d_model, dtype, n_rows);
     if (split == 1 || !mfma_hidden(d_hidden)) return 0;
     const int bm = small_bm(d_hidden);
@@ -280,7 +303,7 @@ hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
     GateArgs a = a0;
     if (a.n_rows <= TINY_ROWS) {
         if (a.dtype == SPKV_BF16)
-            launch_tiny<__bf16>(a, s);
+            hipLaunchKernelGGL(gate_tile_kernel, dim3(gate_tile_items(a.d_model, a.d_hidden)), dim3(NT), 0, s, a);
         else
             launch_tiny<float>(a, s);
     } else if (a.dtype == SPKV_BF16 && mfma_hidden(a.d_hidden)) {

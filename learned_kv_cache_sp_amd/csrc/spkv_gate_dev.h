@@ -1,9 +1,11 @@
 // Device pieces of the few-row gate (SP-KV, arXiv 2605.14037, section 2.1,
-// Eq. (1)-(2)), shared by the gate kernel and the fused decode step:
-//   gate_unit_share  -- workgroup j: hidden unit j for every row, its share
-//                       W2[k][j] * a_j of every logit stored device-wide
-//   gate_finish      -- the last workgroup: shares added in unit order,
-//                       sigmoid and threshold
+// Eq. (1)-(2)), shared by the gate kernels and the fused decode step:
+//   gate_unit_share / gate_finish (f32): workgroup j takes hidden unit j for
+//     every row and stores its share W2[k][j] * a_j of every logit; the last
+//     workgroup adds the shares in unit order, then sigmoid and threshold
+//   gate_tile_share / gate_tile_finish (bf16): workgroups take 16-unit tiles
+//     of the first layer on MFMA; the finishing workgroup adds the parts,
+//     then ReLU, the second layer, sigmoid and threshold
 #pragma once
 
 #include "spkv_internal.h"
@@ -109,6 +111,109 @@ __device__ void gate_finish(const GateArgs &a, const float *part, uint8_t *keep_
     }
     if (o < outs && q == 0) {
         const float u = gate_sigmoid(s + b2o);
+        const uint8_t z = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+        if (a.utility) a.utility[o] = u;
+        if (a.keep) a.keep[o] = z;
+        if (keep_lds) keep_lds[o] = z;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Few rows (<= 16), bf16, on MFMA.  Work item (tile, kpart): the first-layer
+// pre-activations W1 h of hidden units 16*tile .. 16*tile+15 for every row,
+// summed over the kpart-th part of d_model.  v_mfma_f32_16x16x32_bf16 with
+// A = the hidden rows (row = lane % 16) and B = the W1 rows (unit = lane %
+// 16), both read K-contiguous straight from memory: each lane loads 16 bytes
+// per 32-wide slice.  A part is at most 4 waves x GT_SLICES slices, so every
+// load of a wave is in flight at once.
+constexpr int GT_SLICES = 16;
+
+__host__ __device__ inline int gate_tile_kparts(int d_model) {
+    const int steps = d_model / 32;
+    return (steps + 4 * GT_SLICES - 1) / (4 * GT_SLICES);
+}
+__host__ __device__ inline int gate_tile_items(int d_model, int d_hidden) {
+    return (d_hidden / 16) * gate_tile_kparts(d_model);
+}
+
+typedef __bf16 gt_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float gt_f32x4 __attribute__((ext_vector_type(4)));
+
+// All 256 threads.  part: [items][16 rows][16 units] floats, stored
+// device-wide (rows past n_rows hold sums of a repeated row, never used);
+// red: LDS scratch of 4 x 16 x 17 floats.
+__device__ inline void gate_tile_share(const GateArgs &a, int item, float *part, float *red) {
+    const int kparts = gate_tile_kparts(a.d_model);
+    const int tile = item / kparts;
+    const int kpart = item - tile * kparts;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int steps = a.d_model / 32;
+    const int spk = (steps + kparts - 1) / kparts;
+    const int s_lo = kpart * spk;
+    const int s_hi = min(steps, s_lo + spk);
+    const int n = (int)a.n_rows;
+    const int row = i16 < n ? i16 : n - 1;
+    const __bf16 *hrow = (const __bf16 *)a.hidden + (int64_t)row * a.ld_hidden + 8 * q4;
+    const __bf16 *wrow = (const __bf16 *)a.w1 + (int64_t)(16 * tile + i16) * a.d_model + 8 * q4;
+    gt_bf16x8 av[GT_SLICES], bv[GT_SLICES];
+#pragma unroll
+    for (int u = 0; u < GT_SLICES; ++u) {
+        const int s = s_lo + wave + 4 * u;
+        const int se = s < s_hi ? s : s_lo;  // in bounds; zeroed below
+        av[u] = *(const gt_bf16x8 *)(hrow + 32 * se);
+        bv[u] = *(const gt_bf16x8 *)(wrow + 32 * se);
+    }
+    gt_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < GT_SLICES; ++u) {
+        const int s = s_lo + wave + 4 * u;
+        const gt_bf16x8 ab = s < s_hi ? av[u] : gt_bf16x8{};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bv[u], acc, 0, 0, 0);
+    }
+    // D: row 4*q4 + r, unit i16; the 4 waves' sums added in wave order
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * q4 + r) * 17 + i16] = acc[r];
+    __syncthreads();
+    {
+        const int r = threadIdx.x >> 4;
+        const int j = threadIdx.x & 15;
+        const float v = ((red[(0 * 16 + r) * 17 + j] + red[(1 * 16 + r) * 17 + j]) + red[(2 * 16 + r) * 17 + j]) +
+                        red[(3 * 16 + r) * 17 + j];
+        store_dev(part + (size_t)item * 256 + r * 16 + j, v);
+    }
+}
+
+// All 256 threads of the finishing workgroup, once every item is stored:
+// a_j = ReLU(sum over parts in order + b1_j) staged in act (LDS, n_rows x
+// d_hidden floats), then logit (r, k) = sum over j in order of W2[k][j] a_j,
+// + b2, u = sigmoid(logit), keep = u >= tau (NaN -> 0).  utility / keep in
+// a may be NULL; keep_lds (may be NULL) receives the bits too.
+__device__ inline void gate_tile_finish(const GateArgs &a, const float *part, float *act, uint8_t *keep_lds) {
+    const int kparts = gate_tile_kparts(a.d_model);
+    const int n = (int)a.n_rows;
+    const int hg = a.d_hidden;
+    const int nkv = a.n_kv;
+    for (int idx = threadIdx.x; idx < n * hg; idx += 256) {
+        const int r = idx / hg;
+        const int j = idx - r * hg;
+        const float *p = part + (size_t)(j >> 4) * kparts * 256 + r * 16 + (j & 15);
+        float pre = 0.f;
+        for (int kp = 0; kp < kparts; ++kp) pre += load_dev(p + (size_t)kp * 256);
+        act[idx] = gate_relu(pre + a.b1[j]);
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < n * nkv; o += 256) {
+        const int r = o / nkv;
+        const int k = o - r * nkv;
+        const float *w2 = a.w2 + (size_t)k * hg;
+        const float *ar = act + r * hg;
+        float s = 0.f;
+#pragma unroll 16
+        for (int j = 0; j < hg; ++j) s = fmaf(w2[j], ar[j], s);
+        const float u = gate_sigmoid(s + a.b2[k]);
         const uint8_t z = (u >= a.tau) ? 1 : 0;  // NaN -> 0
         if (a.utility) a.utility[o] = u;
         if (a.keep) a.keep[o] = z;

@@ -99,14 +99,15 @@ struct DecodeArgs {
     int32_t max_items;  // partial slots in ws
     // fused step (spkv_decode_step): the gate of the batch's new rows and
     // their append run inside the attention launch
-    int32_t n_cut;      // workgroups that also run a gate unit ...
-    int32_t share_cut;  // ... and take this many fewer attention steps
+    int32_t share_cut;  // fused step: attention steps fewer for the workgroups that run a gate item
     GateArgs gate;      // n_rows = batch; outputs utility / keep
     const char *k_new, *v_new;  // new rows: row b, key head g at + (b*ld_new + g*hd) elements
     int64_t ld_new;
 };
 // fused_hidden: d_hidden of the gate for the fused step, 0 for attention only
-size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_hidden = 0);
+// fused_model / fused_hidden: the gate's d_model and d_hidden for spkv_decode_step (0: plain attention)
+size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_model = 0,
+                       int fused_hidden = 0);
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid);
 int decode_blocks_per_cu();
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

@@ -29,6 +29,7 @@ SPKV_E_HIP = -3
 SPKV_E_CAPACITY = -4
 SPKV_E_WORKSPACE = -5
 SPKV_E_ROWS = -6
+SPKV_E_TIMEOUT = -7
 
 SPKV_F32 = 0
 SPKV_BF16 = 1
@@ -38,6 +39,7 @@ SPKV_APPEND_WINDOW = 2
 STATUS_POOL_FULL = 1
 STATUS_TABLE_FULL = 2
 STATUS_BAD_ROWS = 4
+STATUS_STEP_TIMEOUT = 8
 
 
 class SpkvError(RuntimeError):

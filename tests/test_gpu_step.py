@@ -90,7 +90,7 @@ def _run(wl, ctxs, steps, tau, page, seed, shared_ws=False):
             rks, rvs = sep.read_ring(b, g)
             assert torch.equal(rkf, rks) and torch.equal(rvf, rvs), f"ring b={b} g={g}"
     # the workspace counters are back at zero (the next call relies on it)
-    ws_head = ws_step[: (B * wl.n_kv * 64 + 64)].cpu().numpy()
+    ws_head = ws_step[: (B * wl.n_kv * 64 + 2 * 64)].cpu().numpy()
     assert not ws_head.any()
     return worst, worst_l, split
 
