@@ -14,7 +14,7 @@
 // differ between runs, the logical content never does.
 //
 // Layout written: key rows [page][slot][hd] (16-byte coalesced copies), value
-// rows transposed [page][hd][slot] (staged through LDS so that consecutive
+// rows transposed [page][hd][slot] (transposed in registers: consecutive
 // lanes write consecutive slots), positions [page][slot].
 #include "spkv_internal.h"
 
@@ -23,11 +23,7 @@ namespace {
 
 constexpr int NT = 256;     // threads per workgroup
 constexpr int TILE = 256;   // rows per tile (one row per thread)
-constexpr int STAGE = 64;   // value rows staged in LDS per transpose batch
-constexpr int LDS_V_BYTES = STAGE * (128 + 2) * 4;
 
-template <typename T> struct Pad { static constexpr int value = 1; };
-template <> struct Pad<uint16_t> { static constexpr int value = 2; };
 
 __device__ inline int block_rank(bool flag, int *lds_waves, int *total) {
     const int lane = threadIdx.x & 63;
@@ -107,45 +103,54 @@ __device__ int grow_head(const CacheView &c, int b, int g, int old_len, int want
 }
 
 // Copy n rows (source row ids in src_rows[]) of key head g:
-//   key rows  -> kdst(kk) (row-major, 16-byte chunks)
-//   value rows -> vdst(kk, e) (one element each, transposed via LDS)
+//   key rows   -> kdst(kk) (row-major, 16-byte chunks)
+//   value rows -> vdst(kk, e) (transposed: one element each)
+// Each thread loads KB 16-byte pieces before storing any: the stores could
+// alias the sources as far as the compiler knows, so a load-store loop would
+// wait for every load in turn.  Values are transposed in registers: the 64
+// lanes of a wave take one 16-byte piece of 64 consecutive rows, and each of
+// the piece's elements goes to its value row with one store instruction that
+// writes consecutive slots.  Ends with a barrier (src_rows may be refilled).
 template <typename T, typename KDst, typename VDst>
-__device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_rows, KDst kdst,
-                          VDst vdst, char *lds_v) {
+__device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_rows, KDst kdst, VDst vdst) {
     constexpr int ES = sizeof(T);
-    constexpr int PAD = Pad<T>::value;
+    constexpr int EPC = 16 / ES;   // elements per piece
+    constexpr int KB = 8;
     const int hd = a.c.head_dim;
-    const int cpr = hd * ES / 16;  // 16-byte chunks per row
+    const int cpr = hd / EPC;      // pieces per row
     const int64_t ld_bytes = a.ld_kv * ES;
-    // keys: straight row copies
-    for (int idx = threadIdx.x; idx < n * cpr; idx += NT) {
-        const int kk = idx / cpr;
-        const int ch = idx - kk * cpr;
-        const char *src = a.k + (int64_t)src_rows[kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16;
-        *(uint4 *)(kdst(kk) + ch * 16) = *(const uint4 *)src;
-    }
-    // values: stage up to STAGE rows, then write transposed
-    const int stride = hd + PAD;  // elements per staged row
-    for (int s0 = 0; s0 < n; s0 += STAGE) {
-        const int m = min(STAGE, n - s0);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < m * cpr; idx += NT) {
-            const int kk = idx / cpr;
-            const int ch = idx - kk * cpr;
-            const char *src = a.v + (int64_t)src_rows[s0 + kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16;
-            const uint4 val = *(const uint4 *)src;
-            uint32_t *dst = (uint32_t *)(lds_v + ((int64_t)kk * stride) * ES + ch * 16);
-            dst[0] = val.x;
-            dst[1] = val.y;
-            dst[2] = val.z;
-            dst[3] = val.w;
+    const int np = n * cpr;
+    // keys: piece idx = row * cpr + chunk (a row's pieces on neighbouring
+    // lanes); values: piece idx = chunk * n + row (consecutive rows on
+    // neighbouring lanes).  Both batches are loaded before either is stored.
+    for (int base = 0; base < np; base += NT * KB) {
+        uint4 kv[KB], vv[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int idx = base + u * NT + (int)threadIdx.x;
+            if (idx < np) {
+                const int kk = idx / cpr;
+                const int ch = idx - kk * cpr;
+                kv[u] = *(const uint4 *)(a.k + (int64_t)src_rows[kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16);
+                const int vc = idx / n;
+                const int vk = idx - vc * n;
+                vv[u] = *(const uint4 *)(a.v + (int64_t)src_rows[vk] * ld_bytes + (int64_t)g * hd * ES + vc * 16);
+            }
         }
-        __syncthreads();
-        const T *lv = (const T *)lds_v;
-        for (int idx = threadIdx.x; idx < m * hd; idx += NT) {
-            const int kk = idx % m;
-            const int e = idx / m;
-            *vdst(s0 + kk, e) = lv[kk * stride + e];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int idx = base + u * NT + (int)threadIdx.x;
+            if (idx < np) {
+                const int kk = idx / cpr;
+                const int ch = idx - kk * cpr;
+                *(uint4 *)(kdst(kk) + ch * 16) = kv[u];
+                const int vc = idx / n;
+                const int vk = idx - vc * n;
+                T el[EPC];
+                __builtin_memcpy(el, &vv[u], 16);
+#pragma unroll
+                for (int i = 0; i < EPC; ++i) *vdst(vk, vc * EPC + i) = el[i];
+            }
         }
     }
     __syncthreads();
@@ -157,7 +162,7 @@ __device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_row
 template <typename T>
 __device__ void scatter_tile(const CompactArgs &a, int b, int g, int r0, int row_lo, int row_hi,
                              int dst0, int new_len, int pos_base, int *lds_rows, int *lds_waves,
-                             char *lds_v) {
+                             int *lds_pages) {
     const CacheView &c = a.c;
     const int i = row_lo + threadIdx.x;
     const bool flag = (i < row_hi) && a.keep[(int64_t)(r0 + i) * c.n_kv + g] != 0;
@@ -171,47 +176,56 @@ __device__ void scatter_tile(const CompactArgs &a, int b, int g, int r0, int row
     const int P = c.page_size;
     const int32_t *pt = c.page_table + ((int64_t)b * c.n_kv + g) * c.max_pages;
     constexpr int ES = sizeof(T);
+    // page ids of the destination entries, read once (the copies below store
+    // through char pointers, which may alias the table as far as the
+    // compiler knows: a table read per store would wait for every load)
+    const int pg0 = dst0 >> c.page_shift;
+    const int npg = ((dst0 + n - 1) >> c.page_shift) - pg0 + 1;  // <= TILE / 32 + 1
+    if ((int)threadIdx.x < npg) lds_pages[threadIdx.x] = pt[pg0 + threadIdx.x];
+    __syncthreads();
     for (int kk = threadIdx.x; kk < n; kk += NT) {
         const int j = dst0 + kk;
-        const int page = pt[j >> c.page_shift];
+        const int page = lds_pages[(j >> c.page_shift) - pg0];
         c.pos_pages[(int64_t)page * P + (j & (P - 1))] = pos_base + (lds_rows[kk] - r0);
     }
     auto kdst = [&](int kk) -> char * {
         const int j = dst0 + kk;
-        const int page = pt[j >> c.page_shift];
+        const int page = lds_pages[(j >> c.page_shift) - pg0];
         return c.k_pages + (((int64_t)page * P + (j & (P - 1))) * hd) * ES;
     };
     auto vdst = [&](int kk, int e) -> T * {
         const int j = dst0 + kk;
-        const int page = pt[j >> c.page_shift];
+        const int page = lds_pages[(j >> c.page_shift) - pg0];
         return (T *)c.v_pages + ((int64_t)page * hd + e) * P + (j & (P - 1));
     };
-    copy_rows<T>(a, g, n, lds_rows, kdst, vdst, lds_v);
+    copy_rows<T>(a, g, n, lds_rows, kdst, vdst);
 }
 
 // Write rows [row_lo, row_hi) of sequence b (key head g) into the ring.
 template <typename T>
 __device__ void window_rows(const CompactArgs &a, int b, int g, int r0, int row_lo, int row_hi,
-                            int pos_base, int *lds_rows, char *lds_v) {
+                            int pos_base, int *lds_rows) {
     const CacheView &c = a.c;
-    const int n = row_hi - row_lo;
-    if (n <= 0) return;
-    for (int kk = threadIdx.x; kk < n; kk += NT) lds_rows[kk] = r0 + row_lo + kk;
-    __syncthreads();
     const int hd = c.head_dim;
     const int w = c.window;
     constexpr int ES = sizeof(T);
     const int64_t bg = (int64_t)b * c.n_kv + g;
-    const int first_pos = pos_base + row_lo;
-    auto kdst = [&](int kk) -> char * {
-        const int slot = (first_pos + kk) % w;
-        return c.ring_k + ((bg * w + slot) * hd) * ES;
-    };
-    auto vdst = [&](int kk, int e) -> T * {
-        const int slot = (first_pos + kk) % w;
-        return (T *)c.ring_v + (bg * hd + e) * w + slot;
-    };
-    copy_rows<T>(a, g, n, lds_rows, kdst, vdst, lds_v);
+    // at most TILE rows (lds_rows) at a time; a window may hold up to 1024
+    for (int lo = row_lo; lo < row_hi; lo += TILE) {
+        const int n = min(TILE, row_hi - lo);
+        for (int kk = threadIdx.x; kk < n; kk += NT) lds_rows[kk] = r0 + lo + kk;
+        __syncthreads();
+        const int first_pos = pos_base + lo;
+        auto kdst = [&](int kk) -> char * {
+            const int slot = (first_pos + kk) % w;
+            return c.ring_k + ((bg * w + slot) * hd) * ES;
+        };
+        auto vdst = [&](int kk, int e) -> T * {
+            const int slot = (first_pos + kk) % w;
+            return (T *)c.ring_v + (bg * hd + e) * w + slot;
+        };
+        copy_rows<T>(a, g, n, lds_rows, kdst, vdst);  // ends with a barrier
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -221,8 +235,8 @@ template <typename T>
 __global__ void __launch_bounds__(NT) compact_small_kernel(CompactArgs a) {
     __shared__ int lds_rows[TILE];
     __shared__ int lds_waves[NT / 64];
+    __shared__ int lds_pages[16];
     __shared__ int lds_misc[4];
-    __shared__ __attribute__((aligned(16))) char lds_v[LDS_V_BYTES];
     const int b = blockIdx.x;
     const int g = blockIdx.y;
     int r0, nb;
@@ -241,11 +255,11 @@ __global__ void __launch_bounds__(NT) compact_small_kernel(CompactArgs a) {
             c.lengths[bg] = new_len;
             if (a.append_offsets) a.append_offsets[bg] = old_len;
         }
-        scatter_tile<T>(a, b, g, r0, 0, nb, old_len, new_len, p0, lds_rows, lds_waves, lds_v);
+        scatter_tile<T>(a, b, g, r0, 0, nb, old_len, new_len, p0, lds_rows, lds_waves, lds_pages);
     }
     if (a.flags & SPKV_APPEND_WINDOW) {
         __syncthreads();
-        window_rows<T>(a, b, g, r0, max(0, nb - c.window), nb, p0, lds_rows, lds_v);
+        window_rows<T>(a, b, g, r0, max(0, nb - c.window), nb, p0, lds_rows);
     }
 }
 
@@ -405,7 +419,7 @@ template <typename T>
 __global__ void __launch_bounds__(NT) compact_scatter_kernel(CompactArgs a) {
     __shared__ int lds_rows[TILE];
     __shared__ int lds_waves[NT / 64];
-    __shared__ __attribute__((aligned(16))) char lds_v[LDS_V_BYTES];
+    __shared__ int lds_pages[16];
     const int j = blockIdx.x;
     const int b = blockIdx.y;
     const int g = blockIdx.z;
@@ -422,13 +436,13 @@ __global__ void __launch_bounds__(NT) compact_scatter_kernel(CompactArgs a) {
         const int old_len = lens[bg * 2];
         const int new_len = lens[bg * 2 + 1];
         const int dst0 = old_len + a.ws[bg * a.max_tiles + j];
-        scatter_tile<T>(a, b, g, r0, row_lo, row_hi, dst0, new_len, p0, lds_rows, lds_waves, lds_v);
+        scatter_tile<T>(a, b, g, r0, row_lo, row_hi, dst0, new_len, p0, lds_rows, lds_waves, lds_pages);
     }
     if (a.flags & SPKV_APPEND_WINDOW) {
         const int w_lo = max(row_lo, nb - c.window);
         if (w_lo < row_hi) {
             __syncthreads();
-            window_rows<T>(a, b, g, r0, w_lo, row_hi, p0, lds_rows, lds_v);
+            window_rows<T>(a, b, g, r0, w_lo, row_hi, p0, lds_rows);
         }
     }
 }
@@ -463,7 +477,9 @@ hipError_t launch_compact(const CompactArgs &a0, hipStream_t s) {
             hipLaunchKernelGGL(compact_row_kernel<float>, grid, dim3(64), 0, s, a);
         return hipGetLastError();
     }
-    if (a.max_rows <= TILE) {
+    if (a.max_rows <= TILE || !(a.flags & SPKV_APPEND_GLOBAL)) {
+        // one workgroup per (b, g); a window-only append of any size copies
+        // just the last `window` rows of each sequence there
         dim3 grid(c.batch, c.n_kv);
         if (bf16)
             hipLaunchKernelGGL(compact_small_kernel<uint16_t>, grid, dim3(NT), 0, s, a);

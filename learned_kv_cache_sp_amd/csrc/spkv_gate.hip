@@ -68,6 +68,148 @@ __device__ void gate_epilogue(const GateArgs &a, const float *act, int ld, int64
 __device__ inline float relu_keep_nan(float x) { return x < 0.f ? 0.f : x; }
 
 // ---------------------------------------------------------------------------
+// bf16, many rows (d_model a multiple of 64): 64 rows x all HG hidden units per
+// workgroup, one 16-row MFMA tile per wave; iteration j covers d_model
+// columns [64 j, 64 j + 64).  The hidden rows -- the HBM stream, each row
+// read by one wave only -- go straight into registers, P iterations ahead of
+// their use.  W1 -- the same for every workgroup and L2-resident -- is shared
+// by the 4 waves through a ring of P + 1 LDS stages filled P iterations
+// ahead by direct global -> LDS loads (unit u's 64 columns = 128 bytes:
+// 16-byte chunk c at u*128 + 16*(c ^ ((u >> 1) & 7)), so the 16 lanes that
+// read one operand group hit 16 different bank groups).
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int HG, int JC> struct GatePipe {
+    // One depth for both streams: vector-memory loads complete in issue
+    // order, so waiting for W1's pieces of iteration j also waits for every
+    // hidden-row load issued before them -- a deeper register prefetch than
+    // the W1 ring would not keep more bytes in flight.  The W1 ring (HG / 64
+    // times the hidden-row bytes of an iteration) is what fills the LDS.
+    static constexpr int P = HG <= 128 ? 8 : 3;
+    static constexpr int NSTAGE = P + 1;
+    static constexpr int SBYTES = HG * 128;              // W1 stage: HG units x 64 columns
+    static constexpr int LB = SBYTES / 1024 / 4;         // direct loads per wave and stage
+    static constexpr int LA = 2;                         // hidden-row loads per wave and iteration
+    static constexpr int EPI = 64 * (HG + 1) * 4 + 16 * (HG + 1) * 4;
+    static constexpr int LDS = NSTAGE * SBYTES > EPI ? NSTAGE * SBYTES : EPI;
+};
+
+// s_waitcnt vmcnt(n), n in [0, N] (the immediate must be a constant)
+template <int N>
+__device__ inline void wait_vm(int n) {
+    if constexpr (N > 0) {
+        if (n >= N) {
+            __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+            return;
+        }
+        wait_vm<N - 1>(n);
+    } else {
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    }
+}
+
+// JC > 0: d_model = 64 JC fixed at compile time, so the loop unrolls fully,
+// the wait counts fold to constants and the compiler tracks each hidden-row
+// load to its use (a run-time trip count makes it wait for every load at the
+// top of each unrolled block).
+template <int HG, int JC>
+__global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
+    using C = GatePipe<HG, JC>;
+    constexpr int P = C::P;
+    constexpr int NTL = HG / 16;  // unit tiles
+    static_assert((P - 1) * (C::LB + C::LA) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    const int J = JC > 0 ? JC : a.d_model / 64;  // iterations
+    const int64_t my_row = min(row0 + wave * 16 + i16, a.n_rows - 1);  // rows past n re-read the last
+    const __bf16 *hrow = (const __bf16 *)a.hidden + my_row * a.ld_hidden + 8 * q4;
+    const char *w1 = (const char *)a.w1;
+    const int64_t w1_row_bytes = (int64_t)a.d_model * 2;
+
+    // W1 columns [64 j, 64 j + 64) of all units -> stage st
+    auto issue_w1 = [&](int j, int st) {
+#pragma unroll
+        for (int u = 0; u < C::LB; ++u) {
+            const int i = wave + 4 * u;         // 1 KB piece: units 8 i .. 8 i + 7
+            const int unit = 8 * i + (lane >> 3);
+            const int c = (lane & 7) ^ ((unit >> 1) & 7);
+            const char *src = w1 + unit * w1_row_bytes + (int64_t)(64 * j + 8 * c) * 2;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds + st * C::SBYTES + i * 1024), 16, 0, 0);
+        }
+    };
+    bf16x8 av[P][2];
+    auto issue_h = [&](int j, bf16x8 (&dst)[2]) {
+        dst[0] = *(const bf16x8 *)(hrow + 64 * j);
+        dst[1] = *(const bf16x8 *)(hrow + 64 * j + 32);
+    };
+
+    f32x4 acc[NTL];
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: iterations 0 .. P-1 in flight (W1 then hidden rows, per iteration)
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        if (i < J) {
+            issue_w1(i, i);
+            issue_h(i, av[i]);
+        }
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < (JC > 0 ? JC : J); j0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int j = j0 + u;
+            if (j < J) {
+                // this wave's loads of iteration j are done once at most the
+                // younger iterations' loads are outstanding
+                wait_vm<63>(min(P - 1, J - 1 - j) * (C::LB + C::LA));
+                // every wave's W1 pieces of j have landed, and every wave is
+                // done reading stage (j - 1) (its reads were consumed by its
+                // MFMAs): a plain barrier, no fence (a fence would also wait
+                // for the hidden-row loads still in flight)
+                __builtin_amdgcn_s_barrier();
+                if (j + P < J) issue_w1(j + P, (j + P) % C::NSTAGE);
+                const char *st = lds + (j % C::NSTAGE) * C::SBYTES;
+                // all operand reads of the iteration first, so that their
+                // latencies overlap each other and the MFMAs
+                bf16x8 bv[2][NTL];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int n = 0; n < NTL; ++n) {
+                        const int unit = 16 * n + i16;
+                        bv[ks][n] = *(const bf16x8 *)(st + unit * 128 + (((4 * ks + q4) ^ ((unit >> 1) & 7)) << 4));
+                    }
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int n = 0; n < NTL; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][ks], bv[ks][n], acc[n], 0, 0, 0);
+                if (j + P < J) issue_h(j + P, av[u]);
+            }
+        }
+    }
+    __syncthreads();  // the stages become the epilogue's scratch
+    float *act = (float *)lds;                       // [64][HG + 1]
+    float *lds_w2 = act + 64 * (HG + 1);             // [16][HG + 1]
+#pragma unroll
+    for (int n = 0; n < NTL; ++n) {
+        const int jj = 16 * n + i16;
+        const float bias = a.b1[jj];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) act[(wave * 16 + 4 * q4 + r) * (HG + 1) + jj] = relu_keep_nan(acc[n][r] + bias);
+    }
+    __syncthreads();
+    gate_epilogue<HG>(a, act, HG + 1, row0, 64, lds_w2);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA kernel.  Workgroup tile: (16 * WM) rows x HG hidden units; waves
 // are arranged WM (rows) x (4 / WM) (hidden units).  blockIdx.y = d_model
 // slice when n_split > 1.
@@ -311,6 +453,23 @@ hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
             const int bm = small_bm(a.d_hidden);
             const int tiles = (int)((a.n_rows + bm - 1) / bm);
             launch_mfma<1>(a, tiles, s);
+        } else if (a.d_model % 64 == 0) {
+            const dim3 grid((unsigned)((a.n_rows + 63) / 64));
+            if (a.d_model == 4096) {
+                switch (a.d_hidden) {
+                case 32: hipLaunchKernelGGL((gate_pipe_kernel<32, 64>), grid, dim3(NT), 0, s, a); break;
+                case 64: hipLaunchKernelGGL((gate_pipe_kernel<64, 64>), grid, dim3(NT), 0, s, a); break;
+                case 128: hipLaunchKernelGGL((gate_pipe_kernel<128, 64>), grid, dim3(NT), 0, s, a); break;
+                default: hipLaunchKernelGGL((gate_pipe_kernel<256, 64>), grid, dim3(NT), 0, s, a); break;
+                }
+            } else {
+                switch (a.d_hidden) {
+                case 32: hipLaunchKernelGGL((gate_pipe_kernel<32, 0>), grid, dim3(NT), 0, s, a); break;
+                case 64: hipLaunchKernelGGL((gate_pipe_kernel<64, 0>), grid, dim3(NT), 0, s, a); break;
+                case 128: hipLaunchKernelGGL((gate_pipe_kernel<128, 0>), grid, dim3(NT), 0, s, a); break;
+                default: hipLaunchKernelGGL((gate_pipe_kernel<256, 0>), grid, dim3(NT), 0, s, a); break;
+                }
+            }
         } else {
             const int tiles = (int)((a.n_rows + 63) / 64);
             launch_mfma<4>(a, tiles, s);

@@ -133,6 +133,49 @@ def test_capacity_overflow_is_flagged():
         np.testing.assert_array_equal(k.float().cpu().numpy(), K[ref, g])
 
 
+@pytest.mark.parametrize("window,rows", [(128, 3000), (512, 2000), (1024, 1500), (1024, 700)])
+def test_window_only_appends_of_long_chunks(window, rows):
+    # window-only appends of more rows than one tile, windows longer than a
+    # tile: the ring holds exactly the last `window` positions of each sequence
+    import dataclasses
+    wl = dataclasses.replace(inputs.WORKLOADS["decode_32k"], window=window)
+    B = 2
+    data = [_seq_data(wl, rows + 37 * b, b, 13, [0.3] * 8) for b in range(B)]
+    cache = tl.new_cache(wl, B, rows + 37 * B)
+    n = [rows + 37 * b for b in range(B)]
+    tl.append(cache, None, [data[b][0][:n[b]] for b in range(B)], [data[b][1][:n[b]] for b in range(B)],
+              [0] * B, W_)
+    torch.cuda.synchronize()
+    assert spkv.spkv_cache_check(cache) == 0
+    assert int(cache.lengths.sum()) == 0
+    for b in range(B):
+        K, V, _ = data[b]
+        for g in (0, 5):
+            rk, rv = cache.read_ring(b, g)
+            rk, rv = rk.float().cpu().numpy(), rv.float().cpu().numpy()
+            for p in range(max(0, n[b] - window), n[b]):
+                np.testing.assert_array_equal(rk[p % window], K[p, g])
+                np.testing.assert_array_equal(rv[p % window], V[p, g])
+
+
+def test_negative_positions_are_flagged():
+    wl = inputs.WORKLOADS["decode_32k"]
+    K, V, Z = _seq_data(wl, 300, 0, 14, [0.5] * 8)
+    cache = tl.new_cache(wl, 2, 300)
+    kd, vd, keep = tl.dev(K, torch.bfloat16), tl.dev(V, torch.bfloat16), tl.dev(Z)
+    for ro_, p0_, mr in (([0, 1, 2], [-5, 7], 1), ([0, 120, 300], [-1, 0], 180), ([0, 150, 300], [0, -3], 150),
+                         ([0, 290, 300], [-2, 0], 290)):
+        cache = tl.new_cache(wl, 2, 300)
+        spkv.spkv_compact_append(cache, keep, kd, vd, tl.dev(np.array(ro_, np.int32)),
+                                 tl.dev(np.array(p0_, np.int32)), mr, G_ | W_)
+        torch.cuda.synchronize()
+        with pytest.raises(spkv.SpkvError) as ei:
+            spkv.spkv_cache_check(cache)
+        assert ei.value.code == spkv.SPKV_E_ROWS
+        bad = 0 if p0_[0] < 0 else 1
+        assert int(cache.lengths[bad].sum()) == 0  # the sequence with a negative position was skipped
+
+
 def test_bad_row_offsets_are_flagged():
     wl = inputs.WORKLOADS["decode_32k"]
     K, V, Z = _seq_data(wl, 300, 0, 12, [0.5] * 8)

@@ -14,10 +14,12 @@ import spkv_testlib as tl
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, n_rows, seed=7, tau=None, d_hidden=None):
+def _run(wl, n_rows, seed=7, tau=None, d_hidden=None, d_model=None):
     import dataclasses
     if d_hidden is not None:
         wl = dataclasses.replace(wl, d_hidden=d_hidden)
+    if d_model is not None:
+        wl = dataclasses.replace(wl, d_model=d_model)
     w = tl.calibrated_weights(wl)
     H = inputs.normal((n_rows, wl.d_model), seed, 99, dtype=wl.dtype)
     H, u_ref, z_ref = tl.resample_band(wl, w, H, seed, 99)
@@ -34,21 +36,36 @@ def _run(wl, n_rows, seed=7, tau=None, d_hidden=None):
     ("tiny", 1, None),             # few rows: one workgroup per hidden unit
     ("tiny", 16, None),
     ("decode_32k", 1, None),
-    ("decode_32k", 8, None),       # bf16 decode step (few-row kernel)
+    ("decode_32k", 8, None),       # bf16 decode step (few-row MFMA tiles)
     ("decode_32k", 16, None),      # largest few-row batch
     ("decode_32k", 3, 256),
     ("decode_32k", 12, 48),
     ("decode_32k", 17, None),      # bf16, d_model split over workgroups
     ("decode_32k", 64, None),      # largest split batch
-    ("decode_32k", 65, None),      # first full-tile batch, ragged tail
+    ("decode_32k", 65, None),      # first full-tile batch, ragged tail (pipelined kernel, d_model 4096)
     ("decode_32k", 1500, None),    # several 64-row tiles
     ("decode_32k", 40, 32),        # d_hidden 32 on the split path
     ("decode_32k", 300, 256),
+    ("decode_32k", 200, 32),       # pipelined kernel, every unit width
+    ("decode_32k", 129, 64),
     ("decode_32k", 50, 48),        # d_hidden without an MFMA tiling: VALU kernel
 ])
 def test_gate_matches_oracle(name, n_rows, d_hidden):
     u, z, u_ref, z_ref = _run(inputs.WORKLOADS[name], n_rows, d_hidden=d_hidden)
     print(f"[gate {name} n={n_rows} hg={d_hidden}] max|du|={tl.max_abs(u, u_ref):.3e} kept={z.mean():.3f}")
+    np.testing.assert_array_equal(z, z_ref)
+    assert tl.max_abs(u, u_ref) <= tl.U_TOL
+
+
+@pytest.mark.parametrize("d_model,n_rows,d_hidden", [
+    (1088, 300, 128),   # pipelined kernel, run-time trip count not a multiple of its depth
+    (128, 100, 256),    # two iterations: fewer than the pipeline depth
+    (640, 70, 64),
+    (96, 130, 128),     # d_model not a multiple of 64: the plain MFMA kernel
+])
+def test_gate_other_model_widths(d_model, n_rows, d_hidden):
+    u, z, u_ref, z_ref = _run(inputs.WORKLOADS["decode_32k"], n_rows, d_hidden=d_hidden, d_model=d_model)
+    print(f"[gate d_model={d_model} n={n_rows} hg={d_hidden}] max|du|={tl.max_abs(u, u_ref):.3e} kept={z.mean():.3f}")
     np.testing.assert_array_equal(z, z_ref)
     assert tl.max_abs(u, u_ref) <= tl.U_TOL
 
