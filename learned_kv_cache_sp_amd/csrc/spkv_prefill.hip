@@ -19,8 +19,12 @@
 // values).  Both layouts are XOR-swizzled so MFMA operand reads are free of
 // bank conflicts.  Per wave and 32 keys:
 //   S^T[32 keys x 16 pairs] = K . Q^T       (v_mfma_f32_16x16x32_bf16)
-//   O^T[hd x 16 pairs]     += V^T . P^T     (P as a bf16 pair, f32-accurate)
+//   O^T[hd x 16 pairs]     += V^T . P^T     (P rounded to bf16, f32 accumulate)
 // for each of its 2 pair tiles, online softmax with a lazily updated max.
+// The weights P enter the second product as bf16 (relative error <= 2^-9 per
+// weight; the normaliser l sums them in f32): this kernel is MFMA-bound, and
+// a bf16 hi/lo pair (f32-accurate, as the memory-bound decode kernel uses)
+// would cost half as many MFMAs again.
 // Row tiles are handed out last-first: later rows see more keys.
 //
 // f32 (and a fallback for shapes the MFMA tiling does not take): VALU, one
@@ -468,7 +472,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            bf16x8 pb[PF_PT], pl[PF_PT];
+            bf16x8 pb[PF_PT];
 #pragma unroll
             for (int ptl = 0; ptl < PF_PT; ++ptl) {
                 float psum = 0.f;
@@ -477,7 +481,6 @@ prefill_bf16_kernel(PrefillArgs a) {
                     const float pe = __builtin_amdgcn_exp2f(fmaf(sc[hh][ptl][e >> 2][e & 3], sl2, nbase[ptl]));  // -inf -> 0
                     psum += pe;
                     pb[ptl][e] = (__bf16)pe;
-                    pl[ptl][e] = (__bf16)(pe - (float)pb[ptl][e]);
                 }
                 l[ptl] += psum;
             }
@@ -488,9 +491,7 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int ptl = 0; ptl < PF_PT; ++ptl)
                     o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ptl], o[ptl][nt], 0, 0, 0);
-#pragma unroll
-                for (int ptl = 0; ptl < PF_PT; ++ptl)
-                    o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[ptl], o[ptl][nt], 0, 0, 0);
+
             }
         }
     };

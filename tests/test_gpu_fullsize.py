@@ -166,4 +166,4 @@ def test_prefill_64k_full_size_sampled_rows():
     lse = np.stack([got_l[r] for r in sample])
     print(f"[prefill_64k full] rows={len(sample)} max|dout|={tl.max_abs(out, ro_):.2e} "
           f"max|dlse|={tl.max_abs(lse, rl_):.2e}")
-    assert tl.max_abs(out, ro_) <= tl.TOL_REGRESS and tl.max_abs(lse, rl_) <= tl.TOL_REGRESS
+    assert tl.max_abs(out, ro_) <= tl.TOL_PREFILL and tl.max_abs(lse, rl_) <= tl.TOL_REGRESS

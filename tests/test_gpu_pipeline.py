@@ -75,4 +75,4 @@ def test_pipeline_bf16_reduced_8b_layer():
     wl = inputs.WORKLOADS["prefill_64k"]
     e_o, e_l, keep = run_pipeline(wl, 1500, 6, 512, wl.seed)
     print(f"[pipeline bf16] max|dout|={e_o:.2e} max|dlse|={e_l:.2e} keep={keep}")
-    assert e_o <= tl.TOL_REGRESS and e_l <= tl.TOL_REGRESS
+    assert e_o <= tl.TOL_PREFILL and e_l <= tl.TOL_REGRESS

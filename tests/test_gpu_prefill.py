@@ -55,7 +55,7 @@ def test_prefill_bf16_8b_shape(T, chunk, rates):
     rows = np.arange(T)
     ro, rl = oracle.attention(tok["Q"], rows, tok["K"], tok["V"], z, wl.window, threads=tl.oracle_threads())
     print(f"[prefill bf16 T={T} chunk={chunk}] max|dout|={tl.max_abs(out, ro):.2e} max|dlse|={tl.max_abs(lse, rl):.2e}")
-    assert tl.max_abs(out, ro) <= tl.TOL_REGRESS and tl.max_abs(lse, rl) <= tl.TOL_REGRESS
+    assert tl.max_abs(out, ro) <= tl.TOL_PREFILL and tl.max_abs(lse, rl) <= tl.TOL_REGRESS
 
 
 def test_prefill_chunked_equals_one_shot():
