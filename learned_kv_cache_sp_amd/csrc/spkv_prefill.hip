@@ -205,11 +205,6 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int nb_d = n_part / PF_KB;                        // whole cached blocks (direct loads)
     const int nb_g = (n_part + PF_KB - 1) / PF_KB;          // all cached blocks
     const int nb_b = (t_max - s_lo + 1 + PF_KB - 1) / PF_KB;  // band blocks
-    const bool pt_lds = nb_d > 0 && ((nb_d * PF_KB - 1) >> c.page_shift) < PF_PTMAX;
-    if (pt_lds) {
-        const int np_ = ((nb_d * PF_KB - 1) >> c.page_shift) + 1;
-        for (int i = threadIdx.x; i < np_; i += PF_NT) lds_pt[i] = pt[i];
-    }
 
     const int lane = threadIdx.x & 63;
     const int wave = pf_uniform(threadIdx.x >> 6);
@@ -232,10 +227,12 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int cc = 0; cc < HD / 32; ++cc) qr[ptl][cc] = ok ? *(const bf16x8 *)(qp + 32 * cc) : bf16x8{};
     }
-    __syncthreads();  // page ids staged
-
     // ---- whole cached blocks: direct global -> LDS loads ---------------------
-    auto page_of = [&](int ent) -> int { return pt_lds ? lds_pt[ent >> c.page_shift] : pt[ent >> c.page_shift]; };
+    // Page ids come from LDS (lds_pt holds a window of the page table): a page
+    // id read from global memory just before each load would make every issue
+    // wait for all loads in flight, the pipeline's included.
+    int pg_base = 0;  // page index held by lds_pt[0]
+    auto page_of = [&](int ent) -> int { return lds_pt[(ent >> c.page_shift) - pg_base]; };
     auto issue_direct = [&](int j, int st) {
         const int e0 = j * PF_KB;
 #pragma unroll
@@ -497,22 +494,36 @@ prefill_bf16_kernel(PrefillArgs a) {
     };
 
     // ---- phase 1: whole cached blocks, PF_ST-stage pipeline -----------------
-    // Block j lives in stage j % PF_ST.  Before computing j a wave waits for
-    // its own loads of j (those of j + 1 may stay in flight), then the
-    // barrier makes every wave's loads of j visible and guarantees that every
-    // wave is done with j - 1, whose stage then receives j + 2.
+    // Windows of blocks whose page ids fit lds_pt (one window unless the list
+    // is very long).  Block j of a window lives in stage j % PF_ST.  Before
+    // computing j a wave waits for its own loads of j (those of j + 1 may
+    // stay in flight); then a plain barrier -- a fenced one would wait for
+    // the direct loads of j + 1 as well -- makes every wave's loads of j
+    // visible and guarantees that every wave is done reading j - 1 (its
+    // reads were consumed by its MFMAs), whose stage then receives j + 2.
     constexpr int WAIT_ONE = (LPB & 15) | (7 << 4) | (15 << 8) | ((LPB >> 4) << 14);  // vmcnt(LPB)
     constexpr int WAIT_ALL = (7 << 4) | (15 << 8);                                      // vmcnt(0)
-    if (nb_d > 0) issue_direct(0, 0);
-    if (nb_d > 1) issue_direct(1, 1);
-    for (int j = 0; j < nb_d; ++j) {
-        if (j + 1 < nb_d) __builtin_amdgcn_s_waitcnt(WAIT_ONE);
-        else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
-        __syncthreads();
-        if (j + 2 < nb_d) issue_direct(j + 2, (j + 2) % PF_ST);
-        compute_block(j % PF_ST, (j + 1) * PF_KB <= n_full ? 0 : 1);
+    const int win_blocks = (PF_PTMAX << c.page_shift) / PF_KB;  // >= 2048 (page size >= 32)
+    __syncthreads();  // query operands loaded, lds_cnt no longer read
+    for (int wb0 = 0; wb0 < nb_d; wb0 += win_blocks) {
+        const int wb1 = min(nb_d, wb0 + win_blocks);
+        pg_base = (wb0 * PF_KB) >> c.page_shift;
+        const int np_ = (((wb1 * PF_KB) - 1) >> c.page_shift) + 1 - pg_base;
+        for (int i = threadIdx.x; i < np_; i += PF_NT) lds_pt[i] = pt[pg_base + i];
+        __syncthreads();  // page ids staged (no direct loads in flight here)
+        const int n = wb1 - wb0;
+        issue_direct(wb0, 0);
+        if (n > 1) issue_direct(wb0 + 1, 1);
+        for (int jj = 0; jj < n; ++jj) {
+            const int j = wb0 + jj;
+            if (jj + 1 < n) __builtin_amdgcn_s_waitcnt(WAIT_ONE);
+            else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+            __builtin_amdgcn_s_barrier();
+            if (jj + 2 < n) issue_direct(j + 2, (jj + 2) % PF_ST);
+            compute_block(jj % PF_ST, (j + 1) * PF_KB <= n_full ? 0 : 1);
+        }
+        __syncthreads();  // every stage and lds_pt are free again (nothing in flight)
     }
-    __syncthreads();  // every stage is free again
 
     // ---- phase 2: partial cached block and band blocks (a few per
     // workgroup), staged through registers; the stores of block blk + 1 go
