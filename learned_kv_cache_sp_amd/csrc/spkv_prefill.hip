@@ -176,9 +176,14 @@ prefill_bf16_kernel(PrefillArgs a) {
     constexpr int VI = VBYTES / 1024;
     constexpr int KRPI = 1024 / (2 * HD);        // key rows per direct load
     constexpr int LPB = (KI + VI) / PF_NW + 1;   // direct loads per wave and block (+ positions)
-    __shared__ __attribute__((aligned(1024))) char lds_kb[PF_ST][KBYTES];
-    __shared__ __attribute__((aligned(1024))) char lds_vb[PF_ST][VBYTES];
-    __shared__ __attribute__((aligned(16))) int lds_pos[PF_ST][PF_KB];
+    // one array per stage: with every stage index a compile-time constant in
+    // the pipeline loop, the compiler can tell that reading one stage does
+    // not touch the direct loads in flight into another (with one indexed
+    // array it waits for all of them before every read)
+    static_assert(PF_ST == 3, "three stages");
+    __shared__ __attribute__((aligned(1024))) char lds_kb0[KBYTES], lds_kb1[KBYTES], lds_kb2[KBYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_vb0[VBYTES], lds_vb1[VBYTES], lds_vb2[VBYTES];
+    __shared__ __attribute__((aligned(16))) int lds_pos0[PF_KB], lds_pos1[PF_KB], lds_pos2[PF_KB];
     __shared__ int lds_pt[PF_PTMAX];
     __shared__ int lds_cnt[2];
 
@@ -233,7 +238,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     // wait for all loads in flight, the pipeline's included.
     int pg_base = 0;  // page index held by lds_pt[0]
     auto page_of = [&](int ent) -> int { return lds_pt[(ent >> c.page_shift) - pg_base]; };
-    auto issue_direct = [&](int j, int st) {
+    auto issue_direct = [&](int j, char *kbuf, char *vbuf, int *pbuf) {
         const int e0 = j * PF_KB;
 #pragma unroll
         for (int u = 0; u < KI / PF_NW; ++u) {
@@ -242,7 +247,7 @@ prefill_bf16_kernel(PrefillArgs a) {
             const int cch = (lane % CPR) ^ swz_k<HD>(r);
             const int ent = e0 + r;
             const char *src = c.k_pages + (((int64_t)page_of(ent) * P + (ent & (P - 1))) * HD + 8 * cch) * 2;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_kb[st] + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(kbuf + i * 1024), 16, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < VI / PF_NW; ++u) {
@@ -251,13 +256,13 @@ prefill_bf16_kernel(PrefillArgs a) {
             const int cch = (lane & 7) ^ swz_v(e);
             const int ent = e0 + 8 * cch;
             const char *src = c.v_pages + (((int64_t)page_of(ent) * HD + e) * P + (ent & (P - 1))) * 2;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_vb[st] + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(vbuf + i * 1024), 16, 0, 0);
         }
         {
             // positions of the 64 entries (every wave loads the same values)
             const int ent = e0 + lane;
             const int32_t *src = c.pos_pages + (int64_t)page_of(ent) * P + (ent & (P - 1));
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)&lds_pos[st][0], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)pbuf, 4, 0, 0);
         }
     };
 
@@ -343,19 +348,19 @@ prefill_bf16_kernel(PrefillArgs a) {
             if (threadIdx.x < PF_KB) pst = s0 + threadIdx.x;
         }
     };
-    auto store_staged = [&](int blk, int st) {
+    auto store_staged = [&](int blk, char *kbuf, char *vbuf, int *pbuf) {
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
             const int id = threadIdx.x + u * PF_NT;
             const int kk = id / CPR, ch = id % CPR;
-            *(i32x4 *)(lds_kb[st] + koff<HD>(kk, ch)) = kst[u];
+            *(i32x4 *)(kbuf + koff<HD>(kk, ch)) = kst[u];
         }
         if (blk < nb_g) {
 #pragma unroll
             for (int u = 0; u < VCH; ++u) {
                 const int id = threadIdx.x + u * PF_NT;
                 const int e = id / (PF_KB / 8), kc = id % (PF_KB / 8);
-                *(i32x4 *)(lds_vb[st] + voff(e, kc)) = vst[u];
+                *(i32x4 *)(vbuf + voff(e, kc)) = vst[u];
             }
         } else {
 #pragma unroll
@@ -365,10 +370,10 @@ prefill_bf16_kernel(PrefillArgs a) {
                 const bf16x8 vv = __builtin_bit_cast(bf16x8, vst[u]);
 #pragma unroll
                 for (int e2 = 0; e2 < 8; ++e2)
-                    *(__bf16 *)(lds_vb[st] + voff(8 * dc + e2, kk2 >> 3) + 2 * (kk2 & 7)) = vv[e2];
+                    *(__bf16 *)(vbuf + voff(8 * dc + e2, kk2 >> 3) + 2 * (kk2 & 7)) = vv[e2];
             }
         }
-        if (threadIdx.x < PF_KB) lds_pos[st][threadIdx.x] = pst;
+        if (threadIdx.x < PF_KB) pbuf[threadIdx.x] = pst;
     };
 
     // ---- per-wave online softmax state over its pair tiles -------------------
@@ -398,9 +403,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     // pair tile for the whole block, then exponentials and value products
     // without branches, the products of the pair tiles alternating so that
     // no MFMA waits on the one before.
-    auto compute_block = [&](int st, int kind) {
-        const char *kb = lds_kb[st];
-        const char *vb = lds_vb[st];
+    auto compute_block = [&](const char *kb, const char *vb, const int *pb_pos, int kind) {
         f32x4 sc[2][PF_PT][2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -428,8 +431,8 @@ prefill_bf16_kernel(PrefillArgs a) {
         if (kind != 0) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const i32x4 p0 = *(const i32x4 *)&lds_pos[st][32 * hh + 8 * q4];
-                const i32x4 p1 = *(const i32x4 *)&lds_pos[st][32 * hh + 8 * q4 + 4];
+                const i32x4 p0 = *(const i32x4 *)&pb_pos[32 * hh + 8 * q4];
+                const i32x4 p1 = *(const i32x4 *)&pb_pos[32 * hh + 8 * q4 + 4];
 #pragma unroll
                 for (int ptl = 0; ptl < PF_PT; ++ptl) {
                     const int t = trow[ptl];
@@ -512,15 +515,22 @@ prefill_bf16_kernel(PrefillArgs a) {
         for (int i = threadIdx.x; i < np_; i += PF_NT) lds_pt[i] = pt[pg_base + i];
         __syncthreads();  // page ids staged (no direct loads in flight here)
         const int n = wb1 - wb0;
-        issue_direct(wb0, 0);
-        if (n > 1) issue_direct(wb0 + 1, 1);
-        for (int jj = 0; jj < n; ++jj) {
+        issue_direct(wb0, lds_kb0, lds_vb0, lds_pos0);
+        if (n > 1) issue_direct(wb0 + 1, lds_kb1, lds_vb1, lds_pos1);
+        // one block: stage S holds it, stage (S + 2) % 3 receives block jj + 2
+        auto block = [&](int jj, char *kb, char *vb, int *pb, char *kn, char *vn, int *pn) {
+            __builtin_amdgcn_sched_barrier(0);  // no scheduling across blocks (register pressure)
             const int j = wb0 + jj;
             if (jj + 1 < n) __builtin_amdgcn_s_waitcnt(WAIT_ONE);
             else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
             __builtin_amdgcn_s_barrier();
-            if (jj + 2 < n) issue_direct(j + 2, (jj + 2) % PF_ST);
-            compute_block(jj % PF_ST, (j + 1) * PF_KB <= n_full ? 0 : 1);
+            if (jj + 2 < n) issue_direct(j + 2, kn, vn, pn);
+            compute_block(kb, vb, pb, (j + 1) * PF_KB <= n_full ? 0 : 1);
+        };
+        for (int jj = 0; jj < n; jj += 3) {
+            block(jj, lds_kb0, lds_vb0, lds_pos0, lds_kb2, lds_vb2, lds_pos2);
+            if (jj + 1 < n) block(jj + 1, lds_kb1, lds_vb1, lds_pos1, lds_kb0, lds_vb0, lds_pos0);
+            if (jj + 2 < n) block(jj + 2, lds_kb2, lds_vb2, lds_pos2, lds_kb1, lds_vb1, lds_pos1);
         }
         __syncthreads();  // every stage and lds_pt are free again (nothing in flight)
     }
@@ -531,16 +541,17 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int b0 = nb_d, nb = nb_g + nb_b;
     if (b0 < nb) {
         load_staged(b0);
-        store_staged(b0, 0);
+        store_staged(b0, lds_kb0, lds_vb0, lds_pos0);
     }
     __syncthreads();
     for (int blk = b0; blk < nb; ++blk) {
-        const int st = (blk - b0) & 1;
+        const bool odd = ((blk - b0) & 1) != 0;
         if (blk + 1 < nb) {
             load_staged(blk + 1);
-            store_staged(blk + 1, st ^ 1);
+            store_staged(blk + 1, odd ? lds_kb0 : lds_kb1, odd ? lds_vb0 : lds_vb1, odd ? lds_pos0 : lds_pos1);
         }
-        compute_block(st, blk < nb_g ? 1 : 2);
+        compute_block(odd ? lds_kb1 : lds_kb0, odd ? lds_vb1 : lds_vb0, odd ? lds_pos1 : lds_pos0,
+                      blk < nb_g ? 1 : 2);
         __syncthreads();
     }
 
