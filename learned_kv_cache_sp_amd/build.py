@@ -52,6 +52,9 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
+    # a failed build must not leave the previous library behind to be tested
+    if os.path.exists(LIB):
+        os.remove(LIB)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

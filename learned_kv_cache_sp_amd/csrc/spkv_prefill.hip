@@ -470,9 +470,7 @@ prefill_bf16_kernel(PrefillArgs a) {
             }
             nbase[ptl] = (m[ptl] == -INFINITY) ? 0.f : -m[ptl];
         }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            bf16x8 pb[PF_PT];
+        auto exp_half = [&](int hh, bf16x8 (&pb)[PF_PT]) {
 #pragma unroll
             for (int ptl = 0; ptl < PF_PT; ++ptl) {
                 float psum = 0.f;
@@ -484,16 +482,32 @@ prefill_bf16_kernel(PrefillArgs a) {
                 }
                 l[ptl] += psum;
             }
-            // O^T += V^T . P^T; the V^T operand is shared by the pair tiles
+        };
+        // O^T += V^T . P^T; the V^T operand is shared by the pair tiles
+        auto pv_half = [&](int hh, const bf16x8 (&pb)[PF_PT]) {
 #pragma unroll
             for (int nt = 0; nt < HD / 16; ++nt) {
                 const bf16x8 va = *(const bf16x8 *)(vb + v_lane + nt * 16 * (2 * PF_KB) + (((4 * hh + q4) ^ v_x) << 4));
 #pragma unroll
                 for (int ptl = 0; ptl < PF_PT; ++ptl)
                     o[ptl][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ptl], o[ptl][nt], 0, 0, 0);
-
             }
+        };
+        bf16x8 pb0[PF_PT], pb1[PF_PT];
+        exp_half(0, pb0);
+        __builtin_amdgcn_sched_barrier(0);
+        // the first half's value products with the second half's
+        // exponentials between them (VALU work under the MFMAs)
+        pv_half(0, pb0);
+        exp_half(1, pb1);
+        __builtin_amdgcn_sched_group_barrier(0x100, HD / 16, 0);  // the value operand reads first
+#pragma unroll
+        for (int i = 0; i < (HD / 16) * PF_PT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then some VALU
         }
+        __builtin_amdgcn_sched_barrier(0);
+        pv_half(1, pb1);
     };
 
     // ---- phase 1: whole cached blocks, PF_ST-stage pipeline -----------------
