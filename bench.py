@@ -16,8 +16,9 @@ separate`` times the three calls instead).
 
 Other workloads (``--workload``): ``decode_131k`` (batch 4, 131072 tokens,
 per-head keep 2-60 %), ``ragged_32`` (batch 32, contexts 4096-65536, 15 %,
-hidden states buffered: window append + attention every step, gate + kept
-append of all 32 x 128 buffered rows every 128 steps) and ``prefill_64k``
+hidden states buffered: window append + attention every step -- one
+spkv_decode_step launch without gate -- and gate + kept append of all
+32 x 128 buffered rows every 128 steps) and ``prefill_64k``
 (one step = chunked prefill of a 65536-token sequence in 16384-token chunks:
 gate, kept append, prefill attention, window append per chunk).
 
@@ -299,9 +300,12 @@ def bench_decode(args, wl):
     lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
     gate_ws = spkv.workspace(spkv.spkv_gate_ws_bytes(gw, B * buf))
     comp_ws = spkv.workspace(spkv.spkv_compact_ws_bytes(caches[0], B * buf, buf))
+    # fused: one spkv_decode_step launch per step -- with the gate (no buffer,
+    # up to 16 sequences) or, with a gate buffer, the window append only
     fused = buf == 1 and args.step_mode != "separate" and B <= 16
-    if args.step_mode == "fused" and not fused:
-        raise SystemExit("the fused step takes up to 16 sequences and no gate buffer")
+    ring = buf > 1 and args.step_mode != "separate"
+    if args.step_mode == "fused" and not (fused or ring):
+        raise SystemExit("the fused step with a gate takes up to 16 sequences")
     if fused:
         dec_ws = [spkv.workspace(spkv.spkv_decode_step_ws_bytes(c, gw, nq)) for c in caches]
     else:
@@ -330,7 +334,7 @@ def bench_decode(args, wl):
 
     def pre(s):
         """work of step s before its decode: gate + append (or window append)"""
-        if fused:
+        if fused or ring:
             return
         l, i = s % L, s // L
         f, j = i // buf, i % buf
@@ -357,6 +361,15 @@ def bench_decode(args, wl):
                                       Ql[l, i].data_ptr(), nq * hd, tpos[i].data_ptr(), scale, ul[l, i].data_ptr(),
                                       zl[l, i].data_ptr(), out.data_ptr(), lse.data_ptr(), dws[l][0], dws[l][1],
                                       sp)
+            if rc:
+                raise RuntimeError(lib.spkv_last_error().decode())
+            return
+        if ring:
+            f, j = i // buf, i % buf
+            rc = lib.spkv_decode_step(ctypes.byref(cdescs[l]), None, nq, None, 0, wl.tau, Kl[l, f, 0, j].data_ptr(),
+                                      Vl[l, f, 0, j].data_ptr(), ld_step, Ql[l, i].data_ptr(), nq * hd,
+                                      tpos[i].data_ptr(), scale, None, None, out.data_ptr(), lse.data_ptr(),
+                                      dws[l][0], dws[l][1], sp)
             if rc:
                 raise RuntimeError(lib.spkv_last_error().decode())
             return
@@ -444,6 +457,8 @@ def bench_decode(args, wl):
                 tot += int(vis.sum())
             tot += nkv * min(t + 1, w)
         extra = 0
+        if ring:
+            extra = 2 * B * nkv * hd * 2 * 2  # new K/V rows read and written to the ring
         if fused:
             # the launch also reads W1 and the hidden rows (gate), reads the new
             # K/V rows and writes them to the ring, and writes the kept ones
@@ -481,14 +496,16 @@ def bench_decode(args, wl):
                             "one launch (one token per sequence)" if fused else
                             "spkv_gate + spkv_compact_append + spkv_decode_attn (one token per sequence)"
                             if buf == 1 else
+                            f"spkv_decode_step without gate (window append + attention) every step; spkv_gate + "
+                            f"spkv_compact_append(kept) of {B}x{buf} buffered rows when a buffer fills" if ring else
                             f"spkv_compact_append(window) + spkv_decode_attn every step; spkv_gate + "
                             f"spkv_compact_append(kept) of {B}x{buf} buffered rows when a buffer fills")},
         "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel (%s)" % (
-                         "spkv_decode_step" if fused else "spkv_decode_attn"),
+                         "spkv_decode_step" if fused else "spkv_decode_step, no gate" if ring else "spkv_decode_attn"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic("decode_bf16_kernel", wl.name,
-                                               f"decode_bf16_kernel<{hd}, {'true' if fused else 'false'}>"),
+                                               f"decode_bf16_kernel<{hd}, {1 if fused else 2 if ring else 0}>"),
                      "bytes_per_launch": float(bytes_per.mean()),
                      "launch_us": _stats_us(dec_ms), "launches_per_bracket": L},
         "host_wall_s": round(wall, 4),

@@ -253,6 +253,14 @@ size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads);
  * Capacity overflow drops the row and sets a status bit, and a negative
  * t[b] writes nothing for that sequence and sets SPKV_STATUS_BAD_ROWS, as
  * for spkv_compact_append.
+ * g == NULL: no gate and no GLOBAL append -- the step writes the new rows to
+ *   the ring (spkv_compact_append(WINDOW)) and attends, for a schedule that
+ *   gates buffered hidden states later (Fast KVzip method section, decode
+ *   buffer; SP-KV Eq. 4 needs a token in the persistent cache only once it
+ *   leaves the window).  hidden, tau, utility and keep are ignored; any
+ *   batch size; out and lse are bit-identical to
+ *   spkv_compact_append(WINDOW) followed by spkv_decode_attn; ws as for
+ *   spkv_decode_attn (spkv_decode_step_ws_bytes(c, NULL, n_q_heads)).
  */
 int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g,
                      int32_t n_q_heads, const void *hidden, int64_t ld_hidden,

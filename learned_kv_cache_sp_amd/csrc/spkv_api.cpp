@@ -246,8 +246,8 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int6
 static const int kFusedShareCut = 10;
 
 size_t spkv_decode_step_ws_bytes(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_heads) {
-    if (!c || !g || c->n_kv <= 0 || n_q_heads <= 0) return 0;
-    return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr, g->d_model, g->d_hidden);
+    if (!c || c->n_kv <= 0 || n_q_heads <= 0) return 0;
+    return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr, g ? g->d_model : 0, g ? g->d_hidden : 0);
 }
 
 int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_heads, const void *hidden,
@@ -255,7 +255,45 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
                      int64_t ld_q, const int32_t *t, float scale, float *utility, uint8_t *keep, float *out,
                      float *lse, void *ws, size_t ws_bytes, void *stream) {
     if (int r = check_cache(c)) return r;
-    if (!g) return fail(SPKV_E_INVALID, "gate descriptor is NULL");
+    if (!g) {
+        // no gate: the new rows go to the ring only (their kept pairs are
+        // appended later, e.g. when a gating buffer is flushed)
+        if (c->dtype != SPKV_BF16) return fail(SPKV_E_UNSUPPORTED, "a step without gate needs a bf16 cache");
+        if (n_q_heads < 1 || n_q_heads % c->n_kv)
+            return fail(SPKV_E_INVALID, "n_q_heads %d vs n_kv %d", n_q_heads, c->n_kv);
+        const int G = n_q_heads / c->n_kv;
+        if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+            return fail(SPKV_E_UNSUPPORTED, "group size %d (1, 2, 4, 8 or 16)", G);
+        if (!k || !v || !q || !t || !out) return fail(SPKV_E_INVALID, "k / v / q / t / out NULL");
+        if (!aligned16(k) || !aligned16(v) || !aligned16(q)) return fail(SPKV_E_INVALID, "k / v / q not 16-byte aligned");
+        if (int r = check_ld(ld_kv, (int64_t)c->n_kv * c->head_dim, c->dtype, "ld_kv")) return r;
+        if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
+        if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
+        const int grid = decode_grid();
+        int max_items = 0;
+        const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items);
+        if (!ws || ws_bytes < need) return fail(SPKV_E_WORKSPACE, "decode step workspace %zu < %zu bytes", ws_bytes, need);
+        if (!aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
+        spkv::DecodeArgs a = {};
+        a.c = spkv::make_view(c);
+        a.n_q = n_q_heads;
+        a.group = G;
+        a.q = (const char *)q;
+        a.ld_q = ld_q;
+        a.t = t;
+        a.scale = scale;
+        a.out = out;
+        a.lse = lse;
+        a.ws = (char *)ws;
+        a.grid = grid;
+        a.max_items = max_items;
+        a.k_new = (const char *)k;
+        a.v_new = (const char *)v;
+        a.ld_new = ld_kv;
+        hipError_t e = spkv::launch_decode(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "decode step launch");
+        return SPKV_OK;
+    }
     if (g->dtype != c->dtype) return fail(SPKV_E_INVALID, "gate dtype %d differs from the cache's", g->dtype);
     if (g->n_kv != c->n_kv) return fail(SPKV_E_INVALID, "gate n_kv %d vs cache n_kv %d", g->n_kv, c->n_kv);
     if (g->d_model < 32 || g->d_model % 32)

@@ -358,8 +358,16 @@ __device__ void fused_finisher(const DecodeArgs &a, const float *gshare, int *ga
     if (threadIdx.x == 0) reset_dev(plan_cnt);
 }
 
-template <int HD, bool FUSED>
+// MODE 0: attention only (spkv_decode_attn); MODE_STEP: the whole decode
+// step (gate, append, ring, attention); MODE_RING: the new rows' ring write
+// and attention (spkv_decode_step without a gate)
+constexpr int MODE_STEP = 1;
+constexpr int MODE_RING = 2;
+
+template <int HD, int MODE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) decode_bf16_kernel(DecodeArgs a) {
+    constexpr bool FUSED = MODE == MODE_STEP;  // gate + append + finisher
+    constexpr bool RING = MODE != 0;           // the new rows go into the ring here
     __shared__ int lds_F[MAX_BG + 1];     // first flat step of each (b, g)
     __shared__ int lds_len[MAX_BG];
     __shared__ int lds_t[MAX_BG];
@@ -532,7 +540,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         if (page < 0) {
             const __bf16 *kb = (const __bf16 *)c.ring_k + ((int64_t)bg * w + ls * KSTEP) * HD;
             const __bf16 *vb = (const __bf16 *)c.ring_v + (int64_t)bg * HD * w + ls * KSTEP;
-            if constexpr (FUSED) {
+            if constexpr (RING) {
                 const int tb = uniform(lds_t[bg / c.n_kv]);
                 if (tb >= 0 && ls == (tb % w) / KSTEP) {
                     // the step holding the new token (this wave wrote it into
@@ -724,7 +732,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const bool one = bg_first == bg_last;
     const bool pub_first = !one && first_split;                            // slot 1
     const bool pub_last = one ? (first_split || last_split) : last_split;  // slot 0
-    if constexpr (FUSED) {
+    if constexpr (RING) {
         // the new token's row goes into ring slot t % w; the wave that reads
         // that ring step writes it now, so that the wait at the end of its
         // first staging covers these stores
@@ -902,27 +910,28 @@ bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid) {
 int decode_blocks_per_cu() {
     int n = 1 << 20;
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, false>, NT, 0) == hipSuccess) n = min(n, v);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, false>, NT, 0) == hipSuccess) n = min(n, v);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, true>, NT, 0) == hipSuccess) n = min(n, v);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, true>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, 0>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, 0>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, MODE_STEP>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, MODE_STEP>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<128, MODE_RING>, NT, 0) == hipSuccess) n = min(n, v);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, decode_bf16_kernel<64, MODE_RING>, NT, 0) == hipSuccess) n = min(n, v);
     return max(1, n == (1 << 20) ? 1 : n);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const CacheView &c = a.c;
-    const bool fused = a.gate.d_hidden > 0;
+    const int mode = a.gate.d_hidden > 0 ? MODE_STEP : (a.k_new ? MODE_RING : 0);
     if (c.dtype == SPKV_BF16) {
+        const dim3 grid(a.grid);
         if (c.head_dim == 128) {
-            if (fused)
-                hipLaunchKernelGGL((decode_bf16_kernel<128, true>), dim3(a.grid), dim3(NT), 0, s, a);
-            else
-                hipLaunchKernelGGL((decode_bf16_kernel<128, false>), dim3(a.grid), dim3(NT), 0, s, a);
+            if (mode == MODE_STEP) hipLaunchKernelGGL((decode_bf16_kernel<128, MODE_STEP>), grid, dim3(NT), 0, s, a);
+            else if (mode == MODE_RING) hipLaunchKernelGGL((decode_bf16_kernel<128, MODE_RING>), grid, dim3(NT), 0, s, a);
+            else hipLaunchKernelGGL((decode_bf16_kernel<128, 0>), grid, dim3(NT), 0, s, a);
         } else {
-            if (fused)
-                hipLaunchKernelGGL((decode_bf16_kernel<64, true>), dim3(a.grid), dim3(NT), 0, s, a);
-            else
-                hipLaunchKernelGGL((decode_bf16_kernel<64, false>), dim3(a.grid), dim3(NT), 0, s, a);
+            if (mode == MODE_STEP) hipLaunchKernelGGL((decode_bf16_kernel<64, MODE_STEP>), grid, dim3(NT), 0, s, a);
+            else if (mode == MODE_RING) hipLaunchKernelGGL((decode_bf16_kernel<64, MODE_RING>), grid, dim3(NT), 0, s, a);
+            else hipLaunchKernelGGL((decode_bf16_kernel<64, 0>), grid, dim3(NT), 0, s, a);
         }
     } else {
         const dim3 grid(c.batch * a.n_q);

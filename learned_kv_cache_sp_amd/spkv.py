@@ -355,31 +355,36 @@ def spkv_decode_attn(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: floa
     return out, lse
 
 
-def spkv_decode_step_ws_bytes(cache: Cache, weights: GateWeights, n_q_heads: int) -> int:
-    return int(load_library().spkv_decode_step_ws_bytes(ctypes.byref(cache.desc()), ctypes.byref(weights.desc()),
-                                                        n_q_heads))
+def spkv_decode_step_ws_bytes(cache: Cache, weights: GateWeights | None, n_q_heads: int) -> int:
+    g = None if weights is None else ctypes.byref(weights.desc())
+    return int(load_library().spkv_decode_step_ws_bytes(ctypes.byref(cache.desc()), g, n_q_heads))
 
 
-def spkv_decode_step(cache: Cache, weights: GateWeights, hidden: torch.Tensor, tau: float, k: torch.Tensor,
+def spkv_decode_step(cache: Cache, weights: GateWeights | None, hidden, tau: float, k: torch.Tensor,
                      v: torch.Tensor, q: torch.Tensor, t: torch.Tensor, scale: float, utility=None, keep=None,
                      out=None, lse=None, ws=None, stream=None):
-    """Gate + append (GLOBAL | WINDOW) + decode attention of one step in one launch.
+    """Gate + append (GLOBAL | WINDOW) + decode attention of one step in one launch; with weights
+    None, only the ring write (WINDOW) + attention (hidden, tau ignored).
     hidden [batch, d_model], k / v [batch, n_kv, hd], q [batch, n_q, hd], t [batch] int32.
-    Returns (utility, keep, out, lse)."""
+    Returns (utility, keep, out, lse) (utility and keep None without a gate)."""
     lib = load_library()
     B, nq, hd = q.shape
     dev = q.device
-    nkv = weights.desc().n_kv
-    if keep is None:
-        keep = torch.empty((B, nkv), dtype=torch.uint8, device=dev)
-    if utility is None:
-        utility = torch.empty((B, nkv), dtype=torch.float32, device=dev)
+    gated = weights is not None
+    if gated:
+        nkv = weights.desc().n_kv
+        if keep is None:
+            keep = torch.empty((B, nkv), dtype=torch.uint8, device=dev)
+        if utility is None:
+            utility = torch.empty((B, nkv), dtype=torch.float32, device=dev)
+    else:
+        utility = keep = hidden = None
     if out is None:
         out = torch.empty((B, nq, hd), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
     _need_gpu(hidden, k, v, q, t, keep, utility, out, lse)
-    if hidden.dtype != weights.w1.dtype:
+    if gated and hidden.dtype != weights.w1.dtype:
         raise ValueError("hidden and w1 dtypes differ")
     if q.dtype != cache.dtype or k.dtype != cache.dtype or v.dtype != cache.dtype:
         raise ValueError("q / k / v dtype differs from the cache")
@@ -392,10 +397,10 @@ def spkv_decode_step(cache: Cache, weights: GateWeights, hidden: torch.Tensor, t
     if ws is None and need:
         ws = workspace(need, dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.spkv_decode_step(ctypes.byref(cache.desc()), ctypes.byref(weights.desc()), nq, _ptr(hidden),
-                                _row_stride(hidden), float(tau), _ptr(k), _ptr(v), ld, _ptr(q), _row_stride(q),
-                                _ptr(t), float(scale), _ptr(utility), _ptr(keep), _ptr(out), _ptr(lse), _ptr(ws),
-                                ws_bytes, _stream(stream)))
+    _check(lib.spkv_decode_step(ctypes.byref(cache.desc()), ctypes.byref(weights.desc()) if gated else None, nq,
+                                _ptr(hidden), _row_stride(hidden) if gated else 0, float(tau), _ptr(k), _ptr(v), ld,
+                                _ptr(q), _row_stride(q), _ptr(t), float(scale), _ptr(utility), _ptr(keep), _ptr(out),
+                                _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
     return utility, keep, out, lse
 
 

@@ -204,3 +204,42 @@ def test_decode_step_capacity_overflow_matches_separate_calls():
             _, _, pos = fused.read_head(b, g)
             n = pos.numel()
             np.testing.assert_array_equal(pos.cpu().numpy(), np.arange(n))
+
+
+@pytest.mark.parametrize("B,hd,nq", [(32, 128, 32), (3, 64, 16)])
+def test_ring_only_step_equals_window_append_plus_attn(B, hd, nq):
+    """spkv_decode_step without a gate: the ring write and the attention of
+    the separate calls, bit for bit (same kernel plan), any batch size."""
+    wl = tl.small_workload("decode_32k", batch=B, head_dim=hd, n_q=nq)
+    ctxs = [100 + 53 * b for b in range(B)]
+    steps = 5
+    dt = tl.torch_dtype(wl)
+    li = tl.layer_inputs(wl, [c + steps for c in ctxs], seed=1206)
+    caches = [tl.new_cache(wl, B, max(ctxs) + steps) for _ in range(2)]
+    for cache in caches:
+        tl.append(cache, [li.z[b][:ctxs[b]] for b in range(B)], [li.K[b][:ctxs[b]] for b in range(B)],
+                  [li.V[b][:ctxs[b]] for b in range(B)], [0] * B, G_ | W_)
+    one, sep = caches
+    ws1 = spkv.workspace(spkv.spkv_decode_step_ws_bytes(one, None, wl.n_q))
+    ws2 = spkv.workspace(spkv.spkv_decode_ws_bytes(sep, wl.n_q))
+    ro1 = _i32(np.arange(B + 1))
+    scale = tl.scale_for(wl.head_dim)
+    for s in range(steps):
+        t = [ctxs[b] + s for b in range(B)]
+        td = _i32(t)
+        k, v, q = (tl.dev(np.stack([x[b][t[b]] for b in range(B)]), dt) for x in (li.K, li.V, li.Q))
+        u1, z1, o1, l1 = spkv.spkv_decode_step(one, None, None, 0.0, k, v, q, td, scale, ws=ws1)
+        assert u1 is None and z1 is None
+        spkv.spkv_compact_append(sep, None, k, v, ro1, td, 1, W_)
+        o2, l2 = spkv.spkv_decode_attn(sep, q, td, scale, ws=ws2)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"step {s}"
+        # every sequence's output against the oracle (window + kept before the window)
+        oh = o1.cpu().numpy()
+        for b in (0, B - 1):
+            ro, _ = oracle.attention(li.Q[b][t[b]:t[b] + 1], [t[b]], li.K[b], li.V[b], li.z[b], wl.window, scale,
+                                     threads=tl.oracle_threads())
+            assert tl.max_abs(oh[b], ro[0]) <= tl.TOL_REGRESS
+    torch.cuda.synchronize()
+    assert torch.equal(one.lengths, sep.lengths)
+    assert torch.equal(one.ring_k, sep.ring_k) and torch.equal(one.ring_v, sep.ring_v)
+    assert spkv.spkv_cache_check(one) == 0
