@@ -16,8 +16,10 @@
 //   grid takes an equal contiguous share of that flat list: the load is
 //   balanced whatever the per-head lengths (they differ by 30x in the skewed
 //   workloads).  The grid is persistent (compute units x resident
-//   workgroups); workgroup x takes the contiguous share [x*spg, (x+1)*spg)
-//   and its 4 waves interleave over it, two steps in flight each.
+//   workgroups); workgroup x takes a contiguous share of the list and its 4
+//   waves interleave over it, two steps in flight each.  The shares are
+//   equal once every (b, g) is charged a few extra steps for the hand-over
+//   or output write that a workgroup starting it inside its share pays.
 //   A (b, g) wholly inside one share is finished by that workgroup (the 4
 //   wave states combined in LDS, output written).  A (b, g) spread over
 //   several shares gets one partial (max, sum, unnormalised output per query
@@ -49,6 +51,11 @@ constexpr int NW = 4;
 constexpr int KSTEP = 32;
 constexpr int MAX_BG = 2048;
 constexpr int ROUND = 256;             // steps staged per wave at a time
+// extra (virtual) steps charged to every (b, g) when the shares are cut:
+// starting a (b, g) inside a share costs its workgroup a hand-over or an
+// output write, about 8 steps of streaming time (8 measured best of 0, 4, 8,
+// 12 on the 32K-, 131K-context and ragged batch-32 decode workloads)
+constexpr int BG_COST = 8;
 constexpr int MAX_SLOTS_PER_BG = 256;  // partials merged per pass of the combine
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -429,21 +436,38 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     if (FUSED && threadIdx.x == 0) arrive_nr_dev(plan_cnt);  // the lengths are read
     const int total = uniform(block_scan(BG, [&](int i) { return nws + (lds_len[i] + KSTEP - 1) / KSTEP; },
                                          lds_F, lds_red));
-    // Shares: workgroup x takes [w0(x), w0(x+1)); the first n_cut workgroups
-    // (in a fused step they ran a gate unit first) take cut steps fewer.
-    const int spg0 = (total + n_att - 1) / n_att;
+    // Shares are cut from a list in which every (b, g) is charged BGC extra
+    // steps ahead of its own (a workgroup that starts a (b, g) inside its
+    // share also hands a partial over or writes an output there, which
+    // costs it about that much streaming time): the virtual position of
+    // step s of (b, g) is s + BGC * (bg + 1).  Workgroup x takes the virtual
+    // range [w0(x), w0(x+1)); the first n_cut workgroups (in a fused step
+    // they ran a gate unit first) take cut virtual steps fewer.
+    constexpr int BGC = BG_COST;
+    const int total_v = total + BGC * BG;
+    const int spg0 = (total_v + n_att - 1) / n_att;
     const int n_cut = FUSED ? min(g_items, n_att) : 0;
     const int cut = FUSED ? min(a.share_cut, spg0 / 2) : 0;
-    const int spg = (total + n_cut * cut + n_att - 1) / n_att;  // >= 2 * cut
+    const int spg = (total_v + n_cut * cut + n_att - 1) / n_att;  // >= 2 * cut
     const int cut_end = n_cut * (spg - cut);
-    auto w0 = [&](int x) -> int { return x * spg - min(x, n_cut) * cut; };
-    auto owner = [&](int s) -> int { return s < cut_end ? s / (spg - cut) : n_cut + (s - cut_end) / spg; };
+    auto w0 = [&](int x) -> int { return min(total_v, x * spg - min(x, n_cut) * cut); };
+    auto owner_v = [&](int v) -> int { return v < cut_end ? v / (spg - cut) : n_cut + (v - cut_end) / spg; };
+    auto owner = [&](int s, int bg) -> int { return owner_v(s + BGC * (bg + 1)); };  // s a step of (b, g)
+    // first real step at or after virtual position v
+    auto real_of = [&](int v) -> int {
+        int lo = 0, hi = BG - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (lds_F[mid] + BGC * mid <= v) lo = mid; else hi = mid - 1;
+        }
+        return lds_F[lo] + max(0, v - lds_F[lo] - BGC * (lo + 1));
+    };
     // One partial per (workgroup, (b, g)) that meet, at slot workgroup + bg:
     // ranges are contiguous and in order, so if workgroup x meets (b, g) then
     // x+1 cannot meet an earlier (b, g) -- the slots are distinct, and those
     // of one (b, g) are consecutive, from owner(F[bg]) + bg to owner(F[bg+1]-1) + bg.
-    const int W0 = min(total, w0(blockIdx.x));
-    const int W1 = min(total, w0(blockIdx.x + 1));
+    const int W0 = uniform(real_of(w0(blockIdx.x)));
+    const int W1 = uniform(real_of(w0(blockIdx.x + 1)));
     if (W0 >= W1) return;  // (uniform over the workgroup)
 
     const int lane = threadIdx.x & 63;
@@ -599,8 +623,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         return (int64_t)b * a.n_q + (bg - b * c.n_kv) * G + h;
     };
     auto parts_of = [&](int bg, int &part0, int &n_parts) {
-        part0 = owner(lds_F[bg]) + bg;  // first slot of (b, g)
-        n_parts = owner(lds_F[bg + 1] - 1) + bg - part0 + 1;
+        part0 = owner(lds_F[bg], bg) + bg;  // first slot of (b, g)
+        n_parts = owner(lds_F[bg + 1] - 1, bg) + bg - part0 + 1;
     };
     // Partials are handed between workgroups with 16-byte device-scope
     // (sc1) buffer stores and loads: they bypass the non-coherent per-XCD L2
