@@ -112,6 +112,24 @@ constexpr float PF_LOG2E = 1.4426950408889634f;
 constexpr float PF_LN2 = 0.6931471805599453f;
 
 __device__ inline int pf_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// raw buffer descriptor over `bytes` bytes at base (gfx9 family dword 3)
+__device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+typedef __attribute__((address_space(3))) void lds_void;
+// direct buffer -> LDS loads of 16 and 4 bytes per lane (lane l writes
+// dst + size * l).  The builtin is left out of the host pass, whose checks
+// reject it inside the kernel template.
+__device__ inline void pf_buffer_lds16(__amdgpu_buffer_rsrc_t r, lds_void *dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#endif
+}
+__device__ inline void pf_buffer_lds4(__amdgpu_buffer_rsrc_t r, lds_void *dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+#endif
+}
 
 // position of cached entry j of (b, g)
 __device__ inline int entry_pos(const CacheView &c, const int32_t *pt, int j) {
@@ -164,7 +182,6 @@ template <int HD>
 __device__ inline int koff(int r, int c) { return r * (2 * HD) + ((c ^ swz_k<HD>(r)) << 4); }
 __device__ inline int voff(int e, int c) { return e * (2 * PF_KB) + ((c ^ swz_v(e)) << 4); }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <int HD>
 __global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -238,8 +255,43 @@ prefill_bf16_kernel(PrefillArgs a) {
     // wait for all loads in flight, the pipeline's included.
     int pg_base = 0;  // page index held by lds_pt[0]
     auto page_of = [&](int ent) -> int { return lds_pt[(ent >> c.page_shift) - pg_base]; };
+    // Pages of at least one block (the usual case): a block lies in one page,
+    // so its loads are buffer loads from the page with a scalar base and
+    // per-lane offsets fixed for the whole launch -- no address arithmetic
+    // per block.
+    const bool page_blocks = P >= PF_KB;
+    int dk_off[KI / PF_NW], dv_off[VI / PF_NW];
+#pragma unroll
+    for (int u = 0; u < KI / PF_NW; ++u) {
+        const int i = wave + PF_NW * u;
+        const int r = i * KRPI + lane / CPR;
+        dk_off[u] = (r * HD + 8 * ((lane % CPR) ^ swz_k<HD>(r))) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < VI / PF_NW; ++u) {
+        const int i = wave + PF_NW * u;
+        const int e = i * 8 + (lane >> 3);
+        dv_off[u] = (e * P + 8 * ((lane & 7) ^ swz_v(e))) * 2;
+    }
     auto issue_direct = [&](int j, char *kbuf, char *vbuf, int *pbuf) {
         const int e0 = j * PF_KB;
+        if (page_blocks) {
+            const int page = pf_uniform(page_of(e0));
+            const int slot0 = e0 & (P - 1);
+            const __amdgpu_buffer_rsrc_t rk =
+                pf_rsrc(c.k_pages + ((int64_t)page * P + slot0) * HD * 2, PF_KB * HD * 2);
+            const __amdgpu_buffer_rsrc_t rv =
+                pf_rsrc(c.v_pages + ((int64_t)page * HD * P + slot0) * 2, (HD * P - slot0) * 2);
+            const __amdgpu_buffer_rsrc_t rp = pf_rsrc(c.pos_pages + (int64_t)page * P + slot0, PF_KB * 4);
+#pragma unroll
+            for (int u = 0; u < KI / PF_NW; ++u)
+                pf_buffer_lds16(rk, (lds_void *)(kbuf + (wave + PF_NW * u) * 1024), dk_off[u]);
+#pragma unroll
+            for (int u = 0; u < VI / PF_NW; ++u)
+                pf_buffer_lds16(rv, (lds_void *)(vbuf + (wave + PF_NW * u) * 1024), dv_off[u]);
+            pf_buffer_lds4(rp, (lds_void *)pbuf, lane * 4);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < KI / PF_NW; ++u) {
             const int i = wave + PF_NW * u;

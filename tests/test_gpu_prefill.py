@@ -58,6 +58,20 @@ def test_prefill_bf16_8b_shape(T, chunk, rates):
     assert tl.max_abs(out, ro) <= tl.TOL_PREFILL and tl.max_abs(lse, rl) <= tl.TOL_REGRESS
 
 
+@pytest.mark.parametrize("page", [32, 128, 256])
+def test_prefill_bf16_page_sizes(page):
+    # pages smaller than a 64-key block take the per-lane address path of the
+    # direct loads, larger ones the page-based one with blocks inside a page
+    wl = inputs.WORKLOADS["prefill_64k"]
+    T = 1100
+    tok = inputs.tokens(wl, T, 54, 0)
+    z = inputs.bernoulli_mask(T, [0.5, 0.3, 0.9, 0.3, 0.1, 0.3, 0.7, 1.0], 54, 0)
+    out, lse, _ = prefill_chunks(wl, tok["Q"], tok["K"], tok["V"], z, 500, page=page)
+    ro, rl = oracle.attention(tok["Q"], np.arange(T), tok["K"], tok["V"], z, wl.window, threads=tl.oracle_threads())
+    print(f"[prefill bf16 page={page}] max|dout|={tl.max_abs(out, ro):.2e} max|dlse|={tl.max_abs(lse, rl):.2e}")
+    assert tl.max_abs(out, ro) <= tl.TOL_PREFILL and tl.max_abs(lse, rl) <= tl.TOL_REGRESS
+
+
 def test_prefill_chunked_equals_one_shot():
     wl = inputs.WORKLOADS["prefill_64k"]
     T = 900
