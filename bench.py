@@ -92,6 +92,10 @@ def parse():
                    help="also run a plain 1 GiB elementwise copy (for scaling HBM counters)")
     p.add_argument("--summarize-stats", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--summarize-mfma", metavar="DIR",
+                   help="matrix-core counters (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, "
+                        "SQ_INSTS_VALU_MFMA_MOPS_BF16) per kernel")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM read / copy ceiling")
     p.add_argument("--kernel", default="decode_bf16_kernel")
     return p.parse_args()
 
@@ -186,6 +190,38 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, workload: str) ->
                "bytes_per_launch": round((f_per[k][1] * f_fac + wv * w_fac) * 1024),
                "source": KERNEL_SOURCES[kernel], "source_sha256": _source_hash(kernel)}
         out.append("traffic_json: " + json.dumps(rec))
+    return "\n".join(out)
+
+
+SIMD_NUM = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
+XCD_NUM = 8         # GRBM_GUI_ACTIVE comes summed over the XCDs' GRBM instances
+
+
+def summarize_mfma(d: str) -> str:
+    """Matrix-core utilisation per kernel from one counter pass: busy = summed
+    MFMA-busy cycles / (GPU-active cycles x SIMDs), the rocprof MfmaUtil
+    definition, with the active cycles of one XCD (the counter arrives summed
+    over the 8 XCDs: 8x the kernel's duration in cycles); and the bf16 MFMA
+    work the counters saw (MOPS x 512 FLOP)."""
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    per = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] in names:
+            key = (_short(r["Kernel_Name"]), r.get("Dispatch_Id", ""))
+            per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for (k, _), v in per.items():
+        if all(n in v for n in names):
+            agg.setdefault(k, []).append(v)
+    out = [f"{'kernel':60s} {'n':>4s} {'MFMA_busy_%':>12s} {'active_cycles':>15s} {'MFMA_TFLOP/disp':>16s}"]
+    for k in sorted(agg):
+        if not any(x in k for x in ("gate", "compact", "decode", "prefill")):
+            continue
+        vs = agg[k]
+        busy = np.mean([v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / XCD_NUM * SIMD_NUM) for v in vs]) * 100
+        gui = np.mean([v["GRBM_GUI_ACTIVE"] / XCD_NUM for v in vs])
+        fl = np.mean([v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for v in vs]) / 1e12
+        out.append(f"{k:60s} {len(vs):4d} {busy:12.1f} {gui:15.0f} {fl:16.3f}")
     return "\n".join(out)
 
 
@@ -725,6 +761,29 @@ def cpu_baseline_prefill(wl, budget_s: float) -> dict:
                       f"of all {wl.n_q} query heads over a seeded mask with keep {wl.keep[0]}; {dt:.1f} s"}
 
 
+def hbm_ceiling(torch) -> dict:
+    """Context for "% of peak": what plain library kernels reach on this GPU --
+    a 2 GiB read (sum of float32) and a 1 GiB + 1 GiB device copy, median of 5."""
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
+    y = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    def med(fn, nbytes):
+        ts = []
+        for i in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return round(nbytes / float(np.median(ts)) / 1e9, 1)
+    read = med(lambda: x.sum(), x.numel() * 4)
+    copy = med(lambda: y.copy_(x[: y.numel()]), 2 * y.numel() * 4)
+    del x, y
+    return {"read_GBs": read, "copy_GBs": copy, "unit": "GB/s",
+            "kind": "torch float32 sum over 2 GiB / torch copy of 1 GiB (read + write bytes), median of 5"}
+
+
 # ----------------------------------------------------------------------------
 
 def main():
@@ -734,6 +793,9 @@ def main():
         return
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.kernel, args.workload))
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "one GPU only: this benchmark measures the path on one MI355X; "
@@ -755,6 +817,9 @@ def main():
         torch.neg(a, out=b_)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = CALIBRATION_BYTES
+
+    if not args.no_ceiling:
+        res["hbm_ceiling"] = hbm_ceiling(torch)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, args.cpu_budget)
