@@ -24,6 +24,23 @@ namespace {
 constexpr int NT = 256;     // threads per workgroup
 constexpr int TILE = 256;   // rows per tile (one row per thread)
 
+// 16-byte pieces are handled as a native 4 x u32 vector: copies of the
+// library's struct-based vector type, or through a local element array, keep
+// the loaded pieces in scratch memory instead of registers.
+typedef uint32_t piece_t __attribute__((ext_vector_type(4)));
+
+// element i of a piece
+template <typename T>
+__device__ inline T piece_elem(const piece_t &v, int i) {
+    const uint32_t w = v[(i * (int)sizeof(T)) >> 2];
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, w);
+    } else {
+        static_assert(sizeof(T) == 2, "16- or 32-bit elements");
+        return __builtin_bit_cast(T, (uint16_t)(w >> (16 * (i & 1))));
+    }
+}
+
 
 __device__ inline int block_rank(bool flag, int *lds_waves, int *total) {
     const int lane = threadIdx.x & 63;
@@ -124,17 +141,17 @@ __device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_row
     // lanes); values: piece idx = chunk * n + row (consecutive rows on
     // neighbouring lanes).  Both batches are loaded before either is stored.
     for (int base = 0; base < np; base += NT * KB) {
-        uint4 kv[KB], vv[KB];
+        piece_t kv[KB], vv[KB];
 #pragma unroll
         for (int u = 0; u < KB; ++u) {
             const int idx = base + u * NT + (int)threadIdx.x;
             if (idx < np) {
                 const int kk = idx / cpr;
                 const int ch = idx - kk * cpr;
-                kv[u] = *(const uint4 *)(a.k + (int64_t)src_rows[kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16);
+                kv[u] = *(const piece_t *)(a.k + (int64_t)src_rows[kk] * ld_bytes + (int64_t)g * hd * ES + ch * 16);
                 const int vc = idx / n;
                 const int vk = idx - vc * n;
-                vv[u] = *(const uint4 *)(a.v + (int64_t)src_rows[vk] * ld_bytes + (int64_t)g * hd * ES + vc * 16);
+                vv[u] = *(const piece_t *)(a.v + (int64_t)src_rows[vk] * ld_bytes + (int64_t)g * hd * ES + vc * 16);
             }
         }
 #pragma unroll
@@ -143,13 +160,11 @@ __device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_row
             if (idx < np) {
                 const int kk = idx / cpr;
                 const int ch = idx - kk * cpr;
-                *(uint4 *)(kdst(kk) + ch * 16) = kv[u];
+                *(piece_t *)(kdst(kk) + ch * 16) = kv[u];
                 const int vc = idx / n;
                 const int vk = idx - vc * n;
-                T el[EPC];
-                __builtin_memcpy(el, &vv[u], 16);
 #pragma unroll
-                for (int i = 0; i < EPC; ++i) *vdst(vk, vc * EPC + i) = el[i];
+                for (int i = 0; i < EPC; ++i) *vdst(vk, vc * EPC + i) = piece_elem<T>(vv[u], i);
             }
         }
     }
@@ -298,22 +313,20 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
     const int cpr = hd / EPC;     // chunks per row (<= 32)
     const bool kept = global && a.keep[(int64_t)lo * c.n_kv + g] != 0;
     const int64_t src = (int64_t)lo * a.ld_kv * ES + (int64_t)g * hd * ES + lane * 16;
-    uint4 kv = {}, vv = {};
+    piece_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (lane < cpr) {
-        kv = *(const uint4 *)(a.k + src);
-        vv = *(const uint4 *)(a.v + src);
+        kv = *(const piece_t *)(a.k + src);
+        vv = *(const piece_t *)(a.v + src);
     }
-    T ve[EPC];
-    __builtin_memcpy(ve, &vv, 16);
 
     if (a.flags & SPKV_APPEND_WINDOW) {
         const int w = c.window;
         const int slot = pos % w;
         if (lane < cpr) {
-            *(uint4 *)(c.ring_k + ((bg * w + slot) * hd) * ES + lane * 16) = kv;
+            *(piece_t *)(c.ring_k + ((bg * w + slot) * hd) * ES + lane * 16) = kv;
             T *rv = (T *)c.ring_v + (bg * hd + lane * EPC) * w + slot;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) rv[(int64_t)e * w] = ve[e];
+            for (int e = 0; e < EPC; ++e) rv[(int64_t)e * w] = piece_elem<T>(vv, e);
         }
     }
     if (!kept) return;
@@ -340,10 +353,10 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
     }
     const int j = old_len & (P - 1);
     if (lane < cpr) {
-        *(uint4 *)(c.k_pages + (((int64_t)page * P + j) * hd) * ES + lane * 16) = kv;
+        *(piece_t *)(c.k_pages + (((int64_t)page * P + j) * hd) * ES + lane * 16) = kv;
         T *dv = (T *)c.v_pages + ((int64_t)page * hd + lane * EPC) * P + j;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) dv[(int64_t)e * P] = ve[e];
+        for (int e = 0; e < EPC; ++e) dv[(int64_t)e * P] = piece_elem<T>(vv, e);
     }
     if (lane == 0) {
         c.pos_pages[(int64_t)page * P + j] = pos;
