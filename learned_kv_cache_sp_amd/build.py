@@ -4,11 +4,17 @@ Every source under csrc/ is compiled for gfx950 only, with packed-FP32
 instruction selection disabled, and linked into one shared library next to
 this file.  Objects are compiled in parallel; the whole build takes a few
 tens of seconds on a CPU-only machine.
+
+The build fails if any kernel needs scratch (private) memory: in these
+kernels that only ever means a register array the compiler could not keep in
+registers, which turns a streaming loop into a string of dependent waits.
+The compiler's resource-usage remarks give each kernel's figure.
 """
 from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -38,16 +44,44 @@ def hipcc() -> str:
     return p
 
 
+# Known frames that hold no spilled data: the fused decode step reserves 36
+# bytes for two 2-entry index arrays of its partial merge, which the backend
+# then resolves without a single scratch instruction (checked in its ISA);
+# rewriting them as selects costs the kernel ~1 us.  Exact (kernel, size)
+# pairs: any other size fails the build again.
+SCRATCH_ALLOWED = {("_ZN4spkv12_GLOBAL__N_118decode_bf16_kernelILi128ELi1EEEvNS_10DecodeArgsE", 36)}
+
+
+def scratch_kernels(remarks: str) -> list:
+    """(kernel, bytes per lane) of every kernel with a non-zero scratch size in
+    hipcc's kernel-resource-usage remarks."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc(), *FLAGS]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
+    else:
+        cmd += ["-Rpass-analysis=kernel-resource-usage"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    bad = [k for k in scratch_kernels(r.stderr) if k not in SCRATCH_ALLOWED]
+    if bad:
+        raise RuntimeError(f"{src}: kernels using scratch memory (bytes per lane): {bad}")
     return obj
 
 

@@ -55,3 +55,13 @@ def test_argument_errors_before_any_launch(lib):
     c = spkv.CacheDesc()
     c.batch, c.n_kv, c.head_dim, c.window, c.page_size = 1, 8, 128, 100, 64
     assert lib.spkv_cache_reset(ctypes.byref(c), None) in (spkv.SPKV_E_UNSUPPORTED, spkv.SPKV_E_INVALID)
+
+
+def test_build_flags_kernels_with_scratch():
+    # the build refuses kernels that spill register arrays to scratch memory
+    from learned_kv_cache_sp_amd import build
+    remarks = ("x.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 144 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build.scratch_kernels(remarks) == [("kern_b", 144)]
