@@ -47,6 +47,8 @@ def _load():
     lib.spkv_oracle_gate.restype = ci
     lib.spkv_oracle_compact.argtypes = [i64, i64, vp, i64, vp, vp]
     lib.spkv_oracle_compact.restype = ci
+    lib.spkv_oracle_rethreshold.argtypes = [i64, vp, f64, vp, vp]
+    lib.spkv_oracle_rethreshold.restype = ci
     lib.spkv_oracle_attention.argtypes = [i64, i64, i64, i64, i64, vp, vp, i64, vp, vp,
                                           i64, vp, f64, vp, vp, ci]
     lib.spkv_oracle_attention.restype = ci
@@ -109,6 +111,22 @@ def compact(z, pos0: int = 0):
     if rc != 0:
         raise ValueError("spkv_oracle_compact rejected its arguments")
     return [pos[g, : ln[g]].copy() for g in range(nkv)]
+
+
+def rethreshold(u, tau2: float):
+    """O5: indices of the entries of one cache list whose stored utility
+    passes the new threshold (u >= tau2), in logical order.
+
+    u is one (sequence, key head) list's stored utilities (float32)."""
+    lib = _load()
+    u = np.ascontiguousarray(np.asarray(u, dtype=np.float32).reshape(-1))
+    n = u.shape[0]
+    idx = np.zeros((max(n, 1),), np.int64)
+    ln = np.zeros((1,), np.int64)
+    rc = lib.spkv_oracle_rethreshold(n, _p(u), float(tau2), _p(idx), _p(ln))
+    if rc != 0:
+        raise ValueError("spkv_oracle_rethreshold rejected its arguments")
+    return idx[: ln[0]].copy()
 
 
 def attention(Q, t_rows, K, V, z, w: int, scale: float | None = None, threads: int = 1):

@@ -7,14 +7,15 @@
  *
  * Source of every formula: "Self-Pruned Key-Value Attention: learning when to
  * write by predicting future utility" (arXiv 2605.14037), section 2.1,
- * equations (1)-(4), and the paragraph "efficient implementation at
- * deployment" at the end of section 2.1.
+ * equations (1)-(4), the paragraph "efficient implementation at
+ * deployment" at the end of section 2.1, and the post-hoc threshold of
+ * section 3.3 (hybrids paragraph).
  *
  * Precision: every input is a float32 array whose values are exact (bf16
  * values are a subset of float32); each value is widened to double on use and
  * all arithmetic is done in double, in fixed index order.
  *
- * Parity status of each function is stated in its comment; all three are
+ * Parity status of each function is stated in its comment; every one is
  * pinned by tests that do not call this file's arithmetic a second time
  * (closed forms, library routines, brute force, worked examples).
  */
@@ -129,6 +130,40 @@ int spkv_oracle_compact(int64_t n_rows, int64_t n_kv, const uint8_t *z,
         }
         len_out[g] = n;
     }
+    return 0;
+}
+
+/*
+ * O5 -- re-thresholding a persistent cache.  SP-KV section 2.1 (deployment
+ * paragraph) lets the sparse cache be rebuilt from time to time, and section
+ * 3.3 (hybrids paragraph) notes that sparsity can be changed after training
+ * by moving the threshold.  An entry kept at threshold tau carries its
+ * utility u (Eq. 1); at a new threshold tau2 the keep decision of Eq. (2) is
+ * taken again on that stored value.  For one (sequence, key head) list of n
+ * entries in logical (token) order this is the stable filter
+ *
+ *   idx_out[j] = i_j   where i_0 < i_1 < ... are the entries with u[i] >= tau2
+ *   *len_out   = number of such entries
+ *
+ * A NaN utility fails the comparison and is dropped, as in Eq. (2) for the
+ * gate.  The rebuilt entry j is entry i_j unchanged (key, value, position,
+ * utility).  The comparison is made in double on the exactly converted float
+ * values, which decides the same way as a float comparison.
+ */
+int spkv_oracle_rethreshold(int64_t n, const float *u, double tau2,
+                            int64_t *idx_out, int64_t *len_out)
+{
+    if (n < 0)
+        return -1;
+    int64_t kept = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double ui = (double)u[i];
+        if (ui >= tau2) {
+            idx_out[kept] = i;
+            ++kept;
+        }
+    }
+    *len_out = kept;
     return 0;
 }
 

@@ -357,3 +357,73 @@ def test_bf16_rounding_helper():
     np.testing.assert_array_equal(r, ref)
     y = np.random.default_rng(0).standard_normal(100000).astype(np.float32)
     np.testing.assert_array_equal(inputs.bf16_round(y), torch.from_numpy(y).to(torch.bfloat16).float().numpy())
+
+
+# ----------------------------------------------------------------------------
+# O5: re-threshold of a cache list (SP-KV section 2.1, deployment paragraph;
+# section 3.3, threshold changed after training)
+# ----------------------------------------------------------------------------
+
+def _stored_utilities(n, seed):
+    """Utilities of n rows of one key head, float32 in [0, 1], with exact
+    ties at a few grid values so that the inclusive comparison is exercised."""
+    r = inputs.rng(seed, 71)
+    u = r.random(n).astype(np.float32)
+    u[r.integers(0, n, n // 8)] = np.float32(0.5)
+    u[r.integers(0, n, n // 16)] = np.float32(0.75)
+    return u
+
+
+@pytest.mark.parametrize("tau,tau2", [(0.3, 0.3), (0.3, 0.5), (0.5, 0.75), (0.1, 0.9), (0.0, 1.0)])
+def test_rethreshold_equals_fresh_compaction(tau, tau2):
+    # Filtering the cache kept at tau by u >= tau2 gives the cache that a
+    # fresh compaction at tau2 builds (tau2 >= tau): positions come from the
+    # oracle's compaction of the full row set, a separate function, and from
+    # numpy's flatnonzero.
+    n = 3000
+    u = _stored_utilities(n, 5)
+    z1 = (u >= np.float32(tau)).astype(np.uint8)[:, None]
+    z2 = (u >= np.float32(tau2)).astype(np.uint8)[:, None]
+    kept1 = oracle.compact(z1, pos0=17)[0]
+    stored = u[kept1 - 17]
+    idx = oracle.rethreshold(stored, float(np.float32(tau2)))
+    np.testing.assert_array_equal(kept1[idx], oracle.compact(z2, pos0=17)[0])
+    np.testing.assert_array_equal(idx, np.flatnonzero(stored >= np.float32(tau2)))
+    if tau2 == tau:
+        np.testing.assert_array_equal(idx, np.arange(len(stored)))
+
+
+def test_rethreshold_special_cases():
+    half = np.float32(0.5)
+    # inclusive at the threshold, NaN dropped, order kept
+    u = np.array([0.5, np.nan, 0.49999997, 1.0, 0.5, 0.0], np.float32)
+    np.testing.assert_array_equal(oracle.rethreshold(u, float(half)), [0, 3, 4])
+    # above every utility: nothing; at or below the smallest: everything but NaN
+    assert oracle.rethreshold(u, 1.5).size == 0
+    np.testing.assert_array_equal(oracle.rethreshold(u, 0.0), [0, 2, 3, 4, 5])
+    np.testing.assert_array_equal(oracle.rethreshold(u, -math.inf), [0, 2, 3, 4, 5])
+    # a NaN threshold keeps nothing (every comparison fails)
+    assert oracle.rethreshold(u, math.nan).size == 0
+    # empty list
+    assert oracle.rethreshold(np.zeros(0, np.float32), 0.5).size == 0
+
+
+def test_rethreshold_composes_exhaustively():
+    # Brute force: every list of length <= 5 over four utility values and
+    # every pair of thresholds; two re-thresholds compose into the stricter
+    # one, and each kept index set is the subset whose values pass.
+    vals = np.array([0.25, 0.5, 0.75, np.nan], np.float32)
+    taus = [0.0, 0.25, 0.5, 0.6, 0.75, 1.0]
+    import itertools
+    for n in range(6):
+        for combo in itertools.product(range(4), repeat=n):
+            u = vals[list(combo)] if n else np.zeros(0, np.float32)
+            for a in taus:
+                ia = oracle.rethreshold(u, a)
+                assert all(u[i] >= a for i in ia)
+                assert sum(1 for x in u if x >= a) == len(ia)
+                for b in taus:
+                    if b < a:
+                        continue
+                    ib = oracle.rethreshold(u[ia], b)
+                    np.testing.assert_array_equal(ia[ib], oracle.rethreshold(u, b))
