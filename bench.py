@@ -379,11 +379,11 @@ def bench_decode(args, wl):
         if buf == 1:
             rc |= lib.spkv_gate(ctypes.byref(gdesc), Hl[l, f].data_ptr(), B, d, wl.tau, ul[l, f].data_ptr(),
                                 zl[l, f].data_ptr(), gws[0], gws[1], sp)
-            rc |= lib.spkv_compact_append(cd, zl[l, f].data_ptr(), Kl[l, f].data_ptr(), Vl[l, f].data_ptr(),
+            rc |= lib.spkv_compact_append(cd, zl[l, f].data_ptr(), None, Kl[l, f].data_ptr(), Vl[l, f].data_ptr(),
                                           nkv * hd, ro1.data_ptr(), tpos[i].data_ptr(), B, 1, G_ | W_, None,
                                           cws[0], cws[1], sp)
         else:
-            rc |= lib.spkv_compact_append(cd, None, Kl[l, f, 0, j].data_ptr(), Vl[l, f, 0, j].data_ptr(),
+            rc |= lib.spkv_compact_append(cd, None, None, Kl[l, f, 0, j].data_ptr(), Vl[l, f, 0, j].data_ptr(),
                                           ld_step, ro1.data_ptr(), tpos[i].data_ptr(), B, 1, W_, None,
                                           cws[0], cws[1], sp)
         if rc:
@@ -423,7 +423,7 @@ def bench_decode(args, wl):
             record("f0" if timing else None)
             rc = lib.spkv_gate(ctypes.byref(gdesc), Hl[l, f].data_ptr(), B * buf, d, wl.tau,
                                ul[l, f].data_ptr(), zl[l, f].data_ptr(), gws[0], gws[1], sp)
-            rc |= lib.spkv_compact_append(cd, zl[l, f].data_ptr(), Kl[l, f].data_ptr(), Vl[l, f].data_ptr(),
+            rc |= lib.spkv_compact_append(cd, zl[l, f].data_ptr(), None, Kl[l, f].data_ptr(), Vl[l, f].data_ptr(),
                                           nkv * hd, robuf.data_ptr(), gpos[f].data_ptr(), B * buf, buf, G_,
                                           None, cws[0], cws[1], sp)
             record("f1" if timing else None)

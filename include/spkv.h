@@ -18,7 +18,8 @@
  *   spkv_prefill_attn    a chunk of queries of one sequence over window + kept
  *                        pairs (Eq. 3-4), for chunked prefill
  * and spkv_decode_step runs gate, append and decode attention of one decode
- * step in a single launch.
+ * step in a single launch.  spkv_cache_rethreshold rebuilds a cache at a new,
+ * higher threshold from the utilities stored with its entries.
  *
  * Conventions
  *   - Every call returns an int status (SPKV_OK or a negative SPKV_E_*).
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPKV_VERSION 1
+#define SPKV_VERSION 2
 
 enum {
     SPKV_OK = 0,
@@ -112,6 +113,10 @@ typedef struct spkv_gate_desc {
  * Window ring of the last `window` tokens of every (b, g):
  *   ring_k     [batch, n_kv, window, head_dim]  slot = position % window
  *   ring_v     [batch, n_kv, head_dim, window]  transposed
+ * Optional:
+ *   u_pages    [n_pages, page_size] f32 or NULL: the utility u of each entry,
+ *              stored by the appends when set (spkv_compact_append needs its
+ *              utility argument then); spkv_cache_rethreshold reads it.
  * A fresh cache has lengths = 0, pool_next = 0, status = 0 (spkv_cache_reset).
  * Supported: head_dim in {64, 128}; page_size a power of two in [32, 1024];
  * window a multiple of 32 in [32, 1024].
@@ -134,6 +139,7 @@ typedef struct spkv_cache {
     int32_t *status;
     void *ring_k;
     void *ring_v;
+    float *u_pages; /* may be NULL */
 } spkv_cache;
 
 /*
@@ -165,6 +171,9 @@ size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows);
  *   and keep, at token positions pos0[b], pos0[b]+1, ... (consecutive).
  *   k, v     row r, key head g at  k + r*ld_kv + g*head_dim  (dtype)
  *   keep     [n_rows, n_kv] uint8; read only with SPKV_APPEND_GLOBAL
+ *   utility  [n_rows, n_kv] f32 (spkv_gate's output), read only with
+ *            SPKV_APPEND_GLOBAL and only when c->u_pages is set, and then
+ *            required: the utility of each kept row is stored with its entry.
  *   row_offsets [batch+1], pos0 [batch]: int32 device arrays
  *   max_rows_per_seq: host-side bound on row_offsets[b+1]-row_offsets[b]
  *   flags: SPKV_APPEND_GLOBAL -- for each (b, g), the rows with keep = 1 are
@@ -179,7 +188,8 @@ size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows);
  *   ws  at least spkv_compact_ws_bytes(...) bytes.
  * Capacity overflow drops the rows that do not fit and sets a status bit.
  */
-int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const void *k,
+int spkv_compact_append(const spkv_cache *c, const uint8_t *keep,
+                        const float *utility, const void *k,
                         const void *v, int64_t ld_kv, const int32_t *row_offsets,
                         const int32_t *pos0, int32_t n_rows,
                         int32_t max_rows_per_seq, int32_t flags,
@@ -238,7 +248,9 @@ size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads);
  *   hidden [batch, d_model] dtype (row b at hidden + b*ld_hidden)
  *   k, v   [batch, n_kv, head_dim] dtype (row b at k + b*ld_kv)
  *   q, t, scale, out, lse: as for spkv_decode_attn
- *   utility [batch, n_kv] f32 or NULL; keep [batch, n_kv] uint8
+ *   utility [batch, n_kv] f32 or NULL; keep [batch, n_kv] uint8.  When
+ *       c->u_pages is set, the utility of each appended entry is stored
+ *       there whether or not `utility` is given.
  *   ws  at least spkv_decode_step_ws_bytes(c, g, n_q_heads) bytes, zero-filled
  *       once after allocation (every call leaves its counters at zero; a ws
  *       of this size also serves spkv_decode_attn; zero it again after a
@@ -294,9 +306,39 @@ int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b,
 size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads,
                              int32_t n_rows);
 
+/*
+ * spkv_cache_rethreshold -- rebuild the persistent cache at a new threshold.
+ *   SP-KV lets the sparse cache be rebuilt periodically (section 2.1,
+ *   deployment paragraph) and its sparsity be moved after training by
+ *   changing the threshold (section 3.3, hybrids paragraph).  For every
+ *   (b, g), dst's list becomes the entries of src's list whose stored utility
+ *   satisfies u >= tau, in the same (token) order, with key, value, position
+ *   and utility copied exactly; a NaN utility is dropped.  With tau at or
+ *   above the threshold src was built with, the result is the cache that
+ *   gating at tau and compacting would have built; entries dropped from src
+ *   earlier cannot come back, so a lower tau keeps only what src holds.
+ *   src   a cache with u_pages set; read only.
+ *   dst   same batch, n_kv, head_dim, page_size and dtype.  Its page tables
+ *         and lengths are overwritten; pages are taken from its pool from
+ *         dst->pool_next on (reset dst first to reuse its pool), capacity
+ *         overflow drops entries and sets bits in dst->status as for
+ *         spkv_compact_append.  dst->u_pages may be NULL (the utilities are
+ *         then not kept).  The ring is not touched: point dst's ring at
+ *         src's, or copy it, before attending over dst.  No buffer dst
+ *         writes may overlap a buffer of src.
+ *   tau   the new threshold (not NaN).
+ *   ws    at least spkv_rethreshold_ws_bytes(src) bytes.
+ *   Launches three kernels: kept counts per tile of 256 entries, a scan and
+ *   page allocation per (b, g), the copies per tile.
+ */
+int spkv_cache_rethreshold(const spkv_cache *src, const spkv_cache *dst,
+                           float tau, void *ws, size_t ws_bytes, void *stream);
+size_t spkv_rethreshold_ws_bytes(const spkv_cache *src);
+
 /* Sizes in bytes of each cache buffer (k_pages, v_pages, pos_pages,
  * page_table, lengths, ring_k, ring_v) for the dimensions in *c; returns the
- * sum.  `sizes` may be NULL. */
+ * sum.  `sizes` may be NULL.  u_pages, when used, adds n_pages * page_size
+ * * 4 bytes, not included. */
 size_t spkv_cache_bytes(const spkv_cache *c, size_t sizes[7]);
 
 /* Queue a reset of lengths, pool_next and status to 0 (page contents are left

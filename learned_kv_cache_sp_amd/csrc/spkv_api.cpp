@@ -59,6 +59,7 @@ int check_cache(const spkv_cache *c) {
         if (!aligned16(ptrs[i]) && i != 5 && i != 6)
             return fail(SPKV_E_INVALID, "cache->%s is not 16-byte aligned", names[i]);
     }
+    if (c->u_pages && !aligned16(c->u_pages)) return fail(SPKV_E_INVALID, "cache->u_pages is not 16-byte aligned");
     return SPKV_OK;
 }
 
@@ -150,7 +151,8 @@ size_t spkv_compact_ws_bytes(const spkv_cache *c, int32_t n_rows, int32_t max_ro
     return spkv::compact_ws_bytes(c->batch, c->n_kv, max_rows_per_seq);
 }
 
-int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const void *k, const void *v,
+int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const float *utility, const void *k,
+                        const void *v,
                         int64_t ld_kv, const int32_t *row_offsets, const int32_t *pos0,
                         int32_t n_rows, int32_t max_rows_per_seq, int32_t flags,
                         int32_t *append_offsets, void *ws, size_t ws_bytes, void *stream) {
@@ -163,6 +165,8 @@ int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const void *k,
     if (!k || !v || !row_offsets || !pos0) return fail(SPKV_E_INVALID, "k / v / row_offsets / pos0 NULL");
     if (!aligned16(k) || !aligned16(v)) return fail(SPKV_E_INVALID, "k / v not 16-byte aligned");
     if ((flags & SPKV_APPEND_GLOBAL) && !keep) return fail(SPKV_E_INVALID, "keep is NULL with GLOBAL");
+    if ((flags & SPKV_APPEND_GLOBAL) && c->u_pages && !utility)
+        return fail(SPKV_E_INVALID, "the cache stores utilities (u_pages) but utility is NULL");
     if (int r = check_ld(ld_kv, (int64_t)c->n_kv * c->head_dim, c->dtype, "ld_kv")) return r;
     const size_t need = spkv::compact_ws_bytes(c->batch, c->n_kv, max_rows_per_seq);
     if (need && (!ws || ws_bytes < need))
@@ -170,6 +174,7 @@ int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const void *k,
     spkv::CompactArgs a;
     a.c = spkv::make_view(c);
     a.keep = keep;
+    a.utility = utility;
     a.k = (const char *)k;
     a.v = (const char *)v;
     a.ld_kv = ld_kv;
@@ -403,6 +408,58 @@ int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b, const v
     a.ws = (char *)ws;
     hipError_t e = spkv::launch_prefill(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+size_t spkv_rethreshold_ws_bytes(const spkv_cache *src) {
+    if (!src) return 0;
+    return spkv::rethresh_ws_bytes(src);
+}
+
+namespace {
+struct Span {
+    const char *p;
+    size_t n;
+};
+bool overlap(Span a, Span b) { return a.n && b.n && a.p < b.p + b.n && b.p < a.p + a.n; }
+}  // namespace
+
+int spkv_cache_rethreshold(const spkv_cache *src, const spkv_cache *dst, float tau, void *ws, size_t ws_bytes,
+                           void *stream) {
+    if (int r = check_cache(src)) return r;
+    if (int r = check_cache(dst)) return r;
+    if (src->batch != dst->batch || src->n_kv != dst->n_kv || src->head_dim != dst->head_dim ||
+        src->page_size != dst->page_size || src->dtype != dst->dtype)
+        return fail(SPKV_E_INVALID, "src and dst differ in batch, n_kv, head_dim, page_size or dtype");
+    if (!src->u_pages) return fail(SPKV_E_INVALID, "src->u_pages is NULL (no stored utilities)");
+    if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
+    // dst's writes must not reach anything src's lists are read from
+    size_t ss[7], ds[7];
+    spkv_cache_bytes(src, ss);
+    spkv_cache_bytes(dst, ds);
+    const size_t su = (size_t)(src->n_pages > 0 ? src->n_pages : 0) * src->page_size * 4;
+    const size_t du = (size_t)(dst->n_pages > 0 ? dst->n_pages : 0) * dst->page_size * 4;
+    const Span rd[] = {{(const char *)src->k_pages, ss[0]}, {(const char *)src->v_pages, ss[1]},
+                       {(const char *)src->pos_pages, ss[2]}, {(const char *)src->page_table, ss[3]},
+                       {(const char *)src->lengths, ss[4]}, {(const char *)src->u_pages, su}};
+    const Span wr[] = {{(const char *)dst->k_pages, ds[0]}, {(const char *)dst->v_pages, ds[1]},
+                       {(const char *)dst->pos_pages, ds[2]}, {(const char *)dst->page_table, ds[3]},
+                       {(const char *)dst->lengths, ds[4]}, {(const char *)dst->u_pages, dst->u_pages ? du : 0},
+                       {(const char *)dst->pool_next, 4}, {(const char *)dst->status, 4}};
+    for (const Span &w : wr)
+        for (const Span &r : rd)
+            if (overlap(w, r)) return fail(SPKV_E_INVALID, "a dst buffer overlaps a src buffer");
+    const size_t need = spkv::rethresh_ws_bytes(src);
+    if (!ws || ws_bytes < need) return fail(SPKV_E_WORKSPACE, "re-threshold workspace %zu < %zu bytes", ws_bytes, need);
+    spkv::RethreshArgs a;
+    a.src = spkv::make_view(src);
+    a.dst = spkv::make_view(dst);
+    a.tau = tau;
+    a.ws = (int32_t *)ws;
+    a.max_tiles = 0;
+    hipError_t e = spkv::launch_rethresh(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "re-threshold launch");
     return SPKV_OK;
 }
 

@@ -15,7 +15,14 @@
 //
 // Layout written: key rows [page][slot][hd] (16-byte coalesced copies), value
 // rows transposed [page][hd][slot] (transposed in registers: consecutive
-// lanes write consecutive slots), positions [page][slot].
+// lanes write consecutive slots), positions [page][slot], and when the cache
+// keeps them, utilities [page][slot].
+//
+// The same file holds the re-threshold of a cache (SP-KV section 2.1,
+// deployment paragraph: the cache may be rebuilt from time to time; section
+// 3.3, hybrids paragraph: sparsity can be changed after training through the
+// threshold): a stable filter of every (b, g) list on its stored utilities,
+// ranked the same way and copied page to page.
 #include "spkv_internal.h"
 
 namespace spkv {
@@ -198,10 +205,13 @@ __device__ void scatter_tile(const CompactArgs &a, int b, int g, int r0, int row
     const int npg = ((dst0 + n - 1) >> c.page_shift) - pg0 + 1;  // <= TILE / 32 + 1
     if ((int)threadIdx.x < npg) lds_pages[threadIdx.x] = pt[pg0 + threadIdx.x];
     __syncthreads();
+    const bool store_u = c.u_pages != nullptr && a.utility != nullptr;
     for (int kk = threadIdx.x; kk < n; kk += NT) {
         const int j = dst0 + kk;
         const int page = lds_pages[(j >> c.page_shift) - pg0];
-        c.pos_pages[(int64_t)page * P + (j & (P - 1))] = pos_base + (lds_rows[kk] - r0);
+        const int64_t slot = (int64_t)page * P + (j & (P - 1));
+        c.pos_pages[slot] = pos_base + (lds_rows[kk] - r0);
+        if (store_u) c.u_pages[slot] = a.utility[(int64_t)lds_rows[kk] * c.n_kv + g];
     }
     auto kdst = [&](int kk) -> char * {
         const int j = dst0 + kk;
@@ -312,6 +322,8 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
     const int hd = c.head_dim;
     const int cpr = hd / EPC;     // chunks per row (<= 32)
     const bool kept = global && a.keep[(int64_t)lo * c.n_kv + g] != 0;
+    const bool store_u = global && c.u_pages != nullptr && a.utility != nullptr;
+    const float u = store_u ? a.utility[(int64_t)lo * c.n_kv + g] : 0.f;
     const int64_t src = (int64_t)lo * a.ld_kv * ES + (int64_t)g * hd * ES + lane * 16;
     piece_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (lane < cpr) {
@@ -360,6 +372,7 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
     }
     if (lane == 0) {
         c.pos_pages[(int64_t)page * P + j] = pos;
+        if (store_u) c.u_pages[(int64_t)page * P + j] = u;
         c.lengths[bg] = old_len + 1;
     }
 }
@@ -460,6 +473,166 @@ __global__ void __launch_bounds__(NT) compact_scatter_kernel(CompactArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Re-threshold: src list of (b, g) -> dst list of the entries with u >= tau.
+// Entry e of a list is slot e % P of page page_table[b][g][e / P]; tiles are
+// 256 consecutive entries (one per thread).
+
+// Entries of the (b, g) list, clipped to what its page table can address.
+__device__ inline int list_len(const CacheView &c, int64_t bg) {
+    return min(max(c.lengths[bg], 0), c.max_pages * c.page_size);
+}
+
+// Stored utility of entry e of (b, g) passes tau (NaN fails).  Returns the
+// flat slot (page * P + e % P) through *slot.
+__device__ inline bool passes(const RethreshArgs &a, int64_t bg, int e, int len, int *slot) {
+    const CacheView &c = a.src;
+    if (e >= len) return false;
+    const int page = c.page_table[bg * c.max_pages + (e >> c.page_shift)];
+    *slot = page * c.page_size + (e & (c.page_size - 1));
+    return c.u_pages[*slot] >= a.tau;
+}
+
+__global__ void __launch_bounds__(NT) rethresh_count_kernel(RethreshArgs a) {
+    __shared__ int lds_waves[NT / 64];
+    const int j = blockIdx.x;
+    const int64_t bg = blockIdx.y;
+    const int len = list_len(a.src, bg);
+    if (j * TILE >= len) return;
+    int slot = 0;
+    const bool flag = passes(a, bg, j * TILE + (int)threadIdx.x, len, &slot);
+    int total;
+    (void)block_rank(flag, lds_waves, &total);
+    if (threadIdx.x == 0) a.ws[bg * a.max_tiles + j] = total;
+}
+
+__global__ void __launch_bounds__(NT) rethresh_plan_kernel(RethreshArgs a) {
+    __shared__ int lds_scan[NT];
+    __shared__ int lds_misc[4];
+    const int64_t bg = blockIdx.x;
+    const CacheView &d = a.dst;
+    const int b = (int)(bg / d.n_kv);
+    const int g = (int)(bg - (int64_t)b * d.n_kv);
+    int32_t *cnt = a.ws + bg * a.max_tiles;
+    const int n_tiles = (list_len(a.src, bg) + TILE - 1) / TILE;
+    int carry = 0;
+    for (int base = 0; base < n_tiles; base += NT) {
+        const int j = base + threadIdx.x;
+        const int x = j < n_tiles ? cnt[j] : 0;
+        lds_scan[threadIdx.x] = x;
+        __syncthreads();
+        for (int off = 1; off < NT; off <<= 1) {
+            const int y = threadIdx.x >= off ? lds_scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            lds_scan[threadIdx.x] += y;
+            __syncthreads();
+        }
+        if (j < n_tiles) cnt[j] = carry + lds_scan[threadIdx.x] - x;  // exclusive offset
+        carry += lds_scan[NT - 1];
+        __syncthreads();
+    }
+    const int new_len = grow_head(d, b, g, 0, carry, lds_misc);
+    if (threadIdx.x == 0) {
+        d.lengths[bg] = new_len;
+        a.ws[(int64_t)d.batch * d.n_kv * a.max_tiles + bg] = new_len;
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
+    __shared__ int lds_src[TILE];   // flat source slot of each kept entry, in order
+    __shared__ int lds_waves[NT / 64];
+    __shared__ int lds_pages[16];
+    const int j = blockIdx.x;
+    const int64_t bg = blockIdx.y;
+    const CacheView &s = a.src;
+    const CacheView &d = a.dst;
+    const int len = list_len(s, bg);
+    if (j * TILE >= len) return;
+    int slot = 0;
+    const bool flag = passes(a, bg, j * TILE + (int)threadIdx.x, len, &slot);
+    int total;
+    const int rank = block_rank(flag, lds_waves, &total);
+    if (flag) lds_src[rank] = slot;
+    const int dst0 = a.ws[bg * a.max_tiles + j];
+    const int new_len = a.ws[(int64_t)d.batch * d.n_kv * a.max_tiles + bg];
+    const int n = max(0, min(total, new_len - dst0));
+    if (n == 0) return;  // uniform: no barrier below is skipped by part of the block
+    const int P = d.page_size;
+    const int pg0 = dst0 >> d.page_shift;
+    const int npg = ((dst0 + n - 1) >> d.page_shift) - pg0 + 1;  // <= TILE / 32 + 1
+    if ((int)threadIdx.x < npg) lds_pages[threadIdx.x] = d.page_table[bg * d.max_pages + pg0 + threadIdx.x];
+    __syncthreads();
+    auto dslot = [&](int kk) -> int64_t {
+        const int e = dst0 + kk;
+        return (int64_t)lds_pages[(e >> d.page_shift) - pg0] * P + (e & (P - 1));
+    };
+    for (int kk = threadIdx.x; kk < n; kk += NT) {
+        const int64_t ds = dslot(kk);
+        const int ss = lds_src[kk];
+        d.pos_pages[ds] = s.pos_pages[ss];
+        if (d.u_pages) d.u_pages[ds] = s.u_pages[ss];
+    }
+    constexpr int ES = sizeof(T);
+    constexpr int EPC = 16 / ES;
+    constexpr int KB = 8;
+    const int hd = d.head_dim;
+    const int cpr = hd / EPC;
+    // keys: 16-byte pieces, a row's pieces on neighbouring lanes; a batch of
+    // loads is issued before its stores
+    const int npk = n * cpr;
+    for (int base = 0; base < npk; base += NT * KB) {
+        piece_t kv[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int idx = base + u * NT + (int)threadIdx.x;
+            if (idx < npk) {
+                const int kk = idx / cpr;
+                const int ch = idx - kk * cpr;
+                kv[u] = *(const piece_t *)(s.k_pages + (int64_t)lds_src[kk] * hd * ES + ch * 16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int idx = base + u * NT + (int)threadIdx.x;
+            if (idx < npk) {
+                const int kk = idx / cpr;
+                const int ch = idx - kk * cpr;
+                *(piece_t *)(d.k_pages + dslot(kk) * hd * ES + ch * 16) = kv[u];
+            }
+        }
+    }
+    // values, transposed in both caches: element e of entry kk sits at
+    // [page][e][slot]; consecutive lanes take consecutive entries
+    constexpr int VB = 16;
+    const int npv = n * hd;
+    for (int base = 0; base < npv; base += NT * VB) {
+        T vv[VB];
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+            const int idx = base + u * NT + (int)threadIdx.x;
+            if (idx < npv) {
+                const int e = idx / n;
+                const int kk = idx - e * n;
+                const int ss = lds_src[kk];
+                const int sp = ss >> s.page_shift;
+                vv[u] = ((const T *)s.v_pages)[((int64_t)sp * hd + e) * P + (ss & (P - 1))];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+            const int idx = base + u * NT + (int)threadIdx.x;
+            if (idx < npv) {
+                const int e = idx / n;
+                const int kk = idx - e * n;
+                const int ed = dst0 + kk;
+                const int dp = lds_pages[(ed >> d.page_shift) - pg0];
+                ((T *)d.v_pages)[((int64_t)dp * hd + e) * P + (ed & (P - 1))] = vv[u];
+            }
+        }
+    }
+}
+
 __global__ void cache_reset_kernel(CacheView c) {
     const int n = c.batch * c.n_kv;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
@@ -510,6 +683,31 @@ hipError_t launch_compact(const CompactArgs &a0, hipStream_t s) {
         hipLaunchKernelGGL(compact_scatter_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
     else
         hipLaunchKernelGGL(compact_scatter_kernel<float>, grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+size_t rethresh_ws_bytes(const spkv_cache *src) {
+    const int64_t max_entries = (int64_t)src->max_pages_per_head * src->page_size;
+    const int64_t max_tiles = (max_entries + TILE - 1) / TILE;
+    return (size_t)((int64_t)src->batch * src->n_kv * (max_tiles + 1)) * sizeof(int32_t);
+}
+
+hipError_t launch_rethresh(const RethreshArgs &a0, hipStream_t s) {
+    RethreshArgs a = a0;
+    const int64_t max_entries = (int64_t)a.src.max_pages * a.src.page_size;
+    a.max_tiles = (int32_t)((max_entries + TILE - 1) / TILE);
+    const int BG = a.src.batch * a.src.n_kv;
+    if (a.max_tiles == 0) {
+        // nothing can be stored: every dst list is empty
+        hipLaunchKernelGGL(rethresh_plan_kernel, dim3(BG), dim3(NT), 0, s, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(rethresh_count_kernel, dim3(a.max_tiles, BG), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(rethresh_plan_kernel, dim3(BG), dim3(NT), 0, s, a);
+    if (a.src.dtype == SPKV_BF16)
+        hipLaunchKernelGGL(rethresh_scatter_kernel<uint16_t>, dim3(a.max_tiles, BG), dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL(rethresh_scatter_kernel<float>, dim3(a.max_tiles, BG), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -271,9 +271,10 @@ __device__ inline void compute_step(WaveState<HD> &st, const bf16x8 *qlds,
 // Fused step: append the new row of every (b, g) whose keep bit is set
 // (SP-KV section 2.1, deployment paragraph: only kept pairs enter the
 // persistent cache), as spkv_compact_append does for one row per sequence.
-// 16 threads per (b, g); the new lengths go to new_len (LDS).
+// 16 threads per (b, g); the new lengths go to new_len (LDS).  u (LDS) holds
+// the utilities, stored with the entries when the cache keeps them.
 template <int HD>
-__device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, int *new_len) {
+__device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, const float *u, int *new_len) {
     const CacheView &c = a.c;
     const int BG = c.batch * c.n_kv;
     const int P = c.page_size;
@@ -321,7 +322,10 @@ __device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, int *n
                         *(bf16x8 *)((__bf16 *)c.k_pages + ((int64_t)page * P + j) * HD + 8 * sub) =
                             *(const bf16x8 *)(kn + 8 * sub);
                     for (int e = sub; e < HD; e += TPP) ((__bf16 *)c.v_pages)[((int64_t)page * HD + e) * P + j] = vn[e];
-                    if (sub == 0) c.pos_pages[(int64_t)page * P + j] = tb;
+                    if (sub == 0) {
+                        c.pos_pages[(int64_t)page * P + j] = tb;
+                        if (c.u_pages) c.u_pages[(int64_t)page * P + j] = u[bg];
+                    }
                     newlen = old + 1;
                 }
             }
@@ -348,9 +352,12 @@ __device__ void fused_finisher(const DecodeArgs &a, const float *gshare, int *ga
         if (threadIdx.x == 0) atomicOr(c.status, SPKV_STATUS_STEP_TIMEOUT);
         return;
     }
-    gate_tile_finish(a.gate, gshare, lds_act, lds_keep);
+    // the utilities go after the staged activations (at most FUSED_ROWS
+    // rows of d_hidden <= 256 floats)
+    float *lds_u = lds_act + FUSED_ROWS * 256;
+    gate_tile_finish(a.gate, gshare, lds_act, lds_keep, lds_u);
     __syncthreads();
-    append_new_rows<HD>(a, lds_keep, lds_new_len);
+    append_new_rows<HD>(a, lds_keep, lds_u, lds_new_len);
     __syncthreads();
     if (threadIdx.x == 0) {
         reset_dev(gate_cnt);
@@ -413,6 +420,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         // every workgroup has read the old ones for its plan (the appended
         // entries, at position t, are outside this step's global set).
         if ((int)blockIdx.x == n_att) {
+            // lds_o holds the staged activations and the utilities
+            static_assert(2 * NW * 16 * HD >= FUSED_ROWS * 256 + FUSED_ROWS * 16, "finisher LDS");
             fused_finisher<HD>(a, gshare, gate_cnt, plan_cnt, &lds_o[0][0][0][0], lds_keep, lds_len, lds_flag);
             return;
         }

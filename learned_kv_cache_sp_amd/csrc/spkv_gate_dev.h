@@ -190,8 +190,10 @@ __device__ inline void gate_tile_share(const GateArgs &a, int item, float *part,
 // a_j = ReLU(sum over parts in order + b1_j) staged in act (LDS, n_rows x
 // d_hidden floats), then logit (r, k) = sum over j in order of W2[k][j] a_j,
 // + b2, u = sigmoid(logit), keep = u >= tau (NaN -> 0).  utility / keep in
-// a may be NULL; keep_lds (may be NULL) receives the bits too.
-__device__ inline void gate_tile_finish(const GateArgs &a, const float *part, float *act, uint8_t *keep_lds) {
+// a may be NULL; keep_lds and u_lds (may be NULL) receive the bits and the
+// utilities too.
+__device__ inline void gate_tile_finish(const GateArgs &a, const float *part, float *act, uint8_t *keep_lds,
+                                        float *u_lds = nullptr) {
     const int kparts = gate_tile_kparts(a.d_model);
     const int n = (int)a.n_rows;
     const int hg = a.d_hidden;
@@ -218,6 +220,7 @@ __device__ inline void gate_tile_finish(const GateArgs &a, const float *part, fl
         if (a.utility) a.utility[o] = u;
         if (a.keep) a.keep[o] = z;
         if (keep_lds) keep_lds[o] = z;
+        if (u_lds) u_lds[o] = u;
     }
 }
 

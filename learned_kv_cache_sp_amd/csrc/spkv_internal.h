@@ -22,6 +22,7 @@ struct CacheView {
     int32_t *status;
     char *ring_k;
     char *ring_v;
+    float *u_pages;      // utility of each entry, or NULL
 };
 
 inline CacheView make_view(const spkv_cache *c) {
@@ -46,6 +47,7 @@ inline CacheView make_view(const spkv_cache *c) {
     v.status = c->status;
     v.ring_k = (char *)c->ring_k;
     v.ring_v = (char *)c->ring_v;
+    v.u_pages = c->u_pages;
     return v;
 }
 
@@ -72,6 +74,7 @@ hipError_t launch_gate(const GateArgs &a, hipStream_t s);
 struct CompactArgs {
     CacheView c;
     const uint8_t *keep;
+    const float *utility;  // [n_rows, n_kv]; stored into c.u_pages when both are set
     const char *k;
     const char *v;
     int64_t ld_kv;  // elements
@@ -129,5 +132,15 @@ size_t prefill_ws_bytes(const spkv_cache *c, int n_q, int n_rows);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 hipError_t launch_cache_reset(const CacheView &c, hipStream_t s);
+
+// ---- re-threshold (spkv_cache_rethreshold) ---------------------------------
+struct RethreshArgs {
+    CacheView src, dst;
+    float tau;
+    int32_t *ws;        // tile counts/offsets [B*Hkv*max_tiles] + new lengths [B*Hkv]
+    int32_t max_tiles;  // tiles of 256 entries in the longest possible list
+};
+size_t rethresh_ws_bytes(const spkv_cache *src);
+hipError_t launch_rethresh(const RethreshArgs &a, hipStream_t s);
 
 }  // namespace spkv

@@ -121,7 +121,7 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 STREAM_W1, STREAM_W2, STREAM_H, STREAM_Q, STREAM_K, STREAM_V, STREAM_CAL, STREAM_RESAMPLE, \
-    STREAM_MASK, STREAM_CTX = range(10)
+    STREAM_MASK, STREAM_CTX, STREAM_UTIL = range(11)
 
 
 def layer_weights(wl: Workload, seed: int | None = None) -> dict:
@@ -160,6 +160,19 @@ def bernoulli_mask(n: int, rates, seed: int, *stream: int) -> np.ndarray:
     """Keep bits [n, len(rates)] drawn independently with the given rates."""
     r = rng(seed, STREAM_MASK, *stream).random((n, len(rates)))
     return (r < np.asarray(rates)[None, :]).astype(np.uint8)
+
+
+def utilities(n: int, n_kv: int, seed: int, *stream: int) -> np.ndarray:
+    """Stored utilities [n, n_kv] float32: uniform in [0, 1), with exact ties
+    at 0.5 and 0.75 on about 1/8 and 1/16 of the entries and NaN on about
+    1/64 (a utility the threshold comparison must drop)."""
+    r = rng(seed, STREAM_UTIL, *stream)
+    u = r.random((n, n_kv)).astype(np.float32)
+    pick = r.random((n, n_kv))
+    u[pick < 1 / 8] = np.float32(0.5)
+    u[(pick >= 1 / 8) & (pick < 3 / 16)] = np.float32(0.75)
+    u[(pick >= 3 / 16) & (pick < 3 / 16 + 1 / 64)] = np.float32(np.nan)
+    return u
 
 
 def ragged_contexts(wl: Workload, seed: int | None = None) -> np.ndarray:

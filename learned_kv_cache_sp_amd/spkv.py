@@ -64,13 +64,14 @@ class CacheDesc(ctypes.Structure):
         ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p), ("pos_pages", ctypes.c_void_p),
         ("page_table", ctypes.c_void_p), ("lengths", ctypes.c_void_p), ("pool_next", ctypes.c_void_p),
         ("status", ctypes.c_void_p), ("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
+        ("u_pages", ctypes.c_void_p),
     ]
 
 
 EXPORTS = [
     "spkv_gate", "spkv_gate_ws_bytes", "spkv_compact_append", "spkv_compact_ws_bytes",
     "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_decode_step", "spkv_decode_step_ws_bytes",
-    "spkv_prefill_attn", "spkv_prefill_ws_bytes",
+    "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
     "spkv_last_error", "spkv_version",
 ]
@@ -91,7 +92,7 @@ def load_library(path: str = LIB_PATH):
     sig = {
         "spkv_gate": ([G, vp, i64, i64, f32, vp, vp, vp, sz, vp], ctypes.c_int),
         "spkv_gate_ws_bytes": ([G, i64], sz),
-        "spkv_compact_append": ([C, vp, vp, vp, i64, vp, vp, i32, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+        "spkv_compact_append": ([C, vp, vp, vp, vp, i64, vp, vp, i32, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "spkv_compact_ws_bytes": ([C, i32, i32], sz),
         "spkv_decode_attn": ([C, i32, vp, i64, vp, f32, vp, vp, vp, sz, vp], ctypes.c_int),
         "spkv_decode_ws_bytes": ([C, i32], sz),
@@ -101,6 +102,8 @@ def load_library(path: str = LIB_PATH):
         "spkv_prefill_attn": ([C, i32, i32, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp, vp, sz, vp],
                               ctypes.c_int),
         "spkv_prefill_ws_bytes": ([C, i32, i32], sz),
+        "spkv_cache_rethreshold": ([C, C, f32, vp, sz, vp], ctypes.c_int),
+        "spkv_rethreshold_ws_bytes": ([C], sz),
         "spkv_cache_bytes": ([C, vp], sz),
         "spkv_cache_reset": ([C, vp], ctypes.c_int),
         "spkv_cache_check": ([C, vp, vp], ctypes.c_int),
@@ -200,7 +203,8 @@ class Cache:
     """Device buffers of one layer's SP-KV cache (see include/spkv.h, spkv_cache)."""
 
     def __init__(self, batch: int, n_kv: int, head_dim: int, window: int, page_size: int,
-                 n_pages: int, max_pages_per_head: int, dtype=torch.bfloat16, device="cuda"):
+                 n_pages: int, max_pages_per_head: int, dtype=torch.bfloat16, device="cuda",
+                 utilities: bool = False):
         dt = dtype
         self.batch, self.n_kv, self.head_dim, self.window = batch, n_kv, head_dim, window
         self.page_size, self.n_pages, self.max_pages_per_head = page_size, n_pages, max_pages_per_head
@@ -215,6 +219,8 @@ class Cache:
         self.status = z((1,), torch.int32)
         self.ring_k = z((batch, n_kv, window, head_dim))
         self.ring_v = z((batch, n_kv, head_dim, window))
+        # utility of each entry (kept for spkv_cache_rethreshold)
+        self.u_pages = z((n_pages, page_size), torch.float32) if utilities else None
         self._desc = None
 
     @staticmethod
@@ -228,7 +234,7 @@ class Cache:
             d.page_size, d.n_pages, d.max_pages_per_head = self.page_size, self.n_pages, self.max_pages_per_head
             d.dtype = _dtype_code(self.dtype)
             for name in ("k_pages", "v_pages", "pos_pages", "page_table", "lengths", "pool_next",
-                         "status", "ring_k", "ring_v"):
+                         "status", "ring_k", "ring_v", "u_pages"):
                 setattr(d, name, _ptr(getattr(self, name)))
             self._desc = d
         return self._desc
@@ -248,13 +254,29 @@ class Cache:
         pos = self.pos_pages[pages].reshape(npg * P)[:n]
         return k, v, pos
 
+    def read_head_u(self, b: int, g: int):
+        """Stored utilities of the entries of (b, g) in logical order (f32 [n])."""
+        if self.u_pages is None:
+            raise ValueError("this cache does not store utilities")
+        n = int(self.lengths[b, g].item())
+        P = self.page_size
+        npg = (n + P - 1) // P
+        pages = self.page_table[b, g, :npg].long()
+        return self.u_pages[pages].reshape(npg * P)[:n]
+
+    def share_ring(self, other: "Cache"):
+        """Point this cache's ring at other's (for a cache rebuilt from other)."""
+        self.ring_k, self.ring_v = other.ring_k, other.ring_v
+        self._desc = None
+
     def read_ring(self, b: int, g: int):
         """Ring of (b, g): K [w, hd], V [w, hd] indexed by slot = position % w."""
         return self.ring_k[b, g], self.ring_v[b, g].transpose(0, 1)
 
     def snapshot(self) -> dict:
-        return {n: getattr(self, n).clone() for n in ("k_pages", "v_pages", "pos_pages", "page_table",
-                                                      "lengths", "pool_next", "status", "ring_k", "ring_v")}
+        names = ("k_pages", "v_pages", "pos_pages", "page_table", "lengths", "pool_next", "status",
+                 "ring_k", "ring_v", "u_pages")
+        return {n: getattr(self, n).clone() for n in names if getattr(self, n) is not None}
 
     def restore(self, snap: dict):
         for n, t in snap.items():
@@ -305,10 +327,12 @@ def spkv_compact_ws_bytes(cache: Cache, n_rows: int, max_rows_per_seq: int) -> i
 
 def spkv_compact_append(cache: Cache, keep, k: torch.Tensor, v: torch.Tensor, row_offsets: torch.Tensor,
                         pos0: torch.Tensor, max_rows_per_seq: int, flags: int, append_offsets=None,
-                        ws=None, stream=None):
+                        ws=None, stream=None, utility=None):
     """Append rows [n_rows, n_kv, hd] (CSR by row_offsets) to the cache; see spkv.h."""
     lib = load_library()
-    _need_gpu(keep, k, v, row_offsets, pos0, append_offsets)
+    _need_gpu(keep, k, v, row_offsets, pos0, append_offsets, utility)
+    if utility is not None and utility.dtype != torch.float32:
+        raise ValueError("utility must be float32")
     if k.dtype != cache.dtype or v.dtype != cache.dtype:
         raise ValueError("k / v dtype differs from the cache")
     if row_offsets.dtype != torch.int32 or pos0.dtype != torch.int32:
@@ -323,7 +347,7 @@ def spkv_compact_append(cache: Cache, keep, k: torch.Tensor, v: torch.Tensor, ro
     if ws is None and need:
         ws = workspace(need, k.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.spkv_compact_append(ctypes.byref(cache.desc()), _ptr(keep), _ptr(k), _ptr(v), ld,
+    _check(lib.spkv_compact_append(ctypes.byref(cache.desc()), _ptr(keep), _ptr(utility), _ptr(k), _ptr(v), ld,
                                    _ptr(row_offsets), _ptr(pos0), n, int(max_rows_per_seq), int(flags),
                                    _ptr(append_offsets), _ptr(ws), ws_bytes, _stream(stream)))
 
@@ -432,6 +456,21 @@ def spkv_prefill_attn(cache: Cache, b: int, q: torch.Tensor, k: torch.Tensor, v:
                                  _ptr(v), ld_kv, int(pos0), n, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                                  ws_bytes, _stream(stream)))
     return out, lse
+
+
+def spkv_rethreshold_ws_bytes(src: Cache) -> int:
+    return int(load_library().spkv_rethreshold_ws_bytes(ctypes.byref(src.desc())))
+
+
+def spkv_cache_rethreshold(src: Cache, dst: Cache, tau: float, ws=None, stream=None):
+    """Rebuild dst from the entries of src whose stored utility is >= tau; see spkv.h."""
+    lib = load_library()
+    need = spkv_rethreshold_ws_bytes(src)
+    if ws is None and need:
+        ws = workspace(need, src.k_pages.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.spkv_cache_rethreshold(ctypes.byref(src.desc()), ctypes.byref(dst.desc()), float(tau),
+                                      _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def spkv_cache_reset(cache: Cache, stream=None):

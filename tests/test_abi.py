@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_pure_host_helpers(lib):
-    assert lib.spkv_version() == 1
+    assert lib.spkv_version() == 2
     assert lib.spkv_status_str(0) == b"ok"
     assert b"capacity" in lib.spkv_status_str(-4)
     c = spkv.CacheDesc()
