@@ -70,6 +70,7 @@ KERNEL_SOURCES = {
     "gate_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_gate.hip",
     "compact_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "compact_small_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
+    "rethresh_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
 }
 CALIBRATION_BYTES = 1 << 30  # the plain copy: 1 GiB read + 1 GiB written
 
@@ -80,7 +81,7 @@ def parse():
     p.add_argument("--steps", type=int, default=None, help="timed steps (decode 256, prefill 4)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
     p.add_argument("--workload", default="decode_32k",
-                   choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k"])
+                   choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k"])
     p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
     p.add_argument("--step-mode", choices=("auto", "fused", "separate"), default="auto",
@@ -686,6 +687,115 @@ def bench_prefill(args, wl):
 # the oracle on the host cores
 # ----------------------------------------------------------------------------
 
+def bench_rethreshold(args, wl):
+    """Rebuild of the decode_32k cache (8 sequences x 32768 tokens, 20 % of the
+    pairs kept at tau) at a higher threshold that keeps about half of its
+    entries (SP-KV section 2.1, deployment paragraph: periodic rebuild;
+    section 3.3: threshold moved after training).  One step = reset of the
+    destination cache + spkv_cache_rethreshold."""
+    import torch
+    from learned_kv_cache_sp_amd import inputs, spkv
+    dev = "cuda"
+    B, T, nkv, hd, w, P, d = wl.batch, wl.context, wl.n_kv, wl.head_dim, wl.window, 64, wl.d_model
+    G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
+    gw = gate_weights(wl, torch, inputs, spkv, dev)
+    n = B * T
+    max_pages = T // P + 2
+    n_pages = int(B * nkv * (T * max(wl.keep) / P * 1.25 + 8))
+    src = spkv.Cache(B, nkv, hd, w, P, n_pages, max_pages, torch.bfloat16, utilities=True)
+    dst = spkv.Cache(B, nkv, hd, w, P, n_pages, max_pages, torch.bfloat16, utilities=True)
+    dst.share_ring(src)
+    z = torch.empty((n, nkv), dtype=torch.uint8, device=dev)
+    u = torch.empty((n, nkv), dtype=torch.float32, device=dev)
+    CH = 65536
+    for r0 in range(0, n, CH):
+        Hp = inputs.device_normal((min(CH, n - r0), d), wl.seed, 1000 + r0 // CH, torch.bfloat16)
+        spkv.spkv_gate(gw, Hp, wl.tau, utility=u[r0:r0 + Hp.shape[0]], keep=z[r0:r0 + Hp.shape[0]])
+        del Hp
+    K = inputs.device_normal((n, nkv, hd), wl.seed, inputs.STREAM_K, torch.bfloat16)
+    V = inputs.device_normal((n, nkv, hd), wl.seed, inputs.STREAM_V, torch.bfloat16)
+    ro = torch.arange(0, n + 1, T, dtype=torch.int32, device=dev)
+    spkv.spkv_compact_append(src, z, K, V, ro, torch.zeros(B, dtype=torch.int32, device=dev), T, G_ | W_,
+                             utility=u)
+    torch.cuda.synchronize()
+    spkv.spkv_cache_check(src)
+    del K, V
+    kept_u = u[z.bool()]
+    tau2 = float(torch.quantile(kept_u[:: max(1, kept_u.numel() // (1 << 24))].double(), 0.5))
+    ws = spkv.workspace(spkv.spkv_rethreshold_ws_bytes(src))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        spkv.spkv_cache_reset(dst)
+        if ev is not None:
+            ev[0].record(stream)
+        spkv.spkv_cache_rethreshold(src, dst, tau2, ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    spkv.spkv_cache_check(dst)
+    ms = e0.elapsed_time(e1) / args.steps
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    L_src = int(src.lengths.sum().item())
+    L_dst = int(dst.lengths.sum().item())
+    # algorithmic bytes of one rebuild: every stored utility read once; each
+    # surviving entry's key and value rows (2 * hd bf16), position and
+    # utility read and written
+    ent = 2 * hd * 2
+    alg = 4 * L_src + L_dst * ((ent + 4) + (ent + 8))
+    call_s = float(np.mean(call_ms)) * 1e-3
+    achieved = alg / call_s / 1e9
+    return {
+        "metric": "cache entries re-thresholded per second", "value": L_src / (ms * 1e-3),
+        "unit": "entries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rethreshold_32k", "batch": B, "context": T, "n_kv": nkv, "head_dim": hd,
+                   "page_size": P, "tau": wl.tau, "tau2": tau2, "entries_src": L_src, "entries_dst": L_dst,
+                   "step": "spkv_cache_reset(dst) + spkv_cache_rethreshold(src, dst, tau2)"},
+        "roofline": {"bound": "hbm", "kernel": "spkv_cache_rethreshold (count + plan + scatter kernels)",
+                     "achieved": achieved, "peak": 8000.0, "unit": "GB/s", "frac": achieved / 8000.0,
+                     "traffic": stored_traffic("rethresh_scatter_kernel", "rethreshold_32k"),
+                     "algorithmic_bytes_per_launch": alg, "avg_call_us": call_s * 1e6,
+                     "call_us": _stats_us(call_ms)},
+        "wall_s": wall,
+    }
+
+
+def cpu_baseline_rethreshold(wl, budget_s: float) -> dict:
+    """The oracle's re-threshold over a bounded sample of lists shaped like the
+    decode_32k cache (about 6.5k stored utilities per list, from the seeded
+    generator, kept at tau), timed alone."""
+    import oracle
+    from learned_kv_cache_sp_amd import inputs
+    oracle.build(force=False)
+    n_rows = int(wl.context * max(wl.keep) / 0.5)
+    pool = [u[u >= np.float32(wl.tau)] for u in (inputs.utilities(n_rows, 1, wl.seed, i)[:, 0] for i in range(16))]
+    done = lists = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        u = pool[lists % len(pool)]
+        oracle.rethreshold(u, 0.75)
+        done += u.size
+        lists += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "entries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{lists} lists of {pool[0].size}-{max(p.size for p in pool)} stored utilities "
+                      f"({done} entries), oracle.rethreshold only, {el:.1f} s"}
+
+
 def _threads():
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -808,8 +918,12 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    wl = inputs.WORKLOADS[args.workload]
-    res = bench_prefill(args, wl) if wl.chunk else bench_decode(args, wl)
+    if args.workload == "rethreshold_32k":
+        wl = inputs.WORKLOADS["decode_32k"]
+        res = bench_rethreshold(args, wl)
+    else:
+        wl = inputs.WORKLOADS[args.workload]
+        res = bench_prefill(args, wl) if wl.chunk else bench_decode(args, wl)
 
     if args.copy_calibration:
         a = torch.zeros(CALIBRATION_BYTES // 2, dtype=torch.int16, device="cuda")
@@ -822,7 +936,10 @@ def main():
         res["hbm_ceiling"] = hbm_ceiling(torch)
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, args.cpu_budget)
+        if args.workload == "rethreshold_32k":
+            res["cpu_baseline"] = cpu_baseline_rethreshold(wl, args.cpu_budget)
+        else:
+            res["cpu_baseline"] = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, args.cpu_budget)
     print(json.dumps(res))
 
 

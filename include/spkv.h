@@ -327,6 +327,7 @@ size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads,
  *         src's, or copy it, before attending over dst.  No buffer dst
  *         writes may overlap a buffer of src.
  *   tau   the new threshold (not NaN).
+ *   Supported: src->max_pages_per_head * page_size <= 65535 * 256.
  *   ws    at least spkv_rethreshold_ws_bytes(src) bytes.
  *   Launches three kernels: kept counts per tile of 256 entries, a scan and
  *   page allocation per (b, g), the copies per tile.

@@ -434,6 +434,8 @@ int spkv_cache_rethreshold(const spkv_cache *src, const spkv_cache *dst, float t
         return fail(SPKV_E_INVALID, "src and dst differ in batch, n_kv, head_dim, page_size or dtype");
     if (!src->u_pages) return fail(SPKV_E_INVALID, "src->u_pages is NULL (no stored utilities)");
     if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
+    if (((int64_t)src->max_pages_per_head * src->page_size + 255) / 256 > 65535)
+        return fail(SPKV_E_UNSUPPORTED, "src lists may exceed 65535 x 256 entries (max_pages_per_head * page_size)");
     // dst's writes must not reach anything src's lists are read from
     size_t ss[7], ds[7];
     spkv_cache_bytes(src, ss);

@@ -493,10 +493,12 @@ __device__ inline bool passes(const RethreshArgs &a, int64_t bg, int e, int len,
     return c.u_pages[*slot] >= a.tau;
 }
 
+// Grids of the count and scatter kernels run (b, g) fastest: the tiles that
+// exist (short lists end early) are dispatched first, the empty ones last.
 __global__ void __launch_bounds__(NT) rethresh_count_kernel(RethreshArgs a) {
     __shared__ int lds_waves[NT / 64];
-    const int j = blockIdx.x;
-    const int64_t bg = blockIdx.y;
+    const int j = blockIdx.y;
+    const int64_t bg = blockIdx.x;
     const int len = list_len(a.src, bg);
     if (j * TILE >= len) return;
     int slot = 0;
@@ -538,96 +540,180 @@ __global__ void __launch_bounds__(NT) rethresh_plan_kernel(RethreshArgs a) {
     }
 }
 
+// Copies of one tile.  Values are transposed in both caches ([page][hd][slot]):
+// the tile's value columns are staged in LDS with 16-byte loads (every column
+// of the tile: a cache line holds many slots, so the dropped entries' bytes
+// come along anyway), then each value row of the destination is written in
+// 16-byte pieces; only the pieces at the two ends of the tile's destination
+// range, shared with the neighbouring tiles, are written element by element.
+// Each thread takes its own entry's position, utility and (bf16) key row as
+// soon as its keep decision is known and stores them once its rank is known,
+// so that a tile costs few dependent trips to memory.  RT_SPLIT workgroups
+// can share a tile (blockIdx.z), each with 1 / RT_SPLIT of the value rows and
+// of every key row (less LDS per workgroup, more of them resident); on the
+// decode_32k cache one workgroup per tile measured fastest (89 us against
+// 134 us with two).
+constexpr int RT_SPLIT = 1;
+
 template <typename T>
 __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
-    __shared__ int lds_src[TILE];   // flat source slot of each kept entry, in order
+    constexpr int ES = sizeof(T);
+    constexpr int EPC = 16 / ES;          // elements per 16-byte piece
+    constexpr int MAXHD = 128;
+    constexpr bool OWN_KEY = ES == 2;     // bf16: key row (its share) held in registers
+    __shared__ int lds_src[TILE];         // flat source slot of each kept entry, in order
+    __shared__ int lds_loc[TILE];         // its index inside the tile
     __shared__ int lds_waves[NT / 64];
-    __shared__ int lds_pages[16];
-    const int j = blockIdx.x;
-    const int64_t bg = blockIdx.y;
+    __shared__ int lds_pages[16];         // destination pages of the tile's range
+    __shared__ int lds_spages[16];        // source pages of the tile
+    __shared__ __attribute__((aligned(16))) T lds_v[MAXHD / RT_SPLIT][TILE];  // this half's value rows
+    const int j = blockIdx.y;
+    const int64_t bg = blockIdx.x;
+    const int half = blockIdx.z;
     const CacheView &s = a.src;
     const CacheView &d = a.dst;
     const int len = list_len(s, bg);
-    if (j * TILE >= len) return;
-    int slot = 0;
-    const bool flag = passes(a, bg, j * TILE + (int)threadIdx.x, len, &slot);
-    int total;
-    const int rank = block_rank(flag, lds_waves, &total);
-    if (flag) lds_src[rank] = slot;
     const int dst0 = a.ws[bg * a.max_tiles + j];
     const int new_len = a.ws[(int64_t)d.batch * d.n_kv * a.max_tiles + bg];
+    const int e0 = j * TILE;
+    if (e0 >= len) return;
+    const int hd = d.head_dim;            // 64 or 128
+    const int hh = hd / RT_SPLIT;         // value rows of this half: [half * hh, half * hh + hh)
+    const int P = d.page_size;
+    const int cnt = min(TILE, len - e0);
+    const int sp0 = e0 >> s.page_shift;
+    const int nsp = ((e0 + cnt - 1) >> s.page_shift) - sp0 + 1;  // <= TILE / 32
+    // the destination range is at most [dst0, dst0 + min(cnt, new_len - dst0))
+    const int nmax = max(0, min(cnt, new_len - dst0));
+    const int pg0 = dst0 >> d.page_shift;
+    const int npg = nmax > 0 ? ((dst0 + nmax - 1) >> d.page_shift) - pg0 + 1 : 0;  // <= TILE / 32 + 1
+    if ((int)threadIdx.x < nsp) lds_spages[threadIdx.x] = s.page_table[bg * s.max_pages + sp0 + threadIdx.x];
+    if ((int)threadIdx.x >= 64 && (int)threadIdx.x < 64 + npg)
+        lds_pages[threadIdx.x - 64] = d.page_table[bg * d.max_pages + pg0 + threadIdx.x - 64];
+    __syncthreads();
+    const int me = e0 + (int)threadIdx.x;
+    const bool mine = me < len;
+    const int slot = mine ? lds_spages[(me >> s.page_shift) - sp0] * P + (me & (P - 1)) : 0;
+    const float u = mine ? s.u_pages[slot] : 0.f;
+    const int pos = mine ? s.pos_pages[slot] : 0;
+    // stage the value columns of the tile: row e, entries [e0, e0 + cnt)
+    // rounded up to a piece (a piece never crosses a page: P >= 32); every
+    // load is issued before the first LDS store
+    constexpr int NPT = MAXHD / RT_SPLIT * TILE / EPC / NT;  // pieces per thread at most
+    const int ncol = (cnt + EPC - 1) / EPC;       // pieces per row
+    piece_t x[NPT];
+#pragma unroll
+    for (int q = 0; q < NPT; ++q) {
+        const int idx = q * NT + (int)threadIdx.x;
+        if (idx < hh * ncol) {
+            const int r = idx / ncol;
+            const int e = half * hh + r;
+            const int ent = e0 + (idx - r * ncol) * EPC;
+            const int page = lds_spages[(ent >> s.page_shift) - sp0];
+            x[q] = *(const piece_t *)((const T *)s.v_pages + ((int64_t)page * hd + e) * P + (ent & (P - 1)));
+        }
+    }
+    const bool flag = mine && u >= a.tau;  // NaN fails
+    constexpr int KP = OWN_KEY ? MAXHD / EPC / RT_SPLIT : 1;
+    const int k0 = half * hh;             // first key element of this half
+    piece_t kr[KP];
+    if constexpr (OWN_KEY) {
+        if (flag) {
+#pragma unroll
+            for (int ch = 0; ch < KP; ++ch)
+                if (ch * EPC < hh) kr[ch] = *(const piece_t *)(s.k_pages + ((int64_t)slot * hd + k0 + ch * EPC) * ES);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NPT; ++q) {
+        const int idx = q * NT + (int)threadIdx.x;
+        if (idx < hh * ncol) {
+            const int r = idx / ncol;
+            *(piece_t *)&lds_v[r][(idx - r * ncol) * EPC] = x[q];
+        }
+    }
+    int total;
+    const int rank = block_rank(flag, lds_waves, &total);  // its barriers also cover the staging
+    if (flag) {
+        lds_src[rank] = slot;
+        lds_loc[rank] = threadIdx.x;
+    }
     const int n = max(0, min(total, new_len - dst0));
     if (n == 0) return;  // uniform: no barrier below is skipped by part of the block
-    const int P = d.page_size;
-    const int pg0 = dst0 >> d.page_shift;
-    const int npg = ((dst0 + n - 1) >> d.page_shift) - pg0 + 1;  // <= TILE / 32 + 1
-    if ((int)threadIdx.x < npg) lds_pages[threadIdx.x] = d.page_table[bg * d.max_pages + pg0 + threadIdx.x];
-    __syncthreads();
     auto dslot = [&](int kk) -> int64_t {
         const int e = dst0 + kk;
         return (int64_t)lds_pages[(e >> d.page_shift) - pg0] * P + (e & (P - 1));
     };
-    for (int kk = threadIdx.x; kk < n; kk += NT) {
-        const int64_t ds = dslot(kk);
-        const int ss = lds_src[kk];
-        d.pos_pages[ds] = s.pos_pages[ss];
-        if (d.u_pages) d.u_pages[ds] = s.u_pages[ss];
-    }
-    constexpr int ES = sizeof(T);
-    constexpr int EPC = 16 / ES;
-    constexpr int KB = 8;
-    const int hd = d.head_dim;
-    const int cpr = hd / EPC;
-    // keys: 16-byte pieces, a row's pieces on neighbouring lanes; a batch of
-    // loads is issued before its stores
-    const int npk = n * cpr;
-    for (int base = 0; base < npk; base += NT * KB) {
-        piece_t kv[KB];
-#pragma unroll
-        for (int u = 0; u < KB; ++u) {
-            const int idx = base + u * NT + (int)threadIdx.x;
-            if (idx < npk) {
-                const int kk = idx / cpr;
-                const int ch = idx - kk * cpr;
-                kv[u] = *(const piece_t *)(s.k_pages + (int64_t)lds_src[kk] * hd * ES + ch * 16);
-            }
+    if (flag && rank < n) {
+        const int64_t ds = dslot(rank);
+        if (half == 0) {
+            d.pos_pages[ds] = pos;
+            if (d.u_pages) d.u_pages[ds] = u;
         }
+        if constexpr (OWN_KEY) {
 #pragma unroll
-        for (int u = 0; u < KB; ++u) {
-            const int idx = base + u * NT + (int)threadIdx.x;
-            if (idx < npk) {
-                const int kk = idx / cpr;
-                const int ch = idx - kk * cpr;
-                *(piece_t *)(d.k_pages + dslot(kk) * hd * ES + ch * 16) = kv[u];
-            }
+            for (int ch = 0; ch < KP; ++ch)
+                if (ch * EPC < hh) *(piece_t *)(d.k_pages + (ds * hd + k0 + ch * EPC) * ES) = kr[ch];
         }
     }
-    // values, transposed in both caches: element e of entry kk sits at
-    // [page][e][slot]; consecutive lanes take consecutive entries
-    constexpr int VB = 16;
-    const int npv = n * hd;
-    for (int base = 0; base < npv; base += NT * VB) {
-        T vv[VB];
+    __syncthreads();  // lds_src / lds_loc complete
+    if constexpr (!OWN_KEY) {
+        // keys of an f32 cache: 16-byte pieces, a row's pieces on
+        // neighbouring lanes; a batch of loads is issued before its stores
+        constexpr int KB = 8;
+        const int cpr = hh / EPC;         // this half's pieces of a key row
+        const int npk = n * cpr;
+        for (int base = 0; base < npk; base += NT * KB) {
+            piece_t kv[KB];
 #pragma unroll
-        for (int u = 0; u < VB; ++u) {
-            const int idx = base + u * NT + (int)threadIdx.x;
-            if (idx < npv) {
-                const int e = idx / n;
-                const int kk = idx - e * n;
-                const int ss = lds_src[kk];
-                const int sp = ss >> s.page_shift;
-                vv[u] = ((const T *)s.v_pages)[((int64_t)sp * hd + e) * P + (ss & (P - 1))];
+            for (int q = 0; q < KB; ++q) {
+                const int idx = base + q * NT + (int)threadIdx.x;
+                if (idx < npk) {
+                    const int kk = idx / cpr;
+                    const int ch = idx - kk * cpr;
+                    kv[q] = *(const piece_t *)(s.k_pages + ((int64_t)lds_src[kk] * hd + k0) * ES + ch * 16);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < KB; ++q) {
+                const int idx = base + q * NT + (int)threadIdx.x;
+                if (idx < npk) {
+                    const int kk = idx / cpr;
+                    const int ch = idx - kk * cpr;
+                    *(piece_t *)(d.k_pages + (dslot(kk) * hd + k0) * ES + ch * 16) = kv[q];
+                }
             }
         }
+    }
+    // values: destination pieces c cover entries [c * EPC, c * EPC + EPC) of
+    // the (b, g) list; those inside [dst0, dst0 + n) are whole
+    const int c_lo = dst0 / EPC;
+    const int c_hi = (dst0 + n - 1) / EPC;  // inclusive
+    const int nch = c_hi - c_lo + 1;
+    for (int idx = threadIdx.x; idx < hh * nch; idx += NT) {
+        const int r = idx / nch;
+        const int e = half * hh + r;
+        const int c = c_lo + (idx - r * nch);
+        const int first = c * EPC;                       // list entry of the piece's element 0
+        const int64_t row = ((int64_t)lds_pages[(first >> d.page_shift) - pg0] * hd + e) * P + (first & (P - 1));
+        T *dv = (T *)d.v_pages + row;
+        if (first >= dst0 && first + EPC <= dst0 + n) {
+            piece_t y;
 #pragma unroll
-        for (int u = 0; u < VB; ++u) {
-            const int idx = base + u * NT + (int)threadIdx.x;
-            if (idx < npv) {
-                const int e = idx / n;
-                const int kk = idx - e * n;
-                const int ed = dst0 + kk;
-                const int dp = lds_pages[(ed >> d.page_shift) - pg0];
-                ((T *)d.v_pages)[((int64_t)dp * hd + e) * P + (ed & (P - 1))] = vv[u];
+            for (int w = 0; w < 4; ++w) {
+                if constexpr (ES == 4) {
+                    y[w] = __builtin_bit_cast(uint32_t, lds_v[r][lds_loc[first - dst0 + w]]);
+                } else {
+                    const uint32_t lo = __builtin_bit_cast(uint16_t, lds_v[r][lds_loc[first - dst0 + 2 * w]]);
+                    const uint32_t hi = __builtin_bit_cast(uint16_t, lds_v[r][lds_loc[first - dst0 + 2 * w + 1]]);
+                    y[w] = lo | (hi << 16);
+                }
+            }
+            *(piece_t *)dv = y;
+        } else {
+            for (int q = 0; q < EPC; ++q) {
+                const int kk = first + q - dst0;
+                if (kk >= 0 && kk < n) dv[q] = lds_v[r][lds_loc[kk]];
             }
         }
     }
@@ -702,12 +788,12 @@ hipError_t launch_rethresh(const RethreshArgs &a0, hipStream_t s) {
         hipLaunchKernelGGL(rethresh_plan_kernel, dim3(BG), dim3(NT), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(rethresh_count_kernel, dim3(a.max_tiles, BG), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(rethresh_count_kernel, dim3(BG, a.max_tiles), dim3(NT), 0, s, a);
     hipLaunchKernelGGL(rethresh_plan_kernel, dim3(BG), dim3(NT), 0, s, a);
     if (a.src.dtype == SPKV_BF16)
-        hipLaunchKernelGGL(rethresh_scatter_kernel<uint16_t>, dim3(a.max_tiles, BG), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL(rethresh_scatter_kernel<uint16_t>, dim3(BG, a.max_tiles, RT_SPLIT), dim3(NT), 0, s, a);
     else
-        hipLaunchKernelGGL(rethresh_scatter_kernel<float>, dim3(a.max_tiles, BG), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL(rethresh_scatter_kernel<float>, dim3(BG, a.max_tiles, RT_SPLIT), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
