@@ -49,6 +49,8 @@ def _load():
     lib.spkv_oracle_compact.restype = ci
     lib.spkv_oracle_rethreshold.argtypes = [i64, vp, f64, vp, vp]
     lib.spkv_oracle_rethreshold.restype = ci
+    lib.spkv_oracle_head_stats.argtypes = [i64, i64, vp, vp, vp, vp]
+    lib.spkv_oracle_head_stats.restype = ci
     lib.spkv_oracle_attention.argtypes = [i64, i64, i64, i64, i64, vp, vp, i64, vp, vp,
                                           i64, vp, f64, vp, vp, ci]
     lib.spkv_oracle_attention.restype = ci
@@ -127,6 +129,24 @@ def rethreshold(u, tau2: float):
     if rc != 0:
         raise ValueError("spkv_oracle_rethreshold rejected its arguments")
     return idx[: ln[0]].copy()
+
+
+def head_stats(u, z, u_sum=None, kept=None):
+    """O6: per key head, the sum of the utilities (fp64, row order) and the
+    count of kept pairs over the rows of u / z ([n_rows, n_kv]; either may be
+    None), added to u_sum / kept (fresh zeros when None).  Returns both."""
+    lib = _load()
+    ref = u if u is not None else z
+    n, nkv = np.asarray(ref).shape
+    u_c = None if u is None else np.ascontiguousarray(np.asarray(u, dtype=np.float32))
+    z_c = None if z is None else np.ascontiguousarray(np.asarray(z, dtype=np.uint8))
+    us = np.zeros(nkv, np.float64) if u_sum is None else np.array(u_sum, np.float64)
+    kp = np.zeros(nkv, np.int64) if kept is None else np.array(kept, np.int64)
+    rc = lib.spkv_oracle_head_stats(n, nkv, None if u_c is None else _p(u_c), None if z_c is None else _p(z_c),
+                                    _p(us), _p(kp))
+    if rc != 0:
+        raise ValueError("spkv_oracle_head_stats rejected its arguments")
+    return us, kp
 
 
 def attention(Q, t_rows, K, V, z, w: int, scale: float | None = None, threads: int = 1):

@@ -8,8 +8,9 @@
  * Source of every formula: "Self-Pruned Key-Value Attention: learning when to
  * write by predicting future utility" (arXiv 2605.14037), section 2.1,
  * equations (1)-(4), the paragraph "efficient implementation at
- * deployment" at the end of section 2.1, and the post-hoc threshold of
- * section 3.3 (hybrids paragraph).
+ * deployment" at the end of section 2.1, the post-hoc threshold of
+ * section 3.3 (hybrids paragraph), and the per-head statistics of Table 1
+ * and section 4.
  *
  * Precision: every input is a float32 array whose values are exact (bf16
  * values are a subset of float32); each value is widened to double on use and
@@ -164,6 +165,43 @@ int spkv_oracle_rethreshold(int64_t n, const float *u, double tau2,
         }
     }
     *len_out = kept;
+    return 0;
+}
+
+/*
+ * O6 -- per-head utility statistics.  SP-KV reports the density of a model
+ * as the fraction of the pairs outside the local window that the gate keeps
+ * (Table 1 caption), and uses the mean learned utility of each head to pick
+ * the heads that stay global in a local/global hybrid (section 1,
+ * contribution 2; section 4).  Over a set of n_rows gate outputs
+ * (u[s, g], z[s, g]) this is, for each key head g,
+ *
+ *   u_sum[g] += sum over s of u[s, g]     (in row order, in double)
+ *   kept[g]  += number of s with z[s, g] != 0
+ *
+ * accumulated into the outputs so that a long sequence can be fed in parts;
+ * mean utility = u_sum / rows, density = kept / rows.  A NaN utility makes
+ * its head's sum NaN.  u or z may be NULL (that half is skipped).
+ */
+int spkv_oracle_head_stats(int64_t n_rows, int64_t n_kv, const float *u,
+                           const uint8_t *z, double *u_sum, int64_t *kept)
+{
+    if (n_rows < 0 || n_kv <= 0)
+        return -1;
+    for (int64_t g = 0; g < n_kv; ++g) {
+        double acc = 0.0;
+        int64_t cnt = 0;
+        for (int64_t s = 0; s < n_rows; ++s) {
+            if (u)
+                acc += (double)u[s * n_kv + g];
+            if (z && z[s * n_kv + g])
+                ++cnt;
+        }
+        if (u)
+            u_sum[g] += acc;
+        if (z)
+            kept[g] += cnt;
+    }
     return 0;
 }
 

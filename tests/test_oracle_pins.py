@@ -427,3 +427,53 @@ def test_rethreshold_composes_exhaustively():
                         continue
                     ib = oracle.rethreshold(u[ia], b)
                     np.testing.assert_array_equal(ia[ib], oracle.rethreshold(u, b))
+
+
+# ----------------------------------------------------------------------------
+# O6: per-head statistics (SP-KV Table 1 density; section 4 mean utility)
+# ----------------------------------------------------------------------------
+
+def test_head_stats_closed_forms():
+    n, nkv = 1000, 3
+    # constant utilities: the sum is n * c exactly (c and n * c are exact in double)
+    u = np.full((n, nkv), 0.375, np.float32)
+    z = np.zeros((n, nkv), np.uint8)
+    z[::4, 0] = 1
+    z[:, 2] = 1
+    us, kp = oracle.head_stats(u, z)
+    np.testing.assert_array_equal(us, [375.0] * nkv)
+    np.testing.assert_array_equal(kp, [250, 0, 1000])
+    # per-head arithmetic series u[s, g] = (s + g) / 1024: sum = (n(n-1)/2 + n g) / 1024
+    s = np.arange(n, dtype=np.float64)[:, None] + np.arange(nkv)[None, :]
+    us, _ = oracle.head_stats((s / 1024).astype(np.float32), None)
+    np.testing.assert_array_equal(us, [(n * (n - 1) / 2 + n * g) / 1024 for g in range(nkv)])
+
+
+def test_head_stats_matches_numpy_and_accumulates():
+    r = inputs.rng(31, 5)
+    u = r.random((4097, 8)).astype(np.float32)
+    z = (r.random((4097, 8)) < 0.3).astype(np.uint8)
+    us, kp = oracle.head_stats(u, z)
+    np.testing.assert_allclose(us, u.astype(np.float64).sum(0), rtol=1e-13)
+    np.testing.assert_array_equal(kp, np.count_nonzero(z, axis=0))
+    # fed in three parts, the totals are those of one pass; the heads are
+    # independent (a column swap swaps the results)
+    a, k = None, None
+    for lo, hi in ((0, 1000), (1000, 1001), (1001, 4097)):
+        a, k = oracle.head_stats(u[lo:hi], z[lo:hi], a, k)
+    np.testing.assert_allclose(a, us, rtol=1e-13)
+    np.testing.assert_array_equal(k, kp)
+    perm = [3, 1, 0, 2, 7, 6, 5, 4]
+    us2, kp2 = oracle.head_stats(u[:, perm], z[:, perm])
+    np.testing.assert_array_equal(us2, us[perm])
+    np.testing.assert_array_equal(kp2, kp[perm])
+
+
+def test_head_stats_special_cases():
+    u = np.array([[0.5, np.nan], [0.25, 1.0]], np.float32)
+    us, kp = oracle.head_stats(u, np.array([[1, 0], [0, 0]], np.uint8))
+    assert us[0] == 0.75 and math.isnan(us[1])
+    np.testing.assert_array_equal(kp, [1, 0])
+    us, kp = oracle.head_stats(np.zeros((0, 2), np.float32), np.zeros((0, 2), np.uint8), [1.5, 2.0], [3, 4])
+    np.testing.assert_array_equal(us, [1.5, 2.0])
+    np.testing.assert_array_equal(kp, [3, 4])
