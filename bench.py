@@ -71,6 +71,7 @@ KERNEL_SOURCES = {
     "compact_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "compact_small_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "rethresh_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
+    "stats_band_vec_kernel": "learned_kv_cache_sp_amd/csrc/spkv_stats.hip",
 }
 CALIBRATION_BYTES = 1 << 30  # the plain copy: 1 GiB read + 1 GiB written
 
@@ -81,7 +82,8 @@ def parse():
     p.add_argument("--steps", type=int, default=None, help="timed steps (decode 256, prefill 4)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
     p.add_argument("--workload", default="decode_32k",
-                   choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k"])
+                   choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k",
+                            "head_stats_1m"])
     p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
     p.add_argument("--step-mode", choices=("auto", "fused", "separate"), default="auto",
@@ -774,6 +776,74 @@ def bench_rethreshold(args, wl):
     }
 
 
+HEAD_STATS_ROWS, HEAD_STATS_KV = 1 << 20, 8
+
+
+def bench_head_stats(args):
+    """Per-head utility sums and kept counts (SP-KV Table 1 density, section 4
+    mean utility) over 1,048,576 gate output rows x 8 key heads (the gate
+    outputs of 8 sequences of 131,072 tokens), f32 utilities and u8 keep bits
+    from a seeded generator.  One step = one spkv_head_stats call."""
+    import torch
+    from learned_kv_cache_sp_amd import spkv
+    n, nkv = HEAD_STATS_ROWS, HEAD_STATS_KV
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    u = torch.rand((n, nkv), generator=gen, device="cuda", dtype=torch.float32)
+    z = (torch.rand((n, nkv), generator=gen, device="cuda") < 0.2).to(torch.uint8)
+    us = torch.zeros(nkv, dtype=torch.float64, device="cuda")
+    kp = torch.zeros(nkv, dtype=torch.int64, device="cuda")
+    ws = spkv.workspace(spkv.spkv_head_stats_ws_bytes(n, nkv))
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        spkv.spkv_head_stats(u, z, us, kp, ws=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        spkv.spkv_head_stats(u, z, us, kp, ws=ws)
+        evs[i][1].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    alg = 5 * n * nkv  # each utility (4 B) and keep byte read once
+    call_s = float(np.mean(call_ms)) * 1e-3
+    achieved = alg / call_s / 1e9
+    return {
+        "metric": "gate output rows summarised per second", "value": n / (ms * 1e-3), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "head_stats_1m", "rows": n, "n_kv": nkv, "step": "spkv_head_stats"},
+        "roofline": {"bound": "hbm", "kernel": "spkv_head_stats (stats_band_vec_kernel + stats_total_kernel)",
+                     "achieved": achieved, "peak": 8000.0, "unit": "GB/s", "frac": achieved / 8000.0,
+                     "traffic": stored_traffic("stats_band_vec_kernel", "head_stats_1m"),
+                     "algorithmic_bytes_per_launch": alg, "avg_call_us": call_s * 1e6,
+                     "call_us": _stats_us(call_ms)},
+    }
+
+
+def cpu_baseline_head_stats(budget_s: float) -> dict:
+    """The oracle's per-head sums over repeated 131,072-row x 8-head samples."""
+    import oracle
+    oracle.build(force=False)
+    r = np.random.default_rng(5)
+    n = 131072
+    u = r.random((n, HEAD_STATS_KV)).astype(np.float32)
+    z = (r.random((n, HEAD_STATS_KV)) < 0.2).astype(np.uint8)
+    done = calls = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.head_stats(u, z)
+        done += n
+        calls += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} calls of oracle.head_stats on {n} rows x {HEAD_STATS_KV} heads, {el:.1f} s"}
+
+
 def cpu_baseline_rethreshold(wl, budget_s: float) -> dict:
     """The oracle's re-threshold over a bounded sample of lists shaped like the
     decode_32k cache (about 6.5k stored utilities per list, from the seeded
@@ -918,7 +988,10 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    if args.workload == "rethreshold_32k":
+    if args.workload == "head_stats_1m":
+        wl = None
+        res = bench_head_stats(args)
+    elif args.workload == "rethreshold_32k":
         wl = inputs.WORKLOADS["decode_32k"]
         res = bench_rethreshold(args, wl)
     else:
@@ -936,7 +1009,9 @@ def main():
         res["hbm_ceiling"] = hbm_ceiling(torch)
 
     if not args.no_cpu_baseline:
-        if args.workload == "rethreshold_32k":
+        if args.workload == "head_stats_1m":
+            res["cpu_baseline"] = cpu_baseline_head_stats(args.cpu_budget)
+        elif args.workload == "rethreshold_32k":
             res["cpu_baseline"] = cpu_baseline_rethreshold(wl, args.cpu_budget)
         else:
             res["cpu_baseline"] = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, args.cpu_budget)

@@ -19,7 +19,8 @@
  *                        pairs (Eq. 3-4), for chunked prefill
  * and spkv_decode_step runs gate, append and decode attention of one decode
  * step in a single launch.  spkv_cache_rethreshold rebuilds a cache at a new,
- * higher threshold from the utilities stored with its entries.
+ * higher threshold from the utilities stored with its entries, and
+ * spkv_head_stats gives per-head density and mean-utility sums.
  *
  * Conventions
  *   - Every call returns an int status (SPKV_OK or a negative SPKV_E_*).
@@ -335,6 +336,33 @@ size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads,
 int spkv_cache_rethreshold(const spkv_cache *src, const spkv_cache *dst,
                            float tau, void *ws, size_t ws_bytes, void *stream);
 size_t spkv_rethreshold_ws_bytes(const spkv_cache *src);
+
+/*
+ * spkv_head_stats -- per key head statistics of gate outputs: the measure of
+ *   density SP-KV reports (share of the pairs outside the local window that
+ *   are kept: Table 1 caption) and the mean learned utility it ranks heads by
+ *   to choose the global heads of a local/global hybrid (section 1,
+ *   contribution 2; section 4).  For the rows of utility / keep (spkv_gate's
+ *   outputs, [n_rows, n_kv]) it adds, for each key head g,
+ *     u_sum[g]  += sum over rows of utility[., g]   (double)
+ *     n_kept[g] += number of rows with keep[., g] != 0
+ *   so that a sequence can be fed in chunks; mean utility = u_sum / rows,
+ *   density = n_kept / rows (feed only the rows outside the window for the
+ *   density of Table 1).  utility or keep may be NULL (not both; that sum is
+ *   then left alone); u_sum, n_kept are device arrays of n_kv entries.  A
+ *   NaN utility makes its head's sum NaN.  n_rows = 0 adds nothing and
+ *   reads no pointer.
+ *   ws  at least spkv_head_stats_ws_bytes(n_rows, n_kv) bytes (8-byte
+ *       aligned; 0 when n_rows = 0).
+ *   Launches two kernels (band sums, then their total in band order): the
+ *   sums are deterministic; they may differ from a sequential sum in the
+ *   last bits.
+ * Supported: n_kv <= 16, n_rows < 2^31.
+ */
+int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows,
+                    int32_t n_kv, double *u_sum, int64_t *n_kept, void *ws,
+                    size_t ws_bytes, void *stream);
+size_t spkv_head_stats_ws_bytes(int64_t n_rows, int32_t n_kv);
 
 /* Sizes in bytes of each cache buffer (k_pages, v_pages, pos_pages,
  * page_table, lengths, ring_k, ring_v) for the dimensions in *c; returns the

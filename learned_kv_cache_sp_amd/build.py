@@ -26,7 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["spkv_api.cpp", "spkv_gate.hip", "spkv_compact.hip", "spkv_decode.hip", "spkv_prefill.hip"]
+SOURCES = ["spkv_api.cpp", "spkv_gate.hip", "spkv_compact.hip", "spkv_decode.hip", "spkv_prefill.hip", "spkv_stats.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

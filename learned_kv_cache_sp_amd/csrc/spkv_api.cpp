@@ -466,6 +466,39 @@ int spkv_cache_rethreshold(const spkv_cache *src, const spkv_cache *dst, float t
 }
 
 // ----------------------------------------------------------------------------
+size_t spkv_head_stats_ws_bytes(int64_t n_rows, int32_t n_kv) {
+    if (n_rows < 0 || n_kv < 1 || n_kv > 16) return 0;
+    return spkv::stats_ws_bytes(n_rows, n_kv);
+}
+
+int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows, int32_t n_kv, double *u_sum,
+                    int64_t *n_kept, void *ws, size_t ws_bytes, void *stream) {
+    if (n_kv < 1 || n_kv > 16) return fail(SPKV_E_UNSUPPORTED, "n_kv %d (1..16)", n_kv);
+    if (n_rows < 0 || n_rows > (int64_t)INT32_MAX) return fail(SPKV_E_INVALID, "n_rows %lld", (long long)n_rows);
+    if (n_rows == 0) return SPKV_OK;  // nothing to add
+    if (!utility && !keep) return fail(SPKV_E_INVALID, "utility and keep are both NULL");
+    if (utility && !u_sum) return fail(SPKV_E_INVALID, "u_sum is NULL with utility given");
+    if (keep && !n_kept) return fail(SPKV_E_INVALID, "n_kept is NULL with keep given");
+    if ((u_sum && ((uintptr_t)u_sum & 7)) || (n_kept && ((uintptr_t)n_kept & 7)) || (utility && ((uintptr_t)utility & 3)))
+        return fail(SPKV_E_INVALID, "u_sum / n_kept not 8-byte or utility not 4-byte aligned");
+    const size_t need = spkv::stats_ws_bytes(n_rows, n_kv);
+    if (need && (!ws || ws_bytes < need))
+        return fail(SPKV_E_WORKSPACE, "statistics workspace %zu < %zu bytes", ws_bytes, need);
+    if (need && ((uintptr_t)ws & 7)) return fail(SPKV_E_INVALID, "ws not 8-byte aligned");
+    spkv::StatsArgs a = {};
+    a.utility = utility;
+    a.keep = keep;
+    a.n_rows = n_rows;
+    a.n_kv = n_kv;
+    a.u_sum = u_sum;
+    a.n_kept = n_kept;
+    a.ws = ws;
+    hipError_t e = spkv::launch_stats(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "statistics launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
 size_t spkv_cache_bytes(const spkv_cache *c, size_t sizes[7]) {
     if (!c) return 0;
     const size_t es = c->dtype == SPKV_BF16 ? 2 : 4;

@@ -143,4 +143,22 @@ struct RethreshArgs {
 size_t rethresh_ws_bytes(const spkv_cache *src);
 hipError_t launch_rethresh(const RethreshArgs &a, hipStream_t s);
 
+// ---- per-head statistics (spkv_head_stats) ---------------------------------
+struct StatsArgs {
+    const float *utility;   // [n_rows, n_kv] or NULL
+    const uint8_t *keep;    // [n_rows, n_kv] or NULL
+    int64_t n_rows;
+    int32_t n_kv;
+    double *u_sum;          // [n_kv], accumulated
+    int64_t *n_kept;        // [n_kv], accumulated
+    void *ws;
+    // set by the launcher
+    double *ws_u;
+    int64_t *ws_k;
+    int64_t band_rows;      // rows (row path) or elements (vector path) per band
+    int32_t n_bands;
+};
+size_t stats_ws_bytes(int64_t n_rows, int n_kv);
+hipError_t launch_stats(const StatsArgs &a, hipStream_t s);
+
 }  // namespace spkv

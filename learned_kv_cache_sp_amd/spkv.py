@@ -72,6 +72,7 @@ EXPORTS = [
     "spkv_gate", "spkv_gate_ws_bytes", "spkv_compact_append", "spkv_compact_ws_bytes",
     "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_decode_step", "spkv_decode_step_ws_bytes",
     "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
+    "spkv_head_stats", "spkv_head_stats_ws_bytes",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
     "spkv_last_error", "spkv_version",
 ]
@@ -104,6 +105,8 @@ def load_library(path: str = LIB_PATH):
         "spkv_prefill_ws_bytes": ([C, i32, i32], sz),
         "spkv_cache_rethreshold": ([C, C, f32, vp, sz, vp], ctypes.c_int),
         "spkv_rethreshold_ws_bytes": ([C], sz),
+        "spkv_head_stats": ([vp, vp, i64, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "spkv_head_stats_ws_bytes": ([i64, i32], sz),
         "spkv_cache_bytes": ([C, vp], sz),
         "spkv_cache_reset": ([C, vp], ctypes.c_int),
         "spkv_cache_check": ([C, vp, vp], ctypes.c_int),
@@ -471,6 +474,38 @@ def spkv_cache_rethreshold(src: Cache, dst: Cache, tau: float, ws=None, stream=N
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.spkv_cache_rethreshold(ctypes.byref(src.desc()), ctypes.byref(dst.desc()), float(tau),
                                       _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def spkv_head_stats_ws_bytes(n_rows: int, n_kv: int) -> int:
+    return int(load_library().spkv_head_stats_ws_bytes(int(n_rows), int(n_kv)))
+
+
+def spkv_head_stats(utility, keep, u_sum=None, n_kept=None, ws=None, stream=None):
+    """Add per-head utility sums (f64) and kept counts (int64) of the rows of
+    utility / keep [n_rows, n_kv] (either may be None) to u_sum / n_kept
+    (fresh zeros when None).  Returns (u_sum, n_kept)."""
+    lib = load_library()
+    ref = utility if utility is not None else keep
+    if ref is None:
+        raise ValueError("utility and keep are both None")
+    n, nkv = ref.shape
+    dev = ref.device
+    _need_gpu(utility, keep, u_sum, n_kept)
+    if utility is not None and (utility.dtype != torch.float32 or not utility.is_contiguous()):
+        raise ValueError("utility must be contiguous float32")
+    if keep is not None and (keep.dtype != torch.uint8 or not keep.is_contiguous()):
+        raise ValueError("keep must be contiguous uint8")
+    if u_sum is None and utility is not None:
+        u_sum = torch.zeros(nkv, dtype=torch.float64, device=dev)
+    if n_kept is None and keep is not None:
+        n_kept = torch.zeros(nkv, dtype=torch.int64, device=dev)
+    need = spkv_head_stats_ws_bytes(n, nkv)
+    if ws is None and need:
+        ws = workspace(need, dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.spkv_head_stats(_ptr(utility), _ptr(keep), n, nkv, _ptr(u_sum), _ptr(n_kept), _ptr(ws),
+                               ws_bytes, _stream(stream)))
+    return u_sum, n_kept
 
 
 def spkv_cache_reset(cache: Cache, stream=None):
