@@ -2,9 +2,10 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
 libspkv.so.  torch supplies device memory and the stream.  The functions
-``spkv_gate``, ``spkv_compact_append``, ``spkv_decode_attn`` and
-``spkv_prefill_attn`` mirror the C calls of include/spkv.h one to one and
-take torch tensors in place of pointers.  ``Cache`` and ``GateWeights``
+``spkv_gate``, ``spkv_compact_append``, ``spkv_decode_attn``,
+``spkv_prefill_attn``, ``spkv_decode_step``, ``spkv_cache_rethreshold`` and
+``spkv_head_stats`` mirror the C calls of include/spkv.h one to one and take
+torch tensors in place of pointers.  ``Cache`` and ``GateWeights``
 allocate the buffers the C structs point to.
 
 There is no fallback: if libspkv.so is missing or no GPU is visible, the
