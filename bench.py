@@ -18,9 +18,12 @@ Other workloads (``--workload``): ``decode_131k`` (batch 4, 131072 tokens,
 per-head keep 2-60 %), ``ragged_32`` (batch 32, contexts 4096-65536, 15 %,
 hidden states buffered: window append + attention every step -- one
 spkv_decode_step launch without gate -- and gate + kept append of all
-32 x 128 buffered rows every 128 steps) and ``prefill_64k``
+32 x 128 buffered rows every 128 steps), ``prefill_64k``
 (one step = chunked prefill of a 65536-token sequence in 16384-token chunks:
-gate, kept append, prefill attention, window append per chunk).
+gate, kept append, prefill attention, window append per chunk),
+``rethreshold_32k`` (one step = rebuild of the decode_32k cache at a higher
+threshold that keeps half of its entries) and ``head_stats_1m`` (one step =
+per-head utility sums and kept counts of 1,048,576 gate rows x 8 heads).
 
 Inputs are synthetic (seeded) and resident in HBM before timing starts.
 Decode prefixes are gated and compacted through the same calls during set-up.
