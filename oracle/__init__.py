@@ -51,6 +51,9 @@ def _load():
     lib.spkv_oracle_rethreshold.restype = ci
     lib.spkv_oracle_head_stats.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.spkv_oracle_head_stats.restype = ci
+    lib.spkv_oracle_soft_attention.argtypes = [i64, i64, i64, i64, i64, vp, vp, i64, vp, vp,
+                                               i64, vp, f64, f64, f64, f64, vp, vp, ci]
+    lib.spkv_oracle_soft_attention.restype = ci
     lib.spkv_oracle_attention.argtypes = [i64, i64, i64, i64, i64, vp, vp, i64, vp, vp,
                                           i64, vp, f64, vp, vp, ci]
     lib.spkv_oracle_attention.restype = ci
@@ -172,6 +175,31 @@ def attention(Q, t_rows, K, V, z, w: int, scale: float | None = None, threads: i
                                    _p(out), _p(lse), int(threads))
     if rc != 0:
         raise ValueError("spkv_oracle_attention rejected its arguments")
+    return out, lse
+
+
+def soft_attention(Q, t_rows, K, V, u, w: int, tau: float, beta: float = 0.01, c: float = 1e6,
+                   scale: float | None = None, threads: int = 1):
+    """O7, Eq. (5)-(6): every causal key, with the additive soft mask outside
+    the window.  Shapes as attention(); u [T, n_kv] float32 utilities."""
+    lib = _load()
+    Q = _f32(Q)
+    K = _f32(K)
+    V = _f32(V)
+    u = np.ascontiguousarray(np.asarray(u, dtype=np.float32))
+    t_rows = np.ascontiguousarray(np.asarray(t_rows, dtype=np.int64))
+    n_rows, nq, hd = Q.shape
+    T, nkv, hd2 = K.shape
+    assert hd2 == hd and V.shape == K.shape and u.shape == (T, nkv) and t_rows.shape == (n_rows,)
+    if scale is None:
+        scale = 1.0 / np.sqrt(hd)
+    out = np.empty((n_rows, nq, hd), np.float64)
+    lse = np.empty((n_rows, nq), np.float64)
+    rc = lib.spkv_oracle_soft_attention(T, nq, nkv, hd, int(w), _p(Q), _p(t_rows), n_rows, _p(K), _p(V),
+                                        nkv * hd, _p(u), float(tau), float(beta), float(c), float(scale),
+                                        _p(out), _p(lse), int(threads))
+    if rc != 0:
+        raise ValueError("spkv_oracle_soft_attention rejected its arguments")
     return out, lse
 
 

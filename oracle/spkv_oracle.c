@@ -9,8 +9,8 @@
  * write by predicting future utility" (arXiv 2605.14037), section 2.1,
  * equations (1)-(4), the paragraph "efficient implementation at
  * deployment" at the end of section 2.1, the post-hoc threshold of
- * section 3.3 (hybrids paragraph), and the per-head statistics of Table 1
- * and section 4.
+ * section 3.3 (hybrids paragraph), the per-head statistics of Table 1
+ * and section 4, and the soft relaxation of Eq. (5)-(6).
  *
  * Precision: every input is a float32 array whose values are exact (bf16
  * values are a subset of float32); each value is widened to double on use and
@@ -165,6 +165,93 @@ int spkv_oracle_rethreshold(int64_t n, const float *u, double tau2,
         }
     }
     *len_out = kept;
+    return 0;
+}
+
+/*
+ * O7 -- the training-time soft relaxation of the gate, SP-KV section 2.1,
+ * Eq. (5)-(6).  Each pair gets alpha_s = sigmoid((u_s - tau) / beta)
+ * (Eq. 5) and the hard mask of Eq. (4) is replaced by an additive score
+ *
+ *   M_soft(t, s) = 0                    if 0 <= t - s < w   (window)
+ *                = c * (alpha_s - 1)    otherwise, for s <= t
+ *
+ * (Eq. 6; positions after t stay excluded, as in Eq. 4), so that for query
+ * row t, query head h and key head g = h / group:
+ *
+ *   x_s = scale * q . k_s + M_soft(t, s)   over s in [0, t]
+ *   out = sum_s softmax(x)_s v_s,   lse = log sum_s exp(x_s)
+ *
+ * u is [T, n_kv] float (the utilities of Eq. 1).  Written literally: alpha is
+ * formed first and 1 is subtracted (in double).  Same layouts and row rules
+ * as O3.
+ */
+int spkv_oracle_soft_attention(int64_t T, int64_t n_q, int64_t n_kv, int64_t hd,
+                               int64_t w, const float *Q, const int64_t *t_rows,
+                               int64_t n_rows, const float *K, const float *V,
+                               int64_t ld_kv, const float *u, double tau,
+                               double beta, double c, double scale,
+                               double *out, double *lse, int n_threads)
+{
+    if (T < 0 || n_q <= 0 || n_kv <= 0 || hd <= 0 || w < 1 || n_q % n_kv || !(beta > 0.0))
+        return -1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (t_rows[i] < 0 || t_rows[i] >= T)
+            return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t group = n_q / n_kv;
+    int64_t job;
+    const int64_t n_jobs = n_rows * n_q;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+#endif
+    for (job = 0; job < n_jobs; ++job) {
+        const int64_t i = job / n_q;
+        const int64_t h = job % n_q;
+        const int64_t t = t_rows[i];
+        const int64_t g = h / group;
+        const float *q = Q + (i * n_q + h) * hd;
+        double *o = out + (i * n_q + h) * hd;
+        /* every causal key takes part; the scores carry the mask of Eq. (6) */
+        double m = -INFINITY;
+        for (int64_t s = 0; s <= t; ++s) {
+            const float *k = K + s * ld_kv + g * hd;
+            double x = 0.0;
+            for (int64_t e = 0; e < hd; ++e)
+                x += (double)q[e] * (double)k[e];
+            x *= scale;
+            if (t - s >= w) {
+                const double alpha = 1.0 / (1.0 + exp(-((double)u[s * n_kv + g] - tau) / beta));
+                x += c * (alpha - 1.0);
+            }
+            if (x > m)
+                m = x;
+        }
+        for (int64_t e = 0; e < hd; ++e)
+            o[e] = 0.0;
+        double l = 0.0;
+        for (int64_t s = 0; s <= t; ++s) {
+            const float *k = K + s * ld_kv + g * hd;
+            const float *v = V + s * ld_kv + g * hd;
+            double x = 0.0;
+            for (int64_t e = 0; e < hd; ++e)
+                x += (double)q[e] * (double)k[e];
+            x *= scale;
+            if (t - s >= w) {
+                const double alpha = 1.0 / (1.0 + exp(-((double)u[s * n_kv + g] - tau) / beta));
+                x += c * (alpha - 1.0);
+            }
+            const double p = exp(x - m);
+            l += p;
+            for (int64_t e = 0; e < hd; ++e)
+                o[e] += p * (double)v[e];
+        }
+        for (int64_t e = 0; e < hd; ++e)
+            o[e] /= l;
+        if (lse)
+            lse[i * n_q + h] = m + log(l);
+    }
     return 0;
 }
 

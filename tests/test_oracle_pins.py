@@ -477,3 +477,87 @@ def test_head_stats_special_cases():
     us, kp = oracle.head_stats(np.zeros((0, 2), np.float32), np.zeros((0, 2), np.uint8), [1.5, 2.0], [3, 4])
     np.testing.assert_array_equal(us, [1.5, 2.0])
     np.testing.assert_array_equal(kp, [3, 4])
+
+
+# ----------------------------------------------------------------------------
+# O7: soft relaxation, Eq. (5)-(6)
+# ----------------------------------------------------------------------------
+
+def _soft_case(T=40, n_q=4, n_kv=2, hd=16, seed=3):
+    Q, K, V = rand_seq(T, n_q, n_kv, hd, seed)
+    u = inputs.rng(seed, 77).random((T, n_kv)).astype(np.float32)
+    return Q, K, V, u
+
+
+def test_soft_special_cases_reduce_to_known_attention():
+    T, n_q, n_kv, hd, w = 40, 4, 2, 16, 6
+    Q, K, V, u = _soft_case(T, n_q, n_kv, hd)
+    t = np.arange(T)
+    sc = 1 / math.sqrt(hd)
+    G = n_q // n_kv
+    dense = [sdpa_f64(Q[:, h], K[:, h // G], V[:, h // G], causal_allowed(t, T), sc) for h in range(n_q)]
+    # c = 0: no mask at all -> causal attention
+    o, l = oracle.soft_attention(Q, t, K, V, u, w, tau=0.5, c=0.0)
+    # every utility far above tau: alpha = 1 to double precision -> causal
+    o2, l2 = oracle.soft_attention(Q, t, K, V, np.full_like(u, 2.0), w, tau=0.5)
+    # window covering the sequence: Eq. (6) adds nothing -> causal
+    o3, l3 = oracle.soft_attention(Q, t, K, V, u, T, tau=0.5)
+    for h in range(n_q):
+        for oo, ll in ((o, l), (o2, l2), (o3, l3)):
+            np.testing.assert_allclose(oo[:, h], dense[h][0], atol=1e-12)
+            np.testing.assert_allclose(ll[:, h], dense[h][1], atol=1e-12)
+
+
+def test_soft_hard_limit_is_eq4():
+    # beta -> 0 with every |u - tau| >= 0.05: alpha is 0 or 1 and exp(-c) = 0,
+    # so Eq. (6) becomes the hard mask of Eq. (4) with z = [u >= tau]
+    T, n_q, n_kv, hd, w = 48, 4, 2, 16, 5
+    Q, K, V, u = _soft_case(T, n_q, n_kv, hd, seed=8)
+    u = np.where(np.abs(u - 0.5) < 0.05, u + 0.1, u).astype(np.float32)
+    t = np.arange(T)
+    o, l = oracle.soft_attention(Q, t, K, V, u, w, tau=0.5, beta=1e-4)
+    oh, lh = oracle.attention(Q, t, K, V, (u >= 0.5).astype(np.uint8), w)
+    np.testing.assert_allclose(o, oh, atol=1e-12)
+    np.testing.assert_allclose(l, lh, atol=1e-12)
+
+
+def test_soft_two_key_closed_forms():
+    # query row t = 1, window 1: key 1 in the window (score 0, no mask), key 0
+    # outside (score 0, mask c (alpha - 1)); with K = 0 the output is the
+    # weighted mean (v1 + e^b v0) / (1 + e^b) and lse = log(1 + e^b)
+    hd = 4
+    Q = np.ones((1, 1, hd), np.float32)
+    K = np.zeros((2, 1, hd), np.float32)
+    V = np.array([[[1, 2, 3, 4]], [[-1, 0, 1, 0.5]]], np.float32)
+    cases = [
+        (0.5, 0.01, 2.0, -1.0),                                 # u = tau: alpha = 1/2, b = -c/2
+        (float(np.float32(0.5 + 0.01 * math.log(3))), 0.01, 4.0, -1.0),  # alpha = 3/4, b = -c/4
+        (0.3, 0.1, 3.0, 3.0 * (1 / (1 + math.e ** 2) - 1)),    # alpha = sigmoid(-2)
+    ]
+    for u0, beta, c, b_expect in cases:
+        u = np.array([[u0], [0.0]], np.float32)
+        o, l = oracle.soft_attention(Q, [1], K, V, u, 1, tau=0.5, beta=beta, c=c)
+        # the exact alpha of the rounded float utility
+        a = 1 / (1 + math.exp(-(float(np.float32(u0)) - 0.5) / beta))
+        b = c * (a - 1)
+        assert abs(b - b_expect) < 1e-5  # u0 is rounded to float32
+        wgt = math.exp(b)
+        np.testing.assert_allclose(o[0, 0], (V[1, 0] + wgt * V[0, 0]) / (1 + wgt), atol=1e-14)
+        assert abs(l[0, 0] - math.log1p(wgt)) < 1e-14
+
+
+def test_soft_weight_grows_with_utility():
+    # raising one outside key's utility raises its weight: the output moves
+    # towards that key's value (all other keys fixed, K = 0)
+    T, hd, w = 10, 4, 2
+    Q = np.ones((1, 1, hd), np.float32)
+    K = np.zeros((T, 1, hd), np.float32)
+    V = np.zeros((T, 1, hd), np.float32)
+    V[3, 0, 0] = 1.0
+    prev = -1.0
+    for u3 in (0.40, 0.48, 0.5, 0.52, 0.6):
+        u = np.full((T, 1), 0.45, np.float32)
+        u[3, 0] = u3
+        o, _ = oracle.soft_attention(Q, [T - 1], K, V, u, w, tau=0.5, beta=0.01, c=10.0)
+        assert o[0, 0, 0] > prev
+        prev = o[0, 0, 0]
