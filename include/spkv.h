@@ -21,6 +21,7 @@
  * step in a single launch.  spkv_cache_rethreshold rebuilds a cache at a new,
  * higher threshold from the utilities stored with its entries, and
  * spkv_head_stats gives per-head density and mean-utility sums.
+ * spkv_prefill_attn_soft is the forward of the soft relaxation of Eq. (5)-(6).
  *
  * Conventions
  *   - Every call returns an int status (SPKV_OK or a negative SPKV_E_*).
@@ -306,6 +307,27 @@ int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b,
                       void *stream);
 size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads,
                              int32_t n_rows);
+
+/*
+ * spkv_prefill_attn_soft -- spkv_prefill_attn with the training-time soft
+ *   relaxation of the gate (SP-KV section 2.1, Eq. 5-6) in place of the hard
+ *   mask of Eq. (4): every cached entry with position <= t - w takes part
+ *   with the additive score c * (alpha - 1), alpha = sigmoid((u - tau) / beta)
+ *   from its stored utility u (c->u_pages, required); window keys take part
+ *   with no added score.  With every token of the sequence in the cache
+ *   (appended with keep = 1 and its utility), this is the attention over all
+ *   causal keys with the mask of Eq. (6).  Forward only.
+ *   tau (finite), beta > 0 (the pages use 0.01), c_mask >= 0 (the pages use
+ *   1e6); other arguments and call order as for spkv_prefill_attn.
+ *   Utilities must not be NaN.
+ * Supported: a bf16 cache, G <= 16.
+ */
+int spkv_prefill_attn_soft(const spkv_cache *c, int32_t n_q_heads, int32_t b,
+                           const void *q, int64_t ld_q, const void *k,
+                           const void *v, int64_t ld_kv, int32_t pos0,
+                           int32_t n_rows, float scale, float tau, float beta,
+                           float c_mask, float *out, float *lse, void *ws,
+                           size_t ws_bytes, void *stream);
 
 /*
  * spkv_cache_rethreshold -- rebuild the persistent cache at a new threshold.

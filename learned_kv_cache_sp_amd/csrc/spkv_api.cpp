@@ -370,9 +370,17 @@ size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads, int32_t n_r
     return spkv::prefill_ws_bytes(c, n_q_heads, n_rows);
 }
 
-int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b, const void *q, int64_t ld_q,
-                      const void *k, const void *v, int64_t ld_kv, int32_t pos0, int32_t n_rows,
-                      float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+struct SoftArgs {
+    bool on;
+    float tau, beta, c;
+};
+
+int prefill_common(const spkv_cache *c, int32_t n_q_heads, int32_t b, const void *q, int64_t ld_q,
+                   const void *k, const void *v, int64_t ld_kv, int32_t pos0, int32_t n_rows, float scale,
+                   float *out, float *lse, void *ws, size_t ws_bytes, void *stream, SoftArgs soft) {
     if (int r = check_cache(c)) return r;
     if (n_q_heads < 1 || n_q_heads % c->n_kv) return fail(SPKV_E_INVALID, "n_q_heads %d vs n_kv %d", n_q_heads, c->n_kv);
     const int G = n_q_heads / c->n_kv;
@@ -406,9 +414,39 @@ int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b, const v
     a.out = out;
     a.lse = lse;
     a.ws = (char *)ws;
+    a.soft = soft.on ? 1 : 0;
+    a.soft_tau = soft.tau;
+    a.soft_k1 = soft.on ? (float)(1.4426950408889634 / (double)soft.beta) : 0.f;
+    a.soft_cs = soft.on ? (float)((double)soft.c / (double)scale) : 0.f;
     hipError_t e = spkv::launch_prefill(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return SPKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int spkv_prefill_attn(const spkv_cache *c, int32_t n_q_heads, int32_t b, const void *q, int64_t ld_q,
+                      const void *k, const void *v, int64_t ld_kv, int32_t pos0, int32_t n_rows,
+                      float scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_common(c, n_q_heads, b, q, ld_q, k, v, ld_kv, pos0, n_rows, scale, out, lse, ws, ws_bytes,
+                          stream, SoftArgs{false, 0.f, 0.f, 0.f});
+}
+
+int spkv_prefill_attn_soft(const spkv_cache *c, int32_t n_q_heads, int32_t b, const void *q, int64_t ld_q,
+                           const void *k, const void *v, int64_t ld_kv, int32_t pos0, int32_t n_rows,
+                           float scale, float tau, float beta, float c_mask, float *out, float *lse, void *ws,
+                           size_t ws_bytes, void *stream) {
+    if (int r = check_cache(c)) return r;
+    if (!c->u_pages) return fail(SPKV_E_INVALID, "soft mask needs stored utilities (cache->u_pages)");
+    if (c->dtype != SPKV_BF16) return fail(SPKV_E_UNSUPPORTED, "soft mask needs a bf16 cache");
+    if (n_q_heads < 1 || n_q_heads % c->n_kv || n_q_heads / c->n_kv > 16)
+        return fail(SPKV_E_UNSUPPORTED, "soft mask: group size must be 1..16");
+    if (!std::isfinite(tau) || !(beta > 0.f) || !std::isfinite(beta) || !(c_mask >= 0.f) || !std::isfinite(c_mask))
+        return fail(SPKV_E_INVALID, "soft mask: tau finite, beta > 0 and c >= 0 finite");
+    if (!std::isfinite(scale) || scale == 0.f) return fail(SPKV_E_INVALID, "scale not finite or zero");
+    return prefill_common(c, n_q_heads, b, q, ld_q, k, v, ld_kv, pos0, n_rows, scale, out, lse, ws, ws_bytes,
+                          stream, SoftArgs{true, tau, beta, c_mask});
 }
 
 // ----------------------------------------------------------------------------

@@ -127,6 +127,10 @@ struct PrefillArgs {
     float scale;
     float *out, *lse;
     char *ws;
+    // soft mode (spkv_prefill_attn_soft): cached keys outside the window get
+    // -soft_cs / (1 + 2^((u - soft_tau) * soft_k1)) added to their raw score
+    int32_t soft;
+    float soft_tau, soft_k1, soft_cs;  // tau, log2(e) / beta, c / scale
 };
 size_t prefill_ws_bytes(const spkv_cache *c, int n_q, int n_rows);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

@@ -183,7 +183,12 @@ __device__ inline int koff(int r, int c) { return r * (2 * HD) + ((c ^ swz_k<HD>
 __device__ inline int voff(int e, int c) { return e * (2 * PF_KB) + ((c ^ swz_v(e)) << 4); }
 
 
-template <int HD>
+// SOFT: the training-time relaxation of SP-KV (section 2.1, Eq. 5-6) --
+// every cached key outside the window gets the additive score
+// c (alpha - 1) = -c sigmoid((tau - u) / beta), u its stored utility, formed
+// here as -c / (1 + exp((u - tau) / beta)) (the same value without the loss
+// of precision of 1 - alpha near alpha = 1); window keys get none.
+template <int HD, bool SOFT>
 __global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a) {
     constexpr int CPR = HD / 8;                  // 16-byte chunks per key row
@@ -192,7 +197,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     constexpr int KI = KBYTES / 1024;            // 1 KB direct loads per key block
     constexpr int VI = VBYTES / 1024;
     constexpr int KRPI = 1024 / (2 * HD);        // key rows per direct load
-    constexpr int LPB = (KI + VI) / PF_NW + 1;   // direct loads per wave and block (+ positions)
+    constexpr int LPB = (KI + VI) / PF_NW + 1 + (SOFT ? 1 : 0);  // direct loads per wave and block (+ positions, utilities)
     // one array per stage: with every stage index a compile-time constant in
     // the pipeline loop, the compiler can tell that reading one stage does
     // not touch the direct loads in flight into another (with one indexed
@@ -201,6 +206,8 @@ prefill_bf16_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds_kb0[KBYTES], lds_kb1[KBYTES], lds_kb2[KBYTES];
     __shared__ __attribute__((aligned(1024))) char lds_vb0[VBYTES], lds_vb1[VBYTES], lds_vb2[VBYTES];
     __shared__ __attribute__((aligned(16))) int lds_pos0[PF_KB], lds_pos1[PF_KB], lds_pos2[PF_KB];
+    constexpr int UN = SOFT ? PF_KB : 4;  // stored utilities of a block (soft mode)
+    __shared__ __attribute__((aligned(16))) float lds_u0[UN], lds_u1[UN], lds_u2[UN];
     __shared__ int lds_pt[PF_PTMAX];
     __shared__ int lds_cnt[2];
 
@@ -273,7 +280,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         const int e = i * 8 + (lane >> 3);
         dv_off[u] = (e * P + 8 * ((lane & 7) ^ swz_v(e))) * 2;
     }
-    auto issue_direct = [&](int j, char *kbuf, char *vbuf, int *pbuf) {
+    auto issue_direct = [&](int j, char *kbuf, char *vbuf, int *pbuf, float *ubuf) {
         const int e0 = j * PF_KB;
         if (page_blocks) {
             const int page = pf_uniform(page_of(e0));
@@ -290,6 +297,10 @@ prefill_bf16_kernel(PrefillArgs a) {
             for (int u = 0; u < VI / PF_NW; ++u)
                 pf_buffer_lds16(rv, (lds_void *)(vbuf + (wave + PF_NW * u) * 1024), dv_off[u]);
             pf_buffer_lds4(rp, (lds_void *)pbuf, lane * 4);
+            if constexpr (SOFT) {
+                const __amdgpu_buffer_rsrc_t ru = pf_rsrc(c.u_pages + (int64_t)page * P + slot0, PF_KB * 4);
+                pf_buffer_lds4(ru, (lds_void *)ubuf, lane * 4);
+            }
             return;
         }
 #pragma unroll
@@ -315,6 +326,10 @@ prefill_bf16_kernel(PrefillArgs a) {
             const int ent = e0 + lane;
             const int32_t *src = c.pos_pages + (int64_t)page_of(ent) * P + (ent & (P - 1));
             __builtin_amdgcn_global_load_lds(src, (lds_void *)pbuf, 4, 0, 0);
+            if constexpr (SOFT) {
+                const float *usrc = c.u_pages + (int64_t)page_of(ent) * P + (ent & (P - 1));
+                __builtin_amdgcn_global_load_lds(usrc, (lds_void *)ubuf, 4, 0, 0);
+            }
         }
     };
 
@@ -323,6 +338,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     constexpr int VCH = HD * (PF_KB / 8) / PF_NT;   // value chunks per thread
     i32x4 kst[KCH], vst[VCH];
     int pst = 0;
+    float ust = 0.f;
     auto load_staged = [&](int blk) {
         if (blk < nb_g) {
             // cached block with n_ok < 64 valid entries: invalid keys get zero
@@ -359,6 +375,8 @@ prefill_bf16_kernel(PrefillArgs a) {
             if (threadIdx.x < PF_KB) {
                 const int ent = j0 + threadIdx.x;
                 pst = threadIdx.x < n_ok ? c.pos_pages[(int64_t)pt[ent >> c.page_shift] * P + (ent & (P - 1))] : INT_MAX;
+                if constexpr (SOFT)
+                    ust = threadIdx.x < n_ok ? c.u_pages[(int64_t)pt[ent >> c.page_shift] * P + (ent & (P - 1))] : 0.f;
             }
         } else {
             const int s0 = s_lo + (blk - nb_g) * PF_KB;
@@ -400,7 +418,7 @@ prefill_bf16_kernel(PrefillArgs a) {
             if (threadIdx.x < PF_KB) pst = s0 + threadIdx.x;
         }
     };
-    auto store_staged = [&](int blk, char *kbuf, char *vbuf, int *pbuf) {
+    auto store_staged = [&](int blk, char *kbuf, char *vbuf, int *pbuf, float *ubuf) {
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
             const int id = threadIdx.x + u * PF_NT;
@@ -426,6 +444,8 @@ prefill_bf16_kernel(PrefillArgs a) {
             }
         }
         if (threadIdx.x < PF_KB) pbuf[threadIdx.x] = pst;
+        if constexpr (SOFT)
+            if (threadIdx.x < PF_KB) ubuf[threadIdx.x] = ust;
     };
 
     // ---- per-wave online softmax state over its pair tiles -------------------
@@ -455,7 +475,12 @@ prefill_bf16_kernel(PrefillArgs a) {
     // pair tile for the whole block, then exponentials and value products
     // without branches, the products of the pair tiles alternating so that
     // no MFMA waits on the one before.
-    auto compute_block = [&](const char *kb, const char *vb, const int *pb_pos, int kind) {
+    // soft mode: -c / (1 + 2^((u - tau) * log2(e) / beta)), divided by the
+    // score scale (the scores are scaled with the exponent's argument below)
+    auto soft_bias = [&](float u) -> float {
+        return -a.soft_cs / (1.f + __builtin_amdgcn_exp2f((u - a.soft_tau) * a.soft_k1));
+    };
+    auto compute_block = [&](const char *kb, const char *vb, const int *pb_pos, const float *pb_u, int kind) {
         f32x4 sc[2][PF_PT][2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -478,6 +503,22 @@ prefill_bf16_kernel(PrefillArgs a) {
                     for (int tt = 0; tt < 2; ++tt)
                         sc[hh][ptl][tt] =
                             __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], sc[hh][ptl][tt], 0, 0, 0);
+        }
+        // soft mode: the mask of Eq. (6) on cached keys (kinds 0 and 1)
+        if constexpr (SOFT) {
+            if (kind != 2) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const f32x4 u0 = *(const f32x4 *)&pb_u[32 * hh + 8 * q4];
+                    const f32x4 u1 = *(const f32x4 *)&pb_u[32 * hh + 8 * q4 + 4];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float bias = soft_bias(e < 4 ? u0[e] : u1[e - 4]);
+#pragma unroll
+                        for (int ptl = 0; ptl < PF_PT; ++ptl) sc[hh][ptl][e >> 2][e & 3] += bias;
+                    }
+                }
+            }
         }
         // masks; this lane's keys are 32*hh + 8*q4 + e
         if (kind != 0) {
@@ -581,22 +622,22 @@ prefill_bf16_kernel(PrefillArgs a) {
         for (int i = threadIdx.x; i < np_; i += PF_NT) lds_pt[i] = pt[pg_base + i];
         __syncthreads();  // page ids staged (no direct loads in flight here)
         const int n = wb1 - wb0;
-        issue_direct(wb0, lds_kb0, lds_vb0, lds_pos0);
-        if (n > 1) issue_direct(wb0 + 1, lds_kb1, lds_vb1, lds_pos1);
+        issue_direct(wb0, lds_kb0, lds_vb0, lds_pos0, lds_u0);
+        if (n > 1) issue_direct(wb0 + 1, lds_kb1, lds_vb1, lds_pos1, lds_u1);
         // one block: stage S holds it, stage (S + 2) % 3 receives block jj + 2
-        auto block = [&](int jj, char *kb, char *vb, int *pb, char *kn, char *vn, int *pn) {
+        auto block = [&](int jj, char *kb, char *vb, int *pb, float *ub, char *kn, char *vn, int *pn, float *un) {
             __builtin_amdgcn_sched_barrier(0);  // no scheduling across blocks (register pressure)
             const int j = wb0 + jj;
             if (jj + 1 < n) __builtin_amdgcn_s_waitcnt(WAIT_ONE);
             else __builtin_amdgcn_s_waitcnt(WAIT_ALL);
             __builtin_amdgcn_s_barrier();
-            if (jj + 2 < n) issue_direct(j + 2, kn, vn, pn);
-            compute_block(kb, vb, pb, (j + 1) * PF_KB <= n_full ? 0 : 1);
+            if (jj + 2 < n) issue_direct(j + 2, kn, vn, pn, un);
+            compute_block(kb, vb, pb, ub, (j + 1) * PF_KB <= n_full ? 0 : 1);
         };
         for (int jj = 0; jj < n; jj += 3) {
-            block(jj, lds_kb0, lds_vb0, lds_pos0, lds_kb2, lds_vb2, lds_pos2);
-            if (jj + 1 < n) block(jj + 1, lds_kb1, lds_vb1, lds_pos1, lds_kb0, lds_vb0, lds_pos0);
-            if (jj + 2 < n) block(jj + 2, lds_kb2, lds_vb2, lds_pos2, lds_kb1, lds_vb1, lds_pos1);
+            block(jj, lds_kb0, lds_vb0, lds_pos0, lds_u0, lds_kb2, lds_vb2, lds_pos2, lds_u2);
+            if (jj + 1 < n) block(jj + 1, lds_kb1, lds_vb1, lds_pos1, lds_u1, lds_kb0, lds_vb0, lds_pos0, lds_u0);
+            if (jj + 2 < n) block(jj + 2, lds_kb2, lds_vb2, lds_pos2, lds_u2, lds_kb1, lds_vb1, lds_pos1, lds_u1);
         }
         __syncthreads();  // every stage and lds_pt are free again (nothing in flight)
     }
@@ -607,17 +648,18 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int b0 = nb_d, nb = nb_g + nb_b;
     if (b0 < nb) {
         load_staged(b0);
-        store_staged(b0, lds_kb0, lds_vb0, lds_pos0);
+        store_staged(b0, lds_kb0, lds_vb0, lds_pos0, lds_u0);
     }
     __syncthreads();
     for (int blk = b0; blk < nb; ++blk) {
         const bool odd = ((blk - b0) & 1) != 0;
         if (blk + 1 < nb) {
             load_staged(blk + 1);
-            store_staged(blk + 1, odd ? lds_kb0 : lds_kb1, odd ? lds_vb0 : lds_vb1, odd ? lds_pos0 : lds_pos1);
+            store_staged(blk + 1, odd ? lds_kb0 : lds_kb1, odd ? lds_vb0 : lds_vb1, odd ? lds_pos0 : lds_pos1,
+                         odd ? lds_u0 : lds_u1);
         }
         compute_block(odd ? lds_kb1 : lds_kb0, odd ? lds_vb1 : lds_vb0, odd ? lds_pos1 : lds_pos0,
-                      blk < nb_g ? 1 : 2);
+                      odd ? lds_u1 : lds_u0, blk < nb_g ? 1 : 2);
         __syncthreads();
     }
 
@@ -657,10 +699,17 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
     if (c.dtype == SPKV_BF16 && a.group <= 16) {
         const int rows_wg = (16 * PF_PT / a.group) * PF_NW;
         const dim3 g2((a.n_rows + rows_wg - 1) / rows_wg, c.n_kv);
-        if (c.head_dim == 128)
-            hipLaunchKernelGGL(prefill_bf16_kernel<128>, g2, dim3(PF_NT), 0, s, a);
-        else
-            hipLaunchKernelGGL(prefill_bf16_kernel<64>, g2, dim3(PF_NT), 0, s, a);
+        if (a.soft) {
+            if (c.head_dim == 128)
+                hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), g2, dim3(PF_NT), 0, s, a);
+            else
+                hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), g2, dim3(PF_NT), 0, s, a);
+        } else {
+            if (c.head_dim == 128)
+                hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), g2, dim3(PF_NT), 0, s, a);
+            else
+                hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), g2, dim3(PF_NT), 0, s, a);
+        }
         return hipGetLastError();
     }
     if (c.dtype == SPKV_BF16) {

@@ -3,8 +3,8 @@
 Argument marshalling only: every step of the path runs in the HIP kernels of
 libspkv.so.  torch supplies device memory and the stream.  The functions
 ``spkv_gate``, ``spkv_compact_append``, ``spkv_decode_attn``,
-``spkv_prefill_attn``, ``spkv_decode_step``, ``spkv_cache_rethreshold`` and
-``spkv_head_stats`` mirror the C calls of include/spkv.h one to one and take
+``spkv_prefill_attn`` (``soft=`` for ``spkv_prefill_attn_soft``),
+``spkv_decode_step``, ``spkv_cache_rethreshold`` and ``spkv_head_stats`` mirror the C calls of include/spkv.h one to one and take
 torch tensors in place of pointers.  ``Cache`` and ``GateWeights``
 allocate the buffers the C structs point to.
 
@@ -73,7 +73,7 @@ EXPORTS = [
     "spkv_gate", "spkv_gate_ws_bytes", "spkv_compact_append", "spkv_compact_ws_bytes",
     "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_decode_step", "spkv_decode_step_ws_bytes",
     "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
-    "spkv_head_stats", "spkv_head_stats_ws_bytes",
+    "spkv_head_stats", "spkv_head_stats_ws_bytes", "spkv_prefill_attn_soft",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
     "spkv_last_error", "spkv_version",
 ]
@@ -108,6 +108,8 @@ def load_library(path: str = LIB_PATH):
         "spkv_rethreshold_ws_bytes": ([C], sz),
         "spkv_head_stats": ([vp, vp, i64, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "spkv_head_stats_ws_bytes": ([i64, i32], sz),
+        "spkv_prefill_attn_soft": ([C, i32, i32, vp, i64, vp, vp, i64, i32, i32, f32, f32, f32, f32, vp, vp, vp, sz,
+                                    vp], ctypes.c_int),
         "spkv_cache_bytes": ([C, vp], sz),
         "spkv_cache_reset": ([C, vp], ctypes.c_int),
         "spkv_cache_check": ([C, vp, vp], ctypes.c_int),
@@ -437,8 +439,11 @@ def spkv_prefill_ws_bytes(cache: Cache, n_q_heads: int, n_rows: int) -> int:
 
 
 def spkv_prefill_attn(cache: Cache, b: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos0: int,
-                      scale: float, out=None, lse=None, ws=None, stream=None):
-    """Rows pos0 .. pos0+n-1 of sequence b: q [n, n_q, hd], k/v [n, n_kv, hd].  Returns (out, lse)."""
+                      scale: float, out=None, lse=None, ws=None, stream=None, soft=None):
+    """Rows pos0 .. pos0+n-1 of sequence b: q [n, n_q, hd], k/v [n, n_kv, hd].  Returns (out, lse).
+
+    soft = (tau, beta, c) calls spkv_prefill_attn_soft (the mask of Eq. 5-6
+    on the cached keys, from their stored utilities)."""
     lib = load_library()
     n, nq, hd = q.shape
     if out is None:
@@ -456,9 +461,15 @@ def spkv_prefill_attn(cache: Cache, b: int, q: torch.Tensor, k: torch.Tensor, v:
     ld_kv = _row_stride(k)
     if _row_stride(v) != ld_kv:
         raise ValueError("k and v must share a row stride")
-    _check(lib.spkv_prefill_attn(ctypes.byref(cache.desc()), nq, int(b), _ptr(q), _row_stride(q), _ptr(k),
-                                 _ptr(v), ld_kv, int(pos0), n, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
-                                 ws_bytes, _stream(stream)))
+    if soft is not None:
+        tau, beta, c_mask = soft
+        _check(lib.spkv_prefill_attn_soft(ctypes.byref(cache.desc()), nq, int(b), _ptr(q), _row_stride(q), _ptr(k),
+                                          _ptr(v), ld_kv, int(pos0), n, float(scale), float(tau), float(beta),
+                                          float(c_mask), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+    else:
+        _check(lib.spkv_prefill_attn(ctypes.byref(cache.desc()), nq, int(b), _ptr(q), _row_stride(q), _ptr(k),
+                                     _ptr(v), ld_kv, int(pos0), n, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws_bytes, _stream(stream)))
     return out, lse
 
 
