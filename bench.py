@@ -23,7 +23,9 @@ spkv_decode_step launch without gate -- and gate + kept append of all
 gate, kept append, prefill attention, window append per chunk),
 ``rethreshold_32k`` (one step = rebuild of the decode_32k cache at a higher
 threshold that keeps half of its entries) and ``head_stats_1m`` (one step =
-per-head utility sums and kept counts of 1,048,576 gate rows x 8 heads).
+per-head utility sums and kept counts of 1,048,576 gate rows x 8 heads)
+and ``soft_prefill_16k`` (one step = forward of the soft relaxation of
+Eq. 5-6 over a 16384-token sequence).
 
 Inputs are synthetic (seeded) and resident in HBM before timing starts.
 Decode prefixes are gated and compacted through the same calls during set-up.
@@ -86,7 +88,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
     p.add_argument("--workload", default="decode_32k",
                    choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k",
-                            "head_stats_1m"])
+                            "head_stats_1m", "soft_prefill_16k"])
     p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
     p.add_argument("--step-mode", choices=("auto", "fused", "separate"), default="auto",
@@ -779,6 +781,104 @@ def bench_rethreshold(args, wl):
     }
 
 
+def bench_soft_prefill(args, wl):
+    """Forward of the soft relaxation (SP-KV section 2.1, Eq. 5-6) over one
+    16384-token sequence of the 8B-shaped layer: every token enters the cache
+    with its utility, then spkv_prefill_attn_soft attends over all causal keys
+    (window keys unmasked, the others with c (alpha - 1), beta = 0.01,
+    c = 1e6).  One step = cache reset + GLOBAL append of the 16384 rows +
+    soft prefill attention + WINDOW append."""
+    import torch
+    from learned_kv_cache_sp_amd import inputs, spkv
+    T, nq, nkv, hd, w, P = 16384, wl.n_q, wl.n_kv, wl.head_dim, wl.window, 64
+    G_, W_ = spkv.SPKV_APPEND_GLOBAL, spkv.SPKV_APPEND_WINDOW
+    beta, cmask = 0.01, 1e6
+    per_head = T // P + 2
+    cache = spkv.Cache(1, nkv, hd, w, P, nkv * per_head, per_head, torch.bfloat16, utilities=True)
+    Q = inputs.device_normal((T, nq, hd), wl.seed, inputs.STREAM_Q, torch.bfloat16)
+    K = inputs.device_normal((T, nkv, hd), wl.seed, inputs.STREAM_K, torch.bfloat16)
+    V = inputs.device_normal((T, nkv, hd), wl.seed, inputs.STREAM_V, torch.bfloat16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    u = torch.rand((T, nkv), generator=gen, device="cuda", dtype=torch.float32)
+    keep = torch.ones((T, nkv), dtype=torch.uint8, device="cuda")
+    ro = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    p0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, nq, hd), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, nq), dtype=torch.float32, device="cuda")
+    cws = spkv.workspace(spkv.spkv_compact_ws_bytes(cache, T, T))
+    scale = 1.0 / math.sqrt(hd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        spkv.spkv_cache_reset(cache)
+        spkv.spkv_compact_append(cache, keep, K, V, ro, p0, T, G_, ws=cws, utility=u)
+        if ev is not None:
+            ev[0].record(stream)
+        spkv.spkv_prefill_attn(cache, 0, Q, K, V, 0, scale, out=out, lse=lse, soft=(wl.tau, beta, cmask))
+        if ev is not None:
+            ev[1].record(stream)
+        spkv.spkv_compact_append(cache, None, K, V, ro, p0, T, W_, ws=cws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spkv.spkv_cache_check(cache)
+    ms = e0.elapsed_time(e1) / args.steps
+    a_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    pairs = T * (T + 1) // 2          # every causal (row, key) pair, per query head
+    flops = pairs * nq * 4 * hd        # q.k and p.v, 2 flops per multiply-add
+    a_s = float(np.mean(a_ms)) * 1e-3
+    achieved = flops / a_s / 1e12
+    return {
+        "metric": "soft-mask forward tokens/s (Eq. 5-6, 8B shape, 16K tokens)", "value": T / (ms * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "soft_prefill_16k", "tokens": T, "n_q_heads": nq, "n_kv_heads": nkv,
+                   "head_dim": hd, "window": w, "tau": wl.tau, "beta": beta, "c": cmask,
+                   "step": "spkv_cache_reset + spkv_compact_append(GLOBAL, keep all, utilities) + "
+                           "spkv_prefill_attn_soft + spkv_compact_append(WINDOW)"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true> (spkv_prefill_attn_soft)",
+                     "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
+                     "traffic": None, "flops_per_launch": flops, "launch_us": _stats_us(a_ms)},
+    }
+
+
+def cpu_baseline_soft(wl, budget_s: float) -> dict:
+    """The oracle's soft-mask attention for sampled rows of a 16384-token
+    sequence (all 32 query heads per row), timed for about budget_s."""
+    import oracle
+    from learned_kv_cache_sp_amd import inputs
+    oracle.build(force=False)
+    T, nq, nkv, hd = 16384, wl.n_q, wl.n_kv, wl.head_dim
+    th = _threads()
+    K = inputs.normal((T, nkv, hd), 1, 2, dtype="bf16")
+    V = inputs.normal((T, nkv, hd), 1, 3, dtype="bf16")
+    u = np.random.default_rng(1).random((T, nkv)).astype(np.float32)
+    rows = done_pairs = 0
+    t0 = time.perf_counter()
+    r = np.random.default_rng(2)
+    while time.perf_counter() - t0 < budget_s:
+        t = int(r.integers(0, T))
+        q = inputs.normal((1, nq, hd), 1, 10 + rows, dtype="bf16")
+        oracle.soft_attention(q, [t], K, V, u, wl.window, wl.tau, 0.01, 1e6, threads=th)
+        rows += 1
+        done_pairs += t + 1
+    el = time.perf_counter() - t0
+    # tokens/s of the whole forward at the sampled rate of (row, key) pairs
+    pairs_seq = T * (T + 1) / 2
+    return {"value": done_pairs / el / pairs_seq * T, "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "sample": f"{rows} random rows of a {T}-token sequence, all {nq} heads, {el:.1f} s "
+                      f"(scaled by the pairs of the whole forward)"}
+
+
 HEAD_STATS_ROWS, HEAD_STATS_KV = 1 << 20, 8
 
 
@@ -991,7 +1091,10 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    if args.workload == "head_stats_1m":
+    if args.workload == "soft_prefill_16k":
+        wl = inputs.WORKLOADS["prefill_64k"]
+        res = bench_soft_prefill(args, wl)
+    elif args.workload == "head_stats_1m":
         wl = None
         res = bench_head_stats(args)
     elif args.workload == "rethreshold_32k":
@@ -1012,7 +1115,9 @@ def main():
         res["hbm_ceiling"] = hbm_ceiling(torch)
 
     if not args.no_cpu_baseline:
-        if args.workload == "head_stats_1m":
+        if args.workload == "soft_prefill_16k":
+            res["cpu_baseline"] = cpu_baseline_soft(wl, args.cpu_budget)
+        elif args.workload == "head_stats_1m":
             res["cpu_baseline"] = cpu_baseline_head_stats(args.cpu_budget)
         elif args.workload == "rethreshold_32k":
             res["cpu_baseline"] = cpu_baseline_rethreshold(wl, args.cpu_budget)

@@ -208,6 +208,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) int lds_pos0[PF_KB], lds_pos1[PF_KB], lds_pos2[PF_KB];
     constexpr int UN = SOFT ? PF_KB : 4;  // stored utilities of a block (soft mode)
     __shared__ __attribute__((aligned(16))) float lds_u0[UN], lds_u1[UN], lds_u2[UN];
+    __shared__ __attribute__((aligned(16))) float lds_bias[SOFT ? PF_NW : 1][UN];  // per wave: a block's key scores
     __shared__ int lds_pt[PF_PTMAX];
     __shared__ int lds_cnt[2];
 
@@ -504,16 +505,21 @@ prefill_bf16_kernel(PrefillArgs a) {
                         sc[hh][ptl][tt] =
                             __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], sc[hh][ptl][tt], 0, 0, 0);
         }
-        // soft mode: the mask of Eq. (6) on cached keys (kinds 0 and 1)
+        // soft mode: the mask of Eq. (6) on cached keys (kinds 0 and 1).
+        // Lane l forms the added score of key l once and parks it in the
+        // wave's LDS row (LDS operations of one wave complete in order);
+        // every lane then reads the 16 it needs.
         if constexpr (SOFT) {
             if (kind != 2) {
+                float *wb = lds_bias[wave];
+                wb[lane] = soft_bias(pb_u[lane]);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const f32x4 u0 = *(const f32x4 *)&pb_u[32 * hh + 8 * q4];
-                    const f32x4 u1 = *(const f32x4 *)&pb_u[32 * hh + 8 * q4 + 4];
+                    const f32x4 b0 = *(const f32x4 *)&wb[32 * hh + 8 * q4];
+                    const f32x4 b1 = *(const f32x4 *)&wb[32 * hh + 8 * q4 + 4];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float bias = soft_bias(e < 4 ? u0[e] : u1[e - 4]);
+                        const float bias = e < 4 ? b0[e] : b1[e - 4];
 #pragma unroll
                         for (int ptl = 0; ptl < PF_PT; ++ptl) sc[hh][ptl][e >> 2][e & 3] += bias;
                     }
