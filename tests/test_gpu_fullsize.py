@@ -167,3 +167,85 @@ def test_prefill_64k_full_size_sampled_rows():
     print(f"[prefill_64k full] rows={len(sample)} max|dout|={tl.max_abs(out, ro_):.2e} "
           f"max|dlse|={tl.max_abs(lse, rl_):.2e}")
     assert tl.max_abs(out, ro_) <= tl.TOL_PREFILL and tl.max_abs(lse, rl_) <= tl.TOL_REGRESS
+
+
+def test_rethreshold_decode_32k_full_size():
+    # the decode_32k cache (8 x 32768 tokens, 8 key heads, 20 % kept) with
+    # generator utilities, rebuilt at a threshold keeping about half; every
+    # list's positions exact against the oracle (O2 at tau, then O5 at tau2),
+    # keys, values and utilities of sampled lists exact
+    wl = inputs.WORKLOADS["decode_32k"]
+    B, T, nkv, hd, P = wl.batch, wl.context, wl.n_kv, wl.head_dim, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    tau = 0.8  # 20 % of uniform utilities pass
+    u = torch.rand((B * T, nkv), generator=gen, device="cuda", dtype=torch.float32)
+    z = (u >= tau).to(torch.uint8)
+    K = inputs.device_normal((B * T, nkv, hd), 17, inputs.STREAM_K, torch.bfloat16)
+    V = inputs.device_normal((B * T, nkv, hd), 17, inputs.STREAM_V, torch.bfloat16)
+    per_head = int(T * 0.25 / P) + 4
+    src = spkv.Cache(B, nkv, hd, wl.window, P, B * nkv * per_head, per_head, torch.bfloat16, utilities=True)
+    dst = spkv.Cache(B, nkv, hd, wl.window, P, B * nkv * per_head, per_head, torch.bfloat16, utilities=True)
+    ro = torch.arange(0, B * T + 1, T, dtype=torch.int32, device="cuda")
+    spkv.spkv_compact_append(src, z, K, V, ro, torch.zeros(B, dtype=torch.int32, device="cuda"), T, G_ | W_,
+                             utility=u)
+    tau2 = 0.9
+    spkv.spkv_cache_rethreshold(src, dst, tau2)
+    torch.cuda.synchronize()
+    assert spkv.spkv_cache_check(src) == 0 and spkv.spkv_cache_check(dst) == 0
+    uh = u.cpu().numpy()
+    for b in range(B):
+        ub = uh[b * T:(b + 1) * T]
+        for g in range(nkv):
+            kept = oracle.compact((ub[:, g:g + 1] >= np.float32(tau)).astype(np.uint8))[0]
+            rows = kept[oracle.rethreshold(ub[kept, g], float(np.float32(tau2)))]
+            pos = dst.read_head(b, g)[2].cpu().numpy()
+            np.testing.assert_array_equal(pos, rows, err_msg=f"b={b} g={g}")
+            if (b * nkv + g) % 13 == 0:
+                k, v, _ = dst.read_head(b, g)
+                sel = torch.from_numpy(b * T + rows).cuda()
+                assert torch.equal(k, K[sel, g]) and torch.equal(v, V[sel, g])
+                assert torch.equal(dst.read_head_u(b, g), u[sel, g])
+
+
+def test_head_stats_full_size():
+    # 1,048,576 rows x 8 heads, the benchmark's shape and generator
+    n, nkv = 1 << 20, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    u = torch.rand((n, nkv), generator=gen, device="cuda", dtype=torch.float32)
+    z = (torch.rand((n, nkv), generator=gen, device="cuda") < 0.2).to(torch.uint8)
+    us, kp = spkv.spkv_head_stats(u, z)
+    ru, rk = oracle.head_stats(u.cpu().numpy(), z.cpu().numpy())
+    np.testing.assert_array_equal(kp.cpu().numpy(), rk)
+    np.testing.assert_allclose(us.cpu().numpy(), ru, rtol=1e-12)
+
+
+def test_soft_prefill_16k_full_size_sampled_rows():
+    # the soft_prefill_16k workload (16384 tokens, 8B layer, beta 0.01,
+    # c 1e6, every token cached), checked on sampled rows against O7
+    wl = inputs.WORKLOADS["prefill_64k"]
+    T, nq, nkv, hd, w, P = 16384, wl.n_q, wl.n_kv, wl.head_dim, wl.window, 64
+    per_head = T // P + 2
+    cache = spkv.Cache(1, nkv, hd, w, P, nkv * per_head, per_head, torch.bfloat16, utilities=True)
+    Q = inputs.device_normal((T, nq, hd), 23, inputs.STREAM_Q, torch.bfloat16)
+    K = inputs.device_normal((T, nkv, hd), 23, inputs.STREAM_K, torch.bfloat16)
+    V = inputs.device_normal((T, nkv, hd), 23, inputs.STREAM_V, torch.bfloat16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(23)
+    u = torch.rand((T, nkv), generator=gen, device="cuda", dtype=torch.float32)
+    ro = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    p0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    spkv.spkv_compact_append(cache, torch.ones((T, nkv), dtype=torch.uint8, device="cuda"), K, V, ro, p0, T, G_,
+                             utility=u)
+    scale = 1.0 / math.sqrt(hd)
+    out, lse = spkv.spkv_prefill_attn(cache, 0, Q, K, V, 0, scale, soft=(wl.tau, 0.01, 1e6))
+    torch.cuda.synchronize()
+    rows = np.concatenate([[0, 1, w - 1, w, w + 1, T - 1], np.random.default_rng(3).integers(0, T, 10)])
+    Qh, Kh, Vh, uh = host_f32(Q), host_f32(K), host_f32(V), u.cpu().numpy()
+    ro_, rl = oracle.soft_attention(Qh[rows], rows, Kh, Vh, uh, w, wl.tau, 0.01, 1e6, scale,
+                                    threads=tl.oracle_threads())
+    o = out.cpu().numpy()[rows]
+    l = lse.cpu().numpy()[rows]
+    assert tl.max_abs(o, ro_) < tl.TOL_PREFILL
+    assert tl.max_abs(l, rl) < tl.TOL_PREFILL
