@@ -318,7 +318,8 @@ size_t spkv_prefill_ws_bytes(const spkv_cache *c, int32_t n_q_heads,
  *   (appended with keep = 1 and its utility), this is the attention over all
  *   causal keys with the mask of Eq. (6).  Forward only.
  *   tau (finite), beta > 0 (the pages use 0.01), c_mask >= 0 (the pages use
- *   1e6); other arguments and call order as for spkv_prefill_attn.
+ *   1e6), with log2(e) / beta and c_mask / scale finite in float; other
+ *   arguments and call order as for spkv_prefill_attn.
  *   Utilities must not be NaN.
  * Supported: a bf16 cache, G <= 16.
  */

@@ -445,6 +445,10 @@ int spkv_prefill_attn_soft(const spkv_cache *c, int32_t n_q_heads, int32_t b, co
     if (!std::isfinite(tau) || !(beta > 0.f) || !std::isfinite(beta) || !(c_mask >= 0.f) || !std::isfinite(c_mask))
         return fail(SPKV_E_INVALID, "soft mask: tau finite, beta > 0 and c >= 0 finite");
     if (!std::isfinite(scale) || scale == 0.f) return fail(SPKV_E_INVALID, "scale not finite or zero");
+    // the kernel works with log2(e) / beta and c / scale: both must be finite
+    if (!std::isfinite((float)(1.4426950408889634 / (double)beta)) ||
+        !std::isfinite((float)((double)c_mask / (double)scale)))
+        return fail(SPKV_E_INVALID, "soft mask: beta too small or c / scale too large for float");
     return prefill_common(c, n_q_heads, b, q, ld_q, k, v, ld_kv, pos0, n_rows, scale, out, lse, ws, ws_bytes,
                           stream, SoftArgs{true, tau, beta, c_mask});
 }

@@ -349,6 +349,9 @@ def spkv_compact_append(cache: Cache, keep, k: torch.Tensor, v: torch.Tensor, ro
     ld = _row_stride(k)
     if _row_stride(v) != ld:
         raise ValueError("k and v must share a row stride")
+    for name, t in (("keep", keep), ("utility", utility)):
+        if t is not None and (tuple(t.shape) != (n, cache.n_kv) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [{n}, {cache.n_kv}] tensor")
     need = spkv_compact_ws_bytes(cache, n, max_rows_per_seq)
     if ws is None and need:
         ws = workspace(need, k.device)

@@ -75,6 +75,7 @@ def test_soft_prefill_arguments():
     with pytest.raises(spkv.SpkvError):  # no stored utilities
         spkv.spkv_prefill_attn(cache, 0, q, k, k, 0, 0.1, soft=(0.5, 0.01, 1e6))
     cache = spkv.Cache(1, 2, 128, 128, 64, 8, 4, torch.bfloat16, utilities=True)
-    for bad in ((0.5, 0.0, 1e6), (0.5, 0.01, -1.0), (float("nan"), 0.01, 1.0), (0.5, float("inf"), 1.0)):
+    for bad in ((0.5, 0.0, 1e6), (0.5, 0.01, -1.0), (float("nan"), 0.01, 1.0), (0.5, float("inf"), 1.0),
+                (0.5, 1e-45, 1.0), (0.5, 0.01, 3e38)):
         with pytest.raises(spkv.SpkvError):
             spkv.spkv_prefill_attn(cache, 0, q, k, k, 0, 0.1, soft=bad)
