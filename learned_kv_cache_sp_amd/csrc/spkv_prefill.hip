@@ -214,7 +214,15 @@ prefill_bf16_kernel(PrefillArgs a) {
 
     const CacheView &c = a.c;
     const int G = a.group;
-    const int g = blockIdx.y;
+    // Workgroups are dealt to the 8 XCDs in launch order (linear id mod 8).
+    // When n_kv divides 8, the linear id is read as (row tile, key head) with
+    // the head fastest, so every workgroup of head g runs on the XCDs
+    // congruent to g: the workgroups that stream the same cached blocks at
+    // about the same time share an L2.
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const bool xcd_map = (8 % a.c.n_kv) == 0;
+    const int g = xcd_map ? lin % a.c.n_kv : (int)blockIdx.y;
+    const int tile = xcd_map ? lin / a.c.n_kv : (int)blockIdx.x;
     const int b = a.b;
     const int bg = b * c.n_kv + g;
     const int w = c.window;
@@ -222,7 +230,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int rows_wave = (16 * PF_PT) / G;           // query positions per wave
     const int rows_wg = rows_wave * PF_NW;
     // the last row tiles see the most keys: hand them out first
-    const int r_base = (gridDim.x - 1 - blockIdx.x) * rows_wg;  // chunk-relative first row
+    const int r_base = (gridDim.x - 1 - tile) * rows_wg;  // chunk-relative first row
     const int t_min = a.pos0 + r_base;
     const int t_max = a.pos0 + min(a.n_rows, r_base + rows_wg) - 1;
     const int32_t *pt = c.page_table + (int64_t)bg * c.max_pages;
