@@ -153,6 +153,22 @@ def _need_gpu(*ts):
             raise ValueError("libspkv works on device tensors only")
 
 
+def _expect(name: str, t, shape, dtype=None, packed: bool = True):
+    """Raise ValueError unless t has `shape` (and `dtype`).  packed: the whole
+    tensor is contiguous; otherwise only its rows (dim 0 may be strided, as
+    for arguments passed with a row stride)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if packed and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not packed and t.shape[0] > 0 and t.dim() > 1 and not t[0].is_contiguous():
+        raise ValueError(f"{name} rows must be contiguous")
+
+
 def _dtype_code(dt) -> int:
     if dt == torch.bfloat16:
         return SPKV_BF16
@@ -369,16 +385,14 @@ def spkv_decode_attn(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: floa
                      ws=None, stream=None):
     """One query per sequence: q [batch, n_q, hd], t [batch] int32.  Returns (out, lse)."""
     lib = load_library()
-    B, nq, hd = q.shape
+    B, nq, hd = _decode_shapes(cache, q, t)
     if out is None:
         out = torch.empty((B, nq, hd), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+    _expect("out", out, (B, nq, hd), torch.float32)
+    _expect("lse", lse, (B, nq), torch.float32)
     _need_gpu(q, t, out, lse)
-    if q.dtype != cache.dtype:
-        raise ValueError("q dtype differs from the cache")
-    if t.dtype != torch.int32:
-        raise ValueError("t must be int32")
     need = spkv_decode_ws_bytes(cache, nq)
     if ws is None and need:
         ws = workspace(need, q.device)
@@ -386,6 +400,19 @@ def spkv_decode_attn(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: floa
     _check(lib.spkv_decode_attn(ctypes.byref(cache.desc()), nq, _ptr(q), _row_stride(q), _ptr(t),
                                 float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
     return out, lse
+
+
+def _decode_shapes(cache: Cache, q: torch.Tensor, t: torch.Tensor):
+    """q [cache.batch, n_q, head_dim] in the cache dtype with packed rows, t [cache.batch] int32;
+    returns (batch, n_q, head_dim).  The kernels read and write every sequence of the cache."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [batch, n_q, head_dim], got shape {tuple(q.shape)}")
+    B, nq = cache.batch, q.shape[1]
+    if nq < 1 or nq % cache.n_kv:
+        raise ValueError(f"n_q = {nq} is not a multiple of n_kv = {cache.n_kv}")
+    _expect("q", q, (B, nq, cache.head_dim), cache.dtype, packed=False)
+    _expect("t", t, (B,), torch.int32)
+    return B, nq, cache.head_dim
 
 
 def spkv_decode_step_ws_bytes(cache: Cache, weights: GateWeights | None, n_q_heads: int) -> int:
@@ -401,28 +428,31 @@ def spkv_decode_step(cache: Cache, weights: GateWeights | None, hidden, tau: flo
     hidden [batch, d_model], k / v [batch, n_kv, hd], q [batch, n_q, hd], t [batch] int32.
     Returns (utility, keep, out, lse) (utility and keep None without a gate)."""
     lib = load_library()
-    B, nq, hd = q.shape
+    B, nq, hd = _decode_shapes(cache, q, t)
     dev = q.device
     gated = weights is not None
+    nkv = cache.n_kv
     if gated:
-        nkv = weights.desc().n_kv
+        if weights.w2.shape[0] != nkv:
+            raise ValueError(f"the gate has {weights.w2.shape[0]} outputs, the cache {nkv} key heads")
         if keep is None:
             keep = torch.empty((B, nkv), dtype=torch.uint8, device=dev)
         if utility is None:
             utility = torch.empty((B, nkv), dtype=torch.float32, device=dev)
+        _expect("hidden", hidden, (B, weights.w1.shape[1]), weights.w1.dtype, packed=False)
+        _expect("keep", keep, (B, nkv), torch.uint8)
+        _expect("utility", utility, (B, nkv), torch.float32)
     else:
         utility = keep = hidden = None
     if out is None:
         out = torch.empty((B, nq, hd), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, nq), dtype=torch.float32, device=dev)
+    _expect("k", k, (B, nkv, hd), cache.dtype, packed=False)
+    _expect("v", v, (B, nkv, hd), cache.dtype, packed=False)
+    _expect("out", out, (B, nq, hd), torch.float32)
+    _expect("lse", lse, (B, nq), torch.float32)
     _need_gpu(hidden, k, v, q, t, keep, utility, out, lse)
-    if gated and hidden.dtype != weights.w1.dtype:
-        raise ValueError("hidden and w1 dtypes differ")
-    if q.dtype != cache.dtype or k.dtype != cache.dtype or v.dtype != cache.dtype:
-        raise ValueError("q / k / v dtype differs from the cache")
-    if t.dtype != torch.int32:
-        raise ValueError("t must be int32")
     ld = _row_stride(k)
     if _row_stride(v) != ld:
         raise ValueError("k and v must share a row stride")
@@ -448,15 +478,23 @@ def spkv_prefill_attn(cache: Cache, b: int, q: torch.Tensor, k: torch.Tensor, v:
     soft = (tau, beta, c) calls spkv_prefill_attn_soft (the mask of Eq. 5-6
     on the cached keys, from their stored utilities)."""
     lib = load_library()
+    if q.dim() != 3:
+        raise ValueError(f"q must be [n_rows, n_q, head_dim], got shape {tuple(q.shape)}")
     n, nq, hd = q.shape
+    if not 0 <= int(b) < cache.batch:
+        raise ValueError(f"sequence {b} is outside the cache's batch of {cache.batch}")
+    if nq < 1 or nq % cache.n_kv:
+        raise ValueError(f"n_q = {nq} is not a multiple of n_kv = {cache.n_kv}")
+    _expect("q", q, (n, nq, cache.head_dim), cache.dtype, packed=False)
+    _expect("k", k, (n, cache.n_kv, cache.head_dim), cache.dtype, packed=False)
+    _expect("v", v, (n, cache.n_kv, cache.head_dim), cache.dtype, packed=False)
     if out is None:
         out = torch.empty((n, nq, hd), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((n, nq), dtype=torch.float32, device=q.device)
+    _expect("out", out, (n, nq, hd), torch.float32)
+    _expect("lse", lse, (n, nq), torch.float32)
     _need_gpu(q, k, v, out, lse)
-    for x in (q, k, v):
-        if x.dtype != cache.dtype:
-            raise ValueError("q / k / v dtype differs from the cache")
     need = spkv_prefill_ws_bytes(cache, nq, n)
     if ws is None and need:
         ws = workspace(need, q.device)
