@@ -232,6 +232,31 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q,
 size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads);
 
 /*
+ * spkv_decode_attn_noalloc -- spkv_decode_attn without a workspace argument,
+ *   for callers that cannot allocate device memory (code under HIP graph
+ *   capture, serving loops or harnesses that forbid allocation).  Same
+ *   arguments, results and errors as spkv_decode_attn (the same kernel runs;
+ *   outputs are bit-identical for the same inputs), but the split-K partials
+ *   and arrival counters live in a built-in device array of 4 MiB per GPU,
+ *   held from the first call on that GPU until the process ends.  The call
+ *   allocates nothing.
+ *   Limit: the bf16 path needs 512.5 KiB of counters plus
+ *   (compute units + batch * n_kv) * (G * head_dim + 32) * 4 bytes of
+ *   partials (about 1.2 MiB for batch 8, 8 key heads, G 4, head_dim 128 on
+ *   256 compute units); a cache beyond 4 MiB is refused with
+ *   SPKV_E_WORKSPACE before any launch.  f32 caches need no scratch.
+ *   The first call on a GPU queues a zero fill of the array on `stream`
+ *   ahead of its launch; every launch leaves the counters at zero again.
+ *   All calls on one GPU share the array: calls that overlap in time on one
+ *   GPU (other streams, other threads) race and give wrong results; queue
+ *   them on one stream or order them.
+ */
+int spkv_decode_attn_noalloc(const spkv_cache *c, int32_t n_q_heads,
+                             const void *q, int64_t ld_q, const int32_t *t,
+                             float scale, float *out, float *lse,
+                             void *stream);
+
+/*
  * spkv_decode_step -- one whole decode step of one layer in one launch:
  *   spkv_gate on the new token's hidden state of every sequence (Eq. 1-2),
  *   spkv_compact_append of its key/value row with

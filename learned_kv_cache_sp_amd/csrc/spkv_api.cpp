@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "spkv.h"
 #include "spkv_internal.h"
@@ -72,6 +73,45 @@ int check_ld(int64_t ld, int64_t min_ld, int dtype, const char *what) {
 
 // persistent grid for the decode kernel: CUs x resident workgroups per CU
 int g_decode_grid = 0;
+
+// Scratch of spkv_decode_attn_noalloc, for callers that cannot allocate
+// (code under graph capture, serving loops that forbid it).  Each GPU the
+// library runs on holds its own copy until the process ends; host code only
+// ever uses the device address hipGetSymbolAddress gives for it.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+__global__ void scratch_zero_kernel(uint4 *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Device address of the current device's scratch.  The first call on a
+// device looks it up and queues a zero fill of it on `stream` (the decode
+// kernel's counters must start at zero; every launch leaves them at zero).
+int noalloc_scratch(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SPKV_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        hipLaunchKernelGGL(scratch_zero_kernel, dim3(256), dim3(256), 0, stream, (uint4 *)p,
+                           kNoAllocScratchBytes / sizeof(uint4));
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch zero fill");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPKV_OK;
+}
 
 }  // namespace
 
@@ -209,9 +249,9 @@ size_t spkv_decode_ws_bytes(const spkv_cache *c, int32_t n_q_heads) {
     return spkv::decode_ws_bytes(c, n_q_heads, decode_grid(), nullptr);
 }
 
-int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int64_t ld_q,
-                     const int32_t *t, float scale, float *out, float *lse, void *ws,
-                     size_t ws_bytes, void *stream) {
+static int decode_attn_impl(const spkv_cache *c, int32_t n_q_heads, const void *q, int64_t ld_q,
+                            const int32_t *t, float scale, float *out, float *lse, void *ws,
+                            size_t ws_bytes, bool noalloc, void *stream) {
     if (int r = check_cache(c)) return r;
     if (n_q_heads < 1 || n_q_heads % c->n_kv) return fail(SPKV_E_INVALID, "n_q_heads %d vs n_kv %d", n_q_heads, c->n_kv);
     const int G = n_q_heads / c->n_kv;
@@ -224,9 +264,22 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int6
     int max_items = 0;
     const int grid = decode_grid();
     const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items);
-    if (need && (!ws || ws_bytes < need))
-        return fail(SPKV_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
-    if (need && !aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
+    float *part = nullptr;
+    if (noalloc) {
+        size_t part_off = 0;
+        const size_t need_s = need ? spkv::decode_noalloc_layout(c, n_q_heads, grid, &part_off) : 0;
+        if (need_s > kNoAllocScratchBytes)
+            return fail(SPKV_E_WORKSPACE, "decode needs %zu bytes of scratch; the built-in scratch holds %zu "
+                                          "(use spkv_decode_attn with a workspace)", need_s, kNoAllocScratchBytes);
+        if (need_s) {
+            if (int r = noalloc_scratch((hipStream_t)stream, &ws)) return r;
+            part = (float *)((char *)ws + part_off);
+        }
+    } else {
+        if (need && (!ws || ws_bytes < need))
+            return fail(SPKV_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
+        if (need && !aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
+    }
     spkv::DecodeArgs a = {};
     a.c = spkv::make_view(c);
     a.n_q = n_q_heads;
@@ -238,11 +291,23 @@ int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int6
     a.out = out;
     a.lse = lse;
     a.ws = (char *)ws;
+    a.part = part;
     a.grid = grid;
     a.max_items = max_items;
     hipError_t e = spkv::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return SPKV_OK;
+}
+
+int spkv_decode_attn(const spkv_cache *c, int32_t n_q_heads, const void *q, int64_t ld_q,
+                     const int32_t *t, float scale, float *out, float *lse, void *ws,
+                     size_t ws_bytes, void *stream) {
+    return decode_attn_impl(c, n_q_heads, q, ld_q, t, scale, out, lse, ws, ws_bytes, false, stream);
+}
+
+int spkv_decode_attn_noalloc(const spkv_cache *c, int32_t n_q_heads, const void *q, int64_t ld_q,
+                             const int32_t *t, float scale, float *out, float *lse, void *stream) {
+    return decode_attn_impl(c, n_q_heads, q, ld_q, t, scale, out, lse, nullptr, 0, true, stream);
 }
 
 // ----------------------------------------------------------------------------

@@ -408,7 +408,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     int32_t *gate_cnt = cnt + (size_t)BG * CNT_STRIDE;  // fused: gate units stored
     int32_t *plan_cnt = gate_cnt + 64;                  // fused: workgroups that read the lengths
     float *gshare = (float *)(a.ws + ws_header_bytes(BG));
-    float *part = (float *)(a.ws + ws_header_bytes(BG) + fb);
+    float *part = a.part ? a.part : (float *)(a.ws + ws_header_bytes(BG) + fb);
     // attention workgroups (the fused step keeps the last one for its finisher)
     const int n_att = FUSED ? (int)gridDim.x - 1 : (int)gridDim.x;
 
@@ -933,6 +933,15 @@ size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_ou
     if (max_items_out) *max_items_out = max_slots;
     return ws_header_bytes(BG) + fused_bytes(fused_model, fused_hidden) +
            (size_t)max_slots * rec_floats(G, c->head_dim) * sizeof(float);
+}
+
+size_t decode_noalloc_layout(const spkv_cache *c, int n_q, int grid, size_t *part_offset) {
+    // counters for the largest batch * n_kv first, so that they sit at the
+    // same place whatever the cache: every launch leaves them at zero
+    const size_t hdr = round256(ws_header_bytes(MAX_BG));
+    if (part_offset) *part_offset = hdr;
+    const int BG = c->batch * c->n_kv;
+    return hdr + (size_t)(grid + BG) * rec_floats(n_q / c->n_kv, c->head_dim) * sizeof(float);
 }
 
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid) {

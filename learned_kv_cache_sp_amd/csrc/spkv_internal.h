@@ -100,6 +100,7 @@ struct DecodeArgs {
     char *ws;
     int32_t grid;       // persistent workgroups
     int32_t max_items;  // partial slots in ws
+    float *part;        // split-K partials; NULL: in ws after the counters (and the fused gate's sums)
     // fused step (spkv_decode_step): the gate of the batch's new rows and
     // their append run inside the attention launch
     int32_t share_cut;  // fused step: attention steps fewer for the workgroups that run a gate item
@@ -111,6 +112,9 @@ struct DecodeArgs {
 // fused_model / fused_hidden: the gate's d_model and d_hidden for spkv_decode_step (0: plain attention)
 size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_model = 0,
                        int fused_hidden = 0);
+// bf16 scratch of spkv_decode_attn_noalloc: counters laid out for the largest
+// batch * n_kv, then the partials at *part_offset; returns the bytes needed
+size_t decode_noalloc_layout(const spkv_cache *c, int n_q, int grid, size_t *part_offset);
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid);
 int decode_blocks_per_cu();
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

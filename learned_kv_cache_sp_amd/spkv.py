@@ -71,7 +71,7 @@ class CacheDesc(ctypes.Structure):
 
 EXPORTS = [
     "spkv_gate", "spkv_gate_ws_bytes", "spkv_compact_append", "spkv_compact_ws_bytes",
-    "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_decode_step", "spkv_decode_step_ws_bytes",
+    "spkv_decode_attn", "spkv_decode_ws_bytes", "spkv_decode_attn_noalloc", "spkv_decode_step", "spkv_decode_step_ws_bytes",
     "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
     "spkv_head_stats", "spkv_head_stats_ws_bytes", "spkv_prefill_attn_soft",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
@@ -98,6 +98,7 @@ def load_library(path: str = LIB_PATH):
         "spkv_compact_ws_bytes": ([C, i32, i32], sz),
         "spkv_decode_attn": ([C, i32, vp, i64, vp, f32, vp, vp, vp, sz, vp], ctypes.c_int),
         "spkv_decode_ws_bytes": ([C, i32], sz),
+        "spkv_decode_attn_noalloc": ([C, i32, vp, i64, vp, f32, vp, vp, vp], ctypes.c_int),
         "spkv_decode_step": ([C, G, i32, vp, i64, f32, vp, vp, i64, vp, i64, vp, f32, vp, vp, vp, vp, vp, sz, vp],
                              ctypes.c_int),
         "spkv_decode_step_ws_bytes": ([C, G, i32], sz),
@@ -399,6 +400,24 @@ def spkv_decode_attn(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: floa
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.spkv_decode_attn(ctypes.byref(cache.desc()), nq, _ptr(q), _row_stride(q), _ptr(t),
                                 float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def spkv_decode_attn_noalloc(cache: Cache, q: torch.Tensor, t: torch.Tensor, scale: float, out=None, lse=None,
+                             stream=None):
+    """spkv_decode_attn with the library's built-in scratch in place of a workspace
+    (the C call allocates nothing; calls on one GPU must not overlap).  Returns (out, lse)."""
+    lib = load_library()
+    B, nq, hd = _decode_shapes(cache, q, t)
+    if out is None:
+        out = torch.empty((B, nq, hd), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+    _expect("out", out, (B, nq, hd), torch.float32)
+    _expect("lse", lse, (B, nq), torch.float32)
+    _need_gpu(q, t, out, lse)
+    _check(lib.spkv_decode_attn_noalloc(ctypes.byref(cache.desc()), nq, _ptr(q), _row_stride(q), _ptr(t),
+                                        float(scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 
