@@ -261,19 +261,14 @@ static int decode_attn_impl(const spkv_cache *c, int32_t n_q_heads, const void *
     if (!aligned16(q)) return fail(SPKV_E_INVALID, "q not 16-byte aligned");
     if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
     if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
-    int max_items = 0;
     const int grid = decode_grid();
-    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items);
-    float *part = nullptr;
+    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, nullptr, 0, 0, noalloc);
     if (noalloc) {
-        size_t part_off = 0;
-        const size_t need_s = need ? spkv::decode_noalloc_layout(c, n_q_heads, grid, &part_off) : 0;
-        if (need_s > kNoAllocScratchBytes)
+        if (need > kNoAllocScratchBytes)
             return fail(SPKV_E_WORKSPACE, "decode needs %zu bytes of scratch; the built-in scratch holds %zu "
-                                          "(use spkv_decode_attn with a workspace)", need_s, kNoAllocScratchBytes);
-        if (need_s) {
+                                          "(use spkv_decode_attn with a workspace)", need, kNoAllocScratchBytes);
+        if (need) {
             if (int r = noalloc_scratch((hipStream_t)stream, &ws)) return r;
-            part = (float *)((char *)ws + part_off);
         }
     } else {
         if (need && (!ws || ws_bytes < need))
@@ -290,10 +285,8 @@ static int decode_attn_impl(const spkv_cache *c, int32_t n_q_heads, const void *
     a.scale = scale;
     a.out = out;
     a.lse = lse;
-    a.ws = (char *)ws;
-    a.part = part;
     a.grid = grid;
-    a.max_items = max_items;
+    spkv::decode_ws_assign(a, c, n_q_heads, grid, 0, 0, noalloc, (char *)ws);
     hipError_t e = spkv::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return SPKV_OK;
@@ -340,8 +333,7 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
         if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
         if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
         const int grid = decode_grid();
-        int max_items = 0;
-        const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items);
+        const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, nullptr);
         if (!ws || ws_bytes < need) return fail(SPKV_E_WORKSPACE, "decode step workspace %zu < %zu bytes", ws_bytes, need);
         if (!aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
         spkv::DecodeArgs a = {};
@@ -354,9 +346,8 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
         a.scale = scale;
         a.out = out;
         a.lse = lse;
-        a.ws = (char *)ws;
         a.grid = grid;
-        a.max_items = max_items;
+        spkv::decode_ws_assign(a, c, n_q_heads, grid, 0, 0, false, (char *)ws);
         a.k_new = (const char *)k;
         a.v_new = (const char *)v;
         a.ld_new = ld_kv;
@@ -389,8 +380,7 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
     if (int r = check_ld(ld_q, (int64_t)n_q_heads * c->head_dim, c->dtype, "ld_q")) return r;
     if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
     if (!std::isfinite(scale)) return fail(SPKV_E_INVALID, "scale not finite");
-    int max_items = 0;
-    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, &max_items, g->d_model, g->d_hidden);
+    const size_t need = spkv::decode_ws_bytes(c, n_q_heads, grid, nullptr, g->d_model, g->d_hidden);
     if (!ws || ws_bytes < need) return fail(SPKV_E_WORKSPACE, "decode step workspace %zu < %zu bytes", ws_bytes, need);
     if (!aligned16(ws)) return fail(SPKV_E_INVALID, "ws not 16-byte aligned");
     spkv::DecodeArgs a = {};
@@ -403,9 +393,8 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
     a.scale = scale;
     a.out = out;
     a.lse = lse;
-    a.ws = (char *)ws;
     a.grid = grid;
-    a.max_items = max_items;
+    spkv::decode_ws_assign(a, c, n_q_heads, grid, g->d_model, g->d_hidden, false, (char *)ws);
     a.share_cut = kFusedShareCut;
     a.gate.d_model = g->d_model;
     a.gate.d_hidden = g->d_hidden;

@@ -56,7 +56,6 @@ constexpr int ROUND = 256;             // steps staged per wave at a time
 // output write, about 8 steps of streaming time (8 measured best of 0, 4, 8,
 // 12 on the 32K-, 131K-context and ragged batch-32 decode workloads)
 constexpr int BG_COST = 8;
-constexpr int MAX_SLOTS_PER_BG = 256;  // partials merged per pass of the combine
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -402,13 +401,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int w = c.window;
     const int nws = w / KSTEP;  // ring steps per (b, g)
     const int P = c.page_size;
-    int32_t *cnt = (int32_t *)a.ws;
-    const size_t fb = FUSED ? fused_bytes(a.gate.d_model, a.gate.d_hidden) : 0;
+    int32_t *cnt = a.cnt;
     const int g_items = FUSED ? gate_tile_items(a.gate.d_model, a.gate.d_hidden) : 0;
     int32_t *gate_cnt = cnt + (size_t)BG * CNT_STRIDE;  // fused: gate units stored
     int32_t *plan_cnt = gate_cnt + 64;                  // fused: workgroups that read the lengths
-    float *gshare = (float *)(a.ws + ws_header_bytes(BG));
-    float *part = a.part ? a.part : (float *)(a.ws + ws_header_bytes(BG) + fb);
+    float *gshare = a.gshare;
+    float *part = a.part;
     // attention workgroups (the fused step keeps the last one for its finisher)
     const int n_att = FUSED ? (int)gridDim.x - 1 : (int)gridDim.x;
 
@@ -919,29 +917,58 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
 
 }  // namespace
 
-size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_model,
-                       int fused_hidden) {
+namespace {
+
+// Workspace of the bf16 kernel: arrival counters (one 256-byte line per
+// (b, g), then the fused step's two counters), the fused step's gate sums,
+// then the split-K partials.
+// With fixed_counters the counters are laid out for the largest batch * n_kv,
+// so that they sit at the same place whatever the cache.
+struct WsLayout {
+    size_t gshare, part, total;
+    int max_items;
+};
+
+WsLayout ws_layout(const spkv_cache *c, int n_q, int grid, int fused_model, int fused_hidden, bool fixed_counters) {
+    const int BG = c->batch * c->n_kv;
+    const int G = n_q / c->n_kv;
+    WsLayout L;
+    L.gshare = round256(ws_header_bytes(fixed_counters ? MAX_BG : BG));
+    L.part = L.gshare + fused_bytes(fused_model, fused_hidden);
+    // a workgroup's contiguous range meets each (b, g) in at most one
+    // segment, and consecutive (b, g) share at most one workgroup
+    L.max_items = grid + BG;
+    L.total = L.part + (size_t)L.max_items * rec_floats(G, c->head_dim) * sizeof(float);
+    return L;
+}
+
+}  // namespace
+
+size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_model, int fused_hidden,
+                       bool fixed_counters) {
     if (c->dtype != SPKV_BF16) {
         if (max_items_out) *max_items_out = 0;
         return 0;
     }
-    const int BG = c->batch * c->n_kv;
-    const int G = n_q / c->n_kv;
-    // a workgroup's contiguous range meets each (b, g) in at most one
-    // segment, and consecutive (b, g) share at most one workgroup
-    const int max_slots = grid + BG;
-    if (max_items_out) *max_items_out = max_slots;
-    return ws_header_bytes(BG) + fused_bytes(fused_model, fused_hidden) +
-           (size_t)max_slots * rec_floats(G, c->head_dim) * sizeof(float);
+    const WsLayout L = ws_layout(c, n_q, grid, fused_model, fused_hidden, fixed_counters);
+    if (max_items_out) *max_items_out = L.max_items;
+    return L.total;
 }
 
-size_t decode_noalloc_layout(const spkv_cache *c, int n_q, int grid, size_t *part_offset) {
-    // counters for the largest batch * n_kv first, so that they sit at the
-    // same place whatever the cache: every launch leaves them at zero
-    const size_t hdr = round256(ws_header_bytes(MAX_BG));
-    if (part_offset) *part_offset = hdr;
-    const int BG = c->batch * c->n_kv;
-    return hdr + (size_t)(grid + BG) * rec_floats(n_q / c->n_kv, c->head_dim) * sizeof(float);
+void decode_ws_assign(DecodeArgs &a, const spkv_cache *c, int n_q, int grid, int fused_model, int fused_hidden,
+                      bool fixed_counters, char *ws) {
+    if (c->dtype != SPKV_BF16 || !ws) {
+        a.cnt = nullptr;
+        a.gshare = nullptr;
+        a.part = nullptr;
+        a.max_items = 0;
+        return;
+    }
+    const WsLayout L = ws_layout(c, n_q, grid, fused_model, fused_hidden, fixed_counters);
+    a.cnt = (int32_t *)ws;
+    a.gshare = (float *)(ws + L.gshare);
+    a.part = (float *)(ws + L.part);
+    a.max_items = L.max_items;
 }
 
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid) {

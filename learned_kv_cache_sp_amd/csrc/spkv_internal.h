@@ -97,10 +97,13 @@ struct DecodeArgs {
     const int32_t *t;
     float scale;
     float *out, *lse;
-    char *ws;
+    // workspace pieces (decode_ws_assign): arrival counters, the fused
+    // step's gate sums, split-K partials
+    int32_t *cnt;
+    float *gshare;
+    float *part;
     int32_t grid;       // persistent workgroups
-    int32_t max_items;  // partial slots in ws
-    float *part;        // split-K partials; NULL: in ws after the counters (and the fused gate's sums)
+    int32_t max_items;  // partial slots
     // fused step (spkv_decode_step): the gate of the batch's new rows and
     // their append run inside the attention launch
     int32_t share_cut;  // fused step: attention steps fewer for the workgroups that run a gate item
@@ -108,13 +111,13 @@ struct DecodeArgs {
     const char *k_new, *v_new;  // new rows: row b, key head g at + (b*ld_new + g*hd) elements
     int64_t ld_new;
 };
-// fused_hidden: d_hidden of the gate for the fused step, 0 for attention only
-// fused_model / fused_hidden: the gate's d_model and d_hidden for spkv_decode_step (0: plain attention)
+// fused_model / fused_hidden: the gate's d_model and d_hidden for spkv_decode_step (0: plain attention);
+// fixed_counters: counters laid out for the largest batch * n_kv (spkv_decode_attn_noalloc's scratch)
 size_t decode_ws_bytes(const spkv_cache *c, int n_q, int grid, int *max_items_out, int fused_model = 0,
-                       int fused_hidden = 0);
-// bf16 scratch of spkv_decode_attn_noalloc: counters laid out for the largest
-// batch * n_kv, then the partials at *part_offset; returns the bytes needed
-size_t decode_noalloc_layout(const spkv_cache *c, int n_q, int grid, size_t *part_offset);
+                       int fused_hidden = 0, bool fixed_counters = false);
+// points a's workspace pieces into ws (laid out as decode_ws_bytes counts it)
+void decode_ws_assign(DecodeArgs &a, const spkv_cache *c, int n_q, int grid, int fused_model, int fused_hidden,
+                      bool fixed_counters, char *ws);
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid);
 int decode_blocks_per_cu();
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
