@@ -35,13 +35,21 @@ figures are HBM figures, as for a model whose every layer owns its cache.
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel: decode
 attention (algorithmic bytes = visible kept + window entries x 512 B per
-launch) or prefill attention (4 hd flops per visible (row, key) pair and
-query head), divided by the launch time measured with HIP events on the
-launch stream in a second pass over the same number of steps.  ``traffic``
-is read from the committed rocprofv3 counter summary for that kernel and
-workload when its recorded source hash matches the kernel source in this
-tree, else null.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
-of the same workload on the host cores.
+launch, plus the gate's and the appends' bytes in the fused step) or prefill
+attention (4 hd flops per visible (row, key) pair and query head).  Decode
+workloads with one launch per step take the launch time from the timed pass
+(its time per step, an upper bound of the launch); prefill takes it from a
+second pass with HIP events around each launch on the launch stream.
+``traffic`` is read from the committed rocprofv3 counter summary for that
+kernel and workload when its recorded source hash matches the kernel source
+in this tree, else null.  ``hbm_ceiling`` is the library's streaming-read
+kernel (spkv_hbm_read) at the decode launch's byte count and at 2 GiB, and
+the decode roofline also gives its fraction of that measured ceiling.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on every host core this process may use (nproc, affinity, cgroup
+quota and CPU model recorded).  The default decode_32k run also carries a
+``secondary`` list: decode_131k, ragged_32 and prefill_64k, each measured the
+same way with its own default steps.
 
 Profile summaries (no GPU needed):
     python bench.py --summarize-stats DIR
@@ -84,7 +92,8 @@ CALIBRATION_BYTES = 1 << 30  # the plain copy: 1 GiB read + 1 GiB written
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=None, help="timed steps (decode 256, prefill 4)")
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps of --workload (decode 256, prefill 4; secondary lines take their defaults)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
     p.add_argument("--workload", default="decode_32k",
                    choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k",
@@ -103,7 +112,9 @@ def parse():
     p.add_argument("--summarize-mfma", metavar="DIR",
                    help="matrix-core counters (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, "
                         "SQ_INSTS_VALU_MFMA_MOPS_BF16) per kernel")
-    p.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM read / copy ceiling")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM read ceiling")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="decode_32k: skip the decode_131k, ragged_32 and prefill_64k lines")
     p.add_argument("--kernel", default="decode_bf16_kernel")
     return p.parse_args()
 
@@ -486,8 +497,14 @@ def bench_decode(args, wl):
     for l in range(L):
         for b in range(B):
             Estep[l, b, 1:] = np.cumsum(zl_h[l, :, b].reshape(n_fl * buf, nkv), 0)
+    # one decode launch per step (fused / ring): the launch time is taken from
+    # the timed pass itself -- its time per step, an upper bound of the launch
+    # duration -- and the bytes from the same steps; the separate mode has
+    # other launches in its steps and takes the second pass's brackets
+    one_launch = fused or ring
+    byte_steps = range(warm, warm + steps) if one_launch else range(warm + steps, S)
     bytes_per = []
-    for s in range(warm + steps, S):
+    for s in byte_steps:
         l, i = s % L, s // L
         tot = 0
         for b in range(B):
@@ -514,7 +531,8 @@ def bench_decode(args, wl):
     bytes_per = np.array(bytes_per)
     grp_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["d0"], ev["d1"])])
     dec_ms = grp_ms / np.array(ev["n"])          # mean launch time within each bracket
-    achieved = float(bytes_per.mean() / (float(grp_ms.sum() / sum(ev["n"])) * 1e-3) / 1e9)
+    launch_ms = gpu_ms / steps if one_launch else float(grp_ms.sum() / sum(ev["n"]))
+    achieved = float(bytes_per.mean() / (launch_ms * 1e-3) / 1e9)
 
     res = {
         "metric": METRIC,
@@ -551,7 +569,11 @@ def bench_decode(args, wl):
                      "traffic": stored_traffic("decode_bf16_kernel", wl.name,
                                                f"decode_bf16_kernel<{hd}, {1 if fused else 2 if ring else 0}>"),
                      "bytes_per_launch": float(bytes_per.mean()),
-                     "launch_us": _stats_us(dec_ms), "launches_per_bracket": L},
+                     "launch_us": round(launch_ms * 1e3, 2),
+                     "launch_us_from": ("the timed pass: its time per step (one launch per step), an upper "
+                                        "bound of the launch duration" if one_launch else
+                                        f"a second pass: brackets of {L} back-to-back launches"),
+                     "bracketed_launch_us": _stats_us(dec_ms), "launches_per_bracket": L},
         "host_wall_s": round(wall, 4),
     }
     if "f0" in ev:
@@ -970,7 +992,7 @@ def cpu_baseline_rethreshold(wl, budget_s: float) -> dict:
 
 
 def _threads():
-    return max(1, min(16, os.cpu_count() or 1))
+    return host_cpu()[0]
 
 
 def cpu_baseline_decode(wl, budget_s: float) -> dict:
@@ -1044,27 +1066,123 @@ def cpu_baseline_prefill(wl, budget_s: float) -> dict:
                       f"of all {wl.n_q} query heads over a seeded mask with keep {wl.keep[0]}; {dt:.1f} s"}
 
 
-def hbm_ceiling(torch) -> dict:
-    """Context for "% of peak": what plain library kernels reach on this GPU --
-    a 2 GiB read (sum of float32) and a 1 GiB + 1 GiB device copy, median of 5."""
-    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
-    y = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    def med(fn, nbytes):
-        ts = []
-        for i in range(7):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            if i >= 2:
-                ts.append(e0.elapsed_time(e1) * 1e-3)
-        return round(nbytes / float(np.median(ts)) / 1e9, 1)
-    read = med(lambda: x.sum(), x.numel() * 4)
-    copy = med(lambda: y.copy_(x[: y.numel()]), 2 * y.numel() * 4)
-    del x, y
-    return {"read_GBs": read, "copy_GBs": copy, "unit": "GB/s",
-            "kind": "torch float32 sum over 2 GiB / torch copy of 1 GiB (read + write bytes), median of 5"}
+def hbm_ceiling(torch, decode_bytes: float | None) -> dict:
+    """The measured read ceiling: spkv_hbm_read, the library's streaming-read
+    kernel (16-byte loads, nothing computed), over every access order, hint
+    and grid it offers.  Two sizes: the bytes of one decode launch, read from
+    regions rotated over 1.5 GB so that none is still in the 256 MB Infinity
+    Cache when it is read again (as the decode launches' layer caches are),
+    and a 2 GiB buffer.  Launches are timed back to back, 16 between two
+    events, as the decode steps are; the median of 5 brackets is kept."""
+    from learned_kv_cache_sp_amd import spkv
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def sweep(regions, nbytes):
+        rows = []
+        for runs in (False, True):
+            for nt in (False, True):
+                for per_cu in (1, 2, 4, 8):
+                    grid = per_cu * cu
+                    ts = []
+                    for rep in range(6):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for k in range(16):
+                            spkv.spkv_hbm_read(regions[(rep * 16 + k) % len(regions)], sink, nontemporal=nt,
+                                               runs=runs, grid=grid, stream=stream)
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        if rep:
+                            ts.append(e0.elapsed_time(e1) / 16)
+                    us = float(np.median(ts)) * 1e3
+                    rows.append({"order": "runs" if runs else "stride", "nontemporal": nt, "grid": grid,
+                                 "us": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        best = max(rows, key=lambda r: r["GBs"])
+        return {"bytes": int(nbytes), "best": best,
+                "table": [[r["order"], int(r["nontemporal"]), r["grid"], r["GBs"]] for r in rows]}
+
+    res = {"kernel": "spkv_hbm_read (16-byte loads, one read of every byte)", "unit": "GB/s",
+           "table_columns": ["order", "nontemporal", "grid", "GB/s"]}
+    if decode_bytes:
+        nb = int(math.ceil(decode_bytes / 16384.0)) * 16384
+        n_reg = max(2, int(math.ceil(1.5e9 / nb)))
+        big = torch.ones(n_reg * nb // 4, dtype=torch.int32, device="cuda")
+        regions = [big[k * nb // 4:(k + 1) * nb // 4] for k in range(n_reg)]
+        res["decode_sized"] = sweep(regions, nb)
+        del regions, big
+    x = torch.ones((2 << 30) // 4, dtype=torch.int32, device="cuda")
+    res["read_2GiB"] = sweep([x], x.numel() * 4)
+    del x
+    torch.cuda.empty_cache()
+    return res
+
+
+def host_cpu() -> tuple[int, dict]:
+    """The host cores this process may use (affinity, capped by a cgroup CPU
+    quota if one is set) and what identifies them."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = int(q) / int(per)
+    except (OSError, ValueError):
+        pass
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = aff if quota is None else max(1, min(aff, int(quota)))
+    return threads, {"nproc": os.cpu_count(), "affinity_cpus": aff, "cgroup_cpu_quota": quota,
+                     "cpu_model": model, "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_baseline(name: str, wl, budget_s: float) -> dict:
+    if name == "soft_prefill_16k":
+        r = cpu_baseline_soft(wl, budget_s)
+    elif name == "head_stats_1m":
+        r = cpu_baseline_head_stats(budget_s)
+    elif name == "rethreshold_32k":
+        r = cpu_baseline_rethreshold(wl, budget_s)
+    else:
+        r = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, budget_s)
+    r["host"] = host_cpu()[1]
+    return r
+
+
+DEFAULT_STEPS = {"decode": (256, 16), "prefill": (4, 1), "rethreshold_32k": (20, 3), "head_stats_1m": (50, 5),
+                 "soft_prefill_16k": (5, 1)}
+SECONDARY = ["decode_131k", "ragged_32", "prefill_64k"]
+
+
+def run_workload(args, name: str, steps=None, warmup=None) -> dict:
+    import torch
+    from learned_kv_cache_sp_amd import inputs
+    a = argparse.Namespace(**vars(args))
+    kind = name if name in DEFAULT_STEPS else ("prefill" if inputs.WORKLOADS[name].chunk else "decode")
+    a.steps = DEFAULT_STEPS[kind][0] if steps is None else steps
+    a.warmup = DEFAULT_STEPS[kind][1] if warmup is None else warmup
+    if name == "soft_prefill_16k":
+        wl = inputs.WORKLOADS["prefill_64k"]
+        res = bench_soft_prefill(a, wl)
+    elif name == "head_stats_1m":
+        wl = None
+        res = bench_head_stats(a)
+    elif name == "rethreshold_32k":
+        wl = inputs.WORKLOADS["decode_32k"]
+        res = bench_rethreshold(a, wl)
+    else:
+        wl = inputs.WORKLOADS[name]
+        res = bench_prefill(a, wl) if wl.chunk else bench_decode(a, wl)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, wl
 
 
 # ----------------------------------------------------------------------------
@@ -1086,43 +1204,46 @@ def main():
         sys.exit(2)
 
     import torch
-    from learned_kv_cache_sp_amd import inputs
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    if args.workload == "soft_prefill_16k":
-        wl = inputs.WORKLOADS["prefill_64k"]
-        res = bench_soft_prefill(args, wl)
-    elif args.workload == "head_stats_1m":
-        wl = None
-        res = bench_head_stats(args)
-    elif args.workload == "rethreshold_32k":
-        wl = inputs.WORKLOADS["decode_32k"]
-        res = bench_rethreshold(args, wl)
-    else:
-        wl = inputs.WORKLOADS[args.workload]
-        res = bench_prefill(args, wl) if wl.chunk else bench_decode(args, wl)
+    res, wl = run_workload(args, args.workload, args.steps, args.warmup)
+    print(f"[bench] {args.workload}: {res['value']:.1f} {res['unit']}, roofline frac {res['roofline']['frac']}",
+          file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         a = torch.zeros(CALIBRATION_BYTES // 2, dtype=torch.int16, device="cuda")
         b_ = torch.empty_like(a)
         torch.neg(a, out=b_)
         torch.cuda.synchronize()
+        del a, b_
         res["copy_calibration_bytes"] = CALIBRATION_BYTES
 
     if not args.no_ceiling:
-        res["hbm_ceiling"] = hbm_ceiling(torch)
+        dec_bytes = res["roofline"].get("bytes_per_launch") if res["roofline"]["bound"] == "hbm" else None
+        res["hbm_ceiling"] = hbm_ceiling(torch, dec_bytes)
+        if dec_bytes:
+            ceil_gbs = res["hbm_ceiling"]["decode_sized"]["best"]["GBs"]
+            res["roofline"]["measured_ceiling_GBs"] = ceil_gbs
+            res["roofline"]["frac_of_measured_ceiling"] = round(res["roofline"]["achieved"] / ceil_gbs, 4)
 
     if not args.no_cpu_baseline:
-        if args.workload == "soft_prefill_16k":
-            res["cpu_baseline"] = cpu_baseline_soft(wl, args.cpu_budget)
-        elif args.workload == "head_stats_1m":
-            res["cpu_baseline"] = cpu_baseline_head_stats(args.cpu_budget)
-        elif args.workload == "rethreshold_32k":
-            res["cpu_baseline"] = cpu_baseline_rethreshold(wl, args.cpu_budget)
-        else:
-            res["cpu_baseline"] = (cpu_baseline_prefill if wl.chunk else cpu_baseline_decode)(wl, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(args.workload, wl, args.cpu_budget)
+
+    # the other single-GPU workloads, each with its own default steps, its
+    # roofline and its CPU baseline, in the same JSON line
+    if args.workload == "decode_32k" and not args.no_secondary:
+        res["secondary"] = []
+        for name in SECONDARY:
+            t0 = time.perf_counter()
+            r2, wl2 = run_workload(args, name)
+            if not args.no_cpu_baseline:
+                r2["cpu_baseline"] = cpu_baseline(name, wl2, args.cpu_budget)
+            r2["wall_s"] = round(time.perf_counter() - t0, 1)
+            res["secondary"].append(r2)
+            print(f"[bench] {name}: {r2['value']:.1f} {r2['unit']}, roofline frac {r2['roofline']['frac']}",
+                  file=sys.stderr, flush=True)
     print(json.dumps(res))
 
 

@@ -412,6 +412,22 @@ int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows,
                     size_t ws_bytes, void *stream);
 size_t spkv_head_stats_ws_bytes(int64_t n_rows, int32_t n_kv);
 
+/* Streaming read of `bytes` bytes at `src` (device memory): the measured
+ * bandwidth ceiling that the decode attention kernel is compared with.  It
+ * reads every byte once with 16-byte loads and writes nothing (one word of
+ * `sink` only in a case that data cannot produce).  It measures the
+ * hardware and computes nothing of the method.
+ *   flags  SPKV_READ_NONTEMPORAL: loads carry the non-temporal hint;
+ *          SPKV_READ_RUNS: each of the grid x 4 waves streams its own
+ *          contiguous run of 16 KB blocks (the decode kernel's order);
+ *          otherwise every thread steps through the buffer by the whole grid.
+ *   grid   workgroups of 256 threads (1..65536).
+ *   sink   device word, 4-byte aligned (not read).
+ * src must be 16-byte aligned and bytes a multiple of 16384, flags only the
+ * two bits above (SPKV_E_INVALID otherwise); bytes = 0 launches nothing. */
+enum { SPKV_READ_NONTEMPORAL = 1, SPKV_READ_RUNS = 2 };
+int spkv_hbm_read(const void *src, size_t bytes, int32_t flags, int32_t grid, void *sink, void *stream);
+
 /* Sizes in bytes of each cache buffer (k_pages, v_pages, pos_pages,
  * page_table, lengths, ring_k, ring_v) for the dimensions in *c; returns the
  * sum.  `sizes` may be NULL.  u_pages, when used, adds n_pages * page_size

@@ -595,6 +595,21 @@ int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows, i
 }
 
 // ----------------------------------------------------------------------------
+int spkv_hbm_read(const void *src, size_t bytes, int32_t flags, int32_t grid, void *sink, void *stream) {
+    if (bytes == 0) return SPKV_OK;
+    if (!src || !sink) return fail(SPKV_E_INVALID, "src / sink NULL");
+    if (((uintptr_t)src & 15) || (bytes & 16383))
+        return fail(SPKV_E_INVALID, "src not 16-byte aligned or bytes %zu not a multiple of 16384", bytes);
+    if ((uintptr_t)sink & 3) return fail(SPKV_E_INVALID, "sink not 4-byte aligned");
+    if (flags & ~(SPKV_READ_NONTEMPORAL | SPKV_READ_RUNS)) return fail(SPKV_E_INVALID, "flags 0x%x", flags);
+    if (grid < 1 || grid > 65536) return fail(SPKV_E_INVALID, "grid %d (1..65536)", grid);
+    hipError_t e = spkv::launch_hbm_read(src, bytes, (flags & SPKV_READ_NONTEMPORAL) != 0, (flags & SPKV_READ_RUNS) != 0,
+                                         (uint32_t *)sink, grid, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "streaming-read launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
 size_t spkv_cache_bytes(const spkv_cache *c, size_t sizes[7]) {
     if (!c) return 0;
     const size_t es = c->dtype == SPKV_BF16 ? 2 : 4;

@@ -53,6 +53,10 @@ inline CacheView make_view(const spkv_cache *c) {
 
 inline int elem_bytes(int dtype) { return dtype == SPKV_BF16 ? 2 : 4; }
 
+// ---- streaming-read ceiling ---------------------------------------------------
+hipError_t launch_hbm_read(const void *src, size_t bytes, bool nontemporal, bool runs, uint32_t *sink, int grid,
+                           hipStream_t s);
+
 // ---- gate ------------------------------------------------------------------
 struct GateArgs {
     int32_t d_model, d_hidden, n_kv, dtype;

@@ -75,7 +75,7 @@ EXPORTS = [
     "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
     "spkv_head_stats", "spkv_head_stats_ws_bytes", "spkv_prefill_attn_soft",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
-    "spkv_last_error", "spkv_version",
+    "spkv_last_error", "spkv_version", "spkv_hbm_read",
 ]
 
 _lib = None
@@ -117,6 +117,7 @@ def load_library(path: str = LIB_PATH):
         "spkv_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "spkv_last_error": ([], ctypes.c_char_p),
         "spkv_version": ([], ctypes.c_int),
+        "spkv_hbm_read": ([vp, sz, i32, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -591,3 +592,23 @@ def spkv_cache_check(cache: Cache, stream=None) -> int:
     if rc != SPKV_OK:
         raise SpkvError(rc, load_library().spkv_last_error().decode() + f" bits={bits.value}")
     return bits.value
+
+
+def spkv_hbm_read(src, sink, nontemporal: bool = False, runs: bool = False, grid: int = 0, stream=None):
+    """Stream every byte of the device tensor ``src`` once (the measured read ceiling).
+
+    ``src`` is contiguous with a byte size that is a multiple of 16384;
+    ``sink`` is a device tensor with at least one 4-byte element.  ``runs``:
+    every wave reads its own contiguous run of 16 KB blocks, else a
+    grid-stride sweep.  ``grid`` 0 takes 8 workgroups per compute unit."""
+    if not (src.is_cuda and sink.is_cuda):
+        raise ValueError("spkv_hbm_read needs device tensors")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("sink needs one 4-byte element")
+    nbytes = src.numel() * src.element_size()
+    if grid <= 0:
+        grid = 8 * torch.cuda.get_device_properties(src.device).multi_processor_count
+    flags = (1 if nontemporal else 0) | (2 if runs else 0)
+    _check(load_library().spkv_hbm_read(_ptr(src), nbytes, flags, int(grid), _ptr(sink), _stream(stream)))

@@ -104,3 +104,15 @@ def test_well_shaped_cpu_tensors_reach_the_device_check():
     # with every shape right, the only complaint left is that the tensors are not on the GPU
     with pytest.raises(ValueError, match="device tensors"):
         spkv.spkv_decode_attn(cache(), bf(B, NQ, HD), i32(B), 0.125)
+
+
+def test_hbm_read_refuses_bad_arguments():
+    # argument checks happen on the host before any launch
+    lib = spkv.load_library()
+    fake = 1 << 40
+    assert lib.spkv_hbm_read(fake, 1000, 0, 256, fake, None) == spkv.SPKV_E_INVALID      # not 16 KB multiple
+    assert lib.spkv_hbm_read(fake + 8, 16384, 0, 256, fake, None) == spkv.SPKV_E_INVALID  # misaligned
+    assert lib.spkv_hbm_read(fake, 16384, 4, 256, fake, None) == spkv.SPKV_E_INVALID      # unknown flag
+    assert lib.spkv_hbm_read(fake, 16384, 0, 0, fake, None) == spkv.SPKV_E_INVALID        # empty grid
+    assert lib.spkv_hbm_read(None, 16384, 0, 256, fake, None) == spkv.SPKV_E_INVALID
+    assert lib.spkv_hbm_read(fake, 0, 0, 256, fake, None) == spkv.SPKV_OK                 # nothing to read
