@@ -226,26 +226,55 @@ class GateWeights:
 class Cache:
     """Device buffers of one layer's SP-KV cache (see include/spkv.h, spkv_cache)."""
 
+    GUARD_BYTE = 0xA5
+
     def __init__(self, batch: int, n_kv: int, head_dim: int, window: int, page_size: int,
                  n_pages: int, max_pages_per_head: int, dtype=torch.bfloat16, device="cuda",
-                 utilities: bool = False):
+                 utilities: bool = False, guard: int = 0):
+        """guard > 0 (a multiple of 256): every buffer sits between two runs of
+        `guard` canary bytes (GUARD_BYTE), which check_guards() inspects --
+        a test aid for catching writes outside the buffers."""
         dt = dtype
         self.batch, self.n_kv, self.head_dim, self.window = batch, n_kv, head_dim, window
         self.page_size, self.n_pages, self.max_pages_per_head = page_size, n_pages, max_pages_per_head
         self.dtype = dt
-        z = lambda shape, d=dt: torch.zeros(shape, dtype=d, device=device)  # noqa: E731
-        self.k_pages = z((n_pages, page_size, head_dim))
-        self.v_pages = z((n_pages, head_dim, page_size))
-        self.pos_pages = z((n_pages, page_size), torch.int32)
-        self.page_table = torch.full((batch, n_kv, max_pages_per_head), -1, dtype=torch.int32, device=device)
-        self.lengths = z((batch, n_kv), torch.int32)
-        self.pool_next = z((1,), torch.int32)
-        self.status = z((1,), torch.int32)
-        self.ring_k = z((batch, n_kv, window, head_dim))
-        self.ring_v = z((batch, n_kv, head_dim, window))
+        if guard % 256:
+            raise ValueError("guard must be a multiple of 256 bytes")
+        self._guards = []
+
+        def z(shape, d=dt, fill=0, name=""):
+            if not guard:
+                return torch.full(shape, fill, dtype=d, device=device)
+            n = int(np.prod(shape)) * torch.empty((), dtype=d).element_size()
+            body = (n + 255) // 256 * 256
+            raw = torch.full((guard + body + guard,), self.GUARD_BYTE, dtype=torch.uint8, device=device)
+            t = raw[guard:guard + n].view(d).view(shape)
+            t.fill_(fill)
+            self._guards.append((name, raw, guard, n))
+            return t
+
+        self.k_pages = z((n_pages, page_size, head_dim), name="k_pages")
+        self.v_pages = z((n_pages, head_dim, page_size), name="v_pages")
+        self.pos_pages = z((n_pages, page_size), torch.int32, name="pos_pages")
+        self.page_table = z((batch, n_kv, max_pages_per_head), torch.int32, -1, name="page_table")
+        self.lengths = z((batch, n_kv), torch.int32, name="lengths")
+        self.pool_next = z((1,), torch.int32, name="pool_next")
+        self.status = z((1,), torch.int32, name="status")
+        self.ring_k = z((batch, n_kv, window, head_dim), name="ring_k")
+        self.ring_v = z((batch, n_kv, head_dim, window), name="ring_v")
         # utility of each entry (kept for spkv_cache_rethreshold)
-        self.u_pages = z((n_pages, page_size), torch.float32) if utilities else None
+        self.u_pages = z((n_pages, page_size), torch.float32, name="u_pages") if utilities else None
         self._desc = None
+
+    def check_guards(self) -> list:
+        """Names of the buffers whose canary bytes (before, after or in the
+        padding after the buffer) are no longer intact."""
+        bad = []
+        for name, raw, g, n in self._guards:
+            outside = torch.cat([raw[:g], raw[g + n:]])
+            if bool((outside != self.GUARD_BYTE).any()):
+                bad.append(name)
+        return bad
 
     @staticmethod
     def pages_needed(lengths_per_head, page_size: int) -> int:

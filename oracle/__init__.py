@@ -17,7 +17,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "spkv_oracle.c")
-_LIB = os.path.join(_HERE, "libspkv_oracle.so")
+# SPKV_ORACLE_LIB names another build of the same source (the sanitizer
+# build that the test suite makes and loads in a child process)
+_LIB = os.environ.get("SPKV_ORACLE_LIB") or os.path.join(_HERE, "libspkv_oracle.so")
 
 _lib = None
 

@@ -116,3 +116,21 @@ def test_hbm_read_refuses_bad_arguments():
     assert lib.spkv_hbm_read(fake, 16384, 0, 0, fake, None) == spkv.SPKV_E_INVALID        # empty grid
     assert lib.spkv_hbm_read(None, 16384, 0, 256, fake, None) == spkv.SPKV_E_INVALID
     assert lib.spkv_hbm_read(fake, 0, 0, 256, fake, None) == spkv.SPKV_OK                 # nothing to read
+
+
+def test_guard_canaries_detect_a_stray_write():
+    # host-side check of the canary mechanism on a CPU cache: a byte written
+    # just past a buffer (into its padding or its trailing guard) is reported
+    c = spkv.Cache(1, 2, 64, 32, 32, 4, 2, torch.bfloat16, device="cpu", guard=256)
+    assert c.check_guards() == []
+    name, raw, g, n = c._guards[3]          # the page table
+    assert name == "page_table"
+    raw[g + n] = 0
+    assert c.check_guards() == ["page_table"]
+    raw[g + n] = spkv.Cache.GUARD_BYTE
+    raw[g - 1] = 1                           # the byte just before the buffer
+    assert c.check_guards() == ["page_table"]
+    raw[g - 1] = spkv.Cache.GUARD_BYTE
+    c.k_pages.fill_(3.0)                     # writes inside the buffer are fine
+    assert c.check_guards() == []
+    assert bool((c.page_table == -1).all())

@@ -96,3 +96,21 @@ def test_prefill_zero_keys_counts_visible_set():
         n = oracle.visible_count(z[:, g], np.arange(T), wl.window)
         for h in range(g * wl.group, (g + 1) * wl.group):
             assert np.all(np.abs(lse[:, h] - np.log(n)) <= 2e-6 * np.maximum(1.0, np.log(n)))
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("n_q, n_kv", [(8, 8), (16, 1), (32, 2), (48, 3), (64, 16), (256, 16)])
+def test_prefill_bf16_head_shapes(n_q, n_kv, hd):
+    # group sizes 1, 4 and 16, a key-head count (3) that does not divide 8,
+    # the widest query count, both head sizes; two chunks with a ragged tail
+    wl = tl.small_workload("prefill_64k", n_q=n_q, n_kv=n_kv, head_dim=hd, window=64)
+    T = 333 if n_q >= 64 else 530
+    seed = 55 + n_q + n_kv + hd
+    tok = inputs.tokens(wl, T, seed, 0)
+    rates = [0.1 + 0.8 * g / max(1, n_kv - 1) for g in range(n_kv)]
+    z = inputs.bernoulli_mask(T, rates, seed, 0)
+    out, lse, _ = prefill_chunks(wl, tok["Q"], tok["K"], tok["V"], z, 200)
+    ro, rl = oracle.attention(tok["Q"], np.arange(T), tok["K"], tok["V"], z, wl.window, threads=tl.oracle_threads())
+    print(f"[prefill bf16 n_q={n_q} n_kv={n_kv} hd={hd}] max|dout|={tl.max_abs(out, ro):.2e} "
+          f"max|dlse|={tl.max_abs(lse, rl):.2e}")
+    assert tl.max_abs(out, ro) <= tl.TOL_PREFILL and tl.max_abs(lse, rl) <= tl.TOL_REGRESS

@@ -64,8 +64,10 @@ def _run(T, hd, P, chunk, w, tau, beta, c, nkv=2, G=4, seed=4):
 ])
 def test_soft_prefill_matches_oracle(hd, P, chunk, w, beta, c):
     err_o, err_l = _run(1100, hd, P, chunk, w, 0.5, beta, c)
+    print(f"[soft hd={hd} P={P} chunk={chunk} w={w} beta={beta} c={c}] max|dout|={err_o:.2e} max|dlse|={err_l:.2e}")
     assert err_o < tl.TOL_PREFILL, err_o
-    assert err_l < tl.TOL_PREFILL, err_l
+    # the normaliser is summed in f32 from f32 weights, as on the hard path
+    assert err_l < tl.TOL_REGRESS, err_l
 
 
 def test_soft_prefill_arguments():
@@ -79,3 +81,12 @@ def test_soft_prefill_arguments():
                 (0.5, 1e-45, 1.0), (0.5, 0.01, 3e38)):
         with pytest.raises(spkv.SpkvError):
             spkv.spkv_prefill_attn(cache, 0, q, k, k, 0, 0.1, soft=bad)
+
+
+@pytest.mark.parametrize("nkv, G", [(3, 16), (5, 2)])
+def test_soft_prefill_key_heads_not_dividing_8(nkv, G):
+    # key-head counts that do not divide 8, with the widest and a small group
+    err_o, err_l = _run(700, 128, 64, 300, 64, 0.5, 0.01, 1e6, nkv=nkv, G=G, seed=9)
+    print(f"[soft nkv={nkv} G={G}] max|dout|={err_o:.2e} max|dlse|={err_l:.2e}")
+    assert err_o < tl.TOL_PREFILL, err_o
+    assert err_l < tl.TOL_REGRESS, err_l
