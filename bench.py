@@ -81,7 +81,7 @@ KERNEL_SOURCES = {
     "decode_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_decode.hip",
     "prefill_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_prefill.hip",
     "gate_bf16_kernel": "learned_kv_cache_sp_amd/csrc/spkv_gate.hip",
-    "compact_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
+    "compact_onepass_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "compact_small_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "rethresh_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "stats_band_vec_kernel": "learned_kv_cache_sp_amd/csrc/spkv_stats.hip",
@@ -705,7 +705,10 @@ def bench_prefill(args, wl):
                      "TFLOPs": round(float(2.0 * CH * d * wl.d_hidden / (g_ms.mean() * 1e-3) / 1e12), 1)},
             "compaction": {"us": _stats_us(c_ms),
                            "hbm_GBs": round(float((2 * kept_rows.sum() / nc * 2 * hd * 2 + CH * nkv)
-                                                  / (c_ms.mean() * 1e-3) / 1e9), 1)},
+                                                  / (c_ms.mean() * 1e-3) / 1e9), 1),
+                           "launches": "one (spkv_compact_append, GLOBAL, 16384 rows)"},
+            "fraction_of_step": {k: round(float(v.mean() * nc / (gpu_ms / steps)), 4)
+                                 for k, v in (("gate", g_ms), ("compaction", c_ms), ("attention", a_ms))},
         },
         "host_wall_s": round(wall, 4),
     }

@@ -59,7 +59,7 @@ enum {
     SPKV_E_CAPACITY = -4,    /* device flag: page pool or page table exhausted */
     SPKV_E_WORKSPACE = -5,   /* workspace smaller than the *_ws_bytes figure */
     SPKV_E_ROWS = -6,        /* device flag: row_offsets inconsistent with n_rows / max_rows */
-    SPKV_E_TIMEOUT = -7      /* device flag: a wait inside spkv_decode_step ran out */
+    SPKV_E_TIMEOUT = -7      /* device flag: a wait inside a launch ran out */
 };
 
 /* device status bits written by the kernels into cache->status[0] */
@@ -68,9 +68,12 @@ enum {
     SPKV_STATUS_TABLE_FULL = 2, /* a head needed more than max_pages_per_head pages */
     SPKV_STATUS_BAD_ROWS = 4,   /* row_offsets not monotone, a sequence longer than max_rows,
                                    or a negative position; that sequence's rows were skipped */
-    SPKV_STATUS_STEP_TIMEOUT = 8 /* spkv_decode_step: arrivals it waits for did not come (the
-                                   launch had fewer workgroups resident than it needs); the
-                                   step's append or new lengths were not stored */
+    SPKV_STATUS_STEP_TIMEOUT = 8 /* a wait inside a launch ran out: in spkv_decode_step the
+                                   arrivals it waits for did not come (fewer workgroups resident
+                                   than it needs) and the step's append or new lengths were not
+                                   stored; in spkv_compact_append a tile's predecessor or a page
+                                   claim never published (a workspace not at zero) and the
+                                   append was dropped */
 };
 
 typedef enum { SPKV_F32 = 0, SPKV_BF16 = 1 } spkv_dtype;
@@ -187,8 +190,17 @@ size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows);
  *            matter and only those are written).
  *   append_offsets [batch, n_kv] int32, may be NULL: receives the length of
  *            each (b, g) before this append.
- *   ws  at least spkv_compact_ws_bytes(...) bytes.
- * Capacity overflow drops the rows that do not fit and sets a status bit.
+ *   ws  at least spkv_compact_ws_bytes(...) bytes (0 when max_rows_per_seq
+ *       <= 256), 16-byte aligned.  Appends of up to 256 rows per sequence
+ *       take one workgroup per (b, g); larger GLOBAL appends run as one
+ *       launch of 256-row tiles that find their output offsets from each
+ *       other (each tile adds the counts its predecessors publish) and
+ *       share new pages through claim words, all kept in ws: it must be
+ *       zero-filled once after allocation, every call leaves it at zero, and
+ *       calls that share it must not overlap (calls on one stream do not).
+ *       Physical page ids then depend on timing; list contents never do.
+ * Capacity overflow drops the rows that do not fit and sets a status bit
+ * (the list keeps the entries before the first one that did not fit).
  */
 int spkv_compact_append(const spkv_cache *c, const uint8_t *keep,
                         const float *utility, const void *k,

@@ -187,8 +187,8 @@ int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows, int64
 // ----------------------------------------------------------------------------
 size_t spkv_compact_ws_bytes(const spkv_cache *c, int32_t n_rows, int32_t max_rows_per_seq) {
     (void)n_rows;
-    if (!c) return 0;
-    return spkv::compact_ws_bytes(c->batch, c->n_kv, max_rows_per_seq);
+    if (!c || c->page_size < 1 || c->batch < 1 || c->n_kv < 1 || max_rows_per_seq < 0) return 0;
+    return spkv::compact_ws_bytes(c->batch, c->n_kv, c->page_size, max_rows_per_seq);
 }
 
 int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const float *utility, const void *k,
@@ -208,9 +208,10 @@ int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const float *u
     if ((flags & SPKV_APPEND_GLOBAL) && c->u_pages && !utility)
         return fail(SPKV_E_INVALID, "the cache stores utilities (u_pages) but utility is NULL");
     if (int r = check_ld(ld_kv, (int64_t)c->n_kv * c->head_dim, c->dtype, "ld_kv")) return r;
-    const size_t need = spkv::compact_ws_bytes(c->batch, c->n_kv, max_rows_per_seq);
+    const size_t need = spkv::compact_ws_bytes(c->batch, c->n_kv, c->page_size, max_rows_per_seq);
     if (need && (!ws || ws_bytes < need))
         return fail(SPKV_E_WORKSPACE, "compaction workspace %zu < %zu bytes", ws_bytes, need);
+    if (need && ((uintptr_t)ws & 15)) return fail(SPKV_E_INVALID, "compaction workspace not 16-byte aligned");
     spkv::CompactArgs a;
     a.c = spkv::make_view(c);
     a.keep = keep;
@@ -225,7 +226,6 @@ int spkv_compact_append(const spkv_cache *c, const uint8_t *keep, const float *u
     a.flags = flags;
     a.append_offsets = append_offsets;
     a.ws = (int32_t *)ws;
-    a.max_tiles = 0;
     hipError_t e = spkv::launch_compact(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "compaction launch");
     return SPKV_OK;

@@ -24,6 +24,7 @@
 // threshold): a stable filter of every (b, g) list on its stored utilities,
 // ranked the same way and copied page to page.
 #include "spkv_internal.h"
+#include "spkv_device.h"
 
 namespace spkv {
 namespace {
@@ -378,99 +379,324 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large appends: (1) per-tile kept counts, (2) per-(b, g) scan over tiles and
-// page allocation, (3) per-(tile, b, g) ranking and copies.
-__global__ void __launch_bounds__(NT) compact_count_kernel(CompactArgs a) {
-    __shared__ int lds_cnt[NT / 64][16];
-    const int j = blockIdx.x;
-    const int b = blockIdx.y;
-    int r0, nb;
-    if (!seq_rows(a, b, &r0, &nb, j == 0)) return;
-    const CacheView &c = a.c;
-    const int i = j * TILE + threadIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int g = 0; g < c.n_kv; ++g) {
-        const bool flag = i < nb && a.keep[(int64_t)(r0 + i) * c.n_kv + g] != 0;
-        const uint64_t bal = __ballot(flag);
-        if (lane == 0) lds_cnt[wave][g] = __popcll(bal);
+// Large appends, one launch.  A workgroup takes one tile of TILE rows of one
+// (b, g); tiles of a (b, g) are numbered in the order their workgroups start
+// (a counter), so that a tile only ever waits for tiles that are already
+// running.  Each tile
+//   1. ranks its kept rows (ballot) and publishes its count,
+//   2. starts loading the first batch of those rows' key/value pieces,
+//   3. finds the count of all tiles before it (decoupled look-back: one
+//      wave reads the status of its 64 predecessors at a time, adding counts
+//      back to the nearest tile that has published its inclusive prefix)
+//      and publishes its own inclusive prefix,
+//   4. gets the pages its destination entries fall in: a page already in the
+//      list is read from the page table; a new page is claimed by whichever
+//      tile touching it gets there first (compare-and-swap on a claim word),
+//      which takes an id from the pool and publishes it; the others read it,
+//   5. stores the rows, positions and utilities (and ring rows).
+// The last workgroup of a (b, g) to finish sets its new length -- cut at the
+// first entry whose page could not be had, so the list stays a prefix -- and
+// returns the (b, g)'s workspace words to zero.
+//
+// Workspace per (b, g), int32 words: CH_HDR header words (next tile id,
+// arrivals, first dropped entry encoded as INT32_MAX - entry, 0 = none), then
+// one status word per tile (0, ST_A | count or ST_P | inclusive count), then
+// one claim word per new page (0 free, CLAIMING, NO_PAGE or page id + 1).
+constexpr int CH_HDR = 16;
+constexpr uint32_t ST_A = 1u << 30, ST_P = 2u << 30, ST_VAL = (1u << 30) - 1;
+constexpr int CLAIMING = -1, NO_PAGE = -2;
+constexpr int KB = 8;                 // 16-byte pieces per thread and tensor in one batch
+constexpr int WAIT_LIMIT = 1 << 20;   // polls before a wait gives up (about a second)
+
+struct OnepassWs {
+    int64_t stride;     // int32 words per (b, g)
+    int32_t max_tiles, max_claims;
+};
+
+__host__ __device__ inline OnepassWs onepass_ws(int32_t max_rows, int page_size) {
+    OnepassWs w;
+    w.max_tiles = (max_rows + TILE - 1) / TILE;
+    w.max_claims = (max_rows + page_size - 1) / page_size + 1;
+    w.stride = ((int64_t)CH_HDR + w.max_tiles + w.max_claims + 15) / 16 * 16;
+    return w;
+}
+
+__device__ inline uint32_t load_st(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_st(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive count of the tiles before t (wave 0).  false if a predecessor
+// never published (a workspace not left at zero by the previous call).
+__device__ inline bool look_back(const uint32_t *st, int t, int *excl_out) {
+    const int lane = threadIdx.x & 63;
+    int excl = 0;
+    int k = t - 1;
+    int polls = 0;
+    while (k >= 0) {
+        const int idx = k - lane;
+        const uint32_t s = idx >= 0 ? load_st(st + idx) : ST_P;  // before tile 0: prefix 0
+        const uint32_t kind = s >> 30;
+        const uint64_t is_p = __ballot(kind == 2);
+        const uint64_t not_ready = __ballot(kind == 0);
+        const int last = is_p ? __builtin_ctzll(is_p) : 63;   // lanes 0..last count
+        const uint64_t need = last == 63 ? ~0ull : ((2ull << last) - 1);
+        if (not_ready & need) {
+            if (++polls > WAIT_LIMIT) return false;
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        int v = lane <= last ? (int)(s & ST_VAL) : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        excl += v;
+        if (is_p) break;
+        k -= 64;
     }
-    __syncthreads();
-    if (threadIdx.x < c.n_kv) {
-        int s = 0;
-        for (int w = 0; w < NT / 64; ++w) s += lds_cnt[w][threadIdx.x];
-        a.ws[((int64_t)b * c.n_kv + threadIdx.x) * a.max_tiles + j] = s;
+    *excl_out = excl;
+    return true;
+}
+
+// Page ids of the list pages pg0 .. pg0+npg-1 of (b, g) into lds_pages (-1:
+// none could be had).  Wave 0; npg <= 64.  Winners of a claim first take and
+// publish their ids, then the others wait: a winner never waits in between,
+// so every wait ends.  false if a wait ran out.
+__device__ inline bool claim_pages(const CacheView &c, int64_t bg, int pg0, int npg, int first_new,
+                                   int32_t *claim, int32_t *hdr, int *lds_pages) {
+    const int lane = threadIdx.x & 63;
+    const int pidx = pg0 + lane;
+    int32_t *pt = c.page_table + bg * c.max_pages;
+    int id = -1;
+    bool win = false, wait = false;
+    int bits = 0;
+    if (lane < npg) {
+        if (pidx < first_new) {
+            id = pt[pidx];                       // the list's last page, partly filled
+        } else if (pidx >= c.max_pages) {
+            bits = SPKV_STATUS_TABLE_FULL;
+        } else {
+            const int prev = atomicCAS(claim + (pidx - first_new), 0, CLAIMING);
+            win = prev == 0;
+            wait = !win;
+            if (wait && prev != CLAIMING) {
+                id = prev > 0 ? prev - 1 : -1;
+                wait = false;
+            }
+        }
+    }
+    const uint64_t wins = __ballot(win);
+    if (wins) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(c.pool_next, __popcll(wins));
+        base = __shfl(base, 0);
+        if (win) {
+            id = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(wins >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)wins, 0u));
+            if (id >= c.n_pages) {
+                id = -1;
+                bits = SPKV_STATUS_POOL_FULL;
+                __hip_atomic_store(claim + (pidx - first_new), NO_PAGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                pt[pidx] = id;
+                __hip_atomic_store(claim + (pidx - first_new), id + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    bool ok = true;
+    if (wait) {
+        int polls = 0;
+        int v;
+        while ((v = __hip_atomic_load(claim + (pidx - first_new), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+               CLAIMING) {
+            if (++polls > WAIT_LIMIT) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (v == CLAIMING) ok = false;
+        id = v > 0 ? v - 1 : -1;
+    }
+    if (bits) {
+        atomicOr(c.status, bits);
+        // the entries from this page on cannot be stored: the list ends before it
+        atomicMax(hdr + 2, INT32_MAX - pidx * c.page_size);
+    }
+    if (lane < npg) lds_pages[lane] = id;
+    return __ballot(!ok) == 0;
+}
+
+// The key/value pieces of kept rows 0 .. nrow-1 (source rows in rows[]),
+// spread over threads tid = 0 .. nth-1: keys by piece idx = row * cpr +
+// chunk, values by idx = chunk * nrow + row (consecutive rows on
+// neighbouring lanes, for the transposed value store).
+template <typename T>
+__device__ __attribute__((always_inline)) inline void load_batch(const CompactArgs &a, int g, const int *rows,
+                                                                   int nrow, piece_t (&kv)[KB], piece_t (&vv)[KB],
+                                                                   int tid, int nth) {
+    constexpr int ES = sizeof(T);
+    const int hd = a.c.head_dim;
+    const int cpr = hd * ES / 16;
+    const int64_t ld_bytes = a.ld_kv * ES;
+    const int64_t goff = (int64_t)g * hd * ES;
+    const int np = nrow * cpr;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+        const int idx = u * nth + tid;
+        if (idx < np) {
+            const int kk = idx / cpr, ch = idx - kk * cpr;
+            kv[u] = *(const piece_t *)(a.k + rows[kk] * ld_bytes + goff + ch * 16);
+            const int vc = idx / nrow, vk = idx - vc * nrow;
+            vv[u] = *(const piece_t *)(a.v + rows[vk] * ld_bytes + goff + vc * 16);
+        }
     }
 }
 
-__global__ void __launch_bounds__(NT) compact_plan_kernel(CompactArgs a) {
-    __shared__ int lds_scan[NT];
-    __shared__ int lds_misc[4];
-    const int b = blockIdx.x;
-    const int g = blockIdx.y;
-    int r0, nb;
-    if (!seq_rows(a, b, &r0, &nb, false)) return;
-    const CacheView &c = a.c;
-    const int64_t bg = (int64_t)b * c.n_kv + g;
-    int32_t *cnt = a.ws + bg * a.max_tiles;
-    const int n_tiles = (nb + TILE - 1) / TILE;
-    int carry = 0;
-    for (int base = 0; base < n_tiles; base += NT) {
-        const int j = base + threadIdx.x;
-        const int x = j < n_tiles ? cnt[j] : 0;
-        lds_scan[threadIdx.x] = x;
-        __syncthreads();
-        // Hillis-Steele inclusive scan over NT values
-        for (int off = 1; off < NT; off <<= 1) {
-            const int y = threadIdx.x >= off ? lds_scan[threadIdx.x - off] : 0;
-            __syncthreads();
-            lds_scan[threadIdx.x] += y;
-            __syncthreads();
+// Store them to list entries e0 .. e0+nrow-1 (pages in lds_pages, relative to pg0).
+template <typename T>
+__device__ __attribute__((always_inline)) inline void store_batch(const CacheView &c, int e0, int nrow, int pg0,
+                                                                    const int *lds_pages, const piece_t (&kv)[KB],
+                                                                    const piece_t (&vv)[KB], int tid, int nth) {
+    constexpr int ES = sizeof(T);
+    constexpr int EPC = 16 / ES;
+    const int hd = c.head_dim;
+    const int cpr = hd / EPC;
+    const int P = c.page_size;
+    const int np = nrow * cpr;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+        const int idx = u * nth + tid;
+        if (idx < np) {
+            const int kk = idx / cpr, ch = idx - kk * cpr;
+            const int jk = e0 + kk;
+            const int pk = lds_pages[(jk >> c.page_shift) - pg0];
+            if (pk >= 0) *(piece_t *)(c.k_pages + (((int64_t)pk * P + (jk & (P - 1))) * hd) * ES + ch * 16) = kv[u];
+            const int vc = idx / nrow, vk = idx - vc * nrow;
+            const int jv = e0 + vk;
+            const int pv = lds_pages[(jv >> c.page_shift) - pg0];
+            if (pv >= 0) {
+                T *dv = (T *)c.v_pages + ((int64_t)pv * hd + vc * EPC) * P + (jv & (P - 1));
+#pragma unroll
+                for (int i = 0; i < EPC; ++i) dv[(int64_t)i * P] = piece_elem<T>(vv[u], i);
+            }
         }
-        if (j < n_tiles) cnt[j] = carry + lds_scan[threadIdx.x] - x;  // exclusive offset
-        carry += lds_scan[NT - 1];
-        __syncthreads();
-    }
-    const int old_len = c.lengths[bg];
-    const int new_len = grow_head(c, b, g, old_len, old_len + carry, lds_misc);
-    if (threadIdx.x == 0) {
-        c.lengths[bg] = new_len;
-        if (a.append_offsets) a.append_offsets[bg] = old_len;
-        int32_t *lens = a.ws + (int64_t)c.batch * c.n_kv * a.max_tiles;
-        lens[bg * 2] = old_len;
-        lens[bg * 2 + 1] = new_len;
     }
 }
 
 template <typename T>
-__global__ void __launch_bounds__(NT) compact_scatter_kernel(CompactArgs a) {
+__global__ void __launch_bounds__(NT) compact_onepass_kernel(CompactArgs a) {
     __shared__ int lds_rows[TILE];
     __shared__ int lds_waves[NT / 64];
     __shared__ int lds_pages[16];
-    const int j = blockIdx.x;
-    const int b = blockIdx.y;
-    const int g = blockIdx.z;
-    int r0, nb;
-    if (!seq_rows(a, b, &r0, &nb, false)) return;
-    const int row_lo = j * TILE;
-    if (row_lo >= nb) return;
-    const int row_hi = min(nb, row_lo + TILE);
-    const int p0 = a.pos0[b];
+    __shared__ int lds_misc[4];
     const CacheView &c = a.c;
-    const int64_t bg = (int64_t)b * c.n_kv + g;
-    if (a.flags & SPKV_APPEND_GLOBAL) {
-        const int32_t *lens = a.ws + (int64_t)c.batch * c.n_kv * a.max_tiles;
-        const int old_len = lens[bg * 2];
-        const int new_len = lens[bg * 2 + 1];
-        const int dst0 = old_len + a.ws[bg * a.max_tiles + j];
-        scatter_tile<T>(a, b, g, r0, row_lo, row_hi, dst0, new_len, p0, lds_rows, lds_waves, lds_pages);
-    }
-    if (a.flags & SPKV_APPEND_WINDOW) {
-        const int w_lo = max(row_lo, nb - c.window);
-        if (w_lo < row_hi) {
+    const int BG = c.batch * c.n_kv;
+    const int bg = (int)(blockIdx.x % (uint32_t)BG);
+    const int b = bg / c.n_kv, g = bg - b * c.n_kv;
+    const OnepassWs W = onepass_ws(a.max_rows, c.page_size);
+    int32_t *hdr = a.ws + (int64_t)bg * W.stride;
+    uint32_t *st = (uint32_t *)(hdr + CH_HDR);
+    int32_t *claim = hdr + CH_HDR + W.max_tiles;
+    if (threadIdx.x == 0) lds_misc[0] = arrive_dev(hdr);  // this workgroup's tile
+    __syncthreads();
+    const int t = lds_misc[0];
+    int r0 = 0, nb = 0;
+    const bool rows_ok = seq_rows(a, b, &r0, &nb, g == 0 && t == 0);
+    const int n_tiles = rows_ok ? (nb + TILE - 1) / TILE : 0;
+    const int old_len = c.lengths[bg];
+    const int P = c.page_size;
+    const int first_new = (old_len + P - 1) >> c.page_shift;
+    const bool global = (a.flags & SPKV_APPEND_GLOBAL) != 0;
+    if (t < n_tiles) {
+        const int row_lo = t * TILE, row_hi = min(nb, row_lo + TILE);
+        const int p0 = a.pos0[b];
+        if (global) {
+            const int i = row_lo + threadIdx.x;
+            const bool flag = i < row_hi && a.keep[(int64_t)(r0 + i) * c.n_kv + g] != 0;
+            int agg;
+            const int rank = block_rank(flag, lds_waves, &agg);
+            if (flag) lds_rows[rank] = r0 + i;
+            if (threadIdx.x == 0) store_st(st + t, (t == 0 ? ST_P : ST_A) | (uint32_t)agg);
             __syncthreads();
-            window_rows<T>(a, b, g, r0, w_lo, row_hi, p0, lds_rows);
+            // the first batch of the kept rows' pieces is loaded by waves 1-3
+            // while wave 0 finds the prefix and the pages (its own loads would
+            // hold up its polls: loads complete in order)
+            const int cpr = c.head_dim * (int)sizeof(T) / 16;
+            const int RB1 = (NT - 64) * KB / cpr, RB = NT * KB / cpr;  // rows per batch
+            piece_t kv[KB], vv[KB];
+            if (threadIdx.x >= 64) load_batch<T>(a, g, lds_rows, min(RB1, agg), kv, vv, threadIdx.x - 64, NT - 64);
+            if (threadIdx.x < 64) {
+                int excl = 0;
+                bool ok = true;
+                if (t > 0) {
+                    ok = look_back(st, t, &excl);
+                    if (threadIdx.x == 0 && ok) store_st(st + t, ST_P | (uint32_t)(excl + agg));
+                }
+                const int e0 = old_len + excl;
+                const int pg0 = e0 >> c.page_shift;
+                const int npg = agg ? ((e0 + agg - 1) >> c.page_shift) - pg0 + 1 : 0;
+                if (ok && npg) ok = claim_pages(c, bg, pg0, npg, first_new, claim, hdr, lds_pages);
+                if (!ok && threadIdx.x == 0) {
+                    atomicOr(c.status, SPKV_STATUS_STEP_TIMEOUT);
+                    atomicMax(hdr + 2, INT32_MAX - old_len);  // the append is dropped
+                }
+                if (threadIdx.x == 0) {
+                    lds_misc[1] = e0;
+                    lds_misc[2] = ok ? agg : 0;
+                }
+            }
+            __syncthreads();
+            const int e0 = lds_misc[1], n = lds_misc[2];
+            const int pg0 = e0 >> c.page_shift;
+            if (n) {
+                if (threadIdx.x >= 64)
+                    store_batch<T>(c, e0, min(RB1, n), pg0, lds_pages, kv, vv, threadIdx.x - 64, NT - 64);
+                for (int rb = RB1; rb < n; rb += RB) {
+                    load_batch<T>(a, g, lds_rows + rb, min(RB, n - rb), kv, vv, threadIdx.x, NT);
+                    store_batch<T>(c, e0 + rb, min(RB, n - rb), pg0, lds_pages, kv, vv, threadIdx.x, NT);
+                }
+                const bool store_u = c.u_pages != nullptr && a.utility != nullptr;
+                for (int kk = threadIdx.x; kk < n; kk += NT) {
+                    const int j = e0 + kk;
+                    const int page = lds_pages[(j >> c.page_shift) - pg0];
+                    if (page < 0) continue;
+                    const int64_t slot = (int64_t)page * P + (j & (P - 1));
+                    c.pos_pages[slot] = p0 + (lds_rows[kk] - r0);
+                    if (store_u) c.u_pages[slot] = a.utility[(int64_t)lds_rows[kk] * c.n_kv + g];
+                }
+            }
+            __syncthreads();  // lds_rows is reused below
+        }
+        if (a.flags & SPKV_APPEND_WINDOW) {
+            const int w_lo = max(row_lo, nb - c.window);
+            if (w_lo < row_hi) window_rows<T>(a, b, g, r0, w_lo, row_hi, p0, lds_rows);
         }
     }
+    // arrival: the status and claim words this workgroup wrote are complete
+    // (wave 0 wrote them all) before it counts itself in
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_misc[3] = arrive_dev(hdr + 1) == W.max_tiles - 1;
+    }
+    __syncthreads();
+    if (!lds_misc[3]) return;
+    // the last of the (b, g): new length, then the workspace words back to zero
+    if (threadIdx.x == 0) {
+        if (global && rows_ok) {
+            const int total = n_tiles ? (int)(load_st(st + n_tiles - 1) & ST_VAL) : 0;
+            const int enc = load_dev(hdr + 2);
+            const int limit = enc ? INT32_MAX - enc : INT32_MAX;
+            const int new_len = max(old_len, min(old_len + total, limit));
+            c.lengths[bg] = new_len;
+            if (a.append_offsets) a.append_offsets[bg] = old_len;
+            lds_misc[1] = min(W.max_claims, max(0, ((old_len + total + P - 1) >> c.page_shift) - first_new));
+        } else {
+            lds_misc[1] = 0;
+        }
+    }
+    __syncthreads();
+    const int n_claims = lds_misc[1];
+    for (int i = threadIdx.x; i < n_tiles; i += NT) store_st(st + i, 0u);
+    for (int i = threadIdx.x; i < n_claims; i += NT) reset_dev(claim + i);
+    if (threadIdx.x < 3) reset_dev(hdr + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -731,14 +957,12 @@ __global__ void cache_reset_kernel(CacheView c) {
 
 }  // namespace
 
-size_t compact_ws_bytes(int batch, int n_kv, int32_t max_rows) {
+size_t compact_ws_bytes(int batch, int n_kv, int page_size, int32_t max_rows) {
     if (max_rows <= TILE) return 0;
-    const int64_t max_tiles = (max_rows + TILE - 1) / TILE;
-    return (size_t)((int64_t)batch * n_kv * (max_tiles + 2)) * sizeof(int32_t);
+    return (size_t)((int64_t)batch * n_kv * onepass_ws(max_rows, page_size).stride) * sizeof(int32_t);
 }
 
-hipError_t launch_compact(const CompactArgs &a0, hipStream_t s) {
-    CompactArgs a = a0;
+hipError_t launch_compact(const CompactArgs &a, hipStream_t s) {
     const CacheView &c = a.c;
     const bool bf16 = c.dtype == SPKV_BF16;
     if (a.max_rows == 1) {
@@ -759,16 +983,12 @@ hipError_t launch_compact(const CompactArgs &a0, hipStream_t s) {
             hipLaunchKernelGGL(compact_small_kernel<float>, grid, dim3(NT), 0, s, a);
         return hipGetLastError();
     }
-    a.max_tiles = (a.max_rows + TILE - 1) / TILE;
-    if (a.flags & SPKV_APPEND_GLOBAL) {
-        hipLaunchKernelGGL(compact_count_kernel, dim3(a.max_tiles, c.batch), dim3(NT), 0, s, a);
-        hipLaunchKernelGGL(compact_plan_kernel, dim3(c.batch, c.n_kv), dim3(NT), 0, s, a);
-    }
-    dim3 grid(a.max_tiles, c.batch, c.n_kv);
+    // one workgroup per tile and (b, g), (b, g) fastest
+    const int64_t n_wg = (int64_t)onepass_ws(a.max_rows, c.page_size).max_tiles * c.batch * c.n_kv;
     if (bf16)
-        hipLaunchKernelGGL(compact_scatter_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
+        hipLaunchKernelGGL(compact_onepass_kernel<uint16_t>, dim3((uint32_t)n_wg), dim3(NT), 0, s, a);
     else
-        hipLaunchKernelGGL(compact_scatter_kernel<float>, grid, dim3(NT), 0, s, a);
+        hipLaunchKernelGGL(compact_onepass_kernel<float>, dim3((uint32_t)n_wg), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -86,10 +86,9 @@ struct CompactArgs {
     const int32_t *pos0;
     int32_t n_rows, max_rows, flags;
     int32_t *append_offsets;
-    int32_t *ws;  // large path: tile counts/offsets [B*Hkv*max_tiles] + lens [B*Hkv*2]
-    int32_t max_tiles;
+    int32_t *ws;  // large path: per (b, g) tile numbering, look-back status and page claims
 };
-size_t compact_ws_bytes(int batch, int n_kv, int32_t max_rows);
+size_t compact_ws_bytes(int batch, int n_kv, int page_size, int32_t max_rows);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t s);
 
 // ---- decode ----------------------------------------------------------------

@@ -281,3 +281,73 @@ def test_one_row_appends_capacity_and_bad_rows():
         spkv.spkv_cache_check(cache2)
     assert ei.value.code == spkv.SPKV_E_ROWS
     assert int(cache2.lengths[0].sum()) == 0 and int(cache2.lengths[1].sum()) == wl.n_kv
+
+
+@pytest.mark.parametrize("name, n_kv, hd, misalign", [
+    ("decode_32k", 8, 128, False),   # packed keep rows (one 8-byte load per row)
+    ("decode_32k", 8, 128, True),    # keep rows not 8-byte aligned: per-byte count
+    ("decode_32k", 3, 64, False),    # a head count that does not divide 16
+    ("decode_32k", 16, 64, False),
+    ("decode_32k", 1, 128, False),
+    ("tiny", 2, 64, False),          # f32 cache
+])
+def test_large_appends_share_one_workspace(name, n_kv, hd, misalign):
+    # appends of more than 256 rows per sequence run as one launch whose
+    # workgroups coordinate through the workspace; one workspace serves many
+    # calls of different sizes, including one that overflows the pool, and
+    # is back at zero after each
+    wl = tl.small_workload(name, n_kv=n_kv, head_dim=hd, n_q=n_kv)
+    B = 3
+    T = [2600, 1900, 3100]
+    rates = [0.3, 0.05, 0.2, 0.5, 0.7, 0.9, 1.0, 0.0] * 2
+    K, V, Z = zip(*[_seq_data(wl, T[b], b, 33, rates[:n_kv]) for b in range(B)])
+    cache = tl.new_cache(wl, B, max(T))
+    dt = tl.torch_dtype(wl)
+    ws = spkv.workspace(spkv.spkv_compact_ws_bytes(cache, sum(T), 1400))
+    done = [0] * B
+
+    def keep_dev(z):
+        z = z.astype(np.uint8)
+        if not misalign:
+            return tl.dev(z)
+        flat = torch.zeros(z.size + 1, dtype=torch.uint8, device="cuda")
+        flat[1:] = tl.dev(z.reshape(-1))
+        return flat[1:].view(z.shape)
+
+    for step in ([1400, 300, 1000], [257, 1400, 1100], [943, 200, 1000], [0, 0, 0]):
+        counts = [min(step[b], T[b] - done[b]) for b in range(B)]
+        offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        zz = np.concatenate([Z[b][done[b]:done[b] + counts[b]] for b in range(B)])
+        kk = np.concatenate([K[b][done[b]:done[b] + counts[b]] for b in range(B)])
+        vv = np.concatenate([V[b][done[b]:done[b] + counts[b]] for b in range(B)])
+        if offs[-1]:
+            spkv.spkv_compact_append(cache, keep_dev(zz), tl.dev(kk, dt), tl.dev(vv, dt), tl.dev(offs),
+                                     tl.dev(np.array(done, np.int32)), 1400, G_ | W_, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.abs().sum().item()) == 0, "workspace not back at zero"
+        done = [done[b] + counts[b] for b in range(B)]
+        if step == [943, 200, 1000]:
+            # an overflowing append on another cache, through the same workspace
+            need = sum(-(-int(Z[2][:1400, g].sum()) // 64) for g in range(n_kv))
+            assert need >= 2
+            n_small = need // 2              # half the pages the append needs
+            small = spkv.Cache(1, wl.n_kv, wl.head_dim, wl.window, 64, n_pages=n_small, max_pages_per_head=12,
+                               dtype=dt)
+            spkv.spkv_compact_append(small, keep_dev(Z[2][:1400]), tl.dev(K[2][:1400], dt), tl.dev(V[2][:1400], dt),
+                                     tl.dev(np.array([0, 1400], np.int32)), tl.dev(np.array([0], np.int32)), 1400, G_,
+                                     ws=ws)
+            torch.cuda.synchronize()
+            assert int(ws.abs().sum().item()) == 0
+            with pytest.raises(spkv.SpkvError) as ei:
+                spkv.spkv_cache_check(small)
+            assert ei.value.code == spkv.SPKV_E_CAPACITY
+            lists = oracle.compact(Z[2][:1400], 0)
+            for g in range(wl.n_kv):
+                k, v, pos = small.read_head(0, g)
+                assert len(pos) <= min(12 * 64, len(lists[g]))
+                np.testing.assert_array_equal(pos.cpu().numpy(), lists[g][:len(pos)])
+                np.testing.assert_array_equal(v.float().cpu().numpy(), V[2][lists[g][:len(pos)], g])
+            assert int(small.lengths.sum()) <= n_small * 64
+    assert done == T
+    assert spkv.spkv_cache_check(cache) == 0
+    _check_cache(cache, wl, K, V, Z, T)
