@@ -61,6 +61,8 @@ def _load():
     lib.spkv_oracle_attention.restype = ci
     lib.spkv_oracle_visible_count.argtypes = [i64, i64, i64, vp, vp, i64, i64, vp]
     lib.spkv_oracle_visible_count.restype = ci
+    lib.spkv_oracle_sink_gate.argtypes = [i64, i64, i64, i64, i64, i64, vp, i64, vp, vp, f64, vp, vp, ci]
+    lib.spkv_oracle_sink_gate.restype = ci
     lib.spkv_oracle_max_threads.restype = ci
     lib.spkv_oracle_version.restype = ci
     _lib = lib
@@ -103,6 +105,26 @@ def gate(H, W1, b1, W2, b2, tau: float, threads: int = 1):
     if rc != 0:
         raise ValueError(f"spkv_oracle_gate rejected its arguments ({rc})")
     return u, logit, z
+
+
+def sink_gate(H, W, sinks, group: int, tau: float, threads: int = 1):
+    """O8, the sink-attention gate (Fast KVzip page, core method).  Returns
+    (u [n, n_kv] f64, z [n, n_kv] u8).
+
+    H [n, d_model]; W [n_kv, (group + 1) * d_key, d_model] (per head the
+    group query blocks, then the key block); sinks [n_kv, n_sinks, d_key]."""
+    lib = _load()
+    H, W, sinks = _f32(H), _f32(W), _f32(sinks)
+    n, d = H.shape
+    nkv, ns, dk = sinks.shape
+    assert W.shape == (nkv, (group + 1) * dk, d)
+    u = np.empty((n, nkv), np.float64)
+    z = np.empty((n, nkv), np.uint8)
+    rc = lib.spkv_oracle_sink_gate(n, d, nkv, int(group), dk, ns, _p(H), d, _p(W), _p(sinks), float(tau),
+                                   _p(u), _p(z), int(threads))
+    if rc != 0:
+        raise ValueError(f"spkv_oracle_sink_gate rejected its arguments ({rc})")
+    return u, z
 
 
 def compact(z, pos0: int = 0):

@@ -404,3 +404,102 @@ int spkv_oracle_visible_count(int64_t T, int64_t n_kv, int64_t w,
     }
     return 0;
 }
+
+/*
+ * O8 -- the low-rank sink-attention gate of Fast KVzip, an alternative
+ * utility predictor f behind the same keep decision, from the page
+ * "Fast KVzip: efficient and accurate LLM inference with gated KV eviction"
+ * (a summary of arXiv 2601.17668), section "core method" (the gate paragraph)
+ * and section "reproduction" (S = 16, D' = 16).  The page describes it in
+ * words only; the reading written out here (every step is a reading):
+ *
+ *   for key head h, with G = query heads per key head and D' = d_key:
+ *     q_{h,g} = Wq_{h,g} x      (D' values, g = 0 .. G-1)   linear, no bias
+ *     k_h     = Wk_h x          (D' values)                  linear, no bias
+ *     s_{h,j}                   (S learned sink keys, D' values each)
+ *     a_{h,g} = exp(q.k / sqrt(D')) / (exp(q.k / sqrt(D')) + sum_j exp(q.s_j / sqrt(D')))
+ *               -- the attention the token's own key receives against the
+ *               sinks, a softmax over 1 + S keys
+ *     u_h     = max_g a_{h,g}  -- the page's training target is the largest
+ *               attention a pair receives, so the G query heads of a group
+ *               are combined by their maximum
+ *     z_h     = 1 if u_h >= tau else 0   (Eq. (2) of SP-KV, unchanged)
+ *
+ * W [n_kv, (G + 1) * d_key, d_model]: per head, the G * d_key query rows
+ * (g-major) then the d_key key rows.  sinks [n_kv, n_sinks, d_key].
+ * Evaluated as written, in double; the softmax is formed with its maximum
+ * subtracted (the same value).  A NaN gives z = 0.
+ * u_out [n_rows, n_kv] doubles (may be NULL), z_out bytes (may be NULL).
+ * Parity pins: zero hidden state -> 1 / (1 + S); no sinks -> 1; sinks far
+ * against q -> 1; G = S = 1 -> the logistic of the score difference; sink
+ * and query-head permutations; the bilinear rescaling of q against k and
+ * the sinks.  Parity against Fast KVzip itself is unpinned: the page prints
+ * no formula and no worked example.
+ */
+int spkv_oracle_sink_gate(int64_t n_rows, int64_t d_model, int64_t n_kv, int64_t G,
+                          int64_t d_key, int64_t n_sinks, const float *H, int64_t ld_h,
+                          const float *W, const float *sinks, double tau, double *u_out,
+                          uint8_t *z_out, int n_threads)
+{
+    if (n_rows < 0 || d_model <= 0 || n_kv <= 0 || G <= 0 || d_key <= 0 || n_sinks < 0 ||
+        ld_h < d_model || d_key > 256 || G > 64 || n_sinks > 1024)
+        return -1;
+    if (n_threads < 1)
+        n_threads = 1;
+    const int64_t per_head = (G + 1) * d_key;
+    const double inv_sqrt = 1.0 / sqrt((double)d_key);
+    int64_t r;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+#endif
+    for (r = 0; r < n_rows; ++r) {
+        const float *x = H + r * ld_h;
+        double proj[65 * 256]; /* (G + 1) * d_key values of one head */
+        for (int64_t h = 0; h < n_kv; ++h) {
+            const float *Wh = W + h * per_head * d_model;
+            for (int64_t o = 0; o < per_head; ++o) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < d_model; ++i)
+                    acc += (double)Wh[o * d_model + i] * (double)x[i];
+                proj[o] = acc;
+            }
+            const double *k = proj + G * d_key;
+            double u = -1.0;
+            int nan = 0;
+            for (int64_t g = 0; g < G; ++g) {
+                const double *q = proj + g * d_key;
+                double own = 0.0;
+                for (int64_t e = 0; e < d_key; ++e)
+                    own += q[e] * k[e];
+                own *= inv_sqrt;
+                double m = own;
+                double sc[1024];
+                for (int64_t j = 0; j < n_sinks; ++j) {
+                    const float *s = sinks + (h * n_sinks + j) * d_key;
+                    double d = 0.0;
+                    for (int64_t e = 0; e < d_key; ++e)
+                        d += q[e] * (double)s[e];
+                    sc[j] = d * inv_sqrt;
+                    if (sc[j] > m)
+                        m = sc[j];
+                }
+                double den = exp(own - m);
+                const double num = den;
+                for (int64_t j = 0; j < n_sinks; ++j)
+                    den += exp(sc[j] - m);
+                const double a = num / den;
+                if (a != a)
+                    nan = 1;
+                if (a > u)
+                    u = a;
+            }
+            if (nan)
+                u = NAN;
+            if (u_out)
+                u_out[r * n_kv + h] = u;
+            if (z_out)
+                z_out[r * n_kv + h] = (uint8_t)(u >= tau ? 1 : 0);
+        }
+    }
+    return 0;
+}

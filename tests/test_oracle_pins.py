@@ -561,3 +561,141 @@ def test_soft_weight_grows_with_utility():
         o, _ = oracle.soft_attention(Q, [T - 1], K, V, u, w, tau=0.5, beta=0.01, c=10.0)
         assert o[0, 0, 0] > prev
         prev = o[0, 0, 0]
+
+
+# ----------------------------------------------------------------------------
+# O8: the sink-attention gate (Fast KVzip page, core method)
+# ----------------------------------------------------------------------------
+
+def _selector(n_kv, G, dk):
+    """Projection that copies input block (h, o) to output o of head h: with it
+    q_{h,g} and k_h are slices of the hidden state chosen by the test."""
+    per = (G + 1) * dk
+    d = n_kv * per
+    W = np.zeros((n_kv, per, d), np.float32)
+    for h in range(n_kv):
+        W[h, np.arange(per), h * per + np.arange(per)] = 1.0
+    return W, d
+
+
+def _hidden(qs, ks):
+    """qs [n_kv][G][dk], ks [n_kv][dk] -> the hidden row that _selector maps onto them."""
+    return np.concatenate([np.concatenate([np.asarray(q, np.float32).reshape(-1), np.asarray(k, np.float32)])
+                           for q, k in zip(qs, ks)])[None, :]
+
+
+@pytest.mark.parametrize("S", [0, 1, 16])
+def test_sink_gate_zero_state_is_one_over_one_plus_S(S):
+    # h = 0 gives q = k = 0: every score is 0 and the own key gets 1 / (1 + S)
+    r = np.random.default_rng(1)
+    n_kv, G, dk, d = 3, 4, 16, 64
+    W = r.standard_normal((n_kv, (G + 1) * dk, d)).astype(np.float32)
+    sinks = r.standard_normal((n_kv, S, dk)).astype(np.float32)
+    u, z = oracle.sink_gate(np.zeros((2, d), np.float32), W, sinks, G, 0.5)
+    np.testing.assert_allclose(u, 1.0 / (1 + S), rtol=0, atol=1e-15)
+    assert np.all(z == (1.0 / (1 + S) >= 0.5))
+
+
+def test_sink_gate_no_sinks_keeps_everything():
+    r = np.random.default_rng(2)
+    W = r.standard_normal((2, 3 * 8, 40)).astype(np.float32)
+    u, z = oracle.sink_gate(r.standard_normal((5, 40)).astype(np.float32), W, np.zeros((2, 0, 8), np.float32), 2,
+                            0.999)
+    assert np.all(u == 1.0) and np.all(z == 1)
+
+
+@pytest.mark.parametrize("dk", [4, 16])
+def test_sink_gate_one_query_one_sink_is_logistic(dk):
+    # softmax over two scores = logistic of their difference, scaled by 1/sqrt(dk)
+    r = np.random.default_rng(3)
+    n_kv, G = 2, 1
+    W, d = _selector(n_kv, G, dk)
+    qs = r.standard_normal((n_kv, G, dk)).astype(np.float32)
+    ks = r.standard_normal((n_kv, dk)).astype(np.float32)
+    sinks = r.standard_normal((n_kv, 1, dk)).astype(np.float32)
+    u, _ = oracle.sink_gate(_hidden(qs, ks), W, sinks, G, 0.5)
+    for h in range(n_kv):
+        q = qs[h, 0].astype(np.float64)
+        diff = (q @ ks[h] - q @ sinks[h, 0]) / math.sqrt(dk)
+        assert abs(u[0, h] - 1.0 / (1.0 + math.exp(-diff))) < 1e-14
+
+
+def test_sink_gate_far_sinks_and_identical_queries():
+    r = np.random.default_rng(4)
+    n_kv, G, dk, S = 2, 3, 16, 16
+    W, d = _selector(n_kv, G, dk)
+    qs = r.standard_normal((n_kv, G, dk)).astype(np.float32)
+    ks = r.standard_normal((n_kv, dk)).astype(np.float32)
+    # sinks pointing away from every query of the head: their scores go to -inf
+    far = np.stack([np.stack([-40.0 * qs[h].sum(0)] * S) for h in range(n_kv)]).astype(np.float32)
+    u, z = oracle.sink_gate(_hidden(qs, ks), W, far, G, 0.999)
+    assert np.all(u > 1 - 1e-12) and np.all(z == 1)
+    # all query heads equal to the first: the maximum is that one head's value
+    same = np.repeat(qs[:, :1], G, axis=1)
+    sinks = r.standard_normal((n_kv, S, dk)).astype(np.float32)
+    u_same, _ = oracle.sink_gate(_hidden(same, ks), W, sinks, G, 0.5)
+    W1, _ = _selector(n_kv, 1, dk)
+    u_one, _ = oracle.sink_gate(_hidden(qs[:, :1], ks), W1, sinks, 1, 0.5)
+    np.testing.assert_allclose(u_same, u_one, rtol=0, atol=1e-15)
+    # one query head zero: its value is 1 / (1 + S), the gate the maximum
+    zq = qs.copy()
+    zq[:, 1] = 0
+    u_z, _ = oracle.sink_gate(_hidden(zq, ks), W, sinks, G, 0.5)
+    assert np.all(u_z >= 1.0 / (1 + S) - 1e-15)
+
+
+def test_sink_gate_invariances_and_head_order():
+    r = np.random.default_rng(5)
+    n_kv, G, dk, S, d, n = 4, 2, 8, 5, 48, 6
+    H = r.standard_normal((n, d)).astype(np.float32)
+    W = (r.standard_normal((n_kv, (G + 1) * dk, d)) * 0.2).astype(np.float32)
+    sinks = r.standard_normal((n_kv, S, dk)).astype(np.float32)
+    u, _ = oracle.sink_gate(H, W, sinks, G, 0.5)
+    assert np.all((u > 0) & (u < 1))
+    # sinks in another order
+    u2, _ = oracle.sink_gate(H, W, sinks[:, ::-1].copy(), G, 0.5)
+    np.testing.assert_allclose(u2, u, rtol=1e-13, atol=0)
+    # query heads of a group in another order
+    Wp = W.copy()
+    Wp[:, :G * dk] = W[:, :G * dk].reshape(n_kv, G, dk, d)[:, ::-1].reshape(n_kv, G * dk, d)
+    u3, _ = oracle.sink_gate(H, Wp, sinks, G, 0.5)
+    np.testing.assert_allclose(u3, u, rtol=1e-13, atol=0)
+    # q scaled by 2, keys and sinks by 1/2 (exact in binary): scores unchanged
+    Ws = W.copy()
+    Ws[:, :G * dk] *= 2
+    Ws[:, G * dk:] *= 0.5
+    u4, _ = oracle.sink_gate(H, Ws, sinks * 0.5, G, 0.5)
+    np.testing.assert_allclose(u4, u, rtol=1e-13, atol=0)
+    # heads are independent and in order: reversing the heads reverses the columns
+    u5, _ = oracle.sink_gate(H, W[::-1].copy(), sinks[::-1].copy(), G, 0.5)
+    np.testing.assert_allclose(u5, u[:, ::-1], rtol=1e-13, atol=0)
+    # a key aligned further with every query raises the value
+    W6 = W.copy()
+    W6[:, G * dk:] += 0.5 * W[:, :dk] + 0.5 * W[:, dk:2 * dk]
+    u6, _ = oracle.sink_gate(H, W6, sinks, G, 0.5)
+    assert np.mean(u6 > u) > 0.5
+
+
+def test_sink_gate_threshold_inclusive_and_nan():
+    n_kv, G, dk = 1, 1, 4
+    W, d = _selector(n_kv, G, dk)
+    u, z = oracle.sink_gate(np.zeros((1, d), np.float32), W, np.zeros((1, 3, dk), np.float32), G, 0.25)
+    assert u[0, 0] == 0.25 and z[0, 0] == 1    # exactly tau is kept
+    h = np.zeros((1, d), np.float32)
+    h[0, 0] = np.nan
+    u, z = oracle.sink_gate(h, W, np.ones((1, 3, dk), np.float32), G, 0.0)
+    assert np.isnan(u[0, 0]) and z[0, 0] == 0
+
+
+def test_sink_gate_combines_query_heads_by_maximum():
+    # G = 2, S = 1, query head 1 zero (value 1/2): the gate is max(logistic, 1/2),
+    # which tells the maximum from a mean or a sum of the two
+    dk = 4
+    W, d = _selector(1, 2, dk)
+    k = np.array([1.0, 0.0, 0.5, 0.0], np.float32)
+    s = np.array([[0.0, 1.0, 0.0, 0.5]], np.float32)
+    for q0 in (np.array([2.0, 0.0, 1.0, 0.0], np.float32), np.array([0.0, 2.0, 0.0, 1.0], np.float32)):
+        qs = np.stack([q0, np.zeros(dk, np.float32)])[None]
+        u, _ = oracle.sink_gate(_hidden(qs, k[None]), W, s[None], 2, 0.5)
+        a0 = 1.0 / (1.0 + math.exp(-(float(q0 @ k) - float(q0 @ s[0])) / math.sqrt(dk)))
+        assert abs(u[0, 0] - max(a0, 0.5)) < 1e-15
