@@ -97,7 +97,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
     p.add_argument("--workload", default="decode_32k",
                    choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k",
-                            "head_stats_1m", "soft_prefill_16k"])
+                            "head_stats_1m", "soft_prefill_16k", "sink_gate_16k"])
     p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
     p.add_argument("--step-mode", choices=("auto", "fused", "separate"), default="auto",
@@ -904,6 +904,71 @@ def cpu_baseline_soft(wl, budget_s: float) -> dict:
                       f"(scaled by the pairs of the whole forward)"}
 
 
+SINK_ROWS, SINK_G, SINK_S = 16384, 4, 16
+
+
+def bench_sink_gate(args, wl):
+    """The sink-attention gate of the Fast KVzip page (spkv_gate_sink) over one
+    16384-row prefill chunk of the 8B-shaped layer: d_model 4096, 8 key heads,
+    4 query heads per key head, the page's S = 16 sinks and d_key = 16;
+    weights N(0, 1/d_model) in bf16, sinks N(0, 1).  One step = one call."""
+    import torch
+    from learned_kv_cache_sp_amd import inputs, spkv
+    n, d, nkv, G, S = SINK_ROWS, wl.d_model, wl.n_kv, SINK_G, SINK_S
+    W = torch.from_numpy(inputs.normal((nkv, (G + 1) * 16, d), wl.seed, 1) / np.float32(np.sqrt(d)))
+    W = W.to(torch.bfloat16).cuda()
+    sinks = torch.from_numpy(np.random.default_rng(wl.seed).standard_normal((nkv, S, 16)).astype(np.float32)).cuda()
+    g = spkv.SinkGateWeights(W, sinks, G)
+    Hs = [inputs.device_normal((n, d), wl.seed, 4000 + i, torch.bfloat16) for i in range(4)]
+    u = torch.empty((n, nkv), dtype=torch.float32, device="cuda")
+    z = torch.empty((n, nkv), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        spkv.spkv_gate_sink(g, Hs[i % 4], wl.tau, utility=u, keep=z)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        spkv.spkv_gate_sink(g, Hs[i % 4], wl.tau, utility=u, keep=z)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * n * d * (G + 1) * 16 * nkv
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "sink-attention gate rows/s (Fast KVzip gate, 8B shape)", "value": n / (ms * 1e-3),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sink_gate_16k", "rows": n, "d_model": d, "n_kv": nkv, "group": G, "n_sinks": S,
+                   "d_key": 16, "step": "spkv_gate_sink (one launch; the time per step is the launch's)"},
+        "roofline": {"bound": "mfma", "kernel": "gate_pipe_kernel<80, 64, true> (spkv_gate_sink)",
+                     "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "hidden_GBs": round(n * d * 2 / (ms * 1e-3) / 1e9, 1),
+                     "launch_us": round(ms * 1e3, 2)},
+    }
+
+
+def cpu_baseline_sink_gate(wl, budget_s: float) -> dict:
+    """The oracle's sink gate on 64-row samples of the same shapes until about budget_s."""
+    import oracle
+    from learned_kv_cache_sp_amd import inputs
+    oracle.build(force=False)
+    th = _threads()
+    d, nkv, G, S = wl.d_model, wl.n_kv, SINK_G, SINK_S
+    W = inputs.normal((nkv, (G + 1) * 16, d), wl.seed, 1) / np.float32(np.sqrt(d))
+    sinks = np.random.default_rng(wl.seed).standard_normal((nkv, S, 16)).astype(np.float32)
+    rows = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        H = inputs.normal((64, d), wl.seed, 4100 + rows, dtype="bf16")
+        oracle.sink_gate(H, W, sinks, G, wl.tau, threads=th)
+        rows += 64
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "rows/s", "cores": th, "kind": "oracle",
+            "sample": f"{rows} rows in 64-row calls of oracle.sink_gate, {el:.1f} s"}
+
+
 HEAD_STATS_ROWS, HEAD_STATS_KV = 1 << 20, 8
 
 
@@ -1149,6 +1214,8 @@ def host_cpu() -> tuple[int, dict]:
 def cpu_baseline(name: str, wl, budget_s: float) -> dict:
     if name == "soft_prefill_16k":
         r = cpu_baseline_soft(wl, budget_s)
+    elif name == "sink_gate_16k":
+        r = cpu_baseline_sink_gate(wl, budget_s)
     elif name == "head_stats_1m":
         r = cpu_baseline_head_stats(budget_s)
     elif name == "rethreshold_32k":
@@ -1160,7 +1227,7 @@ def cpu_baseline(name: str, wl, budget_s: float) -> dict:
 
 
 DEFAULT_STEPS = {"decode": (256, 16), "prefill": (4, 1), "rethreshold_32k": (20, 3), "head_stats_1m": (50, 5),
-                 "soft_prefill_16k": (5, 1)}
+                 "soft_prefill_16k": (5, 1), "sink_gate_16k": (50, 5)}
 SECONDARY = ["decode_131k", "ragged_32", "prefill_64k"]
 
 
@@ -1174,6 +1241,9 @@ def run_workload(args, name: str, steps=None, warmup=None) -> dict:
     if name == "soft_prefill_16k":
         wl = inputs.WORKLOADS["prefill_64k"]
         res = bench_soft_prefill(a, wl)
+    elif name == "sink_gate_16k":
+        wl = inputs.WORKLOADS["prefill_64k"]
+        res = bench_sink_gate(a, wl)
     elif name == "head_stats_1m":
         wl = None
         res = bench_head_stats(a)

@@ -171,6 +171,45 @@ int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows,
 size_t spkv_gate_ws_bytes(const spkv_gate_desc *g, int64_t n_rows);
 
 /*
+ * The sink-attention gate, an alternative predictor f in front of the same
+ * keep decision (the gate of Fast KVzip: page "Fast KVzip: efficient and
+ * accurate LLM inference with gated KV eviction", section "core method";
+ * S = 16 and d_key = 16 in section "reproduction").  The page gives it in
+ * words; the reading implemented:
+ *   per key head h, with G = group query heads per key head:
+ *     q_{h,g} = Wq_{h,g} x (d_key values), k_h = Wk_h x (d_key values),
+ *     a_{h,g} = softmax over {k_h, sink_{h,1..S}} of q_{h,g} . key / sqrt(d_key),
+ *               taken at k_h (the weight of the token's own key),
+ *     u_h = max_g a_{h,g},  keep = (u_h >= tau).
+ *   w      [n_kv][(group + 1) * d_key][d_model] dtype: per head the group
+ *          query blocks (g-major), then the key block
+ *   sinks  [n_kv][n_sinks][d_key] f32
+ * Supported: bf16, d_model a multiple of 64, n_kv <= 16, group in
+ * {1, 2, 4, 8}, d_key = 16, n_sinks <= 64.
+ */
+typedef struct spkv_sink_gate_desc {
+    int32_t d_model;
+    int32_t n_kv;
+    int32_t group;
+    int32_t d_key;
+    int32_t n_sinks;
+    int32_t dtype; /* spkv_dtype */
+    const void *w;
+    const float *sinks;
+} spkv_sink_gate_desc;
+
+/*
+ * spkv_gate_sink -- the sink-attention gate for n_rows independent rows.
+ *   hidden  [n_rows, ld_hidden] bf16 (first d_model entries of each row)
+ *   utility [n_rows, n_kv] f32, may be NULL;  keep [n_rows, n_kv] uint8
+ * One launch (a workgroup per 64 rows and key head: the projections on
+ * v_mfma_f32_16x16x32_bf16 accumulate in f32, then the scores, softmax and
+ * maximum in f32); no workspace.  A NaN gives keep = 0.
+ */
+int spkv_gate_sink(const spkv_sink_gate_desc *g, const void *hidden, int64_t n_rows, int64_t ld_hidden,
+                   float tau, float *utility, uint8_t *keep, void *stream);
+
+/*
  * spkv_compact_append -- append one batch of rows to the cache.
  *   Rows of sequence b are rows row_offsets[b] .. row_offsets[b+1]-1 of k, v
  *   and keep, at token positions pos0[b], pos0[b]+1, ... (consecutive).

@@ -162,7 +162,7 @@ int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows, int64
     const size_t need = spkv::gate_ws_bytes(g->d_model, g->d_hidden, g->n_kv, g->dtype, n_rows);
     if (need && (!ws || ws_bytes < need))
         return fail(SPKV_E_WORKSPACE, "gate workspace %zu < %zu bytes", ws_bytes, need);
-    spkv::GateArgs a;
+    spkv::GateArgs a = {};
     a.d_model = g->d_model;
     a.d_hidden = g->d_hidden;
     a.n_kv = g->n_kv;
@@ -181,6 +181,47 @@ int spkv_gate(const spkv_gate_desc *g, const void *hidden, int64_t n_rows, int64
     a.n_split = spkv::gate_split_for(g->d_model, g->dtype, n_rows);
     hipError_t e = spkv::launch_gate(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gate launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+int spkv_gate_sink(const spkv_sink_gate_desc *g, const void *hidden, int64_t n_rows, int64_t ld_hidden, float tau,
+                   float *utility, uint8_t *keep, void *stream) {
+    if (!g) return fail(SPKV_E_INVALID, "gate descriptor is NULL");
+    if (g->dtype != SPKV_BF16) return fail(SPKV_E_UNSUPPORTED, "sink gate dtype %d (bf16 only)", g->dtype);
+    if (g->d_model < 64 || g->d_model % 64)
+        return fail(SPKV_E_UNSUPPORTED, "d_model %d (a positive multiple of 64)", g->d_model);
+    if (g->n_kv < 1 || g->n_kv > 16) return fail(SPKV_E_UNSUPPORTED, "n_kv %d (1..16)", g->n_kv);
+    if (g->group != 1 && g->group != 2 && g->group != 4 && g->group != 8)
+        return fail(SPKV_E_UNSUPPORTED, "group %d (1, 2, 4 or 8)", g->group);
+    if (g->d_key != 16) return fail(SPKV_E_UNSUPPORTED, "d_key %d (16)", g->d_key);
+    if (g->n_sinks < 0 || g->n_sinks > 64) return fail(SPKV_E_UNSUPPORTED, "n_sinks %d (0..64)", g->n_sinks);
+    if (!g->w || (g->n_sinks && !g->sinks)) return fail(SPKV_E_INVALID, "gate weights NULL");
+    if (!aligned16(g->w)) return fail(SPKV_E_INVALID, "w not 16-byte aligned");
+    if (n_rows < 0 || n_rows > (int64_t)INT32_MAX) return fail(SPKV_E_INVALID, "n_rows %lld", (long long)n_rows);
+    if (n_rows == 0) return SPKV_OK;
+    if (!hidden || !keep) return fail(SPKV_E_INVALID, "hidden / keep is NULL");
+    if (!aligned16(hidden)) return fail(SPKV_E_INVALID, "hidden not 16-byte aligned");
+    if (int r = check_ld(ld_hidden, g->d_model, g->dtype, "ld_hidden")) return r;
+    if (std::isnan(tau)) return fail(SPKV_E_INVALID, "tau is NaN");
+    spkv::GateArgs a = {};
+    a.d_model = g->d_model;
+    a.d_hidden = (g->group + 1) * g->d_key;
+    a.n_kv = g->n_kv;
+    a.dtype = g->dtype;
+    a.w1 = g->w;
+    a.sinks = g->sinks;
+    a.n_sinks = g->n_sinks;
+    a.group = g->group;
+    a.hidden = hidden;
+    a.n_rows = n_rows;
+    a.ld_hidden = ld_hidden;
+    a.tau = tau;
+    a.utility = utility;
+    a.keep = keep;
+    a.n_split = 1;
+    hipError_t e = spkv::launch_sink_gate(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sink gate launch");
     return SPKV_OK;
 }
 

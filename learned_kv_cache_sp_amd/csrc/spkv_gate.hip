@@ -79,7 +79,62 @@ __device__ inline float relu_keep_nan(float x) { return x < 0.f ? 0.f : x; }
 // read one operand group hit 16 different bank groups).
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int HG, int JC> struct GatePipe {
+// Sink-attention gate (Fast KVzip page, core method), epilogue of one
+// (64-row tile, key head): act[r] holds the head's G query vectors of 16
+// then its key of 16.  Each query head's weight on the token's own key
+// against the n_sinks sink keys (scores scaled by 1/sqrt(16)), softmax with
+// its maximum subtracted; the gate is the largest over the G query heads
+// (a NaN anywhere gives NaN, so keep = 0).
+template <int HG>
+__device__ void sink_epilogue(const GateArgs &a, const float *act, int64_t row0, int head, float *scratch) {
+    constexpr int DK = 16;
+    const int G = HG / DK - 1;
+    const int S = a.n_sinks;
+    float *lds_s = scratch;                // [S][16]
+    float *lds_a = scratch + 64 * DK;      // [64][G]
+    for (int i = threadIdx.x; i < S * DK; i += NT) lds_s[i] = a.sinks[(int64_t)head * S * DK + i];
+    __syncthreads();
+    for (int item = threadIdx.x; item < 64 * G; item += NT) {
+        const int r = item / G, g = item - r * G;
+        const float *q = act + r * (HG + 1) + g * DK;
+        const float *k = act + r * (HG + 1) + G * DK;
+        float own = 0.f;
+#pragma unroll
+        for (int e = 0; e < DK; ++e) own = fmaf(q[e], k[e], own);
+        own *= 0.25f;
+        float m = own;
+        for (int j = 0; j < S; ++j) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < DK; ++e) d = fmaf(q[e], lds_s[j * DK + e], d);
+            m = fmaxf(m, d * 0.25f);
+        }
+        const float num = expf(own - m);
+        float den = num;
+        for (int j = 0; j < S; ++j) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < DK; ++e) d = fmaf(q[e], lds_s[j * DK + e], d);
+            den += expf(d * 0.25f - m);
+        }
+        lds_a[r * G + g] = num / den;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int64_t row = row0 + threadIdx.x;
+        if (row < a.n_rows) {
+            float u = lds_a[threadIdx.x * G];
+            for (int g = 1; g < G; ++g) {
+                const float x = lds_a[threadIdx.x * G + g];
+                u = (x != x || x > u) ? x : u;  // NaN wins
+            }
+            if (a.utility) a.utility[row * a.n_kv + head] = u;
+            a.keep[row * a.n_kv + head] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+        }
+    }
+}
+
+template <int HG, int JC, bool SINK = false> struct GatePipe {
     // One depth for both streams: vector-memory loads complete in issue
     // order, so waiting for W1's pieces of iteration j also waits for every
     // hidden-row load issued before them -- a deeper register prefetch than
@@ -88,9 +143,11 @@ template <int HG, int JC> struct GatePipe {
     static constexpr int P = HG <= 128 ? 8 : 3;
     static constexpr int NSTAGE = P + 1;
     static constexpr int SBYTES = HG * 128;              // W1 stage: HG units x 64 columns
-    static constexpr int LB = SBYTES / 1024 / 4;         // direct loads per wave and stage
+    static constexpr int PIECES = HG / 8;                // 1 KB pieces of a W1 stage (8 units each)
+    static constexpr int LB = (PIECES + 3) / 4;          // direct loads per wave and stage (at most)
     static constexpr int LA = 2;                         // hidden-row loads per wave and iteration
-    static constexpr int EPI = 64 * (HG + 1) * 4 + 16 * (HG + 1) * 4;
+    static constexpr int EPI = SINK ? 64 * (HG + 1) * 4 + 64 * 16 * 4 + 64 * 8 * 4
+                                    : 64 * (HG + 1) * 4 + 16 * (HG + 1) * 4;
     static constexpr int LDS = NSTAGE * SBYTES > EPI ? NSTAGE * SBYTES : EPI;
 };
 
@@ -112,9 +169,9 @@ __device__ inline void wait_vm(int n) {
 // the wait counts fold to constants and the compiler tracks each hidden-row
 // load to its use (a run-time trip count makes it wait for every load at the
 // top of each unrolled block).
-template <int HG, int JC>
+template <int HG, int JC, bool SINK = false>
 __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
-    using C = GatePipe<HG, JC>;
+    using C = GatePipe<HG, JC, SINK>;
     constexpr int P = C::P;
     constexpr int NTL = HG / 16;  // unit tiles
     static_assert((P - 1) * (C::LB + C::LA) <= 63, "vmcnt range");
@@ -123,22 +180,37 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
     const int wave = threadIdx.x >> 6;
     const int i16 = lane & 15;
     const int q4 = lane >> 4;
-    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    // the sink gate runs one workgroup per (64-row tile, key head); the heads
+    // of a tile are launched next to each other and on the same XCD (ids
+    // 8 apart), so the tile's hidden rows are read from HBM about once
+    int64_t tile = blockIdx.x;
+    int head = 0;
+    if constexpr (SINK) {
+        const int x = (int)blockIdx.x;
+        tile = (int64_t)(x / (8 * a.n_kv)) * 8 + (x & 7);
+        head = (x / 8) % a.n_kv;
+    }
+    const int64_t row0 = tile * 64;
+    if (SINK && row0 >= a.n_rows) return;
     const int J = JC > 0 ? JC : a.d_model / 64;  // iterations
     const int64_t my_row = min(row0 + wave * 16 + i16, a.n_rows - 1);  // rows past n re-read the last
     const __bf16 *hrow = (const __bf16 *)a.hidden + my_row * a.ld_hidden + 8 * q4;
-    const char *w1 = (const char *)a.w1;
     const int64_t w1_row_bytes = (int64_t)a.d_model * 2;
+    const char *w1 = (const char *)a.w1 + (int64_t)head * HG * w1_row_bytes;
+    // this wave's share of a stage's pieces (pieces wave, wave + 4, ...)
+    const int lbw = (C::PIECES - wave + 3) / 4;
 
     // W1 columns [64 j, 64 j + 64) of all units -> stage st
     auto issue_w1 = [&](int j, int st) {
 #pragma unroll
         for (int u = 0; u < C::LB; ++u) {
             const int i = wave + 4 * u;         // 1 KB piece: units 8 i .. 8 i + 7
-            const int unit = 8 * i + (lane >> 3);
-            const int c = (lane & 7) ^ ((unit >> 1) & 7);
-            const char *src = w1 + unit * w1_row_bytes + (int64_t)(64 * j + 8 * c) * 2;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds + st * C::SBYTES + i * 1024), 16, 0, 0);
+            if (C::PIECES % 4 == 0 || i < C::PIECES) {
+                const int unit = 8 * i + (lane >> 3);
+                const int c = (lane & 7) ^ ((unit >> 1) & 7);
+                const char *src = w1 + unit * w1_row_bytes + (int64_t)(64 * j + 8 * c) * 2;
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds + st * C::SBYTES + i * 1024), 16, 0, 0);
+            }
         }
     };
     bf16x8 av[P][2];
@@ -167,7 +239,7 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
             if (j < J) {
                 // this wave's loads of iteration j are done once at most the
                 // younger iterations' loads are outstanding
-                wait_vm<63>(min(P - 1, J - 1 - j) * (C::LB + C::LA));
+                wait_vm<63>(min(P - 1, J - 1 - j) * (lbw + C::LA));
                 // every wave's W1 pieces of j have landed, and every wave is
                 // done reading stage (j - 1) (its reads were consumed by its
                 // MFMAs): a plain barrier, no fence (a fence would also wait
@@ -197,6 +269,16 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
     }
     __syncthreads();  // the stages become the epilogue's scratch
     float *act = (float *)lds;                       // [64][HG + 1]
+    if constexpr (SINK) {
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) {
+            const int jj = 16 * n + i16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) act[(wave * 16 + 4 * q4 + r) * (HG + 1) + jj] = acc[n][r];
+        }
+        sink_epilogue<HG>(a, act, row0, head, act + 64 * (HG + 1));
+        return;
+    }
     float *lds_w2 = act + 64 * (HG + 1);             // [16][HG + 1]
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
@@ -480,6 +562,27 @@ hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
             hipLaunchKernelGGL(gate_valu_kernel<__bf16>, dim3((unsigned)a.n_rows), dim3(NT), 0, s, a);
         else
             hipLaunchKernelGGL(gate_valu_kernel<float>, dim3((unsigned)a.n_rows), dim3(NT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int G>
+static void launch_sink_g(const GateArgs &a, hipStream_t s) {
+    constexpr int HG = 16 * (G + 1);
+    const int64_t tiles = (a.n_rows + 63) / 64;
+    const dim3 grid((unsigned)(((tiles + 7) / 8) * 8 * a.n_kv));
+    if (a.d_model == 4096)
+        hipLaunchKernelGGL((gate_pipe_kernel<HG, 64, true>), grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gate_pipe_kernel<HG, 0, true>), grid, dim3(NT), 0, s, a);
+}
+
+hipError_t launch_sink_gate(const GateArgs &a, hipStream_t s) {
+    switch (a.group) {
+    case 1: launch_sink_g<1>(a, s); break;
+    case 2: launch_sink_g<2>(a, s); break;
+    case 4: launch_sink_g<4>(a, s); break;
+    default: launch_sink_g<8>(a, s); break;
     }
     return hipGetLastError();
 }

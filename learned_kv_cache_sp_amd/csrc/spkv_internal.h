@@ -69,10 +69,15 @@ struct GateArgs {
     uint8_t *keep;
     float *ws;          // 256-byte header (arrival counter) + partial sums
     int32_t n_split;    // number of slices of d_model (1 = no workspace)
+    // sink-attention gate: w1 = [n_kv][(group + 1) * 16][d_model] projections,
+    // sinks [n_kv][n_sinks][16]
+    const float *sinks;
+    int32_t n_sinks, group;
 };
 size_t gate_ws_bytes(int d_model, int d_hidden, int n_kv, int dtype, int64_t n_rows);
 int gate_split_for(int d_model, int dtype, int64_t n_rows);
 hipError_t launch_gate(const GateArgs &a, hipStream_t s);
+hipError_t launch_sink_gate(const GateArgs &a, hipStream_t s);
 
 // ---- compaction ------------------------------------------------------------
 struct CompactArgs {

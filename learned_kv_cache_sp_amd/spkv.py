@@ -57,6 +57,14 @@ class GateDesc(ctypes.Structure):
     ]
 
 
+class SinkGateDesc(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("d_key", ctypes.c_int32), ("n_sinks", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("w", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+    ]
+
+
 class CacheDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -75,7 +83,7 @@ EXPORTS = [
     "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
     "spkv_head_stats", "spkv_head_stats_ws_bytes", "spkv_prefill_attn_soft",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
-    "spkv_last_error", "spkv_version", "spkv_hbm_read",
+    "spkv_last_error", "spkv_version", "spkv_hbm_read", "spkv_gate_sink",
 ]
 
 _lib = None
@@ -118,6 +126,7 @@ def load_library(path: str = LIB_PATH):
         "spkv_last_error": ([], ctypes.c_char_p),
         "spkv_version": ([], ctypes.c_int),
         "spkv_hbm_read": ([vp, sz, i32, i32, vp, vp], ctypes.c_int),
+        "spkv_gate_sink": ([ctypes.POINTER(SinkGateDesc), vp, i64, i64, f32, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -220,6 +229,33 @@ class GateWeights:
         d.dtype = _dtype_code(self.w1.dtype)
         d.w1, d.b1, d.w2, d.b2 = (_ptr(self.w1), _ptr(self.b1), _ptr(self.w2), _ptr(self.b2))
         self._desc = d  # keep alive
+        return d
+
+
+@dataclass
+class SinkGateWeights:
+    """Sink-attention gate: w [n_kv, (group + 1) * d_key, d_model] (bf16; per head
+    the group query blocks, then the key block), sinks [n_kv, n_sinks, d_key] f32."""
+    w: torch.Tensor
+    sinks: torch.Tensor
+    group: int
+
+    def desc(self) -> SinkGateDesc:
+        _need_gpu(self.w, self.sinks)
+        if self.w.dim() != 3 or self.sinks.dim() != 3:
+            raise ValueError("w must be [n_kv, (group + 1) * d_key, d_model], sinks [n_kv, n_sinks, d_key]")
+        nkv, per, d_model = self.w.shape
+        ns, dk = self.sinks.shape[1], self.sinks.shape[2]
+        if self.sinks.shape[0] != nkv or per != (self.group + 1) * dk:
+            raise ValueError(f"w {tuple(self.w.shape)} and sinks {tuple(self.sinks.shape)} do not match group "
+                             f"{self.group}")
+        if not self.w.is_contiguous() or not self.sinks.is_contiguous() or self.sinks.dtype != torch.float32:
+            raise ValueError("w must be contiguous, sinks contiguous float32")
+        d = SinkGateDesc()
+        d.d_model, d.n_kv, d.group, d.d_key, d.n_sinks = d_model, nkv, int(self.group), dk, ns
+        d.dtype = _dtype_code(self.w.dtype)
+        d.w, d.sinks = _ptr(self.w), _ptr(self.sinks)
+        self._desc = d
         return d
 
 
@@ -371,6 +407,29 @@ def spkv_gate(weights: GateWeights, hidden: torch.Tensor, tau: float, utility=No
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.spkv_gate(ctypes.byref(desc), _ptr(hidden), n, _row_stride(hidden), float(tau),
                          _ptr(utility), _ptr(keep), _ptr(ws), ws_bytes, _stream(stream)))
+    return utility, keep
+
+
+def spkv_gate_sink(weights: SinkGateWeights, hidden: torch.Tensor, tau: float, utility=None, keep=None,
+                   stream=None):
+    """The sink-attention gate for every row of hidden [n_rows, d_model].  Returns (utility, keep)."""
+    lib = load_library()
+    desc = weights.desc()
+    if hidden.dim() != 2 or hidden.shape[1] != desc.d_model:
+        raise ValueError(f"hidden has shape {tuple(hidden.shape)}, expected [n_rows, {desc.d_model}]")
+    n = hidden.shape[0]
+    dev = hidden.device
+    if keep is None:
+        keep = torch.empty((n, desc.n_kv), dtype=torch.uint8, device=dev)
+    if utility is None:
+        utility = torch.empty((n, desc.n_kv), dtype=torch.float32, device=dev)
+    _expect("keep", keep, (n, desc.n_kv), torch.uint8)
+    _expect("utility", utility, (n, desc.n_kv), torch.float32)
+    _need_gpu(hidden, keep, utility)
+    if hidden.dtype != weights.w.dtype:
+        raise ValueError("hidden and w dtypes differ")
+    _check(lib.spkv_gate_sink(ctypes.byref(desc), _ptr(hidden), n, _row_stride(hidden), float(tau), _ptr(utility),
+                              _ptr(keep), _stream(stream)))
     return utility, keep
 
 
