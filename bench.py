@@ -97,7 +97,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (decode 16, prefill 1)")
     p.add_argument("--workload", default="decode_32k",
                    choices=["decode_32k", "decode_131k", "ragged_32", "prefill_64k", "rethreshold_32k",
-                            "head_stats_1m", "soft_prefill_16k", "sink_gate_16k"])
+                            "head_stats_1m", "soft_prefill_16k", "sink_gate_16k", "decode_32k_b16",
+                            "decode_32k_b16_tau0"])
     p.add_argument("--layers", type=int, default=4, help="decode: layer caches used in rotation")
     p.add_argument("--page-size", type=int, default=64)
     p.add_argument("--step-mode", choices=("auto", "fused", "separate"), default="auto",
@@ -271,6 +272,8 @@ def gate_weights(wl, torch, inputs, spkv, dev):
     gw = spkv.GateWeights(torch.from_numpy(wts["W1"]).to(dev).to(torch.bfloat16),
                           torch.from_numpy(wts["b1"]).to(dev), torch.from_numpy(wts["W2"]).to(dev),
                           torch.zeros(wl.n_kv, dtype=torch.float32, device=dev))
+    if wl.tau <= 0.0:
+        return gw  # tau = 0 keeps every pair whatever the bias
     Hc = inputs.device_normal((65536, wl.d_model), wl.seed, inputs.STREAM_CAL, torch.bfloat16)
     u_cal, _ = spkv.spkv_gate(gw, Hc, wl.tau)
     u64 = u_cal.double().clamp(1e-300, 1 - 1e-16)
@@ -1231,11 +1234,26 @@ DEFAULT_STEPS = {"decode": (256, 16), "prefill": (4, 1), "rethreshold_32k": (20,
 SECONDARY = ["decode_131k", "ragged_32", "prefill_64k"]
 
 
+def workload(name: str):
+    """The named workload; decode_32k_b16 is decode_32k at batch 16 (the batch
+    of SP-KV's decode-kernel comparison, section 3.4), decode_32k_b16_tau0 the
+    same with tau = 0 (every pair kept: full attention through the same
+    kernels), so that their ratio is the speed-up of the configured keep
+    rates over full attention."""
+    import dataclasses
+    from learned_kv_cache_sp_amd import inputs
+    if name == "decode_32k_b16":
+        return dataclasses.replace(inputs.WORKLOADS["decode_32k"], name=name, batch=16)
+    if name == "decode_32k_b16_tau0":
+        return dataclasses.replace(inputs.WORKLOADS["decode_32k"], name=name, batch=16, tau=0.0, keep=(1.0,) * 8)
+    return inputs.WORKLOADS[name]
+
+
 def run_workload(args, name: str, steps=None, warmup=None) -> dict:
     import torch
     from learned_kv_cache_sp_amd import inputs
     a = argparse.Namespace(**vars(args))
-    kind = name if name in DEFAULT_STEPS else ("prefill" if inputs.WORKLOADS[name].chunk else "decode")
+    kind = name if name in DEFAULT_STEPS else ("prefill" if workload(name).chunk else "decode")
     a.steps = DEFAULT_STEPS[kind][0] if steps is None else steps
     a.warmup = DEFAULT_STEPS[kind][1] if warmup is None else warmup
     if name == "soft_prefill_16k":
@@ -1251,7 +1269,7 @@ def run_workload(args, name: str, steps=None, warmup=None) -> dict:
         wl = inputs.WORKLOADS["decode_32k"]
         res = bench_rethreshold(a, wl)
     else:
-        wl = inputs.WORKLOADS[name]
+        wl = workload(name)
         res = bench_prefill(a, wl) if wl.chunk else bench_decode(a, wl)
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

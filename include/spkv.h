@@ -29,7 +29,8 @@
  *     launched and spkv_last_error() (per thread) holds a message.
  *   - Every device pointer is caller-owned and must stay valid until the work
  *     queued on `stream` completes.  The library allocates no memory and keeps
- *     no state between calls except the per-thread error text.
+ *     no state between calls except the per-thread error text and the wait
+ *     limit of spkv_set_wait_limit.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *     queued; no call synchronises, except spkv_cache_check.
  *   - Device pointers must be 16-byte aligned; row strides (`ld_*`) are in
@@ -330,9 +331,12 @@ int spkv_decode_attn_noalloc(const spkv_cache *c, int32_t n_q_heads,
  *       c->u_pages is set, the utility of each appended entry is stored
  *       there whether or not `utility` is given.
  *   ws  at least spkv_decode_step_ws_bytes(c, g, n_q_heads) bytes, zero-filled
- *       once after allocation (every call leaves its counters at zero; a ws
- *       of this size also serves spkv_decode_attn; zero it again after a
- *       step timeout).  Calls sharing a ws must not overlap.
+ *       once after allocation (a ws of this size also serves
+ *       spkv_decode_attn).  Its two step counters only grow, with the totals
+ *       they must reach kept beside them, so a call after a step timeout
+ *       waits for its own arrivals on top of the late ones of the timed-out
+ *       call: the ws needs no new zero fill.  Calls sharing a ws must not
+ *       overlap.
  *   Results: utility, keep, the cache contents, lengths and the ring are
  *   those of the three separate calls, bit for bit; out and lse differ from
  *   spkv_decode_attn's only in the rounding of the split-K merge (the keys
@@ -462,6 +466,15 @@ int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows,
                     int32_t n_kv, double *u_sum, int64_t *n_kept, void *ws,
                     size_t ws_bytes, void *stream);
 size_t spkv_head_stats_ws_bytes(int64_t n_rows, int32_t n_kv);
+
+/* Polls after which the bounded waits inside spkv_decode_step (its
+ * finisher's waits for the gate's and the plan's arrivals) give up and set
+ * SPKV_STATUS_STEP_TIMEOUT.  polls >= 0 sets the limit (0: the waits give
+ * up at once, without polling -- a forced timeout for tests of its
+ * handling); a negative value restores the default (2^20 polls, about a
+ * second).  Applies to launches queued after the call (process-wide, not
+ * synchronised with calls in flight on other threads).  Returns SPKV_OK. */
+int spkv_set_wait_limit(int32_t polls);
 
 /* Streaming read of `bytes` bytes at `src` (device memory): the measured
  * bandwidth ceiling that the decode attention kernel is compared with.  It

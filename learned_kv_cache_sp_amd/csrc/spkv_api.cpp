@@ -437,6 +437,7 @@ int spkv_decode_step(const spkv_cache *c, const spkv_gate_desc *g, int32_t n_q_h
     a.grid = grid;
     spkv::decode_ws_assign(a, c, n_q_heads, grid, g->d_model, g->d_hidden, false, (char *)ws);
     a.share_cut = kFusedShareCut;
+    a.wait_limit = spkv::g_wait_limit;
     a.gate.d_model = g->d_model;
     a.gate.d_hidden = g->d_hidden;
     a.gate.n_kv = g->n_kv;
@@ -632,6 +633,12 @@ int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows, i
     a.ws = ws;
     hipError_t e = spkv::launch_stats(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "statistics launch");
+    return SPKV_OK;
+}
+
+// ----------------------------------------------------------------------------
+int spkv_set_wait_limit(int32_t polls) {
+    spkv::g_wait_limit = polls >= 0 ? polls : spkv::kDefaultWaitLimit;
     return SPKV_OK;
 }
 

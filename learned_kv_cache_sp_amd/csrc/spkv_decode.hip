@@ -72,8 +72,10 @@ __host__ __device__ inline int rec_floats(int G, int HD) { return G * HD + 32; }
 // workspace head: one arrival counter per (b, g), each in its own 256-byte
 // line (the end-of-launch arrivals of all workgroups would otherwise queue on
 // a few lines), then the fused step's two counters (gate units stored,
-// workgroups that have read the lengths), a line each.  Every call leaves all
-// of them at zero, so one workspace may serve both entry points.
+// workgroups that have read the lengths), a line each, with the running total
+// each has to reach 16 words after it.  Every call leaves the per-(b, g)
+// counters at zero; the fused step's two only grow (see fused_finisher), so
+// one workspace may serve both entry points.
 constexpr int CNT_STRIDE = 64;  // ints
 __host__ __device__ inline size_t ws_header_bytes(int BG) { return ((size_t)BG * CNT_STRIDE + 2 * 64) * 4; }
 // then, for the fused step only, the gate's partial first-layer sums
@@ -84,10 +86,6 @@ __host__ __device__ inline size_t round256(size_t x) { return (x + 255) & ~(size
 __host__ __device__ inline size_t fused_bytes(int d_model, int d_hidden) {
     return d_hidden <= 0 ? 0 : round256((size_t)gate_tile_items(d_model, d_hidden) * 256 * 4);
 }
-// polls of the fused step's waits before they give up (each poll takes a
-// device-scope round trip, about a microsecond; the waits normally end within
-// tens of microseconds)
-constexpr int FUSED_SPIN_LIMIT = 1 << 20;
 
 // Inclusive block scan of val(i), i < n, into out[1..n] (out[0] = 0); returns the total.
 template <typename Fn>
@@ -336,16 +334,28 @@ __device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, const 
 // Fused step, the last workgroup of the launch (it takes no attention work):
 // once every gate unit's shares are stored, finish the gate (utilities, keep
 // bits), append the kept rows, and once every other workgroup has read the
-// lengths for its plan, store the new lengths.  The waits are bounded: if
-// one runs out, the step's append or lengths are left undone and a status
-// bit says so.
+// lengths for its plan, store the new lengths.  The two arrival counters only
+// ever grow; the workspace keeps, beside each, the total its arrivals have
+// reached once every call so far has completed, and each call raises that
+// total by its own count before it waits.  The waits are bounded: if one
+// runs out, the step's append or lengths are left undone and a status bit
+// says so -- and the next call on the workspace still waits for its own
+// arrivals on top of this call's late ones, so nothing has to be reset.
 template <int HD>
 __device__ void fused_finisher(const DecodeArgs &a, const float *gshare, int *gate_cnt, int *plan_cnt,
                                float *lds_act, uint8_t *lds_keep, int *lds_new_len, int *lds_flag) {
     const CacheView &c = a.c;
     const int BG = c.batch * c.n_kv;
     const int items = gate_tile_items(a.gate.d_model, a.gate.d_hidden);
-    if (threadIdx.x == 0) lds_flag[0] = wait_count_dev(gate_cnt, items, FUSED_SPIN_LIMIT);
+    int *gate_total = gate_cnt + 16, *plan_total = plan_cnt + 16;
+    int gate_target = 0, plan_target = 0;
+    if (threadIdx.x == 0) {
+        gate_target = (int)((unsigned)load_dev(gate_total) + (unsigned)items);
+        plan_target = (int)((unsigned)load_dev(plan_total) + (unsigned)(gridDim.x - 1));
+        __hip_atomic_store(gate_total, gate_target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(plan_total, plan_target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lds_flag[0] = wait_reach_dev(gate_cnt, gate_target, a.wait_limit);
+    }
     __syncthreads();
     if (!lds_flag[0]) {
         if (threadIdx.x == 0) atomicOr(c.status, SPKV_STATUS_STEP_TIMEOUT);
@@ -358,17 +368,13 @@ __device__ void fused_finisher(const DecodeArgs &a, const float *gshare, int *ga
     __syncthreads();
     append_new_rows<HD>(a, lds_keep, lds_u, lds_new_len);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        reset_dev(gate_cnt);
-        lds_flag[1] = wait_count_dev(plan_cnt, (int)gridDim.x - 1, FUSED_SPIN_LIMIT);
-    }
+    if (threadIdx.x == 0) lds_flag[1] = wait_reach_dev(plan_cnt, plan_target, a.wait_limit);
     __syncthreads();
     if (!lds_flag[1]) {
         if (threadIdx.x == 0) atomicOr(c.status, SPKV_STATUS_STEP_TIMEOUT);
         return;
     }
     for (int i = threadIdx.x; i < BG; i += NT) c.lengths[i] = lds_new_len[i];
-    if (threadIdx.x == 0) reset_dev(plan_cnt);
 }
 
 // MODE 0: attention only (spkv_decode_attn); MODE_STEP: the whole decode
@@ -975,6 +981,11 @@ bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid) {
     // the last workgroup is the finisher; the gate units go to the others
     return c->dtype == SPKV_BF16 && c->batch <= FUSED_ROWS && d_hidden >= 1 && grid >= 2 && c->n_kv <= 16;
 }
+
+// polls of the fused step's waits before they give up (each poll takes a
+// device-scope round trip, about a microsecond; the waits normally end within
+// tens of microseconds)
+int g_wait_limit = kDefaultWaitLimit;
 
 int decode_blocks_per_cu() {
     int n = 1 << 20;

@@ -30,12 +30,13 @@ __device__ inline void arrive_nr_dev(int *counter, int n = 1) {
 __device__ inline int load_dev(const int *p) {
     return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Poll *counter until it reaches n, at most `limit` times; false if it never
-// did.  Only for counts that are bumped by workgroups which never wait for
-// the poller, so the wait ends once they have run.
-__device__ inline bool wait_count_dev(const int *counter, int n, int limit) {
+// Poll *counter until it has reached target (compared modulo 2^32, so
+// counters that only ever grow may wrap), at most `limit` times; false if it
+// never did.  Only for counts that are bumped by workgroups which never wait
+// for the poller, so the wait ends once they have run.
+__device__ inline bool wait_reach_dev(const int *counter, int target, int limit) {
     for (int i = 0; i < limit; ++i) {
-        if (load_dev(counter) >= n) return true;
+        if ((int)((unsigned)load_dev(counter) - (unsigned)target) >= 0) return true;
         __builtin_amdgcn_s_sleep(2);
     }
     return false;

@@ -115,6 +115,7 @@ struct DecodeArgs {
     // fused step (spkv_decode_step): the gate of the batch's new rows and
     // their append run inside the attention launch
     int32_t share_cut;  // fused step: attention steps fewer for the workgroups that run a gate item
+    int32_t wait_limit; // fused step: polls before its finisher's waits give up
     GateArgs gate;      // n_rows = batch; outputs utility / keep
     const char *k_new, *v_new;  // new rows: row b, key head g at + (b*ld_new + g*hd) elements
     int64_t ld_new;
@@ -128,6 +129,8 @@ void decode_ws_assign(DecodeArgs &a, const spkv_cache *c, int n_q, int grid, int
                       bool fixed_counters, char *ws);
 bool decode_fused_ok(const spkv_cache *c, int d_hidden, int grid);
 int decode_blocks_per_cu();
+constexpr int kDefaultWaitLimit = 1 << 20;  // about a second of device-scope polls
+extern int g_wait_limit;  // polls before a bounded wait of the fused step gives up
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
 // ---- prefill ---------------------------------------------------------------

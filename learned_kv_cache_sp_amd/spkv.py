@@ -83,7 +83,7 @@ EXPORTS = [
     "spkv_prefill_attn", "spkv_prefill_ws_bytes", "spkv_cache_rethreshold", "spkv_rethreshold_ws_bytes",
     "spkv_head_stats", "spkv_head_stats_ws_bytes", "spkv_prefill_attn_soft",
     "spkv_cache_bytes", "spkv_cache_reset", "spkv_cache_check", "spkv_status_str",
-    "spkv_last_error", "spkv_version", "spkv_hbm_read", "spkv_gate_sink",
+    "spkv_last_error", "spkv_version", "spkv_hbm_read", "spkv_gate_sink", "spkv_set_wait_limit",
 ]
 
 _lib = None
@@ -127,6 +127,7 @@ def load_library(path: str = LIB_PATH):
         "spkv_version": ([], ctypes.c_int),
         "spkv_hbm_read": ([vp, sz, i32, i32, vp, vp], ctypes.c_int),
         "spkv_gate_sink": ([ctypes.POINTER(SinkGateDesc), vp, i64, i64, f32, vp, vp, vp], ctypes.c_int),
+        "spkv_set_wait_limit": ([i32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -680,6 +681,12 @@ def spkv_cache_check(cache: Cache, stream=None) -> int:
     if rc != SPKV_OK:
         raise SpkvError(rc, load_library().spkv_last_error().decode() + f" bits={bits.value}")
     return bits.value
+
+
+def spkv_set_wait_limit(polls: int):
+    """Polls after which the fused decode step's bounded waits give up
+    (0: at once; negative: the default)."""
+    _check(load_library().spkv_set_wait_limit(int(polls)))
 
 
 def spkv_hbm_read(src, sink, nontemporal: bool = False, runs: bool = False, grid: int = 0, stream=None):

@@ -163,3 +163,12 @@ def append(cache, rows_z, rows_k, rows_v, pos0s, flags, stream=None, append_offs
     spkv.spkv_compact_append(cache, keep, kd, vd, ro, p0, max(1, max(counts)), flags,
                              append_offsets=append_offsets, stream=stream)
     return n
+
+
+def step_counters_settled(ws, batch: int, n_kv: int) -> bool:
+    """The decode workspace head after a completed call: every per-(b, g)
+    arrival counter back at zero, and each of the fused step's two arrival
+    counters equal to the running total kept 16 words after it."""
+    bg = batch * n_kv * 64
+    head = ws[: bg + 128].cpu().numpy()
+    return (not head[:bg].any() and head[bg] == head[bg + 16] and head[bg + 64] == head[bg + 80])
