@@ -26,7 +26,7 @@ namespace {
 
 constexpr int NT = 256;
 // the workspace starts with a 256-byte header holding the arrival counter of
-// the few-row kernel; partial sums follow it
+// the few-row kernels; partial sums follow it
 constexpr int WS_HEADER_FLOATS = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -292,6 +292,198 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Many rows, HG in {64, 128, 256}: 64 rows per workgroup, the hidden units
+// split over the 4 waves (wave w owns unit tiles w * NTW .. w * NTW + NTW - 1
+// for all 64 rows).  Per 64-column iteration the workgroup's hidden tile
+// (64 rows x 128 bytes, the HBM stream) lands in an LDS ring by direct
+// global->LDS loads, a quarter from each wave, and every wave reads it as its
+// B operands; each wave loads its own W1 rows (L2-resident) straight into
+// registers as A operands.  Sharing the hidden tile rather than W1 halves the
+// LDS traffic per iteration (8 KB written + 4 x 8 KB read, against 16 KB
+// written + 4 x 16 KB read when every wave needs all of W1).
+// Layer 1 is computed transposed, a^T[unit][row] = W1 . h^T, so that each
+// lane ends up holding one row and four units of every 16 x 16 tile --
+// exactly the B operand of the f32 16x16x4 MFMA that forms layer 2
+// (logit^T[head][row] = W2 . a^T), four units per step, with no data
+// movement; the 4 waves' partial logits (each over its own units) are added
+// in wave order.
+//
+// One LDS object per ring stage: the compiler then sees the direct loads into
+// one stage and the operand reads of another as disjoint (with one array it
+// makes some reads wait for every load in flight).
+template <int S, int SB>
+__device__ __attribute__((always_inline)) inline char *stage_obj() {
+    __shared__ __attribute__((aligned(1024))) char buf[SB];
+    return buf;
+}
+template <int SB, int N>
+__device__ __attribute__((always_inline)) inline char *stage_at(int st) {
+    if constexpr (N > 1) {
+        if (st == N - 1) return stage_obj<N - 1, SB>();
+        return stage_at<SB, N - 1>(st);
+    } else {
+        return stage_obj<0, SB>();
+    }
+}
+
+template <int HG> struct UnitSplit {
+    static constexpr int NTW = HG / 64;                  // 16-unit tiles per wave
+    static constexpr int LW = 2 * NTW;                   // W1 register loads per wave and iteration
+    static constexpr int LH = 2;                         // hidden-row direct loads per wave and iteration
+    // iterations in flight: the vmcnt field (at most 63 outstanding) and the
+    // W1 registers (D x 8 NTW) bound the depth; a power of two, so that with
+    // d_model = 4096 the loop unrolls completely and every wait count is a
+    // constant
+    static constexpr int D = (LW + LH) <= 4 ? 16 : (LW + LH) <= 8 ? 8 : 4;
+    static constexpr int NSTAGE = D + 1;
+    static constexpr int SBYTES = 64 * 128;              // hidden stage: 64 rows x 64 columns
+    // epilogue: each wave's partial logits, [4 row tiles][16 heads][16 rows]
+    // floats, two waves per stage object
+    static constexpr int PART_WAVE = 4 * 256 * 4;
+    static_assert(2 * PART_WAVE <= SBYTES, "epilogue scratch fits two stages");
+};
+
+// JC: iterations (d_model / 64) when fixed at compile time (0: from d_model)
+template <int HG, int JC>
+__global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
+    using C = UnitSplit<HG>;
+    constexpr int D = C::D;
+    constexpr int NTW = C::NTW;
+    static_assert((D - 1) * (C::LW + C::LH) <= 63, "vmcnt range");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
+    const int J = JC > 0 ? JC : a.d_model / 64;  // iterations
+    // hidden-tile loads: instruction k of this wave fills rows 16 wave + 8 k ..
+    // + 7; lane -> (row, 16-byte slot), slot s of row r holds the row's
+    // column chunk s ^ ((r >> 1) & 7) (conflict-free operand reads)
+    const __bf16 *hsrc[C::LH];
+#pragma unroll
+    for (int k = 0; k < C::LH; ++k) {
+        const int r = 8 * (C::LH * wave + k) + (lane >> 3);
+        const int64_t grow = min(row0 + r, a.n_rows - 1);  // rows past n re-read the last
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        hsrc[k] = (const __bf16 *)a.hidden + grow * a.ld_hidden + 8 * c;
+    }
+    // W1 operand rows of this wave: unit 16 (wave NTW + nn) + i16, 8 q4 .. of each 32-column half
+    const __bf16 *wsrc = (const __bf16 *)a.w1 + (int64_t)(16 * wave * NTW + i16) * a.d_model + 8 * q4;
+
+    auto issue_h = [&](int j, int st) {
+        char *dst = stage_at<C::SBYTES, C::NSTAGE>(st);
+#pragma unroll
+        for (int k = 0; k < C::LH; ++k)
+            __builtin_amdgcn_global_load_lds((const void *)(hsrc[k] + 64 * j),
+                                             (lds_void *)(dst + (C::LH * wave + k) * 1024), 16, 0, 0);
+    };
+    bf16x8 wv[D][NTW][2];
+    auto issue_w = [&](int j, bf16x8 (&dst)[NTW][2]) {
+#pragma unroll
+        for (int nn = 0; nn < NTW; ++nn)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                dst[nn][ks] = *(const bf16x8 *)(wsrc + (int64_t)16 * nn * a.d_model + 64 * j + 32 * ks);
+    };
+
+    f32x4 acc[4][NTW];  // a^T tiles: lane (row 16 rt + i16, units 16 (wave NTW + nn) + 4 q4 + r)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int nn = 0; nn < NTW; ++nn) acc[rt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: iterations 0 .. D-1 in flight (hidden tile, then W1, per iteration)
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        if (i < J) {
+            issue_h(i, i);
+            issue_w(i, wv[i]);
+        }
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < (JC > 0 ? JC : J); j0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int j = j0 + u;
+            if (j < J) {
+                // this wave's loads of iteration j are done once at most the
+                // younger iterations' loads are outstanding
+                wait_vm<63>(min(D - 1, J - 1 - j) * (C::LH + C::LW));
+                // every wave's quarter of hidden tile j has landed, and every
+                // wave is done reading the stage of j - 1: a plain barrier
+                // (a fence would also wait for the loads still in flight)
+                __builtin_amdgcn_s_barrier();
+                if (j + D < J) issue_h(j + D, (j + D) % C::NSTAGE);
+                const char *st = stage_at<C::SBYTES, C::NSTAGE>(j % C::NSTAGE);
+                bf16x8 av[4][2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const int r = 16 * rt + i16;
+                        av[rt][ks] = *(const bf16x8 *)(st + r * 128 + (((4 * ks + q4) ^ ((r >> 1) & 7)) << 4));
+                    }
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                        for (int nn = 0; nn < NTW; ++nn)
+                            acc[rt][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u][nn][ks], av[rt][ks],
+                                                                                  acc[rt][nn], 0, 0, 0);
+                if (j + D < J) issue_w(j + D, wv[u]);
+            }
+        }
+    }
+    // layer 2 on the f32 MFMA: step (nn, c) takes units 16 (wave NTW + nn) +
+    // 4 k + c, k = 0..3; the A operand is W2[head i16][that unit] (zero for
+    // heads past n_kv), the B operand ReLU(a^T + b1) from register c of acc
+    float w2r[NTW][4], b1r[NTW][4];
+#pragma unroll
+    for (int nn = 0; nn < NTW; ++nn)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int unit = 16 * (wave * NTW + nn) + 4 * q4 + c;
+            w2r[nn][c] = i16 < a.n_kv ? a.w2[i16 * HG + unit] : 0.f;
+            b1r[nn][c] = a.b1[unit];
+        }
+    f32x4 lg[4];  // partial logit^T tiles: lane (row 16 rt + i16, heads 4 q4 + r)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        lg[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nn = 0; nn < NTW; ++nn)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                lg[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w2r[nn][c], relu_keep_nan(acc[rt][nn][c] + b1r[nn][c]),
+                                                               lg[rt], 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done with the ring: its first two stages hold the partials
+    float *mine = (float *)(stage_at<C::SBYTES, C::NSTAGE>(wave >> 1) + (wave & 1) * C::PART_WAVE);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mine[rt * 256 + (4 * q4 + r) * 16 + i16] = lg[rt][r];
+    __syncthreads();
+    const float *p01 = (const float *)stage_at<C::SBYTES, C::NSTAGE>(0);
+    const float *p23 = (const float *)stage_at<C::SBYTES, C::NSTAGE>(1);
+    constexpr int PW = C::PART_WAVE / 4;  // floats per wave
+    const int nkv = a.n_kv;
+    for (int idx = threadIdx.x; idx < 64 * nkv; idx += NT) {
+        const int r = idx / nkv;
+        const int k = idx - r * nkv;
+        const int64_t row = row0 + r;
+        if (row >= a.n_rows) continue;
+        const int o = (r >> 4) * 256 + k * 16 + (r & 15);
+        const float logit = (((p01[o] + p01[PW + o]) + p23[o]) + p23[PW + o]) + a.b2[k];
+        const float u = sigmoid_f(logit);
+        if (a.utility) a.utility[row * nkv + k] = u;
+        a.keep[row * nkv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+    }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA kernel.  Workgroup tile: (16 * WM) rows x HG hidden units; waves
 // are arranged WM (rows) x (4 / WM) (hidden units).  blockIdx.y = d_model
 // slice when n_split > 1.
@@ -479,6 +671,7 @@ int gate_split_for(int d_model, int dtype, int64_t n_rows) {
 
 static bool mfma_hidden(int hg) { return hg == 32 || hg == 64 || hg == 128 || hg == 256; }
 
+
 // rows per workgroup on the small-row (split) path: 16 * WM with WM = 2 for
 // d_hidden = 32 (two 16-unit tiles) and 1 otherwise
 static int small_bm(int hg) { return hg == 32 ? 32 : 16; }
@@ -523,6 +716,12 @@ static void launch_mfma(const GateArgs &a, int tiles, hipStream_t s) {
     }
 }
 
+template <int HG>
+static void launch_unitsplit(const GateArgs &a, dim3 grid, hipStream_t s) {
+    if (a.d_model == 4096) hipLaunchKernelGGL((gate_unitsplit_kernel<HG, 64>), grid, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((gate_unitsplit_kernel<HG, 0>), grid, dim3(NT), 0, s, a);
+}
+
 hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
     GateArgs a = a0;
     if (a.n_rows <= TINY_ROWS) {
@@ -537,20 +736,15 @@ hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
             launch_mfma<1>(a, tiles, s);
         } else if (a.d_model % 64 == 0) {
             const dim3 grid((unsigned)((a.n_rows + 63) / 64));
-            if (a.d_model == 4096) {
-                switch (a.d_hidden) {
-                case 32: hipLaunchKernelGGL((gate_pipe_kernel<32, 64>), grid, dim3(NT), 0, s, a); break;
-                case 64: hipLaunchKernelGGL((gate_pipe_kernel<64, 64>), grid, dim3(NT), 0, s, a); break;
-                case 128: hipLaunchKernelGGL((gate_pipe_kernel<128, 64>), grid, dim3(NT), 0, s, a); break;
-                default: hipLaunchKernelGGL((gate_pipe_kernel<256, 64>), grid, dim3(NT), 0, s, a); break;
-                }
-            } else {
-                switch (a.d_hidden) {
-                case 32: hipLaunchKernelGGL((gate_pipe_kernel<32, 0>), grid, dim3(NT), 0, s, a); break;
-                case 64: hipLaunchKernelGGL((gate_pipe_kernel<64, 0>), grid, dim3(NT), 0, s, a); break;
-                case 128: hipLaunchKernelGGL((gate_pipe_kernel<128, 0>), grid, dim3(NT), 0, s, a); break;
-                default: hipLaunchKernelGGL((gate_pipe_kernel<256, 0>), grid, dim3(NT), 0, s, a); break;
-                }
+            const bool fixed = a.d_model == 4096;
+            switch (a.d_hidden) {
+            case 32:
+                if (fixed) hipLaunchKernelGGL((gate_pipe_kernel<32, 64>), grid, dim3(NT), 0, s, a);
+                else hipLaunchKernelGGL((gate_pipe_kernel<32, 0>), grid, dim3(NT), 0, s, a);
+                break;
+            case 64: launch_unitsplit<64>(a, grid, s); break;
+            case 128: launch_unitsplit<128>(a, grid, s); break;
+            default: launch_unitsplit<256>(a, grid, s); break;
             }
         } else {
             const int tiles = (int)((a.n_rows + 63) / 64);

@@ -43,7 +43,9 @@ def _run(wl, n_rows, seed=7, tau=None, d_hidden=None, d_model=None):
     ("decode_32k", 17, None),      # bf16, d_model split over workgroups
     ("decode_32k", 64, None),      # largest split batch
     ("decode_32k", 65, None),      # first full-tile batch, ragged tail (pipelined kernel, d_model 4096)
-    ("decode_32k", 1500, None),    # several 64-row tiles
+    ("decode_32k", 1500, None),    # several 64-row tiles, ragged last tile
+    ("decode_32k", 1024, 64),      # 64-row kernel, d_hidden 64 (16 iterations in flight)
+    ("decode_32k", 2000, 256),     # 64-row kernel, d_hidden 256 (4 in flight)
     ("decode_32k", 40, 32),        # d_hidden 32 on the split path
     ("decode_32k", 300, 256),
     ("decode_32k", 200, 32),       # pipelined kernel, every unit width
@@ -62,6 +64,8 @@ def test_gate_matches_oracle(name, n_rows, d_hidden):
     (128, 100, 256),    # two iterations: fewer than the pipeline depth
     (640, 70, 64),
     (96, 130, 128),     # d_model not a multiple of 64: the plain MFMA kernel
+    (1152, 1300, 128),  # 18 iterations at a run-time trip count
+    (640, 1100, 64),    # 10 iterations, fewer than the depth (16)
 ])
 def test_gate_other_model_widths(d_model, n_rows, d_hidden):
     u, z, u_ref, z_ref = _run(inputs.WORKLOADS["decode_32k"], n_rows, d_hidden=d_hidden, d_model=d_model)
@@ -103,7 +107,7 @@ def test_gate_workspace_reuse_across_batch_sizes():
     wl = inputs.WORKLOADS["decode_32k"]
     w = tl.calibrated_weights(wl)
     gw = tl.gate_weights(w, torch.bfloat16)
-    sizes = [16, 5, 40, 3, 1, 64, 8]
+    sizes = [16, 5, 40, 3, 1, 64, 8, 3000, 20, 1500, 64]   # few-row and many-row kernels
     ws = spkv.workspace(max(spkv.spkv_gate_ws_bytes(gw, n) for n in sizes))
     for i, n in enumerate(sizes):
         H = tl.dev(inputs.normal((n, wl.d_model), 6, i, dtype=wl.dtype), torch.bfloat16)
