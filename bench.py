@@ -84,7 +84,7 @@ KERNEL_SOURCES = {
     "compact_onepass_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "compact_small_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
     "rethresh_scatter_kernel": "learned_kv_cache_sp_amd/csrc/spkv_compact.hip",
-    "stats_band_vec_kernel": "learned_kv_cache_sp_amd/csrc/spkv_stats.hip",
+    "stats_kernel": "learned_kv_cache_sp_amd/csrc/spkv_stats.hip",
 }
 CALIBRATION_BYTES = 1 << 30  # the plain copy: 1 GiB read + 1 GiB written
 
@@ -975,49 +975,68 @@ def cpu_baseline_sink_gate(wl, budget_s: float) -> dict:
 HEAD_STATS_ROWS, HEAD_STATS_KV = 1 << 20, 8
 
 
+HEAD_STATS_COPIES = 8  # input sets rotated so that the 8 x 42 MB exceed the 256 MB Infinity Cache
+
+
 def bench_head_stats(args):
     """Per-head utility sums and kept counts (SP-KV Table 1 density, section 4
     mean utility) over 1,048,576 gate output rows x 8 key heads (the gate
     outputs of 8 sequences of 131,072 tokens), f32 utilities and u8 keep bits
-    from a seeded generator.  One step = one spkv_head_stats call."""
+    from a seeded generator.  One step = one spkv_head_stats call, on one of
+    HEAD_STATS_COPIES input sets in turn (so every call reads from HBM); the
+    C entry point is called with its arguments marshalled once, so that the
+    host keeps ahead of the GPU and the timed pass measures the launches."""
+    import ctypes
     import torch
     from learned_kv_cache_sp_amd import spkv
     n, nkv = HEAD_STATS_ROWS, HEAD_STATS_KV
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
-    u = torch.rand((n, nkv), generator=gen, device="cuda", dtype=torch.float32)
-    z = (torch.rand((n, nkv), generator=gen, device="cuda") < 0.2).to(torch.uint8)
+    sets = []
+    for _ in range(HEAD_STATS_COPIES):
+        u = torch.rand((n, nkv), generator=gen, device="cuda", dtype=torch.float32)
+        z = (torch.rand((n, nkv), generator=gen, device="cuda") < 0.2).to(torch.uint8)
+        sets.append((u, z))
     us = torch.zeros(nkv, dtype=torch.float64, device="cuda")
     kp = torch.zeros(nkv, dtype=torch.int64, device="cuda")
-    ws = spkv.workspace(spkv.spkv_head_stats_ws_bytes(n, nkv))
+    nbytes = spkv.spkv_head_stats_ws_bytes(n, nkv)
+    ws = spkv.workspace(nbytes)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        spkv.spkv_head_stats(u, z, us, kp, ws=ws)
+    lib = spkv.load_library()
+    calls = [(ctypes.c_void_p(u.data_ptr()), ctypes.c_void_p(z.data_ptr()), ctypes.c_int64(n), ctypes.c_int32(nkv),
+              ctypes.c_void_p(us.data_ptr()), ctypes.c_void_p(kp.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+              ctypes.c_size_t(nbytes), ctypes.c_void_p(stream.cuda_stream)) for u, z in sets]
+    fn = lib.spkv_head_stats
+
+    def step(i):
+        rc = fn(*calls[i % len(calls)])
+        if rc != spkv.SPKV_OK:
+            raise spkv.SpkvError(rc, lib.spkv_last_error().decode())
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
-        spkv.spkv_head_stats(u, z, us, kp, ws=ws)
-        evs[i][1].record(stream)
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     alg = 5 * n * nkv  # each utility (4 B) and keep byte read once
-    call_s = float(np.mean(call_ms)) * 1e-3
+    call_s = ms * 1e-3
     achieved = alg / call_s / 1e9
     return {
         "metric": "gate output rows summarised per second", "value": n / (ms * 1e-3), "unit": "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
-        "config": {"workload": "head_stats_1m", "rows": n, "n_kv": nkv, "step": "spkv_head_stats"},
-        "roofline": {"bound": "hbm", "kernel": "spkv_head_stats (stats_band_vec_kernel + stats_total_kernel)",
+        "config": {"workload": "head_stats_1m", "rows": n, "n_kv": nkv, "step": "spkv_head_stats",
+                   "input_sets_rotated": HEAD_STATS_COPIES},
+        "roofline": {"bound": "hbm", "kernel": "spkv_head_stats (stats_kernel<true>, one launch)",
                      "achieved": achieved, "peak": 8000.0, "unit": "GB/s", "frac": achieved / 8000.0,
-                     "traffic": stored_traffic("stats_band_vec_kernel", "head_stats_1m"),
-                     "algorithmic_bytes_per_launch": alg, "avg_call_us": call_s * 1e6,
-                     "call_us": _stats_us(call_ms)},
+                     "traffic": stored_traffic("stats_kernel", "head_stats_1m"),
+                     "algorithmic_bytes_per_launch": alg, "launch_us": call_s * 1e6,
+                     "launch_us_from": "the timed pass: its time per call (one launch per call), an upper bound "
+                                       "of the launch duration"},
     }
 
 

@@ -456,10 +456,13 @@ size_t spkv_rethreshold_ws_bytes(const spkv_cache *src);
  *   NaN utility makes its head's sum NaN.  n_rows = 0 adds nothing and
  *   reads no pointer.
  *   ws  at least spkv_head_stats_ws_bytes(n_rows, n_kv) bytes (8-byte
- *       aligned; 0 when n_rows = 0).
- *   Launches two kernels (band sums, then their total in band order): the
- *   sums are deterministic; they may differ from a sequential sum in the
- *   last bits.
+ *       aligned; 0 when n_rows = 0).  Its first 4352 bytes hold arrival
+ *       counters that must be zero before the first call that uses ws
+ *       (zero-fill it once after allocation); every call leaves them at
+ *       zero.  Calls sharing one ws must not overlap.
+ *   Launches one kernel: each workgroup sums a band of rows, the last to
+ *   finish adds the band sums in band order.  The sums are deterministic;
+ *   they may differ from a sequential sum in the last bits.
  * Supported: n_kv <= 16, n_rows < 2^31.
  */
 int spkv_head_stats(const float *utility, const uint8_t *keep, int64_t n_rows,

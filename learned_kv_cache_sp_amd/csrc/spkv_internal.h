@@ -175,6 +175,7 @@ struct StatsArgs {
     int64_t *n_kept;        // [n_kv], accumulated
     void *ws;
     // set by the launcher
+    int *cnt;               // arrival counter (zero between calls)
     double *ws_u;
     int64_t *ws_k;
     int64_t band_rows;      // rows (row path) or elements (vector path) per band

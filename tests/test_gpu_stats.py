@@ -84,3 +84,20 @@ def test_head_stats_unaligned_rows_take_the_row_path():
     ru, rk = oracle.head_stats(u[1:], z[1:])
     np.testing.assert_array_equal(kp.cpu().numpy(), rk)
     np.testing.assert_allclose(us.cpu().numpy(), ru, rtol=1e-12)
+
+
+def test_head_stats_one_workspace_across_calls():
+    # one workspace shared by calls of both paths and many sizes: each call
+    # leaves its arrival counter at zero for the next, and every result equals
+    # that of a fresh workspace bit for bit
+    sizes = [(262144, 8), (300, 3), (4097, 8), (1, 1), (100003, 16), (5000, 2)]
+    ws = spkv.workspace(max(spkv.spkv_head_stats_ws_bytes(n, k) for n, k in sizes))
+    for i, (n, nkv) in enumerate(sizes):
+        u, z = _inputs(n, nkv, 40 + i)
+        ud, zd = torch.from_numpy(u).cuda(), torch.from_numpy(z).cuda()
+        if i == 5:  # a view one row in: the row path
+            ud, zd = ud[1:], zd[1:]
+        a = spkv.spkv_head_stats(ud, zd, ws=ws)
+        b = spkv.spkv_head_stats(ud, zd)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), (n, nkv)
+    assert not ws[:4352 // 4].any()  # the counter header is back at zero
