@@ -786,7 +786,6 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
     constexpr int ES = sizeof(T);
     constexpr int EPC = 16 / ES;          // elements per 16-byte piece
     constexpr int MAXHD = 128;
-    constexpr bool OWN_KEY = ES == 2;     // bf16: key row (its share) held in registers
     __shared__ int lds_src[TILE];         // flat source slot of each kept entry, in order
     __shared__ int lds_loc[TILE];         // its index inside the tile
     __shared__ int lds_waves[NT / 64];
@@ -840,16 +839,7 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
         }
     }
     const bool flag = mine && u >= a.tau;  // NaN fails
-    constexpr int KP = OWN_KEY ? MAXHD / EPC / RT_SPLIT : 1;
     const int k0 = half * hh;             // first key element of this half
-    piece_t kr[KP];
-    if constexpr (OWN_KEY) {
-        if (flag) {
-#pragma unroll
-            for (int ch = 0; ch < KP; ++ch)
-                if (ch * EPC < hh) kr[ch] = *(const piece_t *)(s.k_pages + ((int64_t)slot * hd + k0 + ch * EPC) * ES);
-        }
-    }
 #pragma unroll
     for (int q = 0; q < NPT; ++q) {
         const int idx = q * NT + (int)threadIdx.x;
@@ -876,16 +866,14 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
             d.pos_pages[ds] = pos;
             if (d.u_pages) d.u_pages[ds] = u;
         }
-        if constexpr (OWN_KEY) {
-#pragma unroll
-            for (int ch = 0; ch < KP; ++ch)
-                if (ch * EPC < hh) *(piece_t *)(d.k_pages + (ds * hd + k0 + ch * EPC) * ES) = kr[ch];
-        }
     }
     __syncthreads();  // lds_src / lds_loc complete
-    if constexpr (!OWN_KEY) {
-        // keys of an f32 cache: 16-byte pieces, a row's pieces on
-        // neighbouring lanes; a batch of loads is issued before its stores
+    {
+        // keys: 16-byte pieces, a row's pieces on neighbouring lanes, so every
+        // load instruction reads whole 128-byte lines and every store
+        // instruction writes consecutive rows (one row per entry and thread
+        // would touch 64 lines of 16 bytes per instruction, about a third of
+        // the throughput); a batch of loads is issued before its stores
         constexpr int KB = 8;
         const int cpr = hh / EPC;         // this half's pieces of a key row
         const int npk = n * cpr;
