@@ -195,7 +195,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, workload: str) ->
            f"WRITE_SIZE {w_cal:.0f} KiB -> factor {w_fac:.4f}",
            f"{'kernel':72s} {'n':>4s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'scaled_MB':>10s}"]
     for k in sorted(set(f_per) | set(w_per)):
-        if not any(x in k for x in ("gate", "compact", "decode", "prefill", "cache_reset")):
+        if not any(x in k for x in ("gate", "compact", "decode", "prefill", "cache_reset", "rethresh", "stats")):
             continue
         nf, fv = f_per.get(k, (0, 0.0))
         _, wv = w_per.get(k, (0, 0.0))
