@@ -944,7 +944,7 @@ def bench_sink_gate(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "sink_gate_16k", "rows": n, "d_model": d, "n_kv": nkv, "group": G, "n_sinks": S,
                    "d_key": 16, "step": "spkv_gate_sink (one launch; the time per step is the launch's)"},
-        "roofline": {"bound": "mfma", "kernel": "gate_pipe_kernel<80, 64, true> (spkv_gate_sink)",
+        "roofline": {"bound": "mfma", "kernel": "gate_sink_tall_kernel<4, 2, 64> (spkv_gate_sink)",
                      "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops, "hidden_GBs": round(n * d * 2 / (ms * 1e-3) / 1e9, 1),

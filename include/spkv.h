@@ -203,9 +203,10 @@ typedef struct spkv_sink_gate_desc {
  * spkv_gate_sink -- the sink-attention gate for n_rows independent rows.
  *   hidden  [n_rows, ld_hidden] bf16 (first d_model entries of each row)
  *   utility [n_rows, n_kv] f32, may be NULL;  keep [n_rows, n_kv] uint8
- * One launch (a workgroup per 64 rows and key head: the projections on
- * v_mfma_f32_16x16x32_bf16 accumulate in f32, then the scores, softmax and
- * maximum in f32); no workspace.  A NaN gives keep = 0.
+ * One launch (a workgroup per 256 rows and 1, 2 or 4 key heads: the
+ * projections on v_mfma_f32_16x16x32_bf16 accumulate in f32, the sink scores
+ * on the f32 MFMA, then the softmax and maximum in f32); no workspace.  A NaN
+ * gives keep = 0.
  */
 int spkv_gate_sink(const spkv_sink_gate_desc *g, const void *hidden, int64_t n_rows, int64_t ld_hidden,
                    float tau, float *utility, uint8_t *keep, void *stream);

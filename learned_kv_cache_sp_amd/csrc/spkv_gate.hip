@@ -79,62 +79,7 @@ __device__ inline float relu_keep_nan(float x) { return x < 0.f ? 0.f : x; }
 // read one operand group hit 16 different bank groups).
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Sink-attention gate (Fast KVzip page, core method), epilogue of one
-// (64-row tile, key head): act[r] holds the head's G query vectors of 16
-// then its key of 16.  Each query head's weight on the token's own key
-// against the n_sinks sink keys (scores scaled by 1/sqrt(16)), softmax with
-// its maximum subtracted; the gate is the largest over the G query heads
-// (a NaN anywhere gives NaN, so keep = 0).
-template <int HG>
-__device__ void sink_epilogue(const GateArgs &a, const float *act, int64_t row0, int head, float *scratch) {
-    constexpr int DK = 16;
-    const int G = HG / DK - 1;
-    const int S = a.n_sinks;
-    float *lds_s = scratch;                // [S][16]
-    float *lds_a = scratch + 64 * DK;      // [64][G]
-    for (int i = threadIdx.x; i < S * DK; i += NT) lds_s[i] = a.sinks[(int64_t)head * S * DK + i];
-    __syncthreads();
-    for (int item = threadIdx.x; item < 64 * G; item += NT) {
-        const int r = item / G, g = item - r * G;
-        const float *q = act + r * (HG + 1) + g * DK;
-        const float *k = act + r * (HG + 1) + G * DK;
-        float own = 0.f;
-#pragma unroll
-        for (int e = 0; e < DK; ++e) own = fmaf(q[e], k[e], own);
-        own *= 0.25f;
-        float m = own;
-        for (int j = 0; j < S; ++j) {
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < DK; ++e) d = fmaf(q[e], lds_s[j * DK + e], d);
-            m = fmaxf(m, d * 0.25f);
-        }
-        const float num = expf(own - m);
-        float den = num;
-        for (int j = 0; j < S; ++j) {
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < DK; ++e) d = fmaf(q[e], lds_s[j * DK + e], d);
-            den += expf(d * 0.25f - m);
-        }
-        lds_a[r * G + g] = num / den;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int64_t row = row0 + threadIdx.x;
-        if (row < a.n_rows) {
-            float u = lds_a[threadIdx.x * G];
-            for (int g = 1; g < G; ++g) {
-                const float x = lds_a[threadIdx.x * G + g];
-                u = (x != x || x > u) ? x : u;  // NaN wins
-            }
-            if (a.utility) a.utility[row * a.n_kv + head] = u;
-            a.keep[row * a.n_kv + head] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
-        }
-    }
-}
-
-template <int HG, int JC, bool SINK = false> struct GatePipe {
+template <int HG, int JC> struct GatePipe {
     // One depth for both streams: vector-memory loads complete in issue
     // order, so waiting for W1's pieces of iteration j also waits for every
     // hidden-row load issued before them -- a deeper register prefetch than
@@ -146,8 +91,7 @@ template <int HG, int JC, bool SINK = false> struct GatePipe {
     static constexpr int PIECES = HG / 8;                // 1 KB pieces of a W1 stage (8 units each)
     static constexpr int LB = (PIECES + 3) / 4;          // direct loads per wave and stage (at most)
     static constexpr int LA = 2;                         // hidden-row loads per wave and iteration
-    static constexpr int EPI = SINK ? 64 * (HG + 1) * 4 + 64 * 16 * 4 + 64 * 8 * 4
-                                    : 64 * (HG + 1) * 4 + 16 * (HG + 1) * 4;
+    static constexpr int EPI = 64 * (HG + 1) * 4 + 16 * (HG + 1) * 4;
     static constexpr int LDS = NSTAGE * SBYTES > EPI ? NSTAGE * SBYTES : EPI;
 };
 
@@ -169,9 +113,9 @@ __device__ inline void wait_vm(int n) {
 // the wait counts fold to constants and the compiler tracks each hidden-row
 // load to its use (a run-time trip count makes it wait for every load at the
 // top of each unrolled block).
-template <int HG, int JC, bool SINK = false>
+template <int HG, int JC>
 __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
-    using C = GatePipe<HG, JC, SINK>;
+    using C = GatePipe<HG, JC>;
     constexpr int P = C::P;
     constexpr int NTL = HG / 16;  // unit tiles
     static_assert((P - 1) * (C::LB + C::LA) <= 63, "vmcnt range");
@@ -180,23 +124,12 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
     const int wave = threadIdx.x >> 6;
     const int i16 = lane & 15;
     const int q4 = lane >> 4;
-    // the sink gate runs one workgroup per (64-row tile, key head); the heads
-    // of a tile are launched next to each other and on the same XCD (ids
-    // 8 apart), so the tile's hidden rows are read from HBM about once
-    int64_t tile = blockIdx.x;
-    int head = 0;
-    if constexpr (SINK) {
-        const int x = (int)blockIdx.x;
-        tile = (int64_t)(x / (8 * a.n_kv)) * 8 + (x & 7);
-        head = (x / 8) % a.n_kv;
-    }
-    const int64_t row0 = tile * 64;
-    if (SINK && row0 >= a.n_rows) return;
+    const int64_t row0 = (int64_t)blockIdx.x * 64;
     const int J = JC > 0 ? JC : a.d_model / 64;  // iterations
     const int64_t my_row = min(row0 + wave * 16 + i16, a.n_rows - 1);  // rows past n re-read the last
     const __bf16 *hrow = (const __bf16 *)a.hidden + my_row * a.ld_hidden + 8 * q4;
     const int64_t w1_row_bytes = (int64_t)a.d_model * 2;
-    const char *w1 = (const char *)a.w1 + (int64_t)head * HG * w1_row_bytes;
+    const char *w1 = (const char *)a.w1;
     // this wave's share of a stage's pieces (pieces wave, wave + 4, ...)
     const int lbw = (C::PIECES - wave + 3) / 4;
 
@@ -269,16 +202,6 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
     }
     __syncthreads();  // the stages become the epilogue's scratch
     float *act = (float *)lds;                       // [64][HG + 1]
-    if constexpr (SINK) {
-#pragma unroll
-        for (int n = 0; n < NTL; ++n) {
-            const int jj = 16 * n + i16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) act[(wave * 16 + 4 * q4 + r) * (HG + 1) + jj] = acc[n][r];
-        }
-        sink_epilogue<HG>(a, act, row0, head, act + 64 * (HG + 1));
-        return;
-    }
     float *lds_w2 = act + 64 * (HG + 1);             // [16][HG + 1]
 #pragma unroll
     for (int n = 0; n < NTL; ++n) {
@@ -480,6 +403,198 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
         const float u = sigmoid_f(logit);
         if (a.utility) a.utility[row * nkv + k] = u;
         a.keep[row * nkv + k] = (u >= a.tau) ? 1 : 0;  // NaN -> 0
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sink-attention gate (Fast KVzip page, core method): per key head, G query
+// vectors and one key of 16 dimensions are projections of the hidden state;
+// each query's weight on the token's own key against the n_sinks sink keys
+// (scores scaled by 1/sqrt(16), softmax with its maximum subtracted) and the
+// largest over the G queries is the utility (a NaN anywhere gives NaN, so
+// keep = 0).  A workgroup takes 256 rows and H key heads (wave w:
+// rows 64 w .. 64 w + 63), i.e. the T = H (G + 1) projections of d_key = 16
+// (G queries and one key per head) as 16-unit tiles.  The projection rows of
+// W1 stream through an LDS ring of direct loads shared by the 4 waves; each
+// wave loads its own hidden rows into registers, P iterations ahead.  The
+// projections are formed transposed (p^T = W1 . h^T), so a lane holds one row
+// and four dimensions (4 k + r) of every tile, and the epilogue works from the
+// accumulators: the own-key score is a 4-lane sum of q . k; the sink scores
+// are an f32 16x16x4 MFMA of the sink keys against q^T (step c takes the
+// dimensions 4 k + c, register c of the tile); then the softmax against the
+// sinks, the maximum over the G queries and the threshold.  Taller tiles and
+// several heads per workgroup cut the bytes each compute unit loads (the
+// weights once per 256 rows, the hidden rows once per H heads).
+template <int G, int H, bool FIXED> struct SinkTall {
+    static constexpr int T = H * (G + 1);                // projection tiles
+    static constexpr int PIECES = 2 * T;                 // 1 KB W1 pieces per stage (8 units x 128 B)
+    static constexpr int LB = (PIECES + 3) / 4;          // direct loads per wave and stage (at most)
+    static constexpr int LA = 8;                         // hidden loads per wave and iteration (4 row tiles x 2)
+    // iterations in flight: 4, or 2 with 10 tiles in the fully unrolled loop
+    // (FIXED: d_model = 4096), whose registers would spill at 4
+    static constexpr int P = (T >= 10 && FIXED) ? 2 : 4;
+    static constexpr int NSTAGE = P + 1;
+    static constexpr int SBYTES = T * 16 * 128;          // W1 stage: T x 16 units x 64 columns
+};
+
+template <int G, int H, int JC>
+__global__ void __launch_bounds__(NT) gate_sink_tall_kernel(GateArgs a) {
+    using C = SinkTall<G, H, (JC > 0)>;
+    constexpr int P = C::P;
+    constexpr int T = C::T;
+    constexpr int DK = 16;
+    static_assert((P - 1) * (C::LB + C::LA) <= 63, "vmcnt range");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15;
+    const int q4 = lane >> 4;
+    // launch id -> (256-row tile, head group): the head groups of a tile are
+    // launched 8 ids apart (the same XCD), so its hidden rows come from HBM
+    // about once
+    const int ngrp = a.n_kv / H;
+    const int x = (int)blockIdx.x;
+    const int64_t tile = (int64_t)(x / (8 * ngrp)) * 8 + (x & 7);
+    const int hgrp = (x / 8) % ngrp;
+    const int64_t row0 = tile * 256;
+    if (row0 >= a.n_rows) return;
+    const int J = JC > 0 ? JC : a.d_model / 64;
+    const int64_t w1_row_bytes = (int64_t)a.d_model * 2;
+    const char *w1 = (const char *)a.w1 + (int64_t)hgrp * T * 16 * w1_row_bytes;  // this group's projection rows
+    const int lbw = (C::PIECES - wave + 3) / 4;
+    const __bf16 *hrow[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int64_t r = min(row0 + 64 * wave + 16 * rt + i16, a.n_rows - 1);  // rows past n re-read the last
+        hrow[rt] = (const __bf16 *)a.hidden + r * a.ld_hidden + 8 * q4;
+    }
+
+    auto issue_w1 = [&](int j, int st) {
+        char *dst = stage_at<C::SBYTES, C::NSTAGE>(st);
+#pragma unroll
+        for (int u = 0; u < C::LB; ++u) {
+            const int i = wave + 4 * u;  // piece: units 8 i .. 8 i + 7
+            if (C::PIECES % 4 == 0 || i < C::PIECES) {
+                const int unit = 8 * i + (lane >> 3);
+                const int c = (lane & 7) ^ ((unit >> 1) & 7);
+                const char *src = w1 + unit * w1_row_bytes + (int64_t)(64 * j + 8 * c) * 2;
+                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
+            }
+        }
+    };
+    bf16x8 hv[P][4][2];
+    auto issue_h = [&](int j, bf16x8 (&dst)[4][2]) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) dst[rt][ks] = *(const bf16x8 *)(hrow[rt] + 64 * j + 32 * ks);
+    };
+
+    f32x4 acc[4][T];  // p^T tiles: lane (row 64 wave + 16 rt + i16, dims 4 q4 + r of projection t)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        if (i < J) {
+            issue_w1(i, i);
+            issue_h(i, hv[i]);
+        }
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < (JC > 0 ? JC : J); j0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int j = j0 + u;
+            if (j < J) {
+                wait_vm<63>(min(P - 1, J - 1 - j) * (lbw + C::LA));
+                __builtin_amdgcn_s_barrier();  // every wave's pieces of j landed; stage j - 1 is free
+                if (j + P < J) issue_w1(j + P, (j + P) % C::NSTAGE);
+                const char *st = stage_at<C::SBYTES, C::NSTAGE>(j % C::NSTAGE);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bf16x8 wv[T];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        const int unit = 16 * t + i16;
+                        wv[t] = *(const bf16x8 *)(st + unit * 128 + (((4 * ks + q4) ^ ((unit >> 1) & 7)) << 4));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+#pragma unroll
+                        for (int rt = 0; rt < 4; ++rt)
+                            acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[t], hv[u][rt][ks], acc[rt][t], 0, 0, 0);
+                }
+                if (j + P < J) issue_h(j + P, hv[u]);
+            }
+        }
+    }
+
+    // epilogue, per wave from its accumulators
+    const int S = a.n_sinks;
+    const int nst = (S + 15) / 16;  // 16-sink tiles (S <= 64)
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        const int head = hgrp * H + h;
+        const float *sk = a.sinks + (int64_t)head * S * DK;
+        float sa[4][4];  // A operands: sink 16 st + i16, dimension 4 q4 + c
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int sj = 16 * st + i16;
+                sa[st][c] = (st < nst && sj < S) ? sk[sj * DK + 4 * q4 + c] : 0.f;
+            }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 kt = acc[rt][h * (G + 1) + G];
+            float umax = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const f32x4 qt = acc[rt][h * (G + 1) + g];
+                float own = fmaf(qt[3], kt[3], fmaf(qt[2], kt[2], fmaf(qt[1], kt[1], qt[0] * kt[0])));
+                own += __shfl_xor(own, 16);
+                own += __shfl_xor(own, 32);
+                own *= 0.25f;
+                f32x4 sc[4];
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    sc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (st < nst) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            sc[st] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[st][c], qt[c], sc[st], 0, 0, 0);
+                    }
+                }
+                // this lane's sinks: 16 st + 4 q4 + r
+                float m = own;
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * st + 4 * q4 + r < S) m = fmaxf(m, sc[st][r] * 0.25f);
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                float den = 0.f;
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * st + 4 * q4 + r < S) den += expf(sc[st][r] * 0.25f - m);
+                den += __shfl_xor(den, 16);
+                den += __shfl_xor(den, 32);
+                const float num = expf(own - m);
+                const float ug = num / (num + den);
+                umax = (g == 0 || ug != ug || ug > umax) ? ug : umax;  // NaN wins
+            }
+            const int64_t row = row0 + 64 * wave + 16 * rt + i16;
+            if (q4 == 0 && row < a.n_rows) {
+                if (a.utility) a.utility[row * a.n_kv + head] = umax;
+                a.keep[row * a.n_kv + head] = (umax >= a.tau) ? 1 : 0;  // NaN -> 0
+            }
+        }
     }
 }
 
@@ -760,15 +875,24 @@ hipError_t launch_gate(const GateArgs &a0, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int G, int H>
+static void launch_sink_tall(const GateArgs &a, hipStream_t s) {
+    const int64_t tiles = (a.n_rows + 255) / 256;
+    const dim3 grid((unsigned)(((tiles + 7) / 8) * 8 * (a.n_kv / H)));
+    if (a.d_model == 4096)
+        hipLaunchKernelGGL((gate_sink_tall_kernel<G, H, 64>), grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((gate_sink_tall_kernel<G, H, 0>), grid, dim3(NT), 0, s, a);
+}
+
+// heads per workgroup: as many as keep the projection tiles at most 10 (the
+// accumulators of 4 row tiles x 10 tiles fill 160 registers) and divide n_kv
 template <int G>
 static void launch_sink_g(const GateArgs &a, hipStream_t s) {
-    constexpr int HG = 16 * (G + 1);
-    const int64_t tiles = (a.n_rows + 63) / 64;
-    const dim3 grid((unsigned)(((tiles + 7) / 8) * 8 * a.n_kv));
-    if (a.d_model == 4096)
-        hipLaunchKernelGGL((gate_pipe_kernel<HG, 64, true>), grid, dim3(NT), 0, s, a);
-    else
-        hipLaunchKernelGGL((gate_pipe_kernel<HG, 0, true>), grid, dim3(NT), 0, s, a);
+    constexpr int HMAX = 10 / (G + 1);
+    if (HMAX >= 4 && a.n_kv % 4 == 0) launch_sink_tall<G, (HMAX >= 4 ? 4 : 1)>(a, s);
+    else if (HMAX >= 2 && a.n_kv % 2 == 0) launch_sink_tall<G, (HMAX >= 2 ? 2 : 1)>(a, s);
+    else launch_sink_tall<G, 1>(a, s);
 }
 
 hipError_t launch_sink_gate(const GateArgs &a, hipStream_t s) {
