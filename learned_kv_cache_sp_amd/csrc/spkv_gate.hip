@@ -220,10 +220,13 @@ __global__ void __launch_bounds__(NT) gate_pipe_kernel(GateArgs a) {
 // for all 64 rows).  Per 64-column iteration the workgroup's hidden tile
 // (64 rows x 128 bytes, the HBM stream) lands in an LDS ring by direct
 // global->LDS loads, a quarter from each wave, and every wave reads it as its
-// B operands; each wave loads its own W1 rows (L2-resident) straight into
-// registers as A operands.  Sharing the hidden tile rather than W1 halves the
-// LDS traffic per iteration (8 KB written + 4 x 8 KB read, against 16 KB
-// written + 4 x 16 KB read when every wave needs all of W1).
+// B operands; each wave loads its own W1 rows (L2-resident) into registers
+// as whole 128-byte lines, eight rows per instruction, and passes them
+// through a small LDS slice of its own into the A-operand layout.  (Loading
+// the operand layout directly -- 16 rows x 64 bytes per instruction -- runs
+// at about a third of the rate per compute unit, and every workgroup loads
+// all of W1.)  Sharing the hidden tile rather than W1 keeps the LDS traffic
+// per iteration low (8 KB written + 4 x 8 KB read for the tile).
 // Layer 1 is computed transposed, a^T[unit][row] = W1 . h^T, so that each
 // lane ends up holding one row and four units of every 16 x 16 tile --
 // exactly the B operand of the f32 16x16x4 MFMA that forms layer 2
@@ -247,6 +250,17 @@ __device__ __attribute__((always_inline)) inline char *stage_at(int st) {
     } else {
         return stage_obj<0, SB>();
     }
+}
+
+// the two W1 slices of the 64-row kernel (each its own LDS object as well)
+template <int S, int SB>
+__device__ __attribute__((always_inline)) inline char *wslice_obj() {
+    __shared__ __attribute__((aligned(1024))) char buf[SB];
+    return buf;
+}
+template <int SB>
+__device__ __attribute__((always_inline)) inline char *wslice(int p) {
+    return p ? wslice_obj<1, SB>() : wslice_obj<0, SB>();
 }
 
 template <int HG> struct UnitSplit {
@@ -290,8 +304,11 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         hsrc[k] = (const __bf16 *)a.hidden + grow * a.ld_hidden + 8 * c;
     }
-    // W1 operand rows of this wave: unit 16 (wave NTW + nn) + i16, 8 q4 .. of each 32-column half
-    const __bf16 *wsrc = (const __bf16 *)a.w1 + (int64_t)(16 * wave * NTW + i16) * a.d_model + 8 * q4;
+    // W1 rows of this wave, loaded as whole 128-byte lines: instruction m
+    // reads units 16 wave NTW + 8 m + (lane >> 3), 16-byte chunk lane & 7 of
+    // the iteration's 64 columns; they go through this wave's LDS slice
+    // (swizzled like the hidden tile) into the MFMA operand layout
+    const __bf16 *wsrc = (const __bf16 *)a.w1 + (int64_t)(16 * wave * NTW + (lane >> 3)) * a.d_model + 8 * (lane & 7);
 
     auto issue_h = [&](int j, int st) {
         char *dst = stage_at<C::SBYTES, C::NSTAGE>(st);
@@ -300,13 +317,13 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
             __builtin_amdgcn_global_load_lds((const void *)(hsrc[k] + 64 * j),
                                              (lds_void *)(dst + (C::LH * wave + k) * 1024), 16, 0, 0);
     };
-    bf16x8 wv[D][NTW][2];
+    bf16x8 wv[D][NTW][2];  // [m / 2][m % 2]: instruction m = 2 nn + ks of the raw lines
     auto issue_w = [&](int j, bf16x8 (&dst)[NTW][2]) {
 #pragma unroll
         for (int nn = 0; nn < NTW; ++nn)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                dst[nn][ks] = *(const bf16x8 *)(wsrc + (int64_t)16 * nn * a.d_model + 64 * j + 32 * ks);
+                dst[nn][ks] = *(const bf16x8 *)(wsrc + (int64_t)8 * (2 * nn + ks) * a.d_model + 64 * j);
     };
 
     f32x4 acc[4][NTW];  // a^T tiles: lane (row 16 rt + i16, units 16 (wave NTW + nn) + 4 q4 + r)
@@ -338,6 +355,13 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
                 __builtin_amdgcn_s_barrier();
                 if (j + D < J) issue_h(j + D, (j + D) % C::NSTAGE);
                 const char *st = stage_at<C::SBYTES, C::NSTAGE>(j % C::NSTAGE);
+                // this wave's W1 lines of j -> its LDS slice (row ur = 8 m + lane / 8)
+                char *ws = wslice<NTW * 2048 * 4>(j & 1) + wave * NTW * 2048;
+#pragma unroll
+                for (int m = 0; m < 2 * NTW; ++m) {
+                    const int ur = 8 * m + (lane >> 3);
+                    *(bf16x8 *)(ws + ur * 128 + (((lane & 7) ^ ((ur >> 1) & 7)) << 4)) = wv[u][m >> 1][m & 1];
+                }
                 bf16x8 av[4][2];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
@@ -346,6 +370,14 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
                         const int r = 16 * rt + i16;
                         av[rt][ks] = *(const bf16x8 *)(st + r * 128 + (((4 * ks + q4) ^ ((r >> 1) & 7)) << 4));
                     }
+                bf16x8 bw[NTW][2];
+#pragma unroll
+                for (int nn = 0; nn < NTW; ++nn)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const int ur = 16 * nn + i16;
+                        bw[nn][ks] = *(const bf16x8 *)(ws + ur * 128 + (((4 * ks + q4) ^ ((ur >> 1) & 7)) << 4));
+                    }
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
@@ -353,7 +385,7 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
                     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                         for (int nn = 0; nn < NTW; ++nn)
-                            acc[rt][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u][nn][ks], av[rt][ks],
+                            acc[rt][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[nn][ks], av[rt][ks],
                                                                                   acc[rt][nn], 0, 0, 0);
                 if (j + D < J) issue_w(j + D, wv[u]);
             }
