@@ -446,10 +446,15 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
 // largest over the G queries is the utility (a NaN anywhere gives NaN, so
 // keep = 0).  A workgroup takes 256 rows and H key heads (wave w:
 // rows 64 w .. 64 w + 63), i.e. the T = H (G + 1) projections of d_key = 16
-// (G queries and one key per head) as 16-unit tiles.  The projection rows of
-// W1 stream through an LDS ring of direct loads shared by the 4 waves; each
-// wave loads its own hidden rows into registers, P iterations ahead.  The
-// projections are formed transposed (p^T = W1 . h^T), so a lane holds one row
+// (G queries and one key per head) as 16-unit tiles.  Every load reads whole
+// 128-byte lines (8 rows x 128 bytes per instruction), P iterations ahead,
+// into registers: a quarter of the iteration's projection rows of W1 per
+// wave, and the wave's own hidden rows; at their iteration they are written
+// to double-buffered LDS -- the W1 stage shared by the 4 waves, the hidden
+// rows in the wave's slice -- and read back in the operand layout (loads in
+// the operand layout, 16 rows x 64 bytes per instruction, and direct
+// global->LDS loads both run at about a third of that rate per compute
+// unit).  The projections are formed transposed (p^T = W1 . h^T), so a lane holds one row
 // and four dimensions (4 k + r) of every tile, and the epilogue works from the
 // accumulators: the own-key score is a 4-lane sum of q . k; the sink scores
 // are an f32 16x16x4 MFMA of the sink keys against q^T (step c takes the
@@ -460,12 +465,11 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
 template <int G, int H, bool FIXED> struct SinkTall {
     static constexpr int T = H * (G + 1);                // projection tiles
     static constexpr int PIECES = 2 * T;                 // 1 KB W1 pieces per stage (8 units x 128 B)
-    static constexpr int LB = (PIECES + 3) / 4;          // direct loads per wave and stage (at most)
-    static constexpr int LA = 8;                         // hidden loads per wave and iteration (4 row tiles x 2)
-    // iterations in flight: 4, or 2 with 10 tiles in the fully unrolled loop
-    // (FIXED: d_model = 4096), whose registers would spill at 4
-    static constexpr int P = (T >= 10 && FIXED) ? 2 : 4;
-    static constexpr int NSTAGE = P + 1;
+    static constexpr int LB = (PIECES + 3) / 4;          // W1 loads per wave and iteration (at most)
+    static constexpr int LA = 8;                         // hidden loads per wave and iteration (64 rows x 128 B)
+    // iterations in flight: 4, or 2 with 6 or more tiles in the fully
+    // unrolled loop (FIXED: d_model = 4096), whose registers would spill at 4
+    static constexpr int P = (T >= 6 && FIXED) ? 2 : 4;
     static constexpr int SBYTES = T * 16 * 128;          // W1 stage: T x 16 units x 64 columns
 };
 
@@ -480,9 +484,6 @@ __global__ void __launch_bounds__(NT) gate_sink_tall_kernel(GateArgs a) {
     const int wave = threadIdx.x >> 6;
     const int i16 = lane & 15;
     const int q4 = lane >> 4;
-    // launch id -> (256-row tile, head group): the head groups of a tile are
-    // launched 8 ids apart (the same XCD), so its hidden rows come from HBM
-    // about once
     const int ngrp = a.n_kv / H;
     const int x = (int)blockIdx.x;
     const int64_t tile = (int64_t)(x / (8 * ngrp)) * 8 + (x & 7);
@@ -491,37 +492,34 @@ __global__ void __launch_bounds__(NT) gate_sink_tall_kernel(GateArgs a) {
     if (row0 >= a.n_rows) return;
     const int J = JC > 0 ? JC : a.d_model / 64;
     const int64_t w1_row_bytes = (int64_t)a.d_model * 2;
-    const char *w1 = (const char *)a.w1 + (int64_t)hgrp * T * 16 * w1_row_bytes;  // this group's projection rows
-    const int lbw = (C::PIECES - wave + 3) / 4;
-    const __bf16 *hrow[4];
+    const char *w1 = (const char *)a.w1 + (int64_t)hgrp * T * 16 * w1_row_bytes;
+    // every load reads whole 128-byte lines (8 rows x 128 B per instruction):
+    // W1 piece i (units 8 i .. 8 i + 7) by wave i % 4, the wave's hidden rows
+    // 64 wave + 8 k + lane / 8; both are written to LDS (swizzled rows) just
+    // before their iteration and read back in the operand layout
+    const char *wsrc = w1 + (int64_t)(lane >> 3) * w1_row_bytes + 16 * (lane & 7);
+    const __bf16 *hsrc[8];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int64_t r = min(row0 + 64 * wave + 16 * rt + i16, a.n_rows - 1);  // rows past n re-read the last
-        hrow[rt] = (const __bf16 *)a.hidden + r * a.ld_hidden + 8 * q4;
+    for (int k = 0; k < 8; ++k) {
+        const int64_t r = min(row0 + 64 * wave + 8 * k + (lane >> 3), a.n_rows - 1);  // rows past n re-read the last
+        hsrc[k] = (const __bf16 *)a.hidden + r * a.ld_hidden + 8 * (lane & 7);
     }
-
-    auto issue_w1 = [&](int j, int st) {
-        char *dst = stage_at<C::SBYTES, C::NSTAGE>(st);
+    bf16x8 wraw[P][C::LB];
+    auto issue_w1 = [&](int j, bf16x8 (&dst)[C::LB]) {
 #pragma unroll
         for (int u = 0; u < C::LB; ++u) {
-            const int i = wave + 4 * u;  // piece: units 8 i .. 8 i + 7
-            if (C::PIECES % 4 == 0 || i < C::PIECES) {
-                const int unit = 8 * i + (lane >> 3);
-                const int c = (lane & 7) ^ ((unit >> 1) & 7);
-                const char *src = w1 + unit * w1_row_bytes + (int64_t)(64 * j + 8 * c) * 2;
-                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
-            }
+            const int i = wave + 4 * u;
+            if (C::PIECES % 4 == 0 || i < C::PIECES)
+                dst[u] = *(const bf16x8 *)(wsrc + (int64_t)8 * i * w1_row_bytes + 128 * j);
         }
     };
-    bf16x8 hv[P][4][2];
-    auto issue_h = [&](int j, bf16x8 (&dst)[4][2]) {
+    bf16x8 hraw[P][8];
+    auto issue_h = [&](int j, bf16x8 (&dst)[8]) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) dst[rt][ks] = *(const bf16x8 *)(hrow[rt] + 64 * j + 32 * ks);
+        for (int k = 0; k < 8; ++k) dst[k] = *(const bf16x8 *)(hsrc[k] + 64 * j);
     };
 
-    f32x4 acc[4][T];  // p^T tiles: lane (row 64 wave + 16 rt + i16, dims 4 q4 + r of projection t)
+    f32x4 acc[4][T];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -530,8 +528,8 @@ __global__ void __launch_bounds__(NT) gate_sink_tall_kernel(GateArgs a) {
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         if (i < J) {
-            issue_w1(i, i);
-            issue_h(i, hv[i]);
+            issue_w1(i, wraw[i]);
+            issue_h(i, hraw[i]);
         }
     }
 #pragma unroll
@@ -540,26 +538,56 @@ __global__ void __launch_bounds__(NT) gate_sink_tall_kernel(GateArgs a) {
         for (int u = 0; u < P; ++u) {
             const int j = j0 + u;
             if (j < J) {
-                wait_vm<63>(min(P - 1, J - 1 - j) * (lbw + C::LA));
-                __builtin_amdgcn_s_barrier();  // every wave's pieces of j landed; stage j - 1 is free
-                if (j + P < J) issue_w1(j + P, (j + P) % C::NSTAGE);
-                const char *st = stage_at<C::SBYTES, C::NSTAGE>(j % C::NSTAGE);
+                wait_vm<63>(min(P - 1, J - 1 - j) * (C::LB + C::LA));
+                // buffer j & 1 was last read in iteration j - 2, before every
+                // wave passed the barrier of j - 1
+                char *wst = stage_at<C::SBYTES, 2>(j & 1);
+#pragma unroll
+                for (int uu = 0; uu < C::LB; ++uu) {
+                    const int i = wave + 4 * uu;
+                    if (C::PIECES % 4 == 0 || i < C::PIECES) {
+                        const int unit = 8 * i + (lane >> 3);
+                        *(bf16x8 *)(wst + unit * 128 + (((lane & 7) ^ ((unit >> 1) & 7)) << 4)) = wraw[u][uu];
+                    }
+                }
+                char *hst = wslice<4 * 64 * 128>(j & 1) + wave * 64 * 128;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int r = 8 * k + (lane >> 3);
+                    *(bf16x8 *)(hst + r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4)) = hraw[u][k];
+                }
+                // the W1 stage of j is complete: a barrier whose fences cover
+                // LDS only (__syncthreads would also wait for every load in flight)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                if (j + P < J) {
+                    issue_w1(j + P, wraw[u]);
+                    issue_h(j + P, hraw[u]);
+                }
+                bf16x8 hv[4][2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const int r = 16 * rt + i16;
+                        hv[rt][ks] = *(const bf16x8 *)(hst + r * 128 + (((4 * ks + q4) ^ ((r >> 1) & 7)) << 4));
+                    }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     bf16x8 wv[T];
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
                         const int unit = 16 * t + i16;
-                        wv[t] = *(const bf16x8 *)(st + unit * 128 + (((4 * ks + q4) ^ ((unit >> 1) & 7)) << 4));
+                        wv[t] = *(const bf16x8 *)(wst + unit * 128 + (((4 * ks + q4) ^ ((unit >> 1) & 7)) << 4));
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int t = 0; t < T; ++t)
 #pragma unroll
                         for (int rt = 0; rt < 4; ++rt)
-                            acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[t], hv[u][rt][ks], acc[rt][t], 0, 0, 0);
+                            acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[t], hv[rt][ks], acc[rt][t], 0, 0, 0);
                 }
-                if (j + P < J) issue_h(j + P, hv[u]);
             }
         }
     }
