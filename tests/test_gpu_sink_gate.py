@@ -54,6 +54,11 @@ def _rows(n, d, W, sinks, G, tau, seed):
     (2, 2, 0, 128, 130),      # no sinks: every pair is kept
     (1, 8, 64, 512, 1),
     (16, 8, 5, 192, 77),
+    (8, 1, 16, 4096, 300),    # 4 heads per workgroup (8 projection tiles), d_model 4096: 2 iterations in flight
+    (6, 2, 5, 4096, 257),     # 2 heads per workgroup (6 tiles), two 256-row tiles, the second of one row
+    (4, 8, 16, 4096, 100),    # one head per workgroup (9 tiles), d_model 4096
+    (5, 2, 3, 640, 513),      # n_kv odd: one head per workgroup, three row tiles
+    (12, 1, 64, 1024, 1030),  # 4 heads per workgroup, 64 sinks (four 16-sink tiles)
 ])
 def test_sink_gate_matches_oracle(n_kv, G, S, d, n):
     W, sinks = _weights(n_kv, G, S, d, 40 + n_kv + G + S)
