@@ -48,8 +48,10 @@ the decode roofline also gives its fraction of that measured ceiling.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on every host core this process may use (nproc, affinity, cgroup
 quota and CPU model recorded).  The default decode_32k run also carries a
-``secondary`` list: decode_131k, ragged_32 and prefill_64k, each measured the
-same way with its own default steps.
+``secondary`` list: decode_131k, ragged_32, prefill_64k and the batch-16
+pair decode_32k_b16 / decode_32k_b16_tau0 (keep rates against every pair
+kept, with their per-step ratio in ``sparse_vs_full_batch16``), each measured
+the same way with its own default steps.
 
 Profile summaries (no GPU needed):
     python bench.py --summarize-stats DIR
@@ -1250,7 +1252,9 @@ def cpu_baseline(name: str, wl, budget_s: float) -> dict:
 
 DEFAULT_STEPS = {"decode": (256, 16), "prefill": (4, 1), "rethreshold_32k": (20, 3), "head_stats_1m": (50, 5),
                  "soft_prefill_16k": (5, 1), "sink_gate_16k": (50, 5)}
-SECONDARY = ["decode_131k", "ragged_32", "prefill_64k"]
+SECONDARY = ["decode_131k", "ragged_32", "prefill_64k", "decode_32k_b16", "decode_32k_b16_tau0"]
+# secondary lines without a CPU baseline (the same oracle work as decode_32k's)
+SECONDARY_NO_CPU = {"decode_32k_b16", "decode_32k_b16_tau0"}
 
 
 def workload(name: str):
@@ -1348,12 +1352,22 @@ def main():
         for name in SECONDARY:
             t0 = time.perf_counter()
             r2, wl2 = run_workload(args, name)
-            if not args.no_cpu_baseline:
+            if not args.no_cpu_baseline and name not in SECONDARY_NO_CPU:
                 r2["cpu_baseline"] = cpu_baseline(name, wl2, args.cpu_budget)
             r2["wall_s"] = round(time.perf_counter() - t0, 1)
             res["secondary"].append(r2)
             print(f"[bench] {name}: {r2['value']:.1f} {r2['unit']}, roofline frac {r2['roofline']['frac']}",
                   file=sys.stderr, flush=True)
+        # SP-KV's own comparison (section 3.4, Fig. 3 right: its sparse decode
+        # kernel against full attention at batch 16) through these kernels:
+        # the configured keep rates against tau = 0 (every pair kept)
+        by = {r["config"]["workload"]: r for r in res["secondary"]}
+        sp, full = by.get("decode_32k_b16"), by.get("decode_32k_b16_tau0")
+        if sp and full:
+            res["sparse_vs_full_batch16"] = {
+                "speedup_per_step": round(full["ms_per_step"] / sp["ms_per_step"], 3),
+                "bytes_ratio": round(full["roofline"]["bytes_per_launch"] / sp["roofline"]["bytes_per_launch"], 3),
+                "sparse_ms_per_step": sp["ms_per_step"], "full_ms_per_step": full["ms_per_step"]}
     print(json.dumps(res))
 
 
