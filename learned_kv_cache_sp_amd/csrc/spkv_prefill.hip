@@ -7,9 +7,10 @@
 // row also sees kept keys of its own chunk once they leave its window (Eq. 4
 // is per token).
 //
-// bf16 (MFMA): a workgroup of 8 waves (2 per SIMD) takes 256 (row, query
-// head) pairs of one key head -- 32 / G query positions per wave, all G
-// heads of the group -- and walks one list of 64-key blocks: the cached
+// bf16 (MFMA): a workgroup of 8 waves (2 per SIMD; 4 waves and two
+// workgroups per compute unit at hd = 64) takes 32 (row, query head) pairs
+// of one key head per wave -- 32 / G query positions, all G heads of the
+// group -- and walks one list of 64-key blocks: the cached
 // entries visible to its first row (no mask), the staircase of cached
 // entries that only later rows see (mask pos <= t - w), and the window band
 // (mask 0 <= t - s < w).  Whole cached blocks stream into LDS through a
@@ -103,12 +104,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int PF_NW = 8;           // waves per workgroup (2 per SIMD)
-constexpr int PF_NT = PF_NW * 64;
+// Workgroup shape per head size.  hd = 128: 8 waves (2 per SIMD) share one
+// workgroup's key/value buffers (148 KB of LDS).  hd = 64: 4 waves, and two
+// workgroups per compute unit (78 KB of LDS each, 2048 page-table entries),
+// so that the two waves of a SIMD belong to different barriers and their
+// phases need not line up: 9 % faster at hd = 64, while at hd = 128 the
+// doubled key/value traffic per flop of half-size workgroups costs more
+// than that (4 % slower) and two would not fit in LDS.
+template <int HD>
+struct PfShape {
+    static constexpr int NW = HD == 64 ? 4 : 8;          // waves per workgroup
+    static constexpr int NT = NW * 64;
+    static constexpr int PTMAX = HD == 64 ? 2048 : 4096;  // page-table entries staged in LDS
+};
 constexpr int PF_PT = 2;           // 16-pair MFMA column tiles per wave
 constexpr int PF_KB = 64;          // keys per block
 constexpr int PF_ST = 4;           // LDS buffers of the direct-load pipeline (two blocks per barrier)
-constexpr int PF_PTMAX = 4096;     // page-table entries staged in LDS
 constexpr float PF_LOG2E = 1.4426950408889634f;
 constexpr float PF_LN2 = 0.6931471805599453f;
 
@@ -140,10 +151,11 @@ __device__ inline int entry_pos(const CacheView &c, const int32_t *pt, int j) {
 
 // number of cached entries of (b, g) with position <= x (positions increase
 // along the list), by two rounds of parallel probes
+template <int NT>
 __device__ int count_upto(const CacheView &c, const int32_t *pt, int len, int x, int *lds_cnt) {
     if (len <= 0 || x < 0) return 0;
     // round 1: NT evenly spaced probes -> a bracket of at most ceil(len/NT) entries
-    const int step = (len + PF_NT - 1) / PF_NT;
+    const int step = (len + NT - 1) / NT;
     const int j = threadIdx.x * step;
     const bool le = j < len && entry_pos(c, pt, j) <= x;
     __syncthreads();
@@ -160,7 +172,7 @@ __device__ int count_upto(const CacheView &c, const int32_t *pt, int len, int x,
     __syncthreads();
     if (threadIdx.x == 0) lds_cnt[1] = 0;
     __syncthreads();
-    for (int jj = lo + 1 + threadIdx.x; jj - threadIdx.x < hi; jj += PF_NT) {
+    for (int jj = lo + 1 + threadIdx.x; jj - threadIdx.x < hi; jj += NT) {
         const bool le2 = jj < hi && entry_pos(c, pt, jj) <= x;
         const uint64_t bal2 = __ballot(le2);
         if ((threadIdx.x & 63) == 0 && bal2) atomicAdd(&lds_cnt[1], __popcll(bal2));
@@ -190,8 +202,11 @@ __device__ inline int voff(int e, int c) { return e * (2 * PF_KB) + ((c ^ swz_v(
 // here as -c / (1 + exp((u - tau) / beta)) (the same value without the loss
 // of precision of 1 - alpha near alpha = 1); window keys get none.
 template <int HD, bool SOFT>
-__global__ void __launch_bounds__(PF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(PfShape<HD>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(PrefillArgs a) {
+    constexpr int PF_NW = PfShape<HD>::NW;
+    constexpr int PF_NT = PfShape<HD>::NT;
+    constexpr int PF_PTMAX = PfShape<HD>::PTMAX;
     constexpr int CPR = HD / 8;                  // 16-byte chunks per key row
     constexpr int KBYTES = PF_KB * 2 * HD;       // key block
     constexpr int VBYTES = HD * 2 * PF_KB;       // transposed value block
@@ -237,8 +252,8 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int len = c.lengths[bg];
 
     // ---- the block list of this workgroup -----------------------------------
-    const int n_full = count_upto(c, pt, len, t_min - w, lds_cnt);  // visible to every row
-    const int n_part = count_upto(c, pt, len, t_max - w, lds_cnt);  // visible to the last row
+    const int n_full = count_upto<PF_NT>(c, pt, len, t_min - w, lds_cnt);  // visible to every row
+    const int n_part = count_upto<PF_NT>(c, pt, len, t_max - w, lds_cnt);  // visible to the last row
     const int s_lo = max(0, t_min - w + 1);                          // window band
     const int nb_d = n_part / PF_KB;                        // whole cached blocks (direct loads)
     const int nb_g = (n_part + PF_KB - 1) / PF_KB;          // all cached blocks
@@ -637,7 +652,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     // computed.  One barrier per 128 keys: against one per 64 keys with a
     // 3-stage ring, 2.5 % more throughput on the 8B layer's chunks.
     constexpr int WAIT_ALL = (7 << 4) | (15 << 8);  // vmcnt(0)
-    const int win_blocks = (PF_PTMAX << c.page_shift) / PF_KB;  // >= 2048 (page size >= 32)
+    const int win_blocks = (PF_PTMAX << c.page_shift) / PF_KB;  // >= 1024 (page size >= 32)
     __syncthreads();  // query operands loaded, lds_cnt no longer read
     for (int wb0 = 0; wb0 < nb_d; wb0 += win_blocks) {
         const int wb1 = min(nb_d, wb0 + win_blocks);
@@ -727,18 +742,17 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
     const CacheView &c = a.c;
     const dim3 grid(a.n_rows, a.n_q);
     if (c.dtype == SPKV_BF16 && a.group <= 16) {
-        const int rows_wg = (16 * PF_PT / a.group) * PF_NW;
-        const dim3 g2((a.n_rows + rows_wg - 1) / rows_wg, c.n_kv);
-        if (a.soft) {
-            if (c.head_dim == 128)
-                hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), g2, dim3(PF_NT), 0, s, a);
-            else
-                hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), g2, dim3(PF_NT), 0, s, a);
+        auto go = [&](auto kernel, int nw) {
+            const int rows_wg = (16 * PF_PT / a.group) * nw;
+            const dim3 g2((a.n_rows + rows_wg - 1) / rows_wg, c.n_kv);
+            hipLaunchKernelGGL(kernel, g2, dim3(nw * 64), 0, s, a);
+        };
+        if (c.head_dim == 128) {
+            if (a.soft) go(prefill_bf16_kernel<128, true>, PfShape<128>::NW);
+            else go(prefill_bf16_kernel<128, false>, PfShape<128>::NW);
         } else {
-            if (c.head_dim == 128)
-                hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), g2, dim3(PF_NT), 0, s, a);
-            else
-                hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), g2, dim3(PF_NT), 0, s, a);
+            if (a.soft) go(prefill_bf16_kernel<64, true>, PfShape<64>::NW);
+            else go(prefill_bf16_kernel<64, false>, PfShape<64>::NW);
         }
         return hipGetLastError();
     }
