@@ -105,8 +105,8 @@ typedef struct spkv_gate_desc {
  * pointer is a caller-owned device buffer.
  *
  * Persistent (global) cache, paged per (sequence b, key head g):
- *   k_pages    [n_pages, page_size, head_dim]   key rows
- *   v_pages    [n_pages, head_dim, page_size]   value rows, stored transposed
+ *   k_pages    n_pages x page_size x head_dim keys   (storage order below)
+ *   v_pages    n_pages x page_size x head_dim values (storage order below)
  *   pos_pages  [n_pages, page_size] int32       token position of each entry
  *   page_table [batch, n_kv, max_pages_per_head] int32: page id of the i-th
  *              page of (b, g); entry j of (b, g) is slot j % page_size of
@@ -117,8 +117,20 @@ typedef struct spkv_gate_desc {
  *   pool_next  [1] int32: next free page (device bump allocator)
  *   status     [1] int32: sticky SPKV_STATUS_* bits
  * Window ring of the last `window` tokens of every (b, g):
- *   ring_k     [batch, n_kv, window, head_dim]  slot = position % window
- *   ring_v     [batch, n_kv, head_dim, window]  transposed
+ *   ring_k     batch x n_kv x window x head_dim keys, slot = position % window
+ *   ring_v     batch x n_kv x window x head_dim values (storage order below)
+ * Storage order of keys and values: a page (and the ring of one (b, g)) is a
+ * run of blocks of 32 consecutive slots, block k holding slots 32k .. 32k+31
+ * at element offset 32k * head_dim.  Within a block, the key of slot r,
+ * dimension d sits at element
+ *     (d / 32) * 1024 + row(r) * 32 + d % 32,
+ *     row(r) = 16 * ((r / 4) % 2) + 4 * (r / 8) + r % 4,
+ * and its value at element d * 32 + r (transposed).  So the keys of a block
+ * are head_dim / 32 tiles of 32 rows x 32 dimensions, each half-tile of 16
+ * rows one contiguous 1 KB run at bf16 (the operand of one 16 x 16 x 32 MFMA
+ * of the decode kernel), and the values 64 contiguous bytes per dimension.
+ * The appends, re-threshold and attention calls all use this order; a
+ * caller that reads the buffers itself has to undo it.
  * Optional:
  *   u_pages    [n_pages, page_size] f32 or NULL: the utility u of each entry,
  *              stored by the appends when set (spkv_compact_append needs its

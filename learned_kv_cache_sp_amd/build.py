@@ -44,14 +44,9 @@ def hipcc() -> str:
     return p
 
 
-# Known frames that hold no spilled data: the fused decode step (at head_dim
-# 64 or 128, depending on how the backend lays the kernel out) reserves a
-# 36-byte frame for two 2-entry index arrays of its partial merge that not a
-# single instruction of the kernel uses (checked in its ISA: no scratch loads
-# or stores); rewriting them as selects costs the kernel ~1 us.  Exact
-# (kernel, size) pairs: any other size fails the build again.
-SCRATCH_ALLOWED = {("_ZN4spkv12_GLOBAL__N_118decode_bf16_kernelILi128ELi1EEEvNS_10DecodeArgsE", 36),
-                   ("_ZN4spkv12_GLOBAL__N_118decode_bf16_kernelILi64ELi1EEEvNS_10DecodeArgsE", 36)}
+# Kernels allowed a non-zero scratch size (exact (kernel, bytes per lane)
+# pairs, each checked in its ISA to hold no spilled data).  None at present.
+SCRATCH_ALLOWED: set = set()
 
 
 def scratch_kernels(remarks: str) -> list:

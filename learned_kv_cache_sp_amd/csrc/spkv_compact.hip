@@ -168,7 +168,7 @@ __device__ void copy_rows(const CompactArgs &a, int g, int n, const int *src_row
             if (idx < np) {
                 const int kk = idx / cpr;
                 const int ch = idx - kk * cpr;
-                *(piece_t *)(kdst(kk) + ch * 16) = kv[u];
+                *(piece_t *)kdst(kk, ch * EPC) = kv[u];
                 const int vc = idx / n;
                 const int vk = idx - vc * n;
 #pragma unroll
@@ -214,15 +214,15 @@ __device__ void scatter_tile(const CompactArgs &a, int b, int g, int r0, int row
         c.pos_pages[slot] = pos_base + (lds_rows[kk] - r0);
         if (store_u) c.u_pages[slot] = a.utility[(int64_t)lds_rows[kk] * c.n_kv + g];
     }
-    auto kdst = [&](int kk) -> char * {
+    auto kdst = [&](int kk, int d) -> char * {
         const int j = dst0 + kk;
         const int page = lds_pages[(j >> c.page_shift) - pg0];
-        return c.k_pages + (((int64_t)page * P + (j & (P - 1))) * hd) * ES;
+        return c.k_pages + ((int64_t)page * P * hd + kv_k_index(j & (P - 1), d, hd)) * ES;
     };
     auto vdst = [&](int kk, int e) -> T * {
         const int j = dst0 + kk;
         const int page = lds_pages[(j >> c.page_shift) - pg0];
-        return (T *)c.v_pages + ((int64_t)page * hd + e) * P + (j & (P - 1));
+        return (T *)c.v_pages + (int64_t)page * P * hd + kv_v_index(j & (P - 1), e, hd);
     };
     copy_rows<T>(a, g, n, lds_rows, kdst, vdst);
 }
@@ -242,13 +242,13 @@ __device__ void window_rows(const CompactArgs &a, int b, int g, int r0, int row_
         for (int kk = threadIdx.x; kk < n; kk += NT) lds_rows[kk] = r0 + lo + kk;
         __syncthreads();
         const int first_pos = pos_base + lo;
-        auto kdst = [&](int kk) -> char * {
+        auto kdst = [&](int kk, int d) -> char * {
             const int slot = (first_pos + kk) % w;
-            return c.ring_k + ((bg * w + slot) * hd) * ES;
+            return c.ring_k + (bg * w * hd + kv_k_index(slot, d, hd)) * ES;
         };
         auto vdst = [&](int kk, int e) -> T * {
             const int slot = (first_pos + kk) % w;
-            return (T *)c.ring_v + (bg * hd + e) * w + slot;
+            return (T *)c.ring_v + bg * w * hd + kv_v_index(slot, e, hd);
         };
         copy_rows<T>(a, g, n, lds_rows, kdst, vdst);  // ends with a barrier
     }
@@ -336,10 +336,10 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
         const int w = c.window;
         const int slot = pos % w;
         if (lane < cpr) {
-            *(piece_t *)(c.ring_k + ((bg * w + slot) * hd) * ES + lane * 16) = kv;
-            T *rv = (T *)c.ring_v + (bg * hd + lane * EPC) * w + slot;
+            *(piece_t *)(c.ring_k + (bg * w * hd + kv_k_index(slot, lane * EPC, hd)) * ES) = kv;
+            T *rv = (T *)c.ring_v + bg * w * hd + kv_v_index(slot, lane * EPC, hd);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) rv[(int64_t)e * w] = piece_elem<T>(vv, e);
+            for (int e = 0; e < EPC; ++e) rv[32 * e] = piece_elem<T>(vv, e);
         }
     }
     if (!kept) return;
@@ -366,10 +366,10 @@ __global__ void __launch_bounds__(64) compact_row_kernel(CompactArgs a) {
     }
     const int j = old_len & (P - 1);
     if (lane < cpr) {
-        *(piece_t *)(c.k_pages + (((int64_t)page * P + j) * hd) * ES + lane * 16) = kv;
-        T *dv = (T *)c.v_pages + ((int64_t)page * hd + lane * EPC) * P + j;
+        *(piece_t *)(c.k_pages + ((int64_t)page * P * hd + kv_k_index(j, lane * EPC, hd)) * ES) = kv;
+        T *dv = (T *)c.v_pages + (int64_t)page * P * hd + kv_v_index(j, lane * EPC, hd);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) dv[(int64_t)e * P] = piece_elem<T>(vv, e);
+        for (int e = 0; e < EPC; ++e) dv[32 * e] = piece_elem<T>(vv, e);
     }
     if (lane == 0) {
         c.pos_pages[(int64_t)page * P + j] = pos;
@@ -568,14 +568,14 @@ __device__ __attribute__((always_inline)) inline void store_batch(const CacheVie
             const int kk = idx / cpr, ch = idx - kk * cpr;
             const int jk = e0 + kk;
             const int pk = lds_pages[(jk >> c.page_shift) - pg0];
-            if (pk >= 0) *(piece_t *)(c.k_pages + (((int64_t)pk * P + (jk & (P - 1))) * hd) * ES + ch * 16) = kv[u];
+            if (pk >= 0) *(piece_t *)(c.k_pages + ((int64_t)pk * P * hd + kv_k_index(jk & (P - 1), ch * EPC, hd)) * ES) = kv[u];
             const int vc = idx / nrow, vk = idx - vc * nrow;
             const int jv = e0 + vk;
             const int pv = lds_pages[(jv >> c.page_shift) - pg0];
             if (pv >= 0) {
-                T *dv = (T *)c.v_pages + ((int64_t)pv * hd + vc * EPC) * P + (jv & (P - 1));
+                T *dv = (T *)c.v_pages + (int64_t)pv * P * hd + kv_v_index(jv & (P - 1), vc * EPC, hd);
 #pragma unroll
-                for (int i = 0; i < EPC; ++i) dv[(int64_t)i * P] = piece_elem<T>(vv[u], i);
+                for (int i = 0; i < EPC; ++i) dv[32 * i] = piece_elem<T>(vv[u], i);
             }
         }
     }
@@ -835,7 +835,7 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
             const int e = half * hh + r;
             const int ent = e0 + (idx - r * ncol) * EPC;
             const int page = lds_spages[(ent >> s.page_shift) - sp0];
-            x[q] = *(const piece_t *)((const T *)s.v_pages + ((int64_t)page * hd + e) * P + (ent & (P - 1)));
+            x[q] = *(const piece_t *)((const T *)s.v_pages + kv_v_index(page * P + (ent & (P - 1)), e, hd));
         }
     }
     const bool flag = mine && u >= a.tau;  // NaN fails
@@ -885,7 +885,7 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
                 if (idx < npk) {
                     const int kk = idx / cpr;
                     const int ch = idx - kk * cpr;
-                    kv[q] = *(const piece_t *)(s.k_pages + ((int64_t)lds_src[kk] * hd + k0) * ES + ch * 16);
+                    kv[q] = *(const piece_t *)(s.k_pages + kv_k_index(lds_src[kk], k0 + ch * EPC, hd) * ES);
                 }
             }
 #pragma unroll
@@ -894,7 +894,7 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
                 if (idx < npk) {
                     const int kk = idx / cpr;
                     const int ch = idx - kk * cpr;
-                    *(piece_t *)(d.k_pages + (dslot(kk) * hd + k0) * ES + ch * 16) = kv[q];
+                    *(piece_t *)(d.k_pages + kv_k_index(dslot(kk), k0 + ch * EPC, hd) * ES) = kv[q];
                 }
             }
         }
@@ -909,7 +909,7 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
         const int e = half * hh + r;
         const int c = c_lo + (idx - r * nch);
         const int first = c * EPC;                       // list entry of the piece's element 0
-        const int64_t row = ((int64_t)lds_pages[(first >> d.page_shift) - pg0] * hd + e) * P + (first & (P - 1));
+        const int64_t row = kv_v_index(lds_pages[(first >> d.page_shift) - pg0] * P + (first & (P - 1)), e, hd);
         T *dv = (T *)d.v_pages + row;
         if (first >= dst0 && first + EPC <= dst0 + n) {
             piece_t y;

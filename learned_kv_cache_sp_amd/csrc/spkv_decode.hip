@@ -141,44 +141,36 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t 
 }
 
 // Loads of one 32-key step into registers, as buffer loads with one 32-bit
-// lane offset per operand (constant parts go to the instruction offset or a
-// scalar offset), so that two steps in flight fit the register budget.
-//   K operand (two 16-key tiles t): lane (i = lane % 16, q = lane / 16)
-//     reads key 8*(i/4) + 4t + i%4, elements 32*cc + 8*q .. +8 for MFMA
-//     step cc -- a 64-byte run of each key row per instruction
-//   V^T operand (hd/16 tiles nt): lane reads V^T row 16*nt + i, keys
-//     8*q .. 8*q+7 of the step (16 bytes)
-template <int HD>
-struct StepLanes {
-    int k_off[2];  // byte offsets in the key block
-    int v_off;     // byte offset in the V^T block (row i, key 8q)
-};
+// lane offset (the constant parts go to the scalar offset).  A step is one
+// 32-slot block of the cache (see the storage order in spkv_internal.h):
+//   K operand (two 16-key tiles t, MFMA step cc): lane (i = lane % 16,
+//     q = lane / 16) reads row 16t + i of the block's dims 32cc .. 32cc+31,
+//     elements 8q .. 8q+7 -- the 64 lanes read one contiguous 1 KB run
+//   V^T operand (hd/16 tiles nt): lane reads dimension 16nt + i, slots
+//     8q .. 8q+7 -- again one 1 KB run
+// Every byte of a step is read by exactly one load, with the non-temporal
+// hint: the blocks are streamed once per launch.
+constexpr int CPOL_NT = 2;
 
-template <int HD>
-__device__ inline StepLanes<HD> step_lanes(int vstride) {
+__device__ inline int step_lane_offset() {
     const int lane = threadIdx.x & 63;
-    const int i = lane & 15;
-    const int q4 = lane >> 4;
-    StepLanes<HD> o;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) o.k_off[t] = ((8 * (i >> 2) + 4 * t + (i & 3)) * HD + 8 * q4) * 2;
-    o.v_off = (i * vstride + 8 * q4) * 2;
-    return o;
+    return (lane & 15) * 64 + (lane >> 4) * 16;
 }
 
 template <int HD, int CPOL = 0>
-__device__ inline void load_step(const __bf16 *kblk, const __bf16 *vblk, int vstride, const StepLanes<HD> &ln,
+__device__ inline void load_step(const __bf16 *kblk, const __bf16 *vblk, int lo,
                                  bf16x8 (&kr)[2][HD / 32], bf16x8 (&vr)[HD / 16]) {
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kblk, KSTEP * HD * 2);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vblk, (uint32_t)(HD * vstride * 2));
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vblk, KSTEP * HD * 2);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int cc = 0; cc < HD / 32; ++cc)
-            kr[t][cc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k_off[t] + 64 * cc, 0, CPOL));
+            kr[t][cc] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lo, 1024 * t + 2048 * cc, CPOL | CPOL_NT));
 #pragma unroll
     for (int nt = 0; nt < HD / 16; ++nt)
-        vr[nt] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.v_off, nt * 16 * vstride * 2, CPOL));
+        vr[nt] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lo, 1024 * nt, CPOL | CPOL_NT));
 }
 
 // valid: bit e set when key 8*(lane/16)+e of the step is visible (used only
@@ -316,9 +308,9 @@ __device__ void append_new_rows(const DecodeArgs &a, const uint8_t *keep, const 
                     const __bf16 *vn = (const __bf16 *)a.v_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
                     const int j = old & (P - 1);
                     if (sub < HD / 8)
-                        *(bf16x8 *)((__bf16 *)c.k_pages + ((int64_t)page * P + j) * HD + 8 * sub) =
+                        *(bf16x8 *)((__bf16 *)c.k_pages + kv_k_index((int64_t)page * P + j, 8 * sub, HD)) =
                             *(const bf16x8 *)(kn + 8 * sub);
-                    for (int e = sub; e < HD; e += TPP) ((__bf16 *)c.v_pages)[((int64_t)page * HD + e) * P + j] = vn[e];
+                    for (int e = sub; e < HD; e += TPP) ((__bf16 *)c.v_pages)[kv_v_index((int64_t)page * P + j, e, HD)] = vn[e];
                     if (sub == 0) {
                         c.pos_pages[(int64_t)page * P + j] = tb;
                         if (c.u_pages) c.u_pages[(int64_t)page * P + j] = u[bg];
@@ -489,8 +481,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int q4 = lane >> 4;
     const float sl2 = a.scale * LOG2E;
     const int rec = rec_floats(G, HD);
-    const StepLanes<HD> lanes_ring = step_lanes<HD>(w);
-    const StepLanes<HD> lanes_page = step_lanes<HD>(P);
+    const int step_lo = step_lane_offset();
     // this wave's steps: W0 + wave + NW * k (the 4 waves of the workgroup
     // walk neighbouring steps, i.e. neighbouring memory)
     const int nk = max(0, (W1 - W0 - wave + NW - 1) / NW);
@@ -576,22 +567,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const int ls = W0 + wave + NW * k - uniform(lds_F[bg]);
         if (page < 0) {
             const __bf16 *kb = (const __bf16 *)c.ring_k + ((int64_t)bg * w + ls * KSTEP) * HD;
-            const __bf16 *vb = (const __bf16 *)c.ring_v + (int64_t)bg * HD * w + ls * KSTEP;
+            const __bf16 *vb = (const __bf16 *)c.ring_v + ((int64_t)bg * w + ls * KSTEP) * HD;
             if constexpr (RING) {
                 const int tb = uniform(lds_t[bg / c.n_kv]);
                 if (tb >= 0 && ls == (tb % w) / KSTEP) {
                     // the step holding the new token (this wave wrote it into
                     // the ring before its first loads): read past the L1 cache
-                    load_step<HD, 1>(kb, vb, w, lanes_ring, kr, vr);
+                    load_step<HD, 1>(kb, vb, step_lo, kr, vr);
                     return;
                 }
             }
-            load_step<HD>(kb, vb, w, lanes_ring, kr, vr);
+            load_step<HD>(kb, vb, step_lo, kr, vr);
         } else {
             const int slot0 = ((ls - nws) * KSTEP) & (P - 1);
             const __bf16 *kb = (const __bf16 *)c.k_pages + ((int64_t)page * P + slot0) * HD;
-            const __bf16 *vb = (const __bf16 *)c.v_pages + (int64_t)page * HD * P + slot0;
-            load_step<HD>(kb, vb, P, lanes_page, kr, vr);
+            const __bf16 *vb = (const __bf16 *)c.v_pages + ((int64_t)page * P + slot0) * HD;
+            load_step<HD>(kb, vb, step_lo, kr, vr);
         }
     };
     auto compute = [&](int k, bf16x8 (&kr)[2][HD / 32], bf16x8 (&vr)[HD / 16]) {
@@ -784,9 +775,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             const __bf16 *kn = (const __bf16 *)a.k_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
             const __bf16 *vn = (const __bf16 *)a.v_new + (int64_t)b * a.ld_new + (int64_t)g * HD;
             if (lane < HD / 8)
-                *(bf16x8 *)((__bf16 *)c.ring_k + ((int64_t)bg * w + slot) * HD + 8 * lane) =
+                *(bf16x8 *)((__bf16 *)c.ring_k + kv_k_index((int64_t)bg * w + slot, 8 * lane, HD)) =
                     *(const bf16x8 *)(kn + 8 * lane);
-            for (int e = lane; e < HD; e += 64) ((__bf16 *)c.ring_v)[((int64_t)bg * HD + e) * w + slot] = vn[e];
+            for (int e = lane; e < HD; e += 64) ((__bf16 *)c.ring_v)[kv_v_index((int64_t)bg * w + slot, e, HD)] = vn[e];
         }
     }
     reset(bg_first);
@@ -889,23 +880,24 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
     }
     float m = -INFINITY, l = 0.f;
     const int t = a.t[b];
-    auto visit = [&](const float *k, const float *v, int vstride) {
+    // key and value of slot j of a page or ring region (block storage order)
+    auto visit = [&](const float *kreg, const float *vreg, int j) {
         float s = 0.f;
-        for (int i = 0; i < PER; ++i) s += q[i] * k[lane + 64 * i];
+        for (int i = 0; i < PER; ++i) s += q[i] * kreg[kv_k_index(j, lane + 64 * i, HD)];
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
         s *= a.scale;
         const float m_new = fmaxf(m, s);
         const float alpha = expf(m - m_new);
         const float p = expf(s - m_new);
         l = l * alpha + p;
-        for (int i = 0; i < PER; ++i) o[i] = o[i] * alpha + p * v[(int64_t)(lane + 64 * i) * vstride];
+        for (int i = 0; i < PER; ++i) o[i] = o[i] * alpha + p * vreg[kv_v_index(j, lane + 64 * i, HD)];
         m = m_new;
     };
     const int w = c.window;
     const float *rk = (const float *)c.ring_k + (int64_t)bg * w * HD;
     const float *rv = (const float *)c.ring_v + (int64_t)bg * HD * w;
     for (int slot = 0; slot < w; ++slot)
-        if (slot <= t) visit(rk + slot * HD, rv + slot, w);
+        if (slot <= t) visit(rk, rv, slot);
     const int len = c.lengths[bg];
     const int P = c.page_size;
     const int32_t *pt = c.page_table + (int64_t)bg * c.max_pages;
@@ -913,8 +905,7 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeArgs a) {
         const int page = pt[j >> c.page_shift];
         const int slot = j & (P - 1);
         if (c.pos_pages[(int64_t)page * P + slot] > t - w) break;  // positions increase
-        visit((const float *)c.k_pages + ((int64_t)page * P + slot) * HD,
-              (const float *)c.v_pages + (int64_t)page * HD * P + slot, P);
+        visit((const float *)c.k_pages + (int64_t)page * P * HD, (const float *)c.v_pages + (int64_t)page * P * HD, slot);
     }
     float *op = a.out + ((int64_t)b * a.n_q + h) * HD;
     for (int i = 0; i < PER; ++i) op[lane + 64 * i] = l > 0.f ? o[i] / l : 0.f;

@@ -53,6 +53,31 @@ inline CacheView make_view(const spkv_cache *c) {
 
 inline int elem_bytes(int dtype) { return dtype == SPKV_BF16 ? 2 : 4; }
 
+// ---- storage order of the key and value entries ------------------------------
+// A page of P slots (and the ring of one (b, g), w slots) is stored as blocks
+// of 32 consecutive slots, each block 32 x head_dim keys followed by nothing
+// else (the values live in their own pages, in blocks at the same offsets).
+// Within a block:
+//   keys   [head_dim / 32][32 rows][32 dims], row p holding slot
+//          kv_slot_of_row(p): rows 16t .. 16t+15 are the A operand of the
+//          t-th 16 x 16 x 32 MFMA tile of the decode step, so that each
+//          16-byte lane load of the tile's operand falls in one contiguous
+//          1 KB run (whole 128-byte lines, read once);
+//   values [head_dim][32 slots] (transposed), 64 bytes per dimension at bf16:
+//          the 16 dimensions of one V^T operand tile are again one 1 KB run.
+// Indices are in elements, relative to the page (page * P * head_dim) or the
+// ring of (b, g) ((b * n_kv + g) * w * head_dim).
+__host__ __device__ inline int kv_row_of_slot(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+__host__ __device__ inline int kv_slot_of_row(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
+__host__ __device__ inline int64_t kv_k_index(int64_t j, int d, int hd) {
+    return (j >> 5) * 32 * hd + (int64_t)((((d >> 5) << 5) + kv_row_of_slot((int)(j & 31))) * 32 + (d & 31));
+}
+__host__ __device__ inline int64_t kv_v_index(int64_t j, int d, int hd) {
+    return (j >> 5) * 32 * hd + (int64_t)d * 32 + (int)(j & 31);
+}
+// A slot index may also count from the start of the pool (page * P + j) or
+// of the ring (bg * w + slot): P and w are multiples of 32.
+
 // ---- streaming-read ceiling ---------------------------------------------------
 hipError_t launch_hbm_read(const void *src, size_t bytes, bool nontemporal, bool runs, uint32_t *sink, int grid,
                            hipStream_t s);

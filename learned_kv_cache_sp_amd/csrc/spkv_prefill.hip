@@ -56,10 +56,14 @@ __global__ void __launch_bounds__(64) prefill_valu_kernel(PrefillArgs a) {
         o[e] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    auto visit = [&](const T *k, const T *v, int64_t vstride) {
+    // j < 0: k, v point at a row of the chunk; else k, v are a page or ring
+    // region and j the slot (block storage order)
+    auto kat = [&](const T *k, int j, int d) -> float { return (float)(j < 0 ? k[d] : k[kv_k_index(j, d, HD)]); };
+    auto vat = [&](const T *v, int j, int d) -> float { return (float)(j < 0 ? v[d] : v[kv_v_index(j, d, HD)]); };
+    auto visit = [&](const T *k, const T *v, int j) {
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) s = fmaf(q[e], (float)k[lane + 64 * e], s);
+        for (int e = 0; e < PER; ++e) s = fmaf(q[e], kat(k, j, lane + 64 * e), s);
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
         s *= a.scale;
         const float m_new = fmaxf(m, s);
@@ -67,7 +71,7 @@ __global__ void __launch_bounds__(64) prefill_valu_kernel(PrefillArgs a) {
         const float p = expf(s - m_new);
         l = l * alpha + p;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = o[e] * alpha + p * (float)v[(int64_t)(lane + 64 * e) * vstride];
+        for (int e = 0; e < PER; ++e) o[e] = o[e] * alpha + p * vat(v, j, lane + 64 * e);
         m = m_new;
     };
     // window band
@@ -75,11 +79,9 @@ __global__ void __launch_bounds__(64) prefill_valu_kernel(PrefillArgs a) {
     for (int s = s_lo; s <= t; ++s) {
         if (s >= a.pos0) {
             const int64_t r = (int64_t)(s - a.pos0) * a.ld_kv + (int64_t)g * HD;
-            visit((const T *)a.k + r, (const T *)a.v + r, 1);
+            visit((const T *)a.k + r, (const T *)a.v + r, -1);
         } else {
-            const int slot = s % w;
-            visit((const T *)c.ring_k + ((int64_t)bg * w + slot) * HD,
-                  (const T *)c.ring_v + (int64_t)bg * HD * w + slot, w);
+            visit((const T *)c.ring_k + (int64_t)bg * w * HD, (const T *)c.ring_v + (int64_t)bg * w * HD, s % w);
         }
     }
     // kept entries older than the window
@@ -90,8 +92,7 @@ __global__ void __launch_bounds__(64) prefill_valu_kernel(PrefillArgs a) {
         const int page = pt[j >> c.page_shift];
         const int slot = j & (P - 1);
         if (c.pos_pages[(int64_t)page * P + slot] > t - w) break;  // positions increase
-        visit((const T *)c.k_pages + ((int64_t)page * P + slot) * HD,
-              (const T *)c.v_pages + (int64_t)page * HD * P + slot, P);
+        visit((const T *)c.k_pages + (int64_t)page * P * HD, (const T *)c.v_pages + (int64_t)page * P * HD, slot);
     }
     float *op = a.out + ((int64_t)i * a.n_q + h) * HD;
 #pragma unroll
@@ -296,13 +297,13 @@ prefill_bf16_kernel(PrefillArgs a) {
     for (int u = 0; u < KI / PF_NW; ++u) {
         const int i = wave + PF_NW * u;
         const int r = i * KRPI + lane / CPR;
-        dk_off[u] = (r * HD + 8 * ((lane % CPR) ^ swz_k<HD>(r))) * 2;
+        dk_off[u] = (int)kv_k_index(r, 8 * ((lane % CPR) ^ swz_k<HD>(r)), HD) * 2;
     }
 #pragma unroll
     for (int u = 0; u < VI / PF_NW; ++u) {
         const int i = wave + PF_NW * u;
         const int e = i * 8 + (lane >> 3);
-        dv_off[u] = (e * P + 8 * ((lane & 7) ^ swz_v(e))) * 2;
+        dv_off[u] = (int)kv_v_index(8 * ((lane & 7) ^ swz_v(e)), e, HD) * 2;
     }
     auto issue_direct = [&](int j, char *kbuf, char *vbuf, int *pbuf, float *ubuf) {
         const int e0 = j * PF_KB;
@@ -312,7 +313,7 @@ prefill_bf16_kernel(PrefillArgs a) {
             const __amdgpu_buffer_rsrc_t rk =
                 pf_rsrc(c.k_pages + ((int64_t)page * P + slot0) * HD * 2, PF_KB * HD * 2);
             const __amdgpu_buffer_rsrc_t rv =
-                pf_rsrc(c.v_pages + ((int64_t)page * HD * P + slot0) * 2, (HD * P - slot0) * 2);
+                pf_rsrc(c.v_pages + ((int64_t)page * P + slot0) * HD * 2, PF_KB * HD * 2);
             const __amdgpu_buffer_rsrc_t rp = pf_rsrc(c.pos_pages + (int64_t)page * P + slot0, PF_KB * 4);
 #pragma unroll
             for (int u = 0; u < KI / PF_NW; ++u)
@@ -333,7 +334,7 @@ prefill_bf16_kernel(PrefillArgs a) {
             const int r = i * KRPI + lane / CPR;
             const int cch = (lane % CPR) ^ swz_k<HD>(r);
             const int ent = e0 + r;
-            const char *src = c.k_pages + (((int64_t)page_of(ent) * P + (ent & (P - 1))) * HD + 8 * cch) * 2;
+            const char *src = c.k_pages + ((int64_t)page_of(ent) * P * HD + kv_k_index(ent & (P - 1), 8 * cch, HD)) * 2;
             __builtin_amdgcn_global_load_lds(src, (lds_void *)(kbuf + i * 1024), 16, 0, 0);
         }
 #pragma unroll
@@ -342,7 +343,7 @@ prefill_bf16_kernel(PrefillArgs a) {
             const int e = i * 8 + (lane >> 3);
             const int cch = (lane & 7) ^ swz_v(e);
             const int ent = e0 + 8 * cch;
-            const char *src = c.v_pages + (((int64_t)page_of(ent) * HD + e) * P + (ent & (P - 1))) * 2;
+            const char *src = c.v_pages + ((int64_t)page_of(ent) * P * HD + kv_v_index(ent & (P - 1), e, HD)) * 2;
             __builtin_amdgcn_global_load_lds(src, (lds_void *)(vbuf + i * 1024), 16, 0, 0);
         }
         {
@@ -380,8 +381,8 @@ prefill_bf16_kernel(PrefillArgs a) {
                 const int id = tid + u * PF_NT;
                 const int kk = id / CPR, ch = id % CPR;
                 const int ent = j0 + kk;
-                kst[u] = kk < n_ok ? *(const i32x4 *)((const __bf16 *)c.k_pages +
-                                                      ((int64_t)pt[ent >> c.page_shift] * P + (ent & (P - 1))) * HD + 8 * ch)
+                kst[u] = kk < n_ok ? *(const i32x4 *)((const __bf16 *)c.k_pages + (int64_t)pt[ent >> c.page_shift] * P * HD +
+                                                      kv_k_index(ent & (P - 1), 8 * ch, HD))
                                    : i32x4{0, 0, 0, 0};
             }
 #pragma unroll
@@ -391,8 +392,8 @@ prefill_bf16_kernel(PrefillArgs a) {
                 const int ent = j0 + 8 * kc;
                 i32x4 v = i32x4{0, 0, 0, 0};
                 if (8 * kc < n_ok) {
-                    v = *(const i32x4 *)((const __bf16 *)c.v_pages + ((int64_t)pt[ent >> c.page_shift] * HD + e) * P +
-                                         (ent & (P - 1)));
+                    v = *(const i32x4 *)((const __bf16 *)c.v_pages + (int64_t)pt[ent >> c.page_shift] * P * HD +
+                                         kv_v_index(ent & (P - 1), e, HD));
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int k0 = 8 * kc + 2 * q;
@@ -420,7 +421,7 @@ prefill_bf16_kernel(PrefillArgs a) {
                     if (s >= a.pos0)
                         kv = *(const i32x4 *)((const __bf16 *)a.k + (int64_t)(s - a.pos0) * a.ld_kv + (int64_t)g * HD + 8 * ch);
                     else
-                        kv = *(const i32x4 *)((const __bf16 *)c.ring_k + ((int64_t)bg * w + (s % w)) * HD + 8 * ch);
+                        kv = *(const i32x4 *)((const __bf16 *)c.ring_k + kv_k_index((int64_t)bg * w + (s % w), 8 * ch, HD));
                 }
                 kst[u] = kv;
             }
@@ -436,10 +437,10 @@ prefill_bf16_kernel(PrefillArgs a) {
                     if (s >= a.pos0) {
                         vv = *(const i32x4 *)((const __bf16 *)a.v + (int64_t)(s - a.pos0) * a.ld_kv + (int64_t)g * HD + 8 * dc);
                     } else {
-                        const __bf16 *rv = (const __bf16 *)c.ring_v + (int64_t)bg * HD * w + (s % w);
+                        const __bf16 *rv = (const __bf16 *)c.ring_v + kv_v_index((int64_t)bg * w + (s % w), 8 * dc, HD);
                         __bf16 tmp[8];
 #pragma unroll
-                        for (int e2 = 0; e2 < 8; ++e2) tmp[e2] = rv[(int64_t)(8 * dc + e2) * w];
+                        for (int e2 = 0; e2 < 8; ++e2) tmp[e2] = rv[32 * e2];
                         vv = __builtin_bit_cast(i32x4, *(bf16x8 *)tmp);
                     }
                 }

@@ -86,6 +86,31 @@ EXPORTS = [
     "spkv_last_error", "spkv_version", "spkv_hbm_read", "spkv_gate_sink", "spkv_set_wait_limit",
 ]
 
+# ---- storage order of cached keys and values ---------------------------------
+# Pages (and the ring of each (b, g)) hold blocks of 32 slots.  A key block is
+# [head_dim / 32][32 rows][32 dims] with row p holding slot _SLOT_OF_ROW[p]
+# (the rows of the decode kernel's two 16 x 16 x 32 MFMA operand tiles), a
+# value block is [head_dim][32 slots].  The tensors keep their declared
+# shapes; these helpers give the logical [slots, head_dim] views.
+_SLOT_OF_ROW = [8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3) for p in range(32)]
+_ROW_OF_SLOT = [_SLOT_OF_ROW.index(r) for r in range(32)]
+
+
+def unblock_keys(x: torch.Tensor) -> torch.Tensor:
+    """Stored key slots [n, hd] (n a multiple of 32, any contiguous storage of
+    that many elements) -> logical keys [n, hd]."""
+    n, hd = x.numel() // x.shape[-1], x.shape[-1]
+    blk = x.reshape(n // 32, hd // 32, 32, 32).permute(0, 2, 1, 3)        # [blk][row][cc][dd]
+    idx = torch.tensor(_ROW_OF_SLOT, device=x.device)
+    return blk.index_select(1, idx).reshape(n, hd)
+
+
+def unblock_values(x: torch.Tensor) -> torch.Tensor:
+    """Stored value slots (n * hd elements, n a multiple of 32) -> logical values [n, hd]."""
+    n, hd = x.numel() // x.shape[-1], x.shape[-1]
+    return x.reshape(n // 32, hd, 32).permute(0, 2, 1).reshape(n, hd)
+
+
 _lib = None
 
 
@@ -339,8 +364,8 @@ class Cache:
         P = self.page_size
         npg = (n + P - 1) // P
         pages = self.page_table[b, g, :npg].long()
-        k = self.k_pages[pages].reshape(npg * P, self.head_dim)[:n]
-        v = self.v_pages[pages].transpose(1, 2).reshape(npg * P, self.head_dim)[:n]
+        k = unblock_keys(self.k_pages[pages].reshape(npg * P, self.head_dim))[:n]
+        v = unblock_values(self.v_pages[pages].reshape(npg * P, self.head_dim))[:n]
         pos = self.pos_pages[pages].reshape(npg * P)[:n]
         return k, v, pos
 
@@ -361,7 +386,7 @@ class Cache:
 
     def read_ring(self, b: int, g: int):
         """Ring of (b, g): K [w, hd], V [w, hd] indexed by slot = position % w."""
-        return self.ring_k[b, g], self.ring_v[b, g].transpose(0, 1)
+        return unblock_keys(self.ring_k[b, g]), unblock_values(self.ring_v[b, g].reshape(self.window, self.head_dim))
 
     def snapshot(self) -> dict:
         names = ("k_pages", "v_pages", "pos_pages", "page_table", "lengths", "pool_next", "status",
