@@ -53,9 +53,9 @@ constexpr int MAX_BG = 2048;
 constexpr int ROUND = 256;             // steps staged per wave at a time
 // extra (virtual) steps charged to every (b, g) when the shares are cut:
 // starting a (b, g) inside a share costs its workgroup a hand-over or an
-// output write, about 8 steps of streaming time (8 measured best of 0, 4, 8,
-// 12 on the 32K-, 131K-context and ragged batch-32 decode workloads)
-constexpr int BG_COST = 8;
+// output write, about 12 steps of streaming time (12 measured best of 4, 8,
+// 12, 16 on the 32K-, 131K-context and ragged batch-32 decode workloads)
+constexpr int BG_COST = 12;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
