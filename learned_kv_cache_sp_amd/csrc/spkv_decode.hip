@@ -489,17 +489,30 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int bg_last = uniform(find_owner(lds_F, BG, W1 - 1));
 
     WaveState<HD> st;
-    auto reset = [&](int bg) {
+    // The query operand of (b, g): every lane loads (lanes of heads >= G
+    // read head 0's row and store zeros), so the HD/32 loads go out together
+    // and are waited for once -- a load per condition would cost a memory
+    // round trip each.
+    auto q_load = [&](int bg, bf16x8 (&qv)[HD / 32]) {
         const int b = bg / c.n_kv;
         const int g = bg - b * c.n_kv;
-        const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.ld_q + (int64_t)(g * G + head) * HD + 8 * q4;
+        const int hq = head < G ? head : 0;
+        const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.ld_q + (int64_t)(g * G + hq) * HD + 8 * q4;
 #pragma unroll
-        for (int cc = 0; cc < HD / 32; ++cc)
-            lds_q[wave][cc][lane] = head < G ? *(const bf16x8 *)(qp + 32 * cc) : bf16x8{};
+        for (int cc = 0; cc < HD / 32; ++cc) qv[cc] = *(const bf16x8 *)(qp + 32 * cc);
+    };
+    auto q_store = [&](const bf16x8 (&qv)[HD / 32]) {
+#pragma unroll
+        for (int cc = 0; cc < HD / 32; ++cc) lds_q[wave][cc][lane] = head < G ? qv[cc] : bf16x8{};
 #pragma unroll
         for (int nt = 0; nt < HD / 16; ++nt) st.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.m = -INFINITY;
         st.l = 0.f;
+    };
+    auto reset = [&](int bg) {
+        bf16x8 qv[HD / 32];
+        q_load(bg, qv);
+        q_store(qv);
     };
 
     // ---- per-wave staging of (b, g), page and visible count of its steps ----
@@ -780,10 +793,16 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             for (int e = lane; e < HD; e += 64) ((__bf16 *)c.ring_v)[kv_v_index((int64_t)bg * w + slot, e, HD)] = vn[e];
         }
     }
-    reset(bg_first);
     int k = 0;  // next step of this wave to compute (its loads are in flight)
+    {
+        // the first (b, g)'s query goes out with the page-id loads of the
+        // first staging, whose wait covers both
+        bf16x8 qv[HD / 32];
+        q_load(bg_first, qv);
+        if (nk > 0) stage_pages(0);
+        q_store(qv);
+    }
     if (nk > 0) {
-        stage_pages(0);
         issue(0, kA, vA);
         stage_counts();
     }
