@@ -97,8 +97,8 @@ _ROW_OF_SLOT = [_SLOT_OF_ROW.index(r) for r in range(32)]
 
 
 def unblock_keys(x: torch.Tensor) -> torch.Tensor:
-    """Stored key slots [n, hd] (n a multiple of 32, any contiguous storage of
-    that many elements) -> logical keys [n, hd]."""
+    """Stored keys of n slots (n a multiple of 32), given as an [n, hd] view of
+    the stored elements -> logical keys [n, hd]."""
     n, hd = x.numel() // x.shape[-1], x.shape[-1]
     blk = x.reshape(n // 32, hd // 32, 32, 32).permute(0, 2, 1, 3)        # [blk][row][cc][dd]
     idx = torch.tensor(_ROW_OF_SLOT, device=x.device)
@@ -106,7 +106,8 @@ def unblock_keys(x: torch.Tensor) -> torch.Tensor:
 
 
 def unblock_values(x: torch.Tensor) -> torch.Tensor:
-    """Stored value slots (n * hd elements, n a multiple of 32) -> logical values [n, hd]."""
+    """Stored values of n slots (n a multiple of 32), given as an [n, hd] view
+    of the stored elements -> logical values [n, hd]."""
     n, hd = x.numel() // x.shape[-1], x.shape[-1]
     return x.reshape(n // 32, hd, 32).permute(0, 2, 1).reshape(n, hd)
 
