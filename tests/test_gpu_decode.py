@@ -97,6 +97,26 @@ def test_decode_group_sizes_and_head_dims(n_q, n_kv, hd):
     assert worst <= tl.TOL_REGRESS and worst_lse <= tl.TOL_REGRESS
 
 
+@pytest.mark.parametrize("window,hd,n_q", [(32, 128, 32), (96, 128, 32), (256, 128, 32), (96, 64, 16), (32, 64, 16)])
+@pytest.mark.parametrize("zero_keys", [False, True])
+def test_decode_windows(window, hd, n_q, zero_keys):
+    # rings of one, three and eight 32-slot blocks; contexts shorter than the
+    # window, within one step of it and far past it; K = 0 pins the visible
+    # set exactly (lse = log |visible|)
+    wl = dataclasses.replace(inputs.WORKLOADS["decode_32k"], window=window, head_dim=hd, n_q=n_q)
+    prefix = [window - 2, window + 1, 3 * window + 17, 1500]
+    worst, worst_lse = _decode_case(wl, prefix, 3, [0.0, 1.0, 0.05, 0.2, 0.3, 0.5, 0.7, 0.9], 37,
+                                    zero_keys=zero_keys, page=32 if hd == 64 else 64)
+    print(f"[decode w={window} hd={hd} zero_keys={zero_keys}] max|dout|={worst:.2e} max|dlse|={worst_lse:.2e}")
+    assert worst <= tl.TOL_REGRESS and worst_lse <= tl.TOL_REGRESS
+
+
+def test_decode_f32_window_96():
+    wl = dataclasses.replace(inputs.WORKLOADS["tiny"], window=96)
+    worst, wl_lse = _decode_case(wl, [94, 300], 4, [0.25, 0.6], 38)
+    assert worst <= tl.TOL_F32 and wl_lse <= tl.TOL_F32
+
+
 def test_decode_zero_keys_counts_visible_set():
     # K = 0 (exact in bf16): softmax is uniform over the visible set, so
     # lse = log |visible| pins key-set membership exactly

@@ -58,6 +58,21 @@ def test_prefill_bf16_8b_shape(T, chunk, rates):
     assert tl.max_abs(out, ro) <= tl.TOL_PREFILL and tl.max_abs(lse, rl) <= tl.TOL_REGRESS
 
 
+@pytest.mark.parametrize("window,hd,n_q,page", [(32, 128, 32, 64), (96, 128, 32, 32), (256, 64, 16, 128)])
+def test_prefill_bf16_windows(window, hd, n_q, page):
+    # the ring (s < pos0) and the chunk's own rows as window keys for rings of
+    # one, three and eight 32-slot blocks, chunks shorter and longer than w
+    import dataclasses
+    wl = dataclasses.replace(inputs.WORKLOADS["prefill_64k"], window=window, head_dim=hd, n_q=n_q)
+    T = 900
+    tok = inputs.tokens(wl, T, 55, 0)
+    z = inputs.bernoulli_mask(T, [0.5, 0.3, 0.9, 0.3, 0.1, 0.3, 0.7, 1.0], 55, 0)
+    out, lse, _ = prefill_chunks(wl, tok["Q"], tok["K"], tok["V"], z, 70 if window >= 96 else 300, page=page)
+    ro, rl = oracle.attention(tok["Q"], np.arange(T), tok["K"], tok["V"], z, wl.window, threads=tl.oracle_threads())
+    print(f"[prefill w={window} hd={hd}] max|dout|={tl.max_abs(out, ro):.2e} max|dlse|={tl.max_abs(lse, rl):.2e}")
+    assert tl.max_abs(out, ro) <= tl.TOL_PREFILL and tl.max_abs(lse, rl) <= tl.TOL_REGRESS
+
+
 @pytest.mark.parametrize("page", [32, 128, 256])
 def test_prefill_bf16_page_sizes(page):
     # pages smaller than a 64-key block take the per-lane address path of the

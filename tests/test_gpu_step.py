@@ -102,6 +102,9 @@ def _run(wl, ctxs, steps, tau, page, seed, shared_ws=False):
     ("decode_32k", dict(batch=16), [64 + 37 * i for i in range(16)], 6, None, 64),  # 16 sequences
     ("decode_32k", dict(batch=3, n_q=8, d_hidden=256), [400, 150, 260], 12, None, 64),  # G 1, d_hidden 256
     ("decode_32k", dict(batch=2, d_hidden=16), [300, 41], 12, None, 64),   # d_hidden 16
+    ("decode_32k", dict(batch=3, window=32), [300, 20, 1000], 40, None, 64),  # one ring block
+    ("decode_32k", dict(batch=2, window=96, head_dim=64, n_q=16), [500, 90], 30, None, 32),  # three
+    ("decode_32k", dict(batch=2, window=256), [600, 250], 20, None, 64),   # eight
 ])
 def test_decode_step_equals_separate_calls(name, over, ctxs, steps, tau, page):
     wl = tl.small_workload(name, **over)
@@ -205,11 +208,11 @@ def test_decode_step_capacity_overflow_matches_separate_calls():
             np.testing.assert_array_equal(pos.cpu().numpy(), np.arange(n))
 
 
-@pytest.mark.parametrize("B,hd,nq", [(32, 128, 32), (3, 64, 16)])
-def test_ring_only_step_equals_window_append_plus_attn(B, hd, nq):
+@pytest.mark.parametrize("B,hd,nq,w", [(32, 128, 32, 128), (3, 64, 16, 128), (4, 128, 32, 32), (3, 64, 16, 96)])
+def test_ring_only_step_equals_window_append_plus_attn(B, hd, nq, w):
     """spkv_decode_step without a gate: the ring write and the attention of
     the separate calls, bit for bit (same kernel plan), any batch size."""
-    wl = tl.small_workload("decode_32k", batch=B, head_dim=hd, n_q=nq)
+    wl = tl.small_workload("decode_32k", batch=B, head_dim=hd, n_q=nq, window=w)
     ctxs = [100 + 53 * b for b in range(B)]
     steps = 5
     dt = tl.torch_dtype(wl)
