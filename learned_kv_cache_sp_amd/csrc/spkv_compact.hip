@@ -835,7 +835,8 @@ __global__ void __launch_bounds__(NT) rethresh_scatter_kernel(RethreshArgs a) {
             const int e = half * hh + r;
             const int ent = e0 + (idx - r * ncol) * EPC;
             const int page = lds_spages[(ent >> s.page_shift) - sp0];
-            x[q] = *(const piece_t *)((const T *)s.v_pages + kv_v_index(page * P + (ent & (P - 1)), e, hd));
+            // every line of the tile's value columns is read once, here
+            x[q] = __builtin_nontemporal_load((const piece_t *)((const T *)s.v_pages + kv_v_index(page * P + (ent & (P - 1)), e, hd)));
         }
     }
     const bool flag = mine && u >= a.tau;  // NaN fails

@@ -310,12 +310,14 @@ __global__ void __launch_bounds__(NT) gate_unitsplit_kernel(GateArgs a) {
     // (swizzled like the hidden tile) into the MFMA operand layout
     const __bf16 *wsrc = (const __bf16 *)a.w1 + (int64_t)(16 * wave * NTW + (lane >> 3)) * a.d_model + 8 * (lane & 7);
 
+    // the hidden rows are read once (cache policy 2: non-temporal); W1 is
+    // read by every workgroup and stays cacheable
     auto issue_h = [&](int j, int st) {
         char *dst = stage_at<C::SBYTES, C::NSTAGE>(st);
 #pragma unroll
         for (int k = 0; k < C::LH; ++k)
             __builtin_amdgcn_global_load_lds((const void *)(hsrc[k] + 64 * j),
-                                             (lds_void *)(dst + (C::LH * wave + k) * 1024), 16, 0, 0);
+                                             (lds_void *)(dst + (C::LH * wave + k) * 1024), 16, 0, 2);
     };
     bf16x8 wv[D][NTW][2];  // [m / 2][m % 2]: instruction m = 2 nn + ks of the raw lines
     auto issue_w = [&](int j, bf16x8 (&dst)[NTW][2]) {
