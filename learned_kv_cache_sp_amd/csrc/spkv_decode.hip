@@ -666,21 +666,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             }
         }
     };
-    // Merge of the partials of up to two (b, g) (this workgroup arrived last
-    // for each), in slot order -- deterministic.  Per batch of MB slots, the
-    // maxima and sums go to LDS and each thread loads the float4 outputs it
-    // owns, all loads issued before any is used: a batch costs one trip to
-    // memory and one barrier.  Uses state slot 0 of LDS as scratch.
-    auto merge = [&](int nm, const int *bgs) {
-        constexpr int MB = 8;
-        constexpr int MAXC = (2 * 16 * HD / 4 + NT - 1) / NT;  // float4 chunks per thread
+    // Merge of the partials of one (b, g) (this workgroup arrived last), in
+    // slot order -- deterministic.  Per batch of MB slots, the maxima and
+    // sums go to LDS and each thread loads the float4 outputs it owns, all
+    // loads issued before any is used: a batch costs one trip to memory and
+    // one barrier (a (b, g) spread over many shares, as the long heads of a
+    // skewed cache are, takes ceil(parts / MB) batches).  Uses state slot 0
+    // of LDS as scratch.
+    auto merge = [&](int bg) {
+        constexpr int MB = 16;
+        constexpr int MAXC = (16 * HD / 4 + NT - 1) / NT;  // float4 chunks per thread
         const int GH = G * HD;
-        const int n4 = nm * GH / 4;
-        int p0[2] = {0, 0}, np[2] = {0, 0};
-        for (int m = 0; m < nm; ++m) parts_of(bgs[m], p0[m], np[m]);
-        const int np_max = max(np[0], np[1]);
-        float *cm = &lds_o[0][0][0][0];  // [2][MB][16] maxima
-        float *cl = cm + 2 * MB * 16;     // [2][MB][16] sums
+        const int n4 = GH / 4;
+        int p0, np;
+        parts_of(bg, p0, np);
+        float *cm = &lds_o[0][0][0][0];  // [MB][16] maxima
+        float *cl = cm + MB * 16;         // [MB][16] sums
         f32x4 Oa[MAXC];
         float Ma[MAXC], La[MAXC];
 #pragma unroll
@@ -689,32 +690,30 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             Ma[ch] = -INFINITY;
             La[ch] = 0.f;
         }
-        for (int c0 = 0; c0 < np_max; c0 += MB) {
+        for (int c0 = 0; c0 < np; c0 += MB) {
             if (c0 > 0) __syncthreads();  // the previous batch's maxima are consumed
             f32x4 ov[MAXC][MB];
 #pragma unroll
             for (int ch = 0; ch < MAXC; ++ch) {
                 if (ch * NT >= n4) break;  // uniform
                 const int f = ch * NT + threadIdx.x;
-                const int m = 4 * f >= GH ? 1 : 0;
-                const uint32_t off = (uint32_t)(((size_t)p0[m] * rec + (4 * f - m * GH)) * sizeof(float));
+                const uint32_t off = (uint32_t)(((size_t)p0 * rec + 4 * f) * sizeof(float));
 #pragma unroll
                 for (int kk = 0; kk < MB; ++kk)
-                    ov[ch][kk] = (f < n4 && c0 + kk < np[m])
+                    ov[ch][kk] = (f < n4 && c0 + kk < np)
                                      ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                     prs, off + (uint32_t)((c0 + kk) * rec * 4), 0, CPOL_SC1))
                                      : f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            if (threadIdx.x < 2 * MB * G) {
-                const int m = threadIdx.x / (MB * G);
-                const int kk = (threadIdx.x / G) % MB;
+            if (threadIdx.x < MB * G) {
+                const int kk = threadIdx.x / G;
                 const int h = threadIdx.x % G;
-                const bool ok = m < nm && c0 + kk < np[m];
-                const uint32_t off = (uint32_t)(((size_t)(p0[m] + c0 + kk) * rec + GH + h) * sizeof(float));
+                const bool ok = c0 + kk < np;
+                const uint32_t off = (uint32_t)(((size_t)(p0 + c0 + kk) * rec + GH + h) * sizeof(float));
                 const float mv = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, CPOL_SC1)) : -INFINITY;
                 const float lv = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, off + 4 * G, 0, CPOL_SC1)) : 0.f;
-                cm[(m * MB + kk) * 16 + h] = mv;
-                cl[(m * MB + kk) * 16 + h] = lv;
+                cm[kk * 16 + h] = mv;
+                cl[kk * 16 + h] = lv;
             }
             __syncthreads();
 #pragma unroll
@@ -722,10 +721,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 if (ch * NT >= n4) break;
                 const int f = ch * NT + threadIdx.x;
                 if (f < n4) {
-                    const int m = 4 * f >= GH ? 1 : 0;
-                    const int h = (4 * f - m * GH) / HD;
-                    const float *mk = cm + m * MB * 16 + h;
-                    const float *lk = cl + m * MB * 16 + h;
+                    const int h = (4 * f) / HD;
+                    const float *mk = cm + h;
+                    const float *lk = cl + h;
                     float M = Ma[ch];
 #pragma unroll
                     for (int kk = 0; kk < MB; ++kk) M = fmaxf(M, mk[kk * 16]);
@@ -750,16 +748,15 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             if (ch * NT >= n4) break;
             const int f = ch * NT + threadIdx.x;
             if (f < n4) {
-                const int m = 4 * f >= GH ? 1 : 0;
-                const int h = (4 * f - m * GH) / HD;
-                const int d = 4 * f - m * GH - h * HD;
+                const int h = (4 * f) / HD;
+                const int d = 4 * f - h * HD;
                 const float L = La[ch];
-                const int64_t oi = out_index(bgs[m], h);
+                const int64_t oi = out_index(bg, h);
                 *(f32x4 *)(a.out + oi * HD + d) = L > 0.f ? Oa[ch] * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
                 if (d == 0 && a.lse) a.lse[oi] = L > 0.f ? (Ma[ch] + log2f(L)) * LN2 : -INFINITY;
             }
         }
-        if (threadIdx.x < nm) reset_dev(&cnt[bgs[threadIdx.x] * CNT_STRIDE]);
+        if (threadIdx.x == 0) reset_dev(&cnt[bg * CNT_STRIDE]);
     };
 
     // ---- the (b, g) segments of this workgroup's range -----------------------
@@ -839,8 +836,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
             }
             __syncthreads();
             if (lds_flag[0]) {
-                const int one_bg = bg_first;
-                merge(1, &one_bg);
+                merge(bg_first);
                 __syncthreads();
             }
         } else if (bg == bg_last && pub_last) {
@@ -876,7 +872,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
         lds_flag[1] = arrive_dev(&cnt[bg_last * CNT_STRIDE]) == np - 1;
     }
     __syncthreads();
-    if (lds_flag[1]) merge(1, &bg_last);
+    if (lds_flag[1]) merge(bg_last);
 }
 
 // ---------------------------------------------------------------------------
