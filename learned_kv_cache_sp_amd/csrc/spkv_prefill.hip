@@ -513,8 +513,24 @@ prefill_bf16_kernel(PrefillArgs a) {
     auto soft_bias = [&](float u) -> float {
         return -a.soft_cs / (1.f + __builtin_amdgcn_exp2f((u - a.soft_tau) * a.soft_k1));
     };
+    // Issue priority: a wave in a matrix-core phase of a block (the scores,
+    // the value products) runs at priority 1, in its exponential / mask
+    // phases at 0, so that of the two waves of a SIMD the one with matrix
+    // work gets the issue slots (soft mode, with more vector work per block:
+    // 2.7 % faster; the plain mode unchanged).
+    auto prio_hi = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto prio_lo = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto compute_block = [&](const char *kb, const char *vb, const int *pb_pos, const float *pb_u, int kind) {
         f32x4 sc[2][PF_PT][2];
+        prio_hi();
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             bf16x8 ka[2][HD / 32];
@@ -537,6 +553,7 @@ prefill_bf16_kernel(PrefillArgs a) {
                         sc[hh][ptl][tt] =
                             __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][cc], qr[ptl][cc], sc[hh][ptl][tt], 0, 0, 0);
         }
+        prio_lo();
         // soft mode: the mask of Eq. (6) on cached keys (kinds 0 and 1).
         // Lane l forms the added score of key l once and parks it in the
         // wave's LDS row (LDS operations of one wave complete in order);
@@ -626,7 +643,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         };
         bf16x8 pb0[PF_PT], pb1[PF_PT];
         exp_half(0, pb0);
-        __builtin_amdgcn_sched_barrier(0);
+        prio_hi();
         // the first half's value products with the second half's
         // exponentials between them (VALU work under the MFMAs)
         pv_half(0, pb0);
@@ -639,6 +656,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         pv_half(1, pb1);
+        prio_lo();
     };
 
     // ---- phase 1: whole cached blocks, two per barrier ----------------------
